@@ -1,0 +1,400 @@
+"""CPU oracle for low-bit KV-cache compression and decode attention.
+
+TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import this module. The product path
+(kv_cache_compression_kvq_amd and its HIP library) never imports, calls or
+links it, and this module imports nothing from the product path.
+
+A plain, slow, readable numpy implementation of what the compressed-cache
+decode path computes:
+
+* quantization parameters in IEEE fp32 (numpy float32 arithmetic, round to
+  nearest even), codes rounded half-to-even and clamped to [0, 2^b - 1];
+* scale and zero-point stored in fp16;
+* OTT outlier-token tracing with the pool replaced by the group mean;
+* attention in fp64 on values dequantized from the stored fp16 scale/zero;
+* H2O accumulated-attention increments and heavy-hitter selection.
+
+Page citations name the page title and the section they come from:
+
+[MiniKV]  "MiniKV: Pushing the Limits of LLM Inference via 2-Bit
+          Layer-Discriminative KV Cache" (arXiv 2411.18077)
+[OTT]     "Accurate KV Cache Quantization with Outlier Tokens Tracing"
+          (papercache.org summary of the ACL 2025 paper)
+[H2O]     "H2O: Heavy-Hitter Oracle for Efficient Generative Inference of
+          Large Language Models"
+[POFE]    "KV cache quantization and eviction: FP8, INT4, H2O and attention
+          sinks" (pofe.ai)
+
+Readings taken where the pages leave a step open (each is also listed with
+its reason in the design notes):
+
+R1  Codes use round-half-to-even. [OTT] "Background" prints a floor, while
+    [POFE] "Minimal implementation" rounds; rounding is what gives the
+    |x - x_hat| <= q/2 bound.
+R2  The range is clamped below at 1e-8 before dividing ([POFE] "Minimal
+    implementation"); codes are computed from the fp32 step q, dequantization
+    uses the stored fp16 scale ([MiniKV] section 4.4: zero-point and scale are
+    kept in FP16).
+R3  One group size G for both axes: keys per channel over G tokens, values per
+    token over G channels ([POFE] "FP8, KIVI and KVQuant": groups of 32 on both
+    axes; [MiniKV] section 5.1: one group size for token- and channel-wise).
+R4  Residual rule: after T tokens, n_q = floor((T - R)/G)*G tokens are
+    quantized, the rest stay fp16 ([POFE] "Minimal implementation"); keys and
+    values are compressed together ([OTT] "Experimental setup").
+R5  Outlier score S_i is the exact L1 norm of the token's fp16 key ([OTT]
+    "Method details" and appendix E); ties in the pool competition go to the
+    older (smaller index) token.
+R6  A token admitted to the pool has its K and V rows replaced, inside the
+    group being quantized, by the per-channel mean of all G rows of that group
+    (outliers included), computed exactly and rounded once to fp16 ([OTT]
+    "Method details": replaced by the mean of all tokens).
+R7  Pool members displaced by better candidates move to an extra pool of
+    capacity E (32 on the page); when an admission needs a displacement and
+    the extra pool is full, tracing stops for good and the rest of that group
+    is quantized as is ([OTT] "Method details" and "Experimental setup").
+R8  Every cached token counts exactly once in attention: pool and extra-pool
+    tokens use their original fp16 K/V and their quantized slots are
+    skipped; tokens at index >= n_q use the fp16 residual rows ([OTT]
+    "Method details", decoding stage; [MiniKV] Algorithm 1, decoding).
+R9  Softmax scale 1/sqrt(d), d = head_dim ([MiniKV] section 2, Eq. 1).
+R10 The H2O score increment is the normalized softmax probability summed over
+    the query heads that share one KV head ([POFE] "Heavy hitters" and
+    "Minimal implementation"; [H2O] accumulated attention).
+R11 Heavy-hitter selection keeps the k highest scores in [0, T - w) ordered by
+    (score descending, index descending) plus the w most recent tokens, and
+    returns ascending indices. Index-descending tie order is what repeated
+    first-occurrence argmin eviction leaves behind ([POFE] "Minimal
+    implementation"; [MiniKV] Algorithm 1, heavy-hitter selection).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+RANGE_FLOOR = np.float32(1e-8)
+
+
+# --------------------------------------------------------------------------
+# Quantizer ([OTT] "Background": uniform / group quantization, step
+# q = (X_max - X_min)/(2^b - 1); [POFE] "The quantiser and why the grouping
+# axis matters" and "Minimal implementation").
+# --------------------------------------------------------------------------
+
+def minmax_quantize(x16: np.ndarray, axis: int, bits: int):
+    """Asymmetric min-max quantization of fp16 data along ``axis``.
+
+    Returns (codes uint8, scale fp16, zero fp16, q fp32). ``scale``, ``zero``
+    and ``q`` keep ``axis`` as a length-1 dimension.
+
+    The step is q = fl32(fl32(max(fl32(mx - mn), 1e-8)) / (2^b - 1)); the code
+    is clamp(rint(fl32(fl32(x - mn) / q)), 0, 2^b - 1) with rint rounding half
+    to even (R1, R2). The zero-point is the group minimum, exact in fp16.
+    """
+    x = np.asarray(x16, dtype=np.float16).astype(np.float32)
+    levels = np.float32(2 ** bits - 1)
+    mn = x.min(axis=axis, keepdims=True)
+    mx = x.max(axis=axis, keepdims=True)
+    rng = np.maximum(mx - mn, RANGE_FLOOR)
+    q = rng / levels
+    t = (x - mn) / q
+    codes = np.clip(np.rint(t), np.float32(0), levels).astype(np.uint8)
+    return codes, q.astype(np.float16), mn.astype(np.float16), q
+
+
+def quantize_key_group(k16: np.ndarray, bits: int):
+    """Keys of one group [G][d]: one (scale, zero) per channel over the G tokens.
+
+    Returns codes [G][d], scale [d], zero [d] (fp16).
+    """
+    codes, s, z, _ = minmax_quantize(k16, axis=0, bits=bits)
+    return codes, s[0], z[0]
+
+
+def quantize_value_rows(v16: np.ndarray, bits: int, gv: int):
+    """Values [n][d]: one (scale, zero) per token for each run of gv channels.
+
+    Returns codes [n][d], scale [n][d/gv], zero [n][d/gv] (fp16).
+    """
+    n, d = v16.shape
+    g = np.asarray(v16).reshape(n, d // gv, gv)
+    codes, s, z, _ = minmax_quantize(g, axis=2, bits=bits)
+    return codes.reshape(n, d), s[:, :, 0], z[:, :, 0]
+
+
+def dequantize(codes: np.ndarray, scale16: np.ndarray, zero16: np.ndarray) -> np.ndarray:
+    """x_hat = code * scale + zero in fp64 from the stored fp16 parameters (R2)."""
+    return codes.astype(np.float64) * scale16.astype(np.float64) + zero16.astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Packing ([MiniKV] section 4.4: bit shifting packs 16 INT2 values into one
+# INT32). Canonical order: within a token row, channel c goes to word
+# c // (32/b) at bit offset b * (c % (32/b)), least significant first.
+# --------------------------------------------------------------------------
+
+def pack_rows(codes: np.ndarray, bits: int) -> np.ndarray:
+    n, d = codes.shape
+    per = 32 // bits
+    words = np.zeros((n, d // per), dtype=np.uint64)
+    for i in range(per):
+        words |= codes[:, i::per].astype(np.uint64) << np.uint64(bits * i)
+    return words.astype(np.uint32)
+
+
+def unpack_rows(words: np.ndarray, bits: int, d: int) -> np.ndarray:
+    n = words.shape[0]
+    per = 32 // bits
+    out = np.zeros((n, d), dtype=np.uint8)
+    mask = (1 << bits) - 1
+    w = words.astype(np.uint64)
+    for i in range(per):
+        out[:, i::per] = ((w >> np.uint64(bits * i)) & np.uint64(mask)).astype(np.uint8)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Residual window (R4).
+# --------------------------------------------------------------------------
+
+def n_quantized(T: int, R: int, G: int) -> int:
+    """Tokens held quantized after T appends: max(0, floor((T - R)/G) * G)."""
+    return max(0, (T - R) // G * G)
+
+
+# --------------------------------------------------------------------------
+# OTT outlier-token tracing ([OTT] "Method details", appendix E).
+# --------------------------------------------------------------------------
+
+def key_l1_score(k16: np.ndarray) -> np.ndarray:
+    """S_i = sum_c |K_{i,c}|, exact.
+
+    fp16 magnitudes are integer multiples of 2^-24 below 2^16, so every
+    partial sum of at most 128 of them is a multiple of 2^-24 below 2^23 and
+    fits the 53-bit fp64 significand: the fp64 sum has no rounding.
+    """
+    return np.abs(np.asarray(k16, dtype=np.float16).astype(np.float64)).sum(axis=-1)
+
+
+def group_mean_fp16(x16: np.ndarray) -> np.ndarray:
+    """Per-channel mean of the G rows of a group, rounded once to fp16 (R6).
+
+    The fp64 sum is exact (see key_l1_score), division by G (a power of two)
+    is exact, and numpy's float64 -> float16 conversion rounds to nearest
+    even directly from the double.
+    """
+    x = np.asarray(x16, dtype=np.float16).astype(np.float64)
+    return (x.sum(axis=0) / x.shape[0]).astype(np.float16)
+
+
+@dataclass
+class PoolMember:
+    score: float
+    idx: int
+    k: np.ndarray  # original fp16 key row
+    v: np.ndarray  # original fp16 value row
+
+
+@dataclass
+class OutlierTracer:
+    """Outlier pool of capacity N plus the extra pool of capacity E (R5-R7)."""
+    N: int
+    E: int
+    pool: list = field(default_factory=list)
+    evicted: list = field(default_factory=list)
+    frozen: bool = False
+
+    def compete(self, idx: np.ndarray, scores: np.ndarray, k16: np.ndarray, v16: np.ndarray):
+        """One quantization step for the G tokens of a group.
+
+        The group's tokens and the current pool are ranked together by
+        (score, index) ascending; the N best form the new pool
+        ([OTT] appendix E). Winners from the group are admitted in that order;
+        each admission into a full pool moves the pool's current worst member
+        to the extra pool. Returns the group positions admitted.
+        """
+        if self.N == 0 or self.frozen:
+            return []
+        cands = [(m.score, m.idx, -1) for m in self.pool]
+        cands += [(float(scores[i]), int(idx[i]), i) for i in range(len(idx))]
+        cands.sort(key=lambda c: (c[0], c[1]))
+        winners = [c[2] for c in cands[: self.N] if c[2] >= 0]
+        admitted = []
+        for i in winners:
+            if len(self.pool) == self.N:
+                worst = max(self.pool, key=lambda m: (m.score, m.idx))
+                if len(self.evicted) == self.E:
+                    self.frozen = True
+                    break
+                self.pool.remove(worst)
+                self.evicted.append(worst)
+            self.pool.append(PoolMember(float(scores[i]), int(idx[i]),
+                                        k16[i].copy(), v16[i].copy()))
+            admitted.append(i)
+        return admitted
+
+
+# --------------------------------------------------------------------------
+# One (batch, KV head) unit of the compressed cache.
+# --------------------------------------------------------------------------
+
+@dataclass
+class CacheParams:
+    bits: int
+    group: int
+    residual: int
+    pool: int = 0
+    evict_cap: int = 32
+    head_dim: int = 128
+
+    @property
+    def gv(self) -> int:
+        return min(self.group, self.head_dim)
+
+
+class UnitCache:
+    """Keys/values of one unit: quantized groups, fp16 residual window, pools."""
+
+    def __init__(self, p: CacheParams):
+        self.p = p
+        d = p.head_dim
+        self.k16 = np.zeros((0, d), dtype=np.float16)  # every appended row, original
+        self.v16 = np.zeros((0, d), dtype=np.float16)
+        self.n_q = 0
+        self.kcodes = np.zeros((0, d), dtype=np.uint8)
+        self.kscale = np.zeros((0, d), dtype=np.float16)  # per group
+        self.kzero = np.zeros((0, d), dtype=np.float16)
+        self.vcodes = np.zeros((0, d), dtype=np.uint8)
+        self.vscale = np.zeros((0, d // p.gv), dtype=np.float16)  # per token
+        self.vzero = np.zeros((0, d // p.gv), dtype=np.float16)
+        self.replaced = np.zeros(0, dtype=bool)  # token was admitted to the pool
+        self.tracer = OutlierTracer(p.pool, p.evict_cap)
+
+    @property
+    def T(self) -> int:
+        return self.k16.shape[0]
+
+    def append(self, k16: np.ndarray, v16: np.ndarray) -> None:
+        """Append fp16 rows; quantize every group that leaves the residual window."""
+        self.k16 = np.concatenate([self.k16, np.asarray(k16, dtype=np.float16)])
+        self.v16 = np.concatenate([self.v16, np.asarray(v16, dtype=np.float16)])
+        G = self.p.group
+        while self.n_q < n_quantized(self.T, self.p.residual, G):
+            self._quantize_group(self.n_q)
+            self.n_q += G
+
+    def _quantize_group(self, t0: int) -> None:
+        G = self.p.group
+        kg = self.k16[t0:t0 + G].copy()
+        vg = self.v16[t0:t0 + G].copy()
+        idx = np.arange(t0, t0 + G)
+        admitted = self.tracer.compete(idx, key_l1_score(kg), kg, vg)
+        replaced = np.zeros(G, dtype=bool)
+        if admitted:
+            mk, mv = group_mean_fp16(kg), group_mean_fp16(vg)
+            for i in admitted:
+                kg[i], vg[i] = mk, mv
+                replaced[i] = True
+        kc, ks, kz = quantize_key_group(kg, self.p.bits)
+        vc, vs, vz = quantize_value_rows(vg, self.p.bits, self.p.gv)
+        self.kcodes = np.concatenate([self.kcodes, kc])
+        self.kscale = np.concatenate([self.kscale, ks[None]])
+        self.kzero = np.concatenate([self.kzero, kz[None]])
+        self.vcodes = np.concatenate([self.vcodes, vc])
+        self.vscale = np.concatenate([self.vscale, vs])
+        self.vzero = np.concatenate([self.vzero, vz])
+        self.replaced = np.concatenate([self.replaced, replaced])
+
+    def dequantized_kv(self):
+        """K_hat, V_hat [T][d] in fp64, each cached token exactly once (R8)."""
+        G, gv, d = self.p.group, self.p.gv, self.p.head_dim
+        n_q = self.n_q
+        K = self.k16.astype(np.float64)  # residual rows stay as stored (fp16)
+        V = self.v16.astype(np.float64)
+        if n_q:
+            ks = np.repeat(self.kscale, G, axis=0)
+            kz = np.repeat(self.kzero, G, axis=0)
+            K[:n_q] = dequantize(self.kcodes, ks, kz)
+            vs = np.repeat(self.vscale, gv, axis=1)
+            vz = np.repeat(self.vzero, gv, axis=1)
+            V[:n_q] = dequantize(self.vcodes, vs, vz)
+        for m in self.tracer.pool + self.tracer.evicted:
+            K[m.idx] = m.k.astype(np.float64)
+            V[m.idx] = m.v.astype(np.float64)
+        return K, V
+
+    def pool_indices(self):
+        return sorted(m.idx for m in self.tracer.pool)
+
+    def evicted_indices(self):
+        return [m.idx for m in self.tracer.evicted]
+
+
+# --------------------------------------------------------------------------
+# Decode attention ([MiniKV] section 2, Eq. 1 and Algorithm 1 decoding;
+# [OTT] "Method details", decoding stage) and H2O scores.
+# --------------------------------------------------------------------------
+
+def unit_attention(K: np.ndarray, V: np.ndarray, q16: np.ndarray):
+    """Attention of the r query heads q16 [r][d] over one unit's K, V [T][d] (fp64).
+
+    Returns out [r][d] and the normalized probabilities p [r][T]:
+    s = K q / sqrt(d); p = exp(s - max s) / sum; out = p V.
+    """
+    d = K.shape[1]
+    q = np.asarray(q16, dtype=np.float16).astype(np.float64)
+    s = (q @ K.T) / math.sqrt(d)
+    s -= s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    p = e / e.sum(axis=1, keepdims=True)
+    return p @ V, p
+
+
+def h2o_increment(p: np.ndarray) -> np.ndarray:
+    """Score increment for one KV head: sum over its query heads of p [r][T] (R10)."""
+    return p.sum(axis=0)
+
+
+class CacheOracle:
+    """All units of a [batch][n_kv_heads] cache, or a chosen subset of them."""
+
+    def __init__(self, p: CacheParams, batch: int, n_kv_heads: int, units=None):
+        self.p = p
+        self.batch, self.n_kv_heads = batch, n_kv_heads
+        self.unit_ids = list(units) if units is not None else [
+            (b, h) for b in range(batch) for h in range(n_kv_heads)]
+        self.units = {u: UnitCache(p) for u in self.unit_ids}
+
+    def append_unit(self, u, k16: np.ndarray, v16: np.ndarray) -> None:
+        self.units[u].append(k16, v16)
+
+    def decode_unit(self, u, q16_group: np.ndarray):
+        """out [r][d] and H2O increment [T] for unit u given its r query heads."""
+        K, V = self.units[u].dequantized_kv()
+        out, p = unit_attention(K, V, q16_group)
+        return out, h2o_increment(p), p
+
+
+# --------------------------------------------------------------------------
+# Heavy-hitter selection ([H2O] accumulated attention; [POFE] "Heavy hitters"
+# and "Minimal implementation"; [MiniKV] Algorithm 1) (R11).
+# --------------------------------------------------------------------------
+
+def topk_keep(scores: np.ndarray, k: int, w: int) -> np.ndarray:
+    """Indices kept per row: top-k of [0, T-w) by (score desc, index desc) + [T-w, T).
+
+    ``scores`` is fp32 [rows][T]; returns int32 [rows][k+w], ascending.
+    """
+    scores = np.asarray(scores, dtype=np.float32)
+    rows, T = scores.shape
+    out = np.empty((rows, k + w), dtype=np.int32)
+    n = T - w
+    idx = np.arange(n)
+    for r in range(rows):
+        s = scores[r, :n].astype(np.float64)
+        order = np.lexsort((-idx, -s))  # primary: score desc, then index desc
+        keep = np.sort(order[:k])
+        out[r] = np.concatenate([keep, np.arange(n, T)]).astype(np.int32)
+    return out

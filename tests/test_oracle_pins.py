@@ -1,0 +1,571 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test checks the oracle against a value printed on the pages, a closed
+form, an invariant, a special case that reduces to a textbook result, or a
+brute force on tiny inputs written independently here (Python Fractions and
+plain loops). Citations name the page title and section.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import kvq_oracle as O
+from tests.fp16ref import half_to_fraction, round_to_half, round_to_half_bits
+
+F32 = np.float32
+
+
+def fr32(x) -> Fraction:
+    return Fraction(float(np.float32(x)))
+
+
+# ---------------------------------------------------------------------------
+# Quantizer ("Accurate KV Cache Quantization with Outlier Tokens Tracing",
+# Background: uniform quantization with step q = (X_max - X_min)/(2^b - 1);
+# "KV cache quantization and eviction", Minimal implementation).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,mn,q", [(2, -1.5, 0.5), (4, -2.0, 0.25), (2, 3.0, 2.0)])
+def test_on_grid_values_are_exact(bits, mn, q):
+    """Values mn + c*q with exactly representable q map to code c, zero error."""
+    L = 2 ** bits - 1
+    codes = np.arange(L + 1)
+    x = (mn + codes * q).astype(np.float16)
+    x = np.concatenate([x, x[::-1]])[:, None]
+    c, s, z, qq = O.minmax_quantize(x, axis=0, bits=bits)
+    assert float(qq[0, 0]) == q and float(s[0, 0]) == q and float(z[0, 0]) == mn
+    assert np.array_equal(c[:, 0], np.concatenate([codes, codes[::-1]]))
+    assert np.array_equal(O.dequantize(c, s, z), x.astype(np.float64))
+
+
+def test_half_points_round_half_to_even():
+    """b=2, range 3 -> q = 1; x = 0.5, 1.5, 2.5 give codes 0, 2, 2.
+
+    Floor would give 0, 1, 2 and round-half-up 1, 2, 3.
+    """
+    x = np.array([0, 3, 0.5, 1.5, 2.5], dtype=np.float16)[:, None]
+    c, _, _, q = O.minmax_quantize(x, axis=0, bits=2)
+    assert float(q[0, 0]) == 1.0
+    assert c[:, 0].tolist() == [0, 3, 0, 2, 2]
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_group_min_is_exact_and_max_is_top_code(bits):
+    rng = np.random.default_rng(1)
+    for _ in range(50):
+        x = (rng.standard_normal((32, 16)) * rng.uniform(0.01, 30)).astype(np.float16)
+        c, s, z, _ = O.minmax_quantize(x, axis=0, bits=bits)
+        imin, imax = x.argmin(axis=0), x.argmax(axis=0)
+        cols = np.arange(16)
+        assert np.all(c[imin, cols] == 0)
+        assert np.all(c[imax, cols] == 2 ** bits - 1)
+        xh = O.dequantize(c, s, z)
+        assert np.array_equal(xh[imin, cols], x[imin, cols].astype(np.float64))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_error_bound_half_step(bits):
+    """|x - (c*q + mn)| <= q/2 in exact arithmetic, up to the fp32 rounding of (x-mn)/q.
+
+    Checked with Fractions on every element; q is the fp32 step as a rational.
+    The stored fp16 scale adds at most c*|s16 - q|.
+    """
+    rng = np.random.default_rng(2)
+    L = 2 ** bits - 1
+    for trial in range(40):
+        x = rng.standard_normal(32) * rng.uniform(0.001, 50)
+        if trial % 4 == 0:
+            x[rng.integers(32)] *= 40  # one far outlier
+        x16 = x.astype(np.float16)[:, None]
+        c, s, z, q = O.minmax_quantize(x16, axis=0, bits=bits)
+        Q = fr32(q[0, 0])
+        S = half_to_fraction(s[0, 0])
+        mn = half_to_fraction(z[0, 0])
+        for i in range(32):
+            xi = half_to_fraction(x16[i, 0])
+            ci = int(c[i, 0])
+            assert 0 <= ci <= L
+            slack = Fraction(1, 2 ** 22) * (abs(xi - mn) + Q)
+            assert abs(xi - (ci * Q + mn)) <= Q / 2 + slack
+            assert abs(xi - (ci * S + mn)) <= Q / 2 + slack + ci * abs(S - Q)
+
+
+def test_constant_group_reconstructs_exactly():
+    """mx == mn: the range is clamped to 1e-8, every code is 0 and x_hat == x."""
+    for v in [0.0, -3.25, 1e-4, 65504.0]:
+        x = np.full((32, 4), v, dtype=np.float16)
+        c, s, z, q = O.minmax_quantize(x, axis=0, bits=2)
+        assert np.all(c == 0)
+        assert float(q[0, 0]) == float(np.float32(1e-8) / np.float32(3))
+        assert np.array_equal(O.dequantize(c, s, z), x.astype(np.float64))
+
+
+def test_quantizer_follows_fp32_steps_exactly():
+    """Each code equals the hand-derived fp32 step computation done with Fractions.
+
+    rint(fl32(fl32(x - mn)/q)) with q = fl32(fl32(mx - mn)/3); fl32 is an
+    independent round-to-nearest-even to binary32 here.
+    """
+    def fl32(fr: Fraction) -> Fraction:
+        if fr == 0:
+            return fr
+        a = abs(fr)
+        e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+        while Fraction(2) ** e > a:
+            e -= 1
+        while Fraction(2) ** (e + 1) <= a:
+            e += 1
+        ulp = Fraction(2) ** (e - 23)
+        n, r = divmod(a, ulp)
+        if r * 2 > ulp or (r * 2 == ulp and n % 2 == 1):
+            n += 1
+        return (n * ulp) * (1 if fr > 0 else -1)
+
+    def rint(fr: Fraction) -> int:
+        n = math.floor(fr)
+        r = fr - n
+        if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+            n += 1
+        return n
+
+    rng = np.random.default_rng(3)
+    for _ in range(30):
+        x16 = (rng.standard_normal(16) * rng.uniform(0.01, 100)).astype(np.float16)
+        c, s, z, q = O.minmax_quantize(x16[:, None], axis=0, bits=2)
+        xs = [half_to_fraction(v) for v in x16]
+        mn, mx = min(xs), max(xs)
+        Q = fl32(fl32(mx - mn) / 3)
+        assert fr32(q[0, 0]) == Q
+        want = [min(3, max(0, rint(fl32(fl32(xi - mn) / Q)))) for xi in xs]
+        assert c[:, 0].tolist() == want
+        assert int(np.asarray(s[0, 0]).view(np.uint16)) == round_to_half_bits(Q)
+
+
+def test_key_and_value_grouping_axes():
+    """Keys: one (scale, zero) per channel over G tokens; values: per token per run of G channels."""
+    rng = np.random.default_rng(4)
+    k = (rng.standard_normal((32, 128)) * 3).astype(np.float16)
+    kc, ks, kz = O.quantize_key_group(k, 2)
+    assert ks.shape == (128,) and kz.shape == (128,)
+    assert np.array_equal(kz, k.min(axis=0))
+    v = rng.standard_normal((5, 128)).astype(np.float16)
+    vc, vs, vz = O.quantize_value_rows(v, 2, 32)
+    assert vs.shape == (5, 4)
+    assert np.array_equal(vz, v.reshape(5, 4, 32).min(axis=2))
+    # a channel-group's codes depend only on that group's 32 values
+    v2 = v.copy()
+    v2[:, 32:] = 7
+    vc2, _, _ = O.quantize_value_rows(v2, 2, 32)
+    assert np.array_equal(vc[:, :32], vc2[:, :32])
+
+
+# ---------------------------------------------------------------------------
+# Packing (MiniKV, section 4.4: 16 INT2 values shifted into one INT32).
+# ---------------------------------------------------------------------------
+
+def test_pack_bit_positions():
+    c2 = np.array([[i % 4 for i in range(16)] * 8], dtype=np.uint8)   # 00,01,10,11 from the LSB
+    assert O.pack_rows(c2, 2).tolist() == [[0xE4E4E4E4] * 8]
+    c4 = np.array([list(range(8)) * 16], dtype=np.uint8)
+    assert O.pack_rows(c4, 4).tolist() == [[0x76543210] * 16]
+    one = np.zeros((1, 128), dtype=np.uint8)
+    one[0, 17] = 3                        # channel 17 -> word 1, bits 2..3
+    w = O.pack_rows(one, 2)
+    assert w[0, 1] == 0b1100 and w.sum() == 0b1100
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_pack_round_trip(bits):
+    rng = np.random.default_rng(5)
+    c = rng.integers(0, 2 ** bits, size=(37, 128)).astype(np.uint8)
+    w = O.pack_rows(c, bits)
+    assert w.shape == (37, 128 * bits // 32)
+    assert np.array_equal(O.unpack_rows(w, bits, 128), c)
+
+
+# ---------------------------------------------------------------------------
+# Byte model and stored layout (page worked values).
+# ---------------------------------------------------------------------------
+
+def test_bits_per_element_matches_pages(golden):
+    from kv_cache_compression_kvq_amd import bytes_model as BM
+    for case in golden["bits_per_element"]["cases"]:
+        assert BM.bits_per_element(case["bits"], case["group"]) == case["bits_per_element"]
+    g = golden["group_bytes"]
+    assert BM.group_bytes(g["bits"], g["group"]) == g["bytes"]
+
+
+def test_llama3_cache_sizes_match_pages(golden):
+    from kv_cache_compression_kvq_amd import bytes_model as BM
+    c = golden["llama3_8b_cache"]
+    per_tok = {k: BM.kv_bytes_per_token(c["layers"], c["n_kv_heads"], c["head_dim"], b)
+               for k, b in [("bf16", 2), ("fp8", 1),
+                            ("int4_g32", BM.bits_per_element(4, 32) / 8),
+                            ("int2_g32", BM.bits_per_element(2, 32) / 8)]}
+    for k, gb in c["GB_128k"].items():
+        assert round(per_tok[k] * c["tokens_128k"] / 1e9, 1) == gb
+    full = per_tok["bf16"] * c["tokens_32k"]
+    assert round(full / 1e9, 1) == c["GB_32k_full"]
+    assert round(full * c["keep_fraction"] / 1e9, 2) == c["GB_32k_kept"]
+    assert round(per_tok["bf16"] * c["fixed_entries"] / 1e6) == c["MB_fixed_entries"]
+    t = golden["kvtc_table1"]
+    assert BM.kv_bytes_per_token(t["layers"], t["n_kv_heads"], t["head_dim"], 2) * t["tokens"] \
+        == t["MiB"] * 2 ** 20
+
+
+def test_minikv_compression_numbers(golden):
+    from kv_cache_compression_kvq_amd import bytes_model as BM
+    m = golden["minikv_compression"]
+    per_tok16 = 2 * m["layers"] * m["hidden"] * 2
+    full = per_tok16 * (m["prompt"] + m["gen"])
+    kept = m["prompt"] * m["budget"] + m["gen"]
+    mini = 2 * m["layers"] * m["hidden"] * kept * BM.bits_per_element(m["bits"], m["group"]) / 8
+    assert round(full / 1e9, 1) == m["GB_full"]
+    # the page prints 0.33 GB (335.5 MB truncated) and an 86 % reduction
+    assert abs(mini / 1e9 - m["GB_minikv"]) < 0.01
+    assert round(100 * (1 - mini / full)) == 86
+
+
+@pytest.mark.parametrize("bits,G", [(2, 32), (4, 32), (2, 128), (4, 16)])
+def test_oracle_storage_is_b_plus_32_over_g_bits(bits, G):
+    """Packed codes + fp16 scale/zero held by the oracle cost b + 32/G bits per element."""
+    rng = np.random.default_rng(6)
+    u = O.UnitCache(O.CacheParams(bits=bits, group=G, residual=0))
+    k = rng.standard_normal((4 * G, 128)).astype(np.float16)
+    u.append(k, k)
+    n = u.n_q * 128
+    kbytes = O.pack_rows(u.kcodes, bits).nbytes + u.kscale.nbytes + u.kzero.nbytes
+    vbytes = O.pack_rows(u.vcodes, bits).nbytes + u.vscale.nbytes + u.vzero.nbytes
+    assert 8 * kbytes / n == bits + 32 / G
+    assert 8 * vbytes / n == bits + 32 / G
+
+
+# ---------------------------------------------------------------------------
+# Residual window ("KV cache quantization and eviction", Minimal implementation,
+# kivi_compress split; MiniKV Algorithm 1 streaming buffer).
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("R,G", [(0, 16), (32, 32), (128, 32), (5, 16), (128, 128)])
+def test_residual_rule(R, G):
+    for T in range(0, 3 * (R + G) + 7):
+        nq = O.n_quantized(T, R, G)
+        assert nq % G == 0 and nq >= 0
+        if T >= R:
+            assert R <= T - nq < R + G
+        else:
+            assert nq == 0
+    # incremental simulation: quantize the oldest G whenever R+G rows are fp16
+    fp16, nq = 0, 0
+    for T in range(1, 400):
+        fp16 += 1
+        while fp16 >= R + G:
+            fp16 -= G
+            nq += G
+        assert nq == O.n_quantized(T, R, G)
+
+
+def test_incremental_and_bulk_appends_agree():
+    rng = np.random.default_rng(7)
+    p = O.CacheParams(bits=2, group=16, residual=8, pool=2, evict_cap=4)
+    k = rng.standard_normal((200, 128)).astype(np.float16)
+    v = rng.standard_normal((200, 128)).astype(np.float16)
+    a, b = O.UnitCache(p), O.UnitCache(p)
+    a.append(k, v)
+    for i in range(0, 200, 7):
+        b.append(k[i:i + 7], v[i:i + 7])
+    for f in ["kcodes", "kscale", "kzero", "vcodes", "vscale", "vzero", "replaced"]:
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f
+    assert a.pool_indices() == b.pool_indices() and a.evicted_indices() == b.evicted_indices()
+
+
+# ---------------------------------------------------------------------------
+# OTT: score, mean replacement, pool competition ("Accurate KV Cache
+# Quantization with Outlier Tokens Tracing", Method details and appendix E).
+# ---------------------------------------------------------------------------
+
+def test_l1_score_is_exact():
+    rng = np.random.default_rng(8)
+    specials = np.array([65504, -65504, 6e-8, -6e-8, 1e-5, 2 ** -14, 0.0], dtype=np.float16)
+    for _ in range(20):
+        x = (rng.standard_normal(128) * rng.choice([1e-6, 1e-3, 1, 300, 20000])).astype(np.float16)
+        x[:7] = specials
+        want = sum(abs(half_to_fraction(v)) for v in x)
+        assert Fraction(float(O.key_l1_score(x))) == want
+
+
+def test_group_mean_rounds_once_to_fp16():
+    """Mean of G rows: exact value rounded to nearest-even fp16, checked against Fractions.
+
+    Includes means that sit just off an fp16 half-way point by less than an
+    fp32 ulp, where rounding through fp32 first would give a different half.
+    """
+    rng = np.random.default_rng(9)
+    for G in [16, 32, 128]:
+        x = (rng.standard_normal((G, 64)) * rng.uniform(0.001, 500)).astype(np.float16)
+        m = O.group_mean_fp16(x)
+        for c in range(64):
+            exact = sum(half_to_fraction(v) for v in x[:, c]) / G
+            assert m[c].view(np.uint16) == round_to_half_bits(exact)
+    # constructed: (1 + 2^-11) + 2^-24 * 2^-? ... exact mean = 1 + 2^-11 + 2^-29
+    G = 32
+    col = np.full(G, 1.0, dtype=np.float16)
+    col[0] = np.float16(1.0 + 2 ** -10)     # contributes 2^-10 / 32
+    col[1] = np.float16(1.0 + 2 ** -10)
+    # mean = 1 + 2^-10 * 2/32 = 1 + 2^-14: far below half an fp16 ulp (2^-11)
+    assert O.group_mean_fp16(col[:, None])[0] == np.float16(1.0)
+    col = np.full(G, 1.0 + 2 ** -10, dtype=np.float16)
+    col[:16] = np.float16(1.0)
+    col[16] = np.float16(1.0 + 2 * 2 ** -10)
+    exact = sum(half_to_fraction(v) for v in col) / G      # 1 + 2^-11 + 2^-15: above half-way
+    assert O.group_mean_fp16(col[:, None])[0].view(np.uint16) == round_to_half_bits(exact)
+    assert O.group_mean_fp16(col[:, None])[0] == np.float16(1.0 + 2 ** -10)
+
+
+def _brute_pool(history, N):
+    """The N smallest (S, idx) among all tokens seen (appendix E, prefix form)."""
+    return sorted(sorted(history)[:N], key=lambda t: t[1])
+
+
+@pytest.mark.parametrize("N,G", [(1, 4), (3, 4), (3, 16), (5, 8)])
+def test_ott_pool_is_prefix_topN_while_not_frozen(N, G):
+    rng = np.random.default_rng(10 + N + G)
+    tr = O.OutlierTracer(N, E=10 ** 6)
+    history, admitted_total = [], 0
+    for g in range(30):
+        idx = np.arange(g * G, (g + 1) * G)
+        s = rng.integers(0, 40, size=G).astype(np.float64)  # many exact ties
+        k = np.zeros((G, 4), dtype=np.float16)
+        adm = tr.compete(idx, s, k, k)
+        admitted_total += len(adm)
+        history += [(float(s[i]), int(idx[i])) for i in range(G)]
+        want = _brute_pool(history, N)
+        got = sorted(((m.score, m.idx) for m in tr.pool), key=lambda t: t[1])
+        assert got == want
+        # admitted tokens are exactly this group's members of the new pool
+        assert sorted(int(idx[i]) for i in adm) == sorted(i for _, i in want if i >= g * G)
+        # everything ever admitted is in the pool or the extra pool
+        assert len(tr.evicted) == max(0, admitted_total - N)
+        ever = {m.idx for m in tr.pool} | {m.idx for m in tr.evicted}
+        assert len(ever) == admitted_total
+
+
+def test_ott_freeze_when_extra_pool_full():
+    """Descending norms: every group beats the pool, so the extra pool fills and tracing stops."""
+    N, E, G = 3, 5, 4
+    u = O.UnitCache(O.CacheParams(bits=2, group=G, residual=0, pool=N, evict_cap=E))
+    T = 12 * G
+    scale = np.linspace(10, 0.1, T).astype(np.float32)
+    rng = np.random.default_rng(11)
+    base = np.abs(rng.standard_normal(128)).astype(np.float32) + np.float32(0.5)
+    k = (base[None, :] * scale[:, None]).astype(np.float16)
+    S = O.key_l1_score(k)
+    assert np.all(np.diff(S) < 0)
+    u.append(k, k)
+    tr = u.tracer
+    assert tr.frozen and len(tr.evicted) == E and len(tr.pool) == N
+    # admissions: group 0 fills the pool (3), then each later admission evicts one;
+    # the (E+1)-th needed eviction freezes: total admitted = N + E.
+    assert int(u.replaced.sum()) == N + E
+    first_frozen_group = (N + E) // 3  # 3 admissions per group (top-3 of each group)
+    assert not u.replaced[(first_frozen_group + 1) * G:].any()
+    # the freezing group keeps the admissions made before the freeze
+    kept = u.replaced[first_frozen_group * G:(first_frozen_group + 1) * G]
+    assert kept.sum() == (N + E) - 3 * first_frozen_group
+
+
+def test_ott_mean_replacement_removes_outlier_from_range():
+    """A low-norm token is admitted; its quantized row is the group mean; the key step shrinks.
+
+    Appendix D: one token at eps in a channel otherwise in [mu - sigma, mu + sigma]
+    inflates q to ((mu + sigma) - eps)/(2^b - 1); with the token replaced by the
+    mean, q <= (max - min(min_others, mean))/(2^b - 1).
+    """
+    G, mu, sigma, eps = 32, 20.0, 2.0, 0.5
+    rng = np.random.default_rng(12)
+    k = rng.standard_normal((G, 128)).astype(np.float32)
+    k[:, 7] = rng.uniform(mu - sigma, mu + sigma, G)
+    k[5, :] *= 0.01
+    k[5, 7] = eps
+    k16 = k.astype(np.float16)
+    v16 = rng.standard_normal((G, 128)).astype(np.float16)
+    S = O.key_l1_score(k16)
+    assert S.argmin() == 5
+    # without tracing
+    u0 = O.UnitCache(O.CacheParams(bits=2, group=G, residual=0, pool=0))
+    u0.append(k16, v16)
+    q_no = fr32(np.float32(k16[:, 7].max()) - np.float32(k16[5, 7])) / 3
+    assert abs(half_to_fraction(u0.kscale[0, 7]) - q_no) <= q_no * Fraction(1, 1024)
+    # with tracing (N = 1)
+    u1 = O.UnitCache(O.CacheParams(bits=2, group=G, residual=0, pool=1, evict_cap=4))
+    u1.append(k16, v16)
+    assert u1.pool_indices() == [5] and u1.replaced.tolist() == [i == 5 for i in range(G)]
+    mean_k = O.group_mean_fp16(k16)
+    others = np.delete(k16[:, 7], 5).astype(np.float64)
+    lo = min(others.min(), float(mean_k[7]))
+    assert float(u1.kscale[0, 7]) <= (others.max() - lo) / 3 * (1 + 2 ** -10)
+    assert float(u1.kscale[0, 7]) < float(u0.kscale[0, 7]) / 4
+    # the quantized slot reconstructs the mean row within half a step per channel
+    kh, vh = u1.dequantized_kv()
+    assert np.array_equal(kh[5], k16[5].astype(np.float64))  # pool row used in attention
+    deq5 = O.dequantize(u1.kcodes[5], u1.kscale[0], u1.kzero[0])
+    assert np.all(np.abs(deq5 - mean_k.astype(np.float64)) <= u1.kscale[0].astype(np.float64) / 2 + 1e-3)
+    assert np.array_equal(u1.tracer.pool[0].v, v16[5])
+    # exact construction: row 5 of K and V replaced by the mean of all G original
+    # rows (outlier included), rounded once to fp16, then quantized as usual
+    def exact_mean(x16):
+        return np.array([round_to_half(sum(half_to_fraction(v) for v in x16[:, c]) / G)
+                         for c in range(x16.shape[1])], dtype=np.float16)
+    kr, vr = k16.copy(), v16.copy()
+    kr[5], vr[5] = exact_mean(k16), exact_mean(v16)
+    kc, ks, kz = O.quantize_key_group(kr, 2)
+    vc, vs, vz = O.quantize_value_rows(vr, 2, G)
+    assert np.array_equal(u1.kcodes, kc) and np.array_equal(u1.kscale[0], ks)
+    assert np.array_equal(u1.kzero[0], kz)
+    assert np.array_equal(u1.vcodes, vc) and np.array_equal(u1.vscale, vs)
+    assert np.array_equal(u1.vzero, vz)
+
+
+def test_ott_score_ties_prefer_older_token():
+    tr = O.OutlierTracer(1, 4)
+    k = np.zeros((4, 2), dtype=np.float16)
+    adm = tr.compete(np.arange(4), np.array([3.0, 1.0, 1.0, 2.0]), k, k)
+    assert adm == [1]
+    adm = tr.compete(np.arange(4, 8), np.array([1.0, 5.0, 5.0, 5.0]), k, k)
+    assert adm == [] and tr.pool[0].idx == 1
+
+
+# ---------------------------------------------------------------------------
+# Attention (MiniKV section 2, Eq. 1 and Algorithm 1, decoding; OTT decoding
+# stage) and H2O scores ("KV cache quantization and eviction", Heavy hitters).
+# ---------------------------------------------------------------------------
+
+def _brute_attention(K, V, q):
+    d = len(q)
+    s = [sum(q[c] * K[j][c] for c in range(d)) / math.sqrt(d) for j in range(len(K))]
+    m = max(s)
+    e = [math.exp(x - m) for x in s]
+    l = sum(e)
+    return [sum(e[j] / l * V[j][c] for j in range(len(K))) for c in range(d)], [x / l for x in e]
+
+
+def test_attention_matches_brute_force():
+    rng = np.random.default_rng(13)
+    K = rng.standard_normal((9, 16)) * 2
+    V = rng.standard_normal((9, 16))
+    q = rng.standard_normal((3, 16)).astype(np.float16)
+    out, p = O.unit_attention(K, V, q)
+    for h in range(3):
+        bo, bp = _brute_attention(K.tolist(), V.tolist(), q[h].astype(np.float64).tolist())
+        assert np.allclose(out[h], bo, rtol=1e-12, atol=1e-14)
+        assert np.allclose(p[h], bp, rtol=1e-12, atol=1e-15)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(14)
+    q = rng.standard_normal((2, 128)).astype(np.float16)
+    V = rng.standard_normal((1, 128))
+    out, p = O.unit_attention(rng.standard_normal((1, 128)), V, q)
+    assert np.array_equal(out, np.repeat(V, 2, axis=0)) and np.all(p == 1)
+    K = np.repeat(rng.standard_normal((1, 128)), 7, axis=0)
+    V = rng.standard_normal((7, 128))
+    out, _ = O.unit_attention(K, V, q)
+    assert np.allclose(out, V.mean(axis=0)[None], rtol=1e-13, atol=1e-15)
+
+
+def test_residual_covering_everything_is_plain_fp16_attention():
+    rng = np.random.default_rng(15)
+    p = O.CacheParams(bits=2, group=32, residual=64)
+    u = O.UnitCache(p)
+    k = rng.standard_normal((50, 128)).astype(np.float16)
+    v = rng.standard_normal((50, 128)).astype(np.float16)
+    u.append(k, v)
+    assert u.n_q == 0
+    K, V = u.dequantized_kv()
+    assert np.array_equal(K, k.astype(np.float64)) and np.array_equal(V, v.astype(np.float64))
+
+
+def test_partitioned_softmax_equals_concatenated():
+    """MiniKV Algorithm 1: softmax over [quantized ; residual] then
+    A_quant deq(V_q) + A_unquant R_V equals per-partition (max, sum, out) merged."""
+    rng = np.random.default_rng(16)
+    p = O.CacheParams(bits=2, group=16, residual=20)
+    u = O.UnitCache(p)
+    k = rng.standard_normal((100, 128)).astype(np.float16)
+    v = rng.standard_normal((100, 128)).astype(np.float16)
+    u.append(k, v)
+    K, V = u.dequantized_kv()
+    q = rng.standard_normal((1, 128)).astype(np.float16)
+    out, _ = O.unit_attention(K, V, q)
+    parts = []
+    for sl in [slice(0, u.n_q), slice(u.n_q, 100)]:
+        s = (q.astype(np.float64) @ K[sl].T)[0] / math.sqrt(128)
+        m = s.max()
+        e = np.exp(s - m)
+        parts.append((m, e.sum(), e @ V[sl]))
+    M = max(m for m, _, _ in parts)
+    Lsum = sum(l * math.exp(m - M) for m, l, _ in parts)
+    merged = sum(o * math.exp(m - M) for m, _, o in parts) / Lsum
+    assert np.allclose(out[0], merged, rtol=1e-12, atol=1e-14)
+
+
+def test_each_token_counted_once_with_pools():
+    rng = np.random.default_rng(17)
+    p = O.CacheParams(bits=2, group=8, residual=8, pool=2, evict_cap=3)
+    u = O.UnitCache(p)
+    k = rng.standard_normal((120, 128)).astype(np.float16)
+    k[::9] *= 0.05
+    v = rng.standard_normal((120, 128)).astype(np.float16)
+    u.append(k, v)
+    assert u.tracer.evicted, "construction should displace pool members"
+    K, V = u.dequantized_kv()
+    for m in u.tracer.pool + u.tracer.evicted:
+        assert np.array_equal(K[m.idx], k[m.idx].astype(np.float64))
+        assert np.array_equal(V[m.idx], v[m.idx].astype(np.float64))
+    assert K.shape[0] == 120
+
+
+def test_h2o_increment_sums_to_gqa_ratio():
+    rng = np.random.default_rng(18)
+    c = O.CacheOracle(O.CacheParams(bits=2, group=16, residual=16), 1, 1)
+    k = rng.standard_normal((300, 128)).astype(np.float16)
+    c.append_unit((0, 0), k, k)
+    q = rng.standard_normal((4, 128)).astype(np.float16)
+    _, inc, p = c.decode_unit((0, 0), q)
+    assert abs(inc.sum() - 4) < 1e-12 and np.all(inc >= 0)
+    assert np.allclose(inc, p.sum(axis=0))
+
+
+# ---------------------------------------------------------------------------
+# Heavy-hitter selection ("KV cache quantization and eviction", Minimal
+# implementation h2o_evict: evict the lowest non-recent score, one per step).
+# ---------------------------------------------------------------------------
+
+def _argmin_eviction(scores, k, w):
+    """Repeatedly evict the first-occurrence argmin outside the fixed recent window."""
+    T = len(scores)
+    alive = list(range(T - w))
+    while len(alive) > k:
+        vals = [scores[i] for i in alive]
+        j = vals.index(min(vals))
+        alive.pop(j)
+    return alive + list(range(T - w, T))
+
+
+@pytest.mark.parametrize("ties", [False, True])
+def test_topk_equals_repeated_argmin_eviction(ties):
+    rng = np.random.default_rng(19)
+    for T, k, w in [(50, 10, 5), (64, 0, 8), (40, 40, 0), (33, 20, 13), (16, 0, 0), (20, 3, 17)]:
+        if ties:
+            s = (rng.integers(0, 3, size=(3, T)) * 0.5).astype(np.float32)
+        else:
+            s = rng.random((3, T)).astype(np.float32)
+        got = O.topk_keep(s, k, w)
+        for r in range(3):
+            assert got[r].tolist() == _argmin_eviction(s[r].tolist(), k, w)
+
+
+def test_topk_tie_order_prefers_newer():
+    s = np.array([[1, 2, 2, 2, 0, 5]], dtype=np.float32)
+    assert O.topk_keep(s, 2, 1).tolist() == [[2, 3, 5]]
