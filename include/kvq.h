@@ -1,0 +1,220 @@
+/*
+ * kvq.h - C ABI of libkvq: low-bit KV-cache compression and decode attention
+ * over the compressed cache, for one AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (page citations name the page title and the
+ * section on it):
+ *
+ *  - Asymmetric min-max quantization to b = 2 or 4 bits, step
+ *    q = (max - min) / (2^b - 1), zero-point = group minimum
+ *    ("Accurate KV Cache Quantization with Outlier Tokens Tracing", section
+ *    "Background"; "KV cache quantization and eviction: FP8, INT4, H2O and
+ *    attention sinks", section "Minimal implementation").
+ *  - KIVI grouping: keys per channel over groups of G tokens, values per
+ *    token over groups of min(G, d) channels; codes packed 16 (b = 2) or 8
+ *    (b = 4) per 32-bit word; scale and zero kept in fp16 ("MiniKV: Pushing
+ *    the Limits of LLM Inference via 2-Bit Layer-Discriminative KV Cache",
+ *    section 4.4).
+ *  - A full-precision residual window: after T tokens the first
+ *    n_q = max(0, floor((T - R) / G) * G) are quantized and the rest stay fp16
+ *    ("KV cache quantization and eviction", section "Minimal implementation").
+ *  - OTT outlier tracing: the tokens with the smallest key L1 norm are kept in
+ *    fp16 in a pool of N, replaced by the group mean before quantization;
+ *    displaced members move to an extra pool of E, and tracing stops when that
+ *    is full ("Accurate KV Cache Quantization with Outlier Tokens Tracing",
+ *    sections "Method details" and "Experimental setup").
+ *  - Decode attention over the quantized, fp16-residual and pool partitions
+ *    with softmax scale 1/sqrt(d) (MiniKV, section 2 Eq. 1 and Algorithm 1),
+ *    and H2O accumulated attention per KV head, summed over the query heads
+ *    that share it ("H2O: Heavy-Hitter Oracle for Efficient Generative
+ *    Inference of Large Language Models", accumulated attention scores;
+ *    "KV cache quantization and eviction", section "Heavy hitters").
+ *  - Heavy-hitter selection: the k highest scores outside a recent window of
+ *    w tokens, plus that window (MiniKV, Algorithm 1; "KV cache quantization
+ *    and eviction", section "Minimal implementation").
+ *
+ * Conventions for every entry point:
+ *
+ *  - Memory: the caller allocates all device memory (cache arena, inputs,
+ *    outputs, workspace). The library never allocates, frees or synchronizes
+ *    the device; all work is enqueued on the given stream (a hipStream_t
+ *    passed as void*; NULL = the null stream).
+ *  - Pointers marked "device" must be device addresses; "host" are host
+ *    addresses. Sizes are element counts unless named *_bytes.
+ *  - Errors: every call validates its arguments on the host before launching
+ *    anything. A call that returns an error has launched nothing and left the
+ *    cache unchanged, except KVQ_ELAUNCH, which reports a failed launch.
+ *  - Threading: calls on distinct caches are independent. Calls on one cache
+ *    must be ordered by the caller (same stream, or explicit events).
+ *  - Shapes: batch B, query heads Hq, KV heads Hkv with Hq = r * Hkv (query
+ *    head h reads KV head h / r), head_dim d = 128. A "unit" is one
+ *    (batch, KV head) pair, u = b * Hkv + h_kv; U = B * Hkv. Every unit of a
+ *    cache holds the same number of tokens T.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvq_status;
+
+#define KVQ_OK            0
+#define KVQ_EINVAL       (-1) /* null pointer, negative or inconsistent size */
+#define KVQ_EUNSUPPORTED (-2) /* a configuration this build does not implement */
+#define KVQ_ECAPACITY    (-3) /* appending beyond max_tokens */
+#define KVQ_EWORKSPACE   (-4) /* arena or workspace smaller than required */
+#define KVQ_ELAUNCH      (-5) /* a HIP launch failed (hipGetLastError) */
+
+/* Static description of a status code. Never returns NULL. */
+const char* kvq_status_string(kvq_status status);
+
+/*
+ * Cache configuration (host POD).
+ *   bits        b in {2, 4}
+ *   group       G in {32, 64, 128}: tokens per key group and, capped at d,
+ *               channels per value group (one group size for both axes, MiniKV
+ *               section 5.1)
+ *   residual    R >= 0, fp16 residual window
+ *   pool        N in [0, 64], OTT outlier pool size (0 disables tracing; the
+ *               page uses 0 for layers 0-1 and 3 elsewhere)
+ *   evict_cap   E in [0, 1024], OTT extra pool size (32 on the page)
+ *   head_dim    d, must be 128
+ *   n_q_heads   Hq, n_kv_heads Hkv: Hq / Hkv = r in {1, 2, 4}
+ *   batch       B >= 1
+ *   max_tokens  capacity in tokens per unit, >= 1
+ */
+typedef struct kvq_config {
+    int32_t bits;
+    int32_t group;
+    int32_t residual;
+    int32_t pool;
+    int32_t evict_cap;
+    int32_t head_dim;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t batch;
+    int32_t max_tokens;
+} kvq_config;
+
+/*
+ * Cache handle (caller-owned host POD). Filled by kvq_cache_init; updated by
+ * kvq_quantize_append. It holds the device address of the caller's arena,
+ * byte offsets of the regions inside it, and the host counters T and n_q.
+ * Snapshot / restore of a cache is a copy of the arena bytes plus this struct.
+ *
+ * Arena regions (each starts 256-byte aligned; u is the unit index, C the
+ * number of 32-token chunks of quantized capacity, Qcap = 32 * C,
+ * RB = R + G ring slots, NG = d / min(G, d) value groups per token):
+ *   kq        packed key codes,   U x C chunks of 16*b*32 bytes (see below)
+ *   vq        packed value codes, U x C chunks of 16*b*32 bytes
+ *   kmeta     fp16 (scale, zero) per key channel: [U][Qcap/G][d][2]
+ *   vmeta     fp16 (scale, zero) per value group:  [U][C][NG][32][2]
+ *             (chunk, then value group, then token within the chunk)
+ *   mask      uint32 [U][C], bit i of word c set when token 32c+i was admitted
+ *             to the outlier pool (its quantized slot holds the group mean)
+ *   kring     fp16 [U][RB][d], token t (n_q <= t < T) at slot t % RB
+ *   vring     fp16 [U][RB][d]
+ *   pool_idx  int32 [U][N] token index of each pool member
+ *   pool_score uint64 [U][N] exact key L1 norm in units of 2^-24
+ *   pool_k    fp16 [U][N][d] original key row;  pool_v likewise
+ *   ev_idx    int32 [U][E]; ev_k, ev_v fp16 [U][E][d] (extra pool, in the
+ *             order members were displaced)
+ *   counters  int32 [U][4]: pool count, extra-pool count, frozen flag, 0
+ *   scores    uint64 [U][Qcap] scratch for key L1 norms during an append
+ * Slots of pool_idx / ev_idx beyond the counters are unspecified.
+ *
+ * Packed code layout. Codes of 32 consecutive quantized tokens form a chunk
+ * laid out for the matrix-core operands of the decode kernel: 64 lanes own
+ * 2b 32-bit words each; word w of lane l is stored at word offset
+ * (w / 4) * 256 + l * 4 + (w % 4) of the chunk. kvq_unpack_codes returns the
+ * canonical view (one byte per code, [token][channel]) for inspection.
+ */
+typedef struct kvq_cache {
+    kvq_config cfg;
+    int64_t tokens;     /* T, tokens held per unit */
+    int64_t n_quant;    /* n_q, tokens held quantized per unit */
+    uint64_t arena;     /* device address of the arena */
+    uint64_t arena_bytes;
+    int64_t q_cap;      /* Qcap */
+    int64_t ring_slots; /* RB */
+    uint64_t off_kq, off_vq, off_kmeta, off_vmeta, off_mask, off_kring, off_vring;
+    uint64_t off_pool_idx, off_pool_score, off_pool_k, off_pool_v;
+    uint64_t off_ev_idx, off_ev_k, off_ev_v, off_counters, off_scores;
+} kvq_cache;
+
+/* Bytes of device memory a cache with this configuration needs (host only).
+ * Returns KVQ_EINVAL / KVQ_EUNSUPPORTED for a bad configuration. */
+kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* arena_bytes);
+
+/*
+ * Bind an empty cache to the caller's arena (device, >= kvq_cache_bytes,
+ * 256-byte aligned) and clear its counters and pool masks on `stream`.
+ * Fills *h (host). The arena stays owned by the caller and must outlive *h.
+ */
+kvq_status kvq_cache_init(const kvq_config* cfg, void* d_arena, size_t arena_bytes,
+                          kvq_cache* h, void* stream);
+
+/*
+ * Append n_new >= 0 tokens to every unit: d_k, d_v are device fp16
+ * [B][Hkv][n_new][d] (keys as the model caches them, after RoPE). Every group
+ * of G tokens that leaves the residual window is quantized: OTT tracing (if
+ * N > 0 and not frozen) picks pool members by key L1 norm and replaces them
+ * with the group mean, then keys are quantized per channel and values per
+ * token. Updates h->tokens and h->n_quant on the host. The inputs may be
+ * reused as soon as the enqueued work has run.
+ * Errors: KVQ_EINVAL (null pointer with n_new > 0, n_new < 0),
+ * KVQ_ECAPACITY (T + n_new > max_tokens).
+ */
+kvq_status kvq_quantize_append(kvq_cache* h, const void* d_k, const void* d_v,
+                               int32_t n_new, void* stream);
+
+/*
+ * Workspace bytes kvq_decode_attention needs for the cache's current T, with
+ * (want_scores != 0) or without H2O score accumulation.
+ */
+kvq_status kvq_decode_workspace(const kvq_cache* h, int32_t want_scores, size_t* ws_bytes);
+
+/*
+ * One decode step of attention over the cache.
+ *   d_q    device fp16 [B][Hq][d] queries
+ *   d_out  device fp32 [B][Hq][d] attention outputs (written)
+ *   d_acc  device fp32 [B][Hkv][T] H2O accumulated scores, or NULL. When
+ *          given, acc[u][j] += sum over the r query heads of KV head u of the
+ *          normalized softmax probability of token j (read-modify-write).
+ *   d_ws   device workspace of ws_bytes >= kvq_decode_workspace(h, d_acc != NULL)
+ * Every cached token counts once: pool members with their fp16 rows (their
+ * quantized slots are skipped), tokens at index >= n_q from the fp16 ring,
+ * the rest dequantized on the fly from the packed codes. Softmax scale is
+ * 1/sqrt(d).
+ * Errors: KVQ_EINVAL (null pointer, T == 0), KVQ_EWORKSPACE.
+ */
+kvq_status kvq_decode_attention(const kvq_cache* h, const void* d_q, float* d_out,
+                                float* d_acc, void* d_ws, size_t ws_bytes, void* stream);
+
+/*
+ * Heavy-hitter selection on fp32 scores (device [rows][T]): for each row keep
+ * the k largest scores among indices [0, T - w), ties broken toward the
+ * larger index, plus the w most recent indices [T - w, T). Writes device
+ * int32 [rows][k + w], ascending. +0 and -0 compare equal; NaN scores are not
+ * supported. Errors: KVQ_EINVAL (null pointer, rows < 0, k < 0, w < 0,
+ * k + w > T).
+ */
+kvq_status kvq_topk_evict(const float* d_scores, int32_t rows, int32_t T, int32_t k,
+                          int32_t w, int32_t* d_idx, void* stream);
+
+/*
+ * Inspection: canonical codes of the quantized tokens, one byte per code,
+ * device uint8 [U][n_q][d] for keys and for values.
+ */
+kvq_status kvq_unpack_codes(const kvq_cache* h, uint8_t* d_kcodes, uint8_t* d_vcodes,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

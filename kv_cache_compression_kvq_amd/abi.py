@@ -1,0 +1,154 @@
+"""Python binding of libkvq (include/kvq.h): argument marshalling only.
+
+Every function here has the name of the C entry point it calls, minus the
+``kvq_`` prefix, and does no computation of its own: tensors are passed as
+device pointers, streams as ``hipStream_t`` handles. The HIP library must be
+built (``__graft_entry__.build()`` or ``python -m
+kv_cache_compression_kvq_amd.build``); loading fails loudly otherwise, and
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_OK = 0
+KVQ_EINVAL = -1
+KVQ_EUNSUPPORTED = -2
+KVQ_ECAPACITY = -3
+KVQ_EWORKSPACE = -4
+KVQ_ELAUNCH = -5
+
+# Entry points declared in include/kvq.h.
+EXPORTS = ("kvq_status_string", "kvq_cache_bytes", "kvq_cache_init", "kvq_quantize_append",
+           "kvq_decode_workspace", "kvq_decode_attention", "kvq_topk_evict", "kvq_unpack_codes")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "bits", "group", "residual", "pool", "evict_cap", "head_dim",
+        "n_q_heads", "n_kv_heads", "batch", "max_tokens")]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("cfg", Config), ("tokens", ctypes.c_int64), ("n_quant", ctypes.c_int64),
+                ("arena", ctypes.c_uint64), ("arena_bytes", ctypes.c_uint64),
+                ("q_cap", ctypes.c_int64), ("ring_slots", ctypes.c_int64)] + [
+        (n, ctypes.c_uint64) for n in (
+            "off_kq", "off_vq", "off_kmeta", "off_vmeta", "off_mask", "off_kring", "off_vring",
+            "off_pool_idx", "off_pool_score", "off_pool_k", "off_pool_v", "off_ev_idx",
+            "off_ev_k", "off_ev_v", "off_counters", "off_scores")]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkvq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libkvq.so not built ({LIB_PATH}); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.kvq_status_string.restype = ctypes.c_char_p
+        L.kvq_status_string.argtypes = [I32]
+        sigs = {
+            "kvq_cache_bytes": [ctypes.POINTER(Config), ctypes.POINTER(SZ)],
+            "kvq_cache_init": [ctypes.POINTER(Config), P, SZ, ctypes.POINTER(Cache), P],
+            "kvq_quantize_append": [ctypes.POINTER(Cache), P, P, I32, P],
+            "kvq_decode_workspace": [ctypes.POINTER(Cache), I32, ctypes.POINTER(SZ)],
+            "kvq_decode_attention": [ctypes.POINTER(Cache), P, P, P, P, SZ, P],
+            "kvq_topk_evict": [P, I32, I32, I32, I32, P, P],
+            "kvq_unpack_codes": [ctypes.POINTER(Cache), P, P, P],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.restype = I32
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(x) -> int | None:
+    """Device pointer of a tensor (or an int address, or None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, st: int) -> None:
+    if st != KVQ_OK:
+        raise KvqError(fn, st)
+
+
+def status_string(status: int) -> str:
+    return lib().kvq_status_string(status).decode()
+
+
+def make_config(*, bits, group, residual, pool=0, evict_cap=32, head_dim=128, n_q_heads,
+                n_kv_heads, batch, max_tokens) -> Config:
+    return Config(bits, group, residual, pool, evict_cap, head_dim, n_q_heads, n_kv_heads,
+                  batch, max_tokens)
+
+
+def cache_bytes(cfg: Config) -> int:
+    n = ctypes.c_size_t()
+    _check("kvq_cache_bytes", lib().kvq_cache_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def cache_init(cfg: Config, arena, arena_bytes: int | None = None, stream=None) -> Cache:
+    h = Cache()
+    nbytes = arena_bytes if arena_bytes is not None else arena.numel() * arena.element_size()
+    _check("kvq_cache_init", lib().kvq_cache_init(ctypes.byref(cfg), _ptr(arena), nbytes,
+                                                  ctypes.byref(h), _stream(stream)))
+    return h
+
+
+def quantize_append(h: Cache, k, v, n_new: int, stream=None) -> None:
+    _check("kvq_quantize_append", lib().kvq_quantize_append(
+        ctypes.byref(h), _ptr(k), _ptr(v), n_new, _stream(stream)))
+
+
+def decode_workspace(h: Cache, want_scores: bool) -> int:
+    n = ctypes.c_size_t()
+    _check("kvq_decode_workspace",
+           lib().kvq_decode_workspace(ctypes.byref(h), int(want_scores), ctypes.byref(n)))
+    return n.value
+
+
+def decode_attention(h: Cache, q, out, acc, ws, ws_bytes: int | None = None, stream=None) -> None:
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check("kvq_decode_attention", lib().kvq_decode_attention(
+        ctypes.byref(h), _ptr(q), _ptr(out), _ptr(acc), _ptr(ws), nbytes, _stream(stream)))
+
+
+def topk_evict(scores, rows: int, T: int, k: int, w: int, idx, stream=None) -> None:
+    _check("kvq_topk_evict", lib().kvq_topk_evict(_ptr(scores), rows, T, k, w, _ptr(idx),
+                                                  _stream(stream)))
+
+
+def unpack_codes(h: Cache, kcodes, vcodes, stream=None) -> None:
+    _check("kvq_unpack_codes", lib().kvq_unpack_codes(ctypes.byref(h), _ptr(kcodes),
+                                                      _ptr(vcodes), _stream(stream)))

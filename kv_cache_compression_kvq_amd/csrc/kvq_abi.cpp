@@ -1,0 +1,260 @@
+// C-ABI layer of libkvq: argument validation, arena layout, split planning.
+// Pure host C++ (no HIP headers): every check runs before any launch, so a
+// call that fails validation enqueues nothing and leaves the cache unchanged.
+#include <cstdlib>
+#include <cstring>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr uint64_t kAlign = 256;
+constexpr int64_t kMaxQuantSplits = 1000;  // merge keeps per-split weights in LDS
+
+uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t n_quantized(int64_t T, int64_t R, int64_t G) {
+    // Tokens held quantized after T appends: the residual window keeps the
+    // last R tokens plus any incomplete group in fp16 ("KV cache quantization
+    // and eviction", section "Minimal implementation").
+    return T > R ? (T - R) / G * G : 0;
+}
+
+kvq_status check_config(const kvq_config* c) {
+    if (!c) return KVQ_EINVAL;
+    if (c->residual < 0 || c->pool < 0 || c->evict_cap < 0 || c->batch < 1 ||
+        c->n_kv_heads < 1 || c->n_q_heads < 1 || c->max_tokens < 1)
+        return KVQ_EINVAL;
+    if (c->n_q_heads % c->n_kv_heads != 0) return KVQ_EINVAL;
+    const int r = c->n_q_heads / c->n_kv_heads;
+    if (c->bits != 2 && c->bits != 4) return KVQ_EUNSUPPORTED;
+    if (c->group != 32 && c->group != 64 && c->group != 128) return KVQ_EUNSUPPORTED;
+    if (c->head_dim != kHeadDim) return KVQ_EUNSUPPORTED;
+    if (r != 1 && r != 2 && r != 4) return KVQ_EUNSUPPORTED;
+    if (c->pool > kMaxPool || c->evict_cap > kMaxEvict) return KVQ_EUNSUPPORTED;
+    if ((int64_t)c->residual + c->group + c->pool + c->evict_cap > kMaxFp16Rows)
+        return KVQ_EUNSUPPORTED;
+    return KVQ_OK;
+}
+
+struct Layout {
+    uint64_t off[16];
+    uint64_t total;
+    int64_t q_cap, chunks, ring;
+};
+
+Layout layout_of(const kvq_config* c) {
+    Layout L{};
+    const uint64_t U = (uint64_t)c->batch * c->n_kv_heads;
+    const uint64_t d = kHeadDim;
+    const uint64_t G = c->group, b = c->bits, N = c->pool, E = c->evict_cap;
+    L.q_cap = n_quantized(c->max_tokens, c->residual, c->group);
+    L.chunks = L.q_cap / kChunk;
+    L.ring = (int64_t)c->residual + c->group;
+    const uint64_t C = L.chunks, NG = d / G;
+    const uint64_t sizes[16] = {
+        U * C * 128 * b * 4,          // kq
+        U * C * 128 * b * 4,          // vq
+        U * (L.q_cap / G) * d * 4,    // kmeta
+        U * C * NG * kChunk * 4,      // vmeta
+        U * C * 4,                    // mask
+        U * L.ring * d * 2,           // kring
+        U * L.ring * d * 2,           // vring
+        U * N * 4,                    // pool_idx
+        U * N * 8,                    // pool_score
+        U * N * d * 2,                // pool_k
+        U * N * d * 2,                // pool_v
+        U * E * 4,                    // ev_idx
+        U * E * d * 2,                // ev_k
+        U * E * d * 2,                // ev_v
+        U * 4 * 4,                    // counters
+        N > 0 ? U * L.q_cap * 8 : 0,  // scores
+    };
+    uint64_t o = 0;
+    for (int i = 0; i < 16; ++i) {
+        L.off[i] = o;
+        o = align_up(o + sizes[i]);
+    }
+    L.total = o;
+    return L;
+}
+
+bool valid_handle(const kvq_cache* h) {
+    return h && check_config(&h->cfg) == KVQ_OK && h->arena != 0 && h->tokens >= 0 &&
+           h->n_quant == n_quantized(h->tokens, h->cfg.residual, h->cfg.group) &&
+           h->tokens <= h->cfg.max_tokens;
+}
+
+kvq_status launch_status(int e) { return e == 0 ? KVQ_OK : KVQ_ELAUNCH; }
+
+}  // namespace
+
+CacheView view_of(const kvq_cache* h) {
+    CacheView v{};
+    char* a = reinterpret_cast<char*>(h->arena);
+    v.kq = reinterpret_cast<uint32_t*>(a + h->off_kq);
+    v.vq = reinterpret_cast<uint32_t*>(a + h->off_vq);
+    v.kmeta = reinterpret_cast<uint32_t*>(a + h->off_kmeta);
+    v.vmeta = reinterpret_cast<uint32_t*>(a + h->off_vmeta);
+    v.mask = reinterpret_cast<uint32_t*>(a + h->off_mask);
+    v.kring = reinterpret_cast<uint16_t*>(a + h->off_kring);
+    v.vring = reinterpret_cast<uint16_t*>(a + h->off_vring);
+    v.pool_idx = reinterpret_cast<int32_t*>(a + h->off_pool_idx);
+    v.pool_score = reinterpret_cast<uint64_t*>(a + h->off_pool_score);
+    v.pool_k = reinterpret_cast<uint16_t*>(a + h->off_pool_k);
+    v.pool_v = reinterpret_cast<uint16_t*>(a + h->off_pool_v);
+    v.ev_idx = reinterpret_cast<int32_t*>(a + h->off_ev_idx);
+    v.ev_k = reinterpret_cast<uint16_t*>(a + h->off_ev_k);
+    v.ev_v = reinterpret_cast<uint16_t*>(a + h->off_ev_v);
+    v.counters = reinterpret_cast<int32_t*>(a + h->off_counters);
+    v.scores = reinterpret_cast<uint64_t*>(a + h->off_scores);
+    v.bits = h->cfg.bits;
+    v.group = h->cfg.group;
+    v.residual = h->cfg.residual;
+    v.pool = h->cfg.pool;
+    v.evict_cap = h->cfg.evict_cap;
+    v.n_q_heads = h->cfg.n_q_heads;
+    v.n_kv_heads = h->cfg.n_kv_heads;
+    v.batch = h->cfg.batch;
+    v.units = h->cfg.batch * h->cfg.n_kv_heads;
+    v.ring_slots = (int32_t)h->ring_slots;
+    v.q_cap = h->q_cap;
+    v.chunks = h->q_cap / kChunk;
+    v.key_groups = h->q_cap / h->cfg.group;
+    return v;
+}
+
+DecodePlan plan_decode(const kvq_cache* h, bool want_scores) {
+    // Split-K over the quantized tokens: about kTargetBlocks workgroups of four
+    // wavefronts in total, each wavefront taking whole key groups, so that a
+    // step fills the 256 compute units even for a single long sequence.
+    static const int64_t kTargetBlocks = [] {
+        const char* s = std::getenv("KVQ_DECODE_BLOCKS");
+        long v = s ? std::strtol(s, nullptr, 10) : 0;
+        return (int64_t)(v > 0 ? v : 1024);
+    }();
+    DecodePlan p{};
+    const int64_t U = (int64_t)h->cfg.batch * h->cfg.n_kv_heads;
+    const int64_t r = h->cfg.n_q_heads / h->cfg.n_kv_heads;
+    const int64_t groups = h->n_quant / h->cfg.group;
+    int64_t s = 0;
+    if (groups > 0) {
+        s = (kTargetBlocks + U - 1) / U;
+        const int64_t by_work = (groups + 3) / 4;
+        if (s > by_work) s = by_work;
+        if (s > kMaxQuantSplits) s = kMaxQuantSplits;
+        if (s < 1) s = 1;
+    }
+    p.splits_q = (int32_t)s;
+    p.splits = (int32_t)s + 1;
+    p.part_floats = U * p.splits * r * (kHeadDim + 2);
+    p.logit_floats = want_scores ? U * r * h->tokens : 0;
+    p.ws_bytes = align_up((uint64_t)p.part_floats * 4) + (uint64_t)p.logit_floats * 4;
+    return p;
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status s) {
+    switch (s) {
+        case KVQ_OK: return "ok";
+        case KVQ_EINVAL: return "invalid argument";
+        case KVQ_EUNSUPPORTED: return "unsupported configuration";
+        case KVQ_ECAPACITY: return "cache capacity exceeded";
+        case KVQ_EWORKSPACE: return "arena or workspace too small";
+        case KVQ_ELAUNCH: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* arena_bytes) {
+    kvq_status st = check_config(cfg);
+    if (st != KVQ_OK) return st;
+    if (!arena_bytes) return KVQ_EINVAL;
+    *arena_bytes = (size_t)layout_of(cfg).total;
+    return KVQ_OK;
+}
+
+kvq_status kvq_cache_init(const kvq_config* cfg, void* d_arena, size_t bytes, kvq_cache* h,
+                          void* stream) {
+    kvq_status st = check_config(cfg);
+    if (st != KVQ_OK) return st;
+    if (!d_arena || !h) return KVQ_EINVAL;
+    if (reinterpret_cast<uintptr_t>(d_arena) % kAlign != 0) return KVQ_EINVAL;
+    const Layout L = layout_of(cfg);
+    if (bytes < L.total) return KVQ_EWORKSPACE;
+    kvq_cache c{};
+    c.cfg = *cfg;
+    c.tokens = 0;
+    c.n_quant = 0;
+    c.arena = reinterpret_cast<uint64_t>(d_arena);
+    c.arena_bytes = bytes;
+    c.q_cap = L.q_cap;
+    c.ring_slots = L.ring;
+    uint64_t* offs[16] = {&c.off_kq, &c.off_vq, &c.off_kmeta, &c.off_vmeta, &c.off_mask,
+                          &c.off_kring, &c.off_vring, &c.off_pool_idx, &c.off_pool_score,
+                          &c.off_pool_k, &c.off_pool_v, &c.off_ev_idx, &c.off_ev_k,
+                          &c.off_ev_v, &c.off_counters, &c.off_scores};
+    for (int i = 0; i < 16; ++i) *offs[i] = L.off[i];
+    st = launch_status(launch_init(view_of(&c), stream));
+    if (st == KVQ_OK) *h = c;
+    return st;
+}
+
+kvq_status kvq_quantize_append(kvq_cache* h, const void* d_k, const void* d_v, int32_t n_new,
+                               void* stream) {
+    if (!valid_handle(h) || n_new < 0) return KVQ_EINVAL;
+    if (n_new == 0) return KVQ_OK;
+    if (!d_k || !d_v) return KVQ_EINVAL;
+    const int64_t t_new = h->tokens + n_new;
+    if (t_new > h->cfg.max_tokens) return KVQ_ECAPACITY;
+    const int64_t nq_new = n_quantized(t_new, h->cfg.residual, h->cfg.group);
+    kvq_status st = launch_status(launch_append(
+        view_of(h), static_cast<const uint16_t*>(d_k), static_cast<const uint16_t*>(d_v),
+        h->tokens, n_new, h->n_quant, nq_new, stream));
+    if (st == KVQ_OK) {
+        h->tokens = t_new;
+        h->n_quant = nq_new;
+    }
+    return st;
+}
+
+kvq_status kvq_decode_workspace(const kvq_cache* h, int32_t want_scores, size_t* ws_bytes) {
+    if (!valid_handle(h) || !ws_bytes) return KVQ_EINVAL;
+    *ws_bytes = plan_decode(h, want_scores != 0).ws_bytes;
+    return KVQ_OK;
+}
+
+kvq_status kvq_decode_attention(const kvq_cache* h, const void* d_q, float* d_out, float* d_acc,
+                                void* d_ws, size_t ws_bytes, void* stream) {
+    if (!valid_handle(h) || !d_q || !d_out || !d_ws) return KVQ_EINVAL;
+    if (h->tokens < 1) return KVQ_EINVAL;
+    const DecodePlan p = plan_decode(h, d_acc != nullptr);
+    if (ws_bytes < p.ws_bytes) return KVQ_EWORKSPACE;
+    return launch_status(launch_decode(view_of(h), h->tokens, h->n_quant, p,
+                                       static_cast<const uint16_t*>(d_q), d_out, d_acc, d_ws,
+                                       stream));
+}
+
+kvq_status kvq_topk_evict(const float* d_scores, int32_t rows, int32_t T, int32_t k, int32_t w,
+                          int32_t* d_idx, void* stream) {
+    if (rows < 0 || T < 0 || k < 0 || w < 0 || (int64_t)k + w > T) return KVQ_EINVAL;
+    if (rows == 0 || k + w == 0) return KVQ_OK;
+    if (!d_scores || !d_idx) return KVQ_EINVAL;
+    return launch_status(launch_topk(d_scores, rows, T, k, w, d_idx, stream));
+}
+
+kvq_status kvq_unpack_codes(const kvq_cache* h, uint8_t* d_kcodes, uint8_t* d_vcodes,
+                            void* stream) {
+    if (!valid_handle(h)) return KVQ_EINVAL;
+    if (h->n_quant == 0) return KVQ_OK;
+    if (!d_kcodes || !d_vcodes) return KVQ_EINVAL;
+    return launch_status(launch_unpack(view_of(h), h->n_quant, d_kcodes, d_vcodes, stream));
+}
+
+}  // extern "C"

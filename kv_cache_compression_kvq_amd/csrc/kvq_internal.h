@@ -1,0 +1,68 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer of libkvq.
+// Not part of the public interface (include/kvq.h is).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int kHeadDim = 128;      // d
+constexpr int kChunk = 32;         // tokens per packed chunk
+constexpr int kMaxPool = 64;       // N limit
+constexpr int kMaxEvict = 1024;    // E limit
+constexpr int kMaxFp16Rows = 2048; // R + G + N + E limit (fp16 partition kept in LDS)
+
+// Device pointers of one cache, resolved from the arena and the handle's offsets.
+struct CacheView {
+    uint32_t* kq;
+    uint32_t* vq;
+    uint32_t* kmeta;     // (scale | zero << 16) per key group and channel
+    uint32_t* vmeta;     // (scale | zero << 16) per chunk, value group, token
+    uint32_t* mask;      // one word per chunk
+    uint16_t* kring;
+    uint16_t* vring;
+    int32_t* pool_idx;
+    uint64_t* pool_score;
+    uint16_t* pool_k;
+    uint16_t* pool_v;
+    int32_t* ev_idx;
+    uint16_t* ev_k;
+    uint16_t* ev_v;
+    int32_t* counters;
+    uint64_t* scores;
+    int32_t bits, group, residual, pool, evict_cap;
+    int32_t n_q_heads, n_kv_heads, batch;
+    int32_t units;       // U = batch * n_kv_heads
+    int32_t ring_slots;  // RB = R + G
+    int64_t q_cap;       // quantized token capacity per unit
+    int64_t chunks;      // q_cap / 32
+    int64_t key_groups;  // q_cap / G
+};
+
+CacheView view_of(const kvq_cache* h);
+
+// Split plan of one decode call.
+struct DecodePlan {
+    int32_t splits_q;    // quantized-partition splits per unit (0 when n_q == 0)
+    int32_t splits;      // splits_q + 1 (the last one is the fp16 partition)
+    int64_t part_floats; // partial records: U * splits * r * (d + 2)
+    int64_t logit_floats;// U * r * T when scores are wanted
+    size_t ws_bytes;
+};
+
+DecodePlan plan_decode(const kvq_cache* h, bool want_scores);
+
+// Launchers (return hipError_t as int; 0 = success).
+int launch_init(const CacheView& v, void* stream);
+int launch_append(const CacheView& v, const uint16_t* k_new, const uint16_t* v_new,
+                  int64_t t_old, int32_t n_new, int64_t nq_old, int64_t nq_new, void* stream);
+int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& plan,
+                  const uint16_t* q, float* out, float* acc, void* ws, void* stream);
+int launch_topk(const float* scores, int32_t rows, int32_t T, int32_t k, int32_t w,
+                int32_t* idx, void* stream);
+int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, void* stream);
+
+}  // namespace kvq

@@ -1,0 +1,469 @@
+// Append path of libkvq on gfx950: OTT outlier tracing, KIVI quantize + pack,
+// fp16 residual ring, plus cache initialisation and the canonical code view.
+//
+// Quantizer ("Accurate KV Cache Quantization with Outlier Tokens Tracing",
+// section "Background"; "KV cache quantization and eviction", section
+// "Minimal implementation"): for a group with minimum mn and maximum mx the
+// step is q = max(mx - mn, 1e-8) / (2^b - 1) in IEEE fp32, each code is
+// clamp(rint((x - mn) / q), 0, 2^b - 1) with ties to even, and the group keeps
+// fp16(q) and mn (MiniKV, section 4.4: scale and zero-point in FP16). Every
+// fp32 operation here is a single correctly rounded IEEE operation: nothing
+// is contracted into an FMA, and division is built correctly rounded.
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+namespace {
+
+constexpr int D = kHeadDim;
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ uint16_t f2h(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
+}
+
+// An fp16 value as an exact integer multiple of 2^-24 (every finite binary16
+// number is one).
+__device__ __forceinline__ int64_t half_fixed(uint16_t h) {
+    const uint32_t e = (h >> 10) & 0x1F, m = h & 0x3FF;
+    const int64_t mag = e ? (int64_t)(1024 + m) << (e - 1) : (int64_t)m;
+    return (h & 0x8000) ? -mag : mag;
+}
+
+// Round S * 2^-(24 + sh) to the nearest binary16 value, ties to even, from
+// the exact integer S. Used for the group mean, which is exact before this one
+// rounding (sum of fixed-point values divided by a power of two).
+__device__ uint16_t fixed_to_half(int64_t S, int sh) {
+    const uint16_t sign = S < 0 ? 0x8000 : 0;
+    const uint64_t A = S < 0 ? (uint64_t)(-S) : (uint64_t)S;
+    if (A == 0) return 0;
+    const int lg = 63 - __builtin_clzll(A) - sh;  // floor(log2) of the value in 2^-24 units
+    const int qe = lg > 10 ? lg - 10 : 0;         // log2 of the binary16 quantum there
+    const int shift = sh + qe;
+    uint64_t n = A;
+    if (shift > 0) {
+        n = A >> shift;
+        const uint64_t rem = A & ((1ull << shift) - 1), half = 1ull << (shift - 1);
+        if (rem > half || (rem == half && (n & 1))) ++n;
+    }
+    const uint64_t vu = n << qe;  // rounded value, 2^-24 units
+    if (vu < 1024) return sign | (uint16_t)vu;  // subnormal
+    const int p = 63 - __builtin_clzll(vu);
+    const int e = p - 9;  // biased exponent
+    if (e >= 31) return sign | 0x7C00;
+    const uint32_t f = (uint32_t)(vu >> (e - 1)) - 1024;
+    return sign | (uint16_t)(e << 10) | (uint16_t)f;
+}
+
+__device__ __forceinline__ uint32_t quant_code(float x, float mn, float q, float levels) {
+    const float t = (x - mn) / q;
+    return (uint32_t)fminf(fmaxf(rintf(t), 0.0f), levels);
+}
+
+// Lower bound on the range before dividing (the reference quantizer clamps
+// max - min at 1e-8); bit pattern of the fp32 nearest to 1e-8.
+__device__ __forceinline__ float range_floor() { return __builtin_bit_cast(float, 0x322BCC77u); }
+
+// Source row of token t of unit u during an append: the residual ring holds
+// tokens appended by earlier calls, the caller's buffer holds this call's.
+__device__ __forceinline__ const uint16_t* src_row(const uint16_t* ring, const uint16_t* fresh,
+                                                   const CacheView& v, int u, int64_t t,
+                                                   int64_t t_old, int32_t n_new) {
+    return t < t_old ? ring + ((int64_t)u * v.ring_slots + t % v.ring_slots) * D
+                     : fresh + ((int64_t)u * n_new + (t - t_old)) * D;
+}
+
+__global__ void init_kernel(CacheView v) {
+    const int64_t nc = (int64_t)v.units * 4, nm = (int64_t)v.units * v.chunks;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nc + nm;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        if (i < nc) v.counters[i] = 0;
+        else v.mask[i - nc] = 0;
+    }
+}
+
+// OTT token score: S_t = sum_c |K_{t,c}|, exact, as a multiple of 2^-24
+// ("Accurate KV Cache Quantization with Outlier Tokens Tracing", sections
+// "Method details" and appendix E: the L1 norm of the key). Sixteen lanes per
+// token, 16 bytes each.
+__global__ __launch_bounds__(256) void ott_score_kernel(CacheView v, const uint16_t* knew,
+                                                        int64_t t_old, int32_t n_new, int64_t t0,
+                                                        int64_t ntok) {
+    const int u = blockIdx.y;
+    const int64_t tl = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
+    const int part = threadIdx.x % 16;
+    uint64_t s = 0;
+    if (tl < ntok) {
+        const uint16_t* row = src_row(v.kring, knew, v, u, t0 + tl, t_old, n_new);
+        const uint4 x = reinterpret_cast<const uint4*>(row)[part];
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t a = half_fixed((uint16_t)(w[i] & 0xFFFF));
+            const int64_t b = half_fixed((uint16_t)(w[i] >> 16));
+            s += (uint64_t)(a < 0 ? -a : a) + (uint64_t)(b < 0 ? -b : b);
+        }
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off, 16);
+    if (part == 0 && tl < ntok) v.scores[(int64_t)u * v.q_cap + t0 + tl] = s;
+}
+
+// OTT pool competition, one wavefront per unit, groups in token order.
+// For each group the tokens ranked by (score, index) together with the pool
+// members and falling among the N best are admitted in that order; an
+// admission into a full pool moves the pool's worst member to the extra pool;
+// when that needs a move and the extra pool already holds E tokens, tracing
+// stops for good ("Accurate KV Cache Quantization with Outlier Tokens
+// Tracing", section "Method details" and appendix E). Admitted tokens get
+// their bit in the chunk mask and their original fp16 rows copied to the pool.
+__global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_t* knew,
+                                                      const uint16_t* vnew, int64_t t_old,
+                                                      int32_t n_new, int64_t g0, int64_t g1) {
+    const int u = blockIdx.x, lane = threadIdx.x;
+    const int G = v.group, N = v.pool, E = v.evict_cap;
+    __shared__ uint64_t sc[128];
+    __shared__ uint64_t psc[kMaxPool];
+    __shared__ int32_t pidx[kMaxPool];
+    __shared__ int32_t slot[kMaxPool];
+    __shared__ uint32_t mwords[4];
+    int32_t* cnt = v.counters + (int64_t)u * 4;
+    int pc = cnt[0], ec = cnt[1], frozen = cnt[2];
+    for (int p = lane; p < N; p += 64) {
+        pidx[p] = v.pool_idx[(int64_t)u * N + p];
+        psc[p] = v.pool_score[(int64_t)u * N + p];
+    }
+    __syncthreads();
+    for (int64_t g = g0; g < g1 && !frozen; ++g) {
+        const int64_t t0 = g * G;
+        for (int i = lane; i < G; i += 64) sc[i] = v.scores[(int64_t)u * v.q_cap + t0 + i];
+        for (int p = lane; p < N; p += 64) slot[p] = -1;
+        if (lane < 4) mwords[lane] = 0;
+        __syncthreads();
+        for (int i = lane; i < G; i += 64) {
+            const uint64_t si = sc[i];
+            const int64_t ti = t0 + i;
+            int rank = 0;
+            for (int p = 0; p < pc; ++p) rank += (psc[p] < si) || (psc[p] == si && pidx[p] < ti);
+            for (int q = 0; q < G; ++q) rank += (sc[q] < si) || (sc[q] == si && q < i);
+            if (rank < N) slot[rank] = i;
+        }
+        __syncthreads();
+        for (int rk = 0; rk < N; ++rk) {
+            const int i = slot[rk];
+            if (i < 0) continue;
+            const int64_t t = t0 + i;
+            int dst;
+            if (pc == N) {
+                int w = 0;
+                for (int p = 1; p < N; ++p)
+                    if (psc[p] > psc[w] || (psc[p] == psc[w] && pidx[p] > pidx[w])) w = p;
+                if (ec == E) {
+                    frozen = 1;
+                    break;
+                }
+                const int64_t ps = (int64_t)u * N + w, es = (int64_t)u * E + ec;
+                if (lane == 0) v.ev_idx[es] = pidx[w];
+                reinterpret_cast<uint32_t*>(v.ev_k + es * D)[lane] =
+                    reinterpret_cast<const uint32_t*>(v.pool_k + ps * D)[lane];
+                reinterpret_cast<uint32_t*>(v.ev_v + es * D)[lane] =
+                    reinterpret_cast<const uint32_t*>(v.pool_v + ps * D)[lane];
+                ++ec;
+                dst = w;
+            } else {
+                dst = pc++;
+            }
+            const int64_t pd = (int64_t)u * N + dst;
+            reinterpret_cast<uint32_t*>(v.pool_k + pd * D)[lane] = reinterpret_cast<const uint32_t*>(
+                src_row(v.kring, knew, v, u, t, t_old, n_new))[lane];
+            reinterpret_cast<uint32_t*>(v.pool_v + pd * D)[lane] = reinterpret_cast<const uint32_t*>(
+                src_row(v.vring, vnew, v, u, t, t_old, n_new))[lane];
+            __syncthreads();
+            if (lane == 0) {
+                pidx[dst] = (int32_t)t;
+                psc[dst] = sc[i];
+                mwords[i / 32] |= 1u << (i % 32);
+            }
+            __syncthreads();
+        }
+        if (lane < G / 32) v.mask[(int64_t)u * v.chunks + t0 / 32 + lane] = mwords[lane];
+        __syncthreads();
+    }
+    for (int p = lane; p < N; p += 64) {
+        v.pool_idx[(int64_t)u * N + p] = pidx[p];
+        v.pool_score[(int64_t)u * N + p] = psc[p];
+    }
+    if (lane == 0) {
+        cnt[0] = pc;
+        cnt[1] = ec;
+        cnt[2] = frozen;
+    }
+}
+
+// Quantize and pack one key group (G tokens) of one unit; 256 threads.
+// Pool members' rows are first replaced, for keys and values alike, by the
+// per-channel mean of all G rows of the group, computed exactly and rounded
+// once to fp16 ("Accurate KV Cache Quantization with Outlier Tokens Tracing",
+// section "Method details"). Keys are then quantized per channel over the G
+// tokens, values per token over runs of G channels (KIVI grouping; MiniKV,
+// section 4.4), and the codes written in the chunk layout of kvq.h.
+template <int BITS, int G>
+__global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* knew,
+                                                   const uint16_t* vnew, int64_t t_old,
+                                                   int32_t n_new, int64_t g0) {
+    constexpr int NG = D / G;          // value groups per token
+    constexpr int CPG = G / kChunk;    // chunks per key group
+    constexpr int WPC = 128 * BITS;    // 32-bit words per chunk
+    constexpr int LG = G == 32 ? 5 : G == 64 ? 6 : 7;
+    const float levels = (float)((1 << BITS) - 1);
+    extern __shared__ __align__(16) uint16_t smem[];
+    uint16_t* kx = smem;        // [G][D] fp16 rows, overwritten by their codes
+    uint16_t* vx = smem + G * D;
+    __shared__ uint16_t meank[D], meanv[D];
+    const int u = blockIdx.y, tid = threadIdx.x;
+    const int64_t g = g0 + blockIdx.x, t0 = g * G;
+
+    for (int e = tid; e < G * 16; e += 256) {
+        const int i = e / 16, part = e % 16;
+        reinterpret_cast<uint4*>(kx)[e] = reinterpret_cast<const uint4*>(
+            src_row(v.kring, knew, v, u, t0 + i, t_old, n_new))[part];
+        reinterpret_cast<uint4*>(vx)[e] = reinterpret_cast<const uint4*>(
+            src_row(v.vring, vnew, v, u, t0 + i, t_old, n_new))[part];
+    }
+    uint32_t mw[CPG];
+    bool any = false;
+#pragma unroll
+    for (int c = 0; c < CPG; ++c) {
+        mw[c] = v.pool > 0 ? v.mask[(int64_t)u * v.chunks + t0 / kChunk + c] : 0u;
+        any |= mw[c] != 0;
+    }
+    __syncthreads();
+    if (any) {
+        if (tid < 2 * D) {
+            const uint16_t* x = tid < D ? kx + tid : vx + (tid - D);
+            int64_t s = 0;
+            for (int i = 0; i < G; ++i) s += half_fixed(x[i * D]);
+            (tid < D ? meank[tid] : meanv[tid - D]) = fixed_to_half(s, LG);
+        }
+        __syncthreads();
+        for (int e = tid; e < G * D; e += 256) {
+            const int i = e / D, c = e % D;
+            if ((mw[i / kChunk] >> (i % kChunk)) & 1u) {
+                kx[e] = meank[c];
+                vx[e] = meanv[c];
+            }
+        }
+        __syncthreads();
+    }
+    if (tid < D) {
+        // keys: channel c over the G tokens
+        const int c = tid;
+        float mn = INFINITY, mx = -INFINITY;
+        for (int i = 0; i < G; ++i) {
+            const float x = h2f(kx[i * D + c]);
+            mn = fminf(mn, x);
+            mx = fmaxf(mx, x);
+        }
+        const float q = fmaxf(mx - mn, range_floor()) / levels;
+        v.kmeta[((int64_t)u * v.key_groups + g) * D + c] = (uint32_t)f2h(q) | ((uint32_t)f2h(mn) << 16);
+        for (int i = 0; i < G; ++i) kx[i * D + c] = (uint16_t)quant_code(h2f(kx[i * D + c]), mn, q, levels);
+    } else {
+        // values: token i, channels [gq*G, gq*G + G)
+        const int j = tid - D, i = j / NG, gq = j % NG;
+        uint16_t* row = vx + i * D + gq * G;
+        float mn = INFINITY, mx = -INFINITY;
+        for (int c = 0; c < G; ++c) {
+            const float x = h2f(row[c]);
+            mn = fminf(mn, x);
+            mx = fmaxf(mx, x);
+        }
+        const float q = fmaxf(mx - mn, range_floor()) / levels;
+        const int64_t t = t0 + i;
+        v.vmeta[(((int64_t)u * v.chunks + t / kChunk) * NG + gq) * kChunk + t % kChunk] =
+            (uint32_t)f2h(q) | ((uint32_t)f2h(mn) << 16);
+        for (int c = 0; c < G; ++c) row[c] = (uint16_t)quant_code(h2f(row[c]), mn, q, levels);
+    }
+    __syncthreads();
+
+    // Pack. Word w of lane l sits at (w/4)*256 + l*4 + w%4 within its chunk.
+    for (int e = tid; e < 2 * CPG * WPC; e += 256) {
+        const bool isv = e >= CPG * WPC;
+        const int r = isv ? e - CPG * WPC : e;
+        const int cc = r / WPC, o = r % WPC;
+        const int w = (o / 256) * 4 + (o % 4), l = (o % 256) / 4;
+        const int kb = l / 16, n = l % 16;
+        uint32_t word = 0;
+        if (!isv) {
+            // lane (token row n of tile tau, channel block kb): codes of channels
+            // 32*ks + 8*kb + {2m, 2m+1} in the low/high halves of the word
+            if (BITS == 2) {
+                const int tau = w / 2;
+                const int tok = cc * kChunk + 16 * tau + n;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int ks = (w % 2) * 2 + q / 4, m = q % 4;
+                    const int ch = 32 * ks + 8 * kb + 2 * m;
+                    word |= (uint32_t)kx[tok * D + ch] << (2 * q);
+                    word |= (uint32_t)kx[tok * D + ch + 1] << (16 + 2 * q);
+                }
+            } else {
+                const int tau = w / 4, ks = w % 4;
+                const int tok = cc * kChunk + 16 * tau + n;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int ch = 32 * ks + 8 * kb + 2 * m;
+                    word |= (uint32_t)kx[tok * D + ch] << (4 * m);
+                    word |= (uint32_t)kx[tok * D + ch + 1] << (16 + 4 * m);
+                }
+            }
+        } else {
+            // lane (channel n of each 16-channel tile nt, token block kb): slot s
+            // holds token 16*(s/4) + 4*kb + s%4; slots {2m, 2m+1} share a word
+            if (BITS == 2) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int nt = 2 * w + q / 4, m = q % 4;
+                    const int c = 16 * nt + n;
+                    const int sa = 2 * m, sb = 2 * m + 1;
+                    const int ta = cc * kChunk + 16 * (sa / 4) + 4 * kb + sa % 4;
+                    const int tb = cc * kChunk + 16 * (sb / 4) + 4 * kb + sb % 4;
+                    word |= (uint32_t)vx[ta * D + c] << (2 * q);
+                    word |= (uint32_t)vx[tb * D + c] << (16 + 2 * q);
+                }
+            } else {
+                const int c = 16 * w + n;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int sa = 2 * m, sb = 2 * m + 1;
+                    const int ta = cc * kChunk + 16 * (sa / 4) + 4 * kb + sa % 4;
+                    const int tb = cc * kChunk + 16 * (sb / 4) + 4 * kb + sb % 4;
+                    word |= (uint32_t)vx[ta * D + c] << (4 * m);
+                    word |= (uint32_t)vx[tb * D + c] << (16 + 4 * m);
+                }
+            }
+        }
+        const int64_t base = ((int64_t)u * v.chunks + g * CPG + cc) * WPC;
+        (isv ? v.vq : v.kq)[base + o] = word;
+    }
+}
+
+// Copy this call's tokens that stay fp16 into the residual ring (slot t % RB).
+__global__ __launch_bounds__(256) void ring_store_kernel(CacheView v, const uint16_t* knew,
+                                                         const uint16_t* vnew, int64_t t_old,
+                                                         int32_t n_new, int64_t ts, int64_t ntok) {
+    const int u = blockIdx.y;
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= ntok * 16) return;
+    const int64_t t = ts + e / 16;
+    const int part = (int)(e % 16);
+    const int64_t src = ((int64_t)u * n_new + (t - t_old)) * D;
+    const int64_t dst = ((int64_t)u * v.ring_slots + t % v.ring_slots) * D;
+    reinterpret_cast<uint4*>(v.kring + dst)[part] = reinterpret_cast<const uint4*>(knew + src)[part];
+    reinterpret_cast<uint4*>(v.vring + dst)[part] = reinterpret_cast<const uint4*>(vnew + src)[part];
+}
+
+// Canonical view: one byte per code, [unit][token][channel].
+__global__ __launch_bounds__(256) void unpack_kernel(CacheView v, int64_t n_q, uint8_t* kc,
+                                                     uint8_t* vc) {
+    const int64_t total = (int64_t)v.units * n_q * D;
+    const int b = v.bits;
+    const int wpc = 128 * b;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int c = (int)(e % D);
+        const int64_t t = (e / D) % n_q;
+        const int u = (int)(e / (D * n_q));
+        const int64_t chunk = t / kChunk;
+        const int tt = (int)(t % kChunk);
+        const uint32_t* kbase = v.kq + ((int64_t)u * v.chunks + chunk) * wpc;
+        const uint32_t* vbase = v.vq + ((int64_t)u * v.chunks + chunk) * wpc;
+        const uint32_t mask = (1u << b) - 1;
+        {   // key code
+            const int tau = tt / 16, row = tt % 16;
+            const int ks = c / 32, kb = (c % 32) / 8, s = c % 8, m = s / 2, hi = s % 2;
+            const int l = row + 16 * kb;
+            int w, bit;
+            if (b == 2) { w = 2 * tau + ks / 2; bit = 2 * ((ks % 2) * 4 + m) + 16 * hi; }
+            else { w = 4 * tau + ks; bit = 4 * m + 16 * hi; }
+            kc[e] = (uint8_t)((kbase[(w / 4) * 256 + l * 4 + w % 4] >> bit) & mask);
+        }
+        {   // value code
+            const int tau = tt / 16, r16 = tt % 16, kb = r16 / 4, s = 4 * tau + r16 % 4;
+            const int m = s / 2, hi = s % 2, nt = c / 16, n = c % 16;
+            const int l = n + 16 * kb;
+            int w, bit;
+            if (b == 2) { w = nt / 2; bit = 2 * ((nt % 2) * 4 + m) + 16 * hi; }
+            else { w = nt; bit = 4 * m + 16 * hi; }
+            vc[e] = (uint8_t)((vbase[(w / 4) * 256 + l * 4 + w % 4] >> bit) & mask);
+        }
+    }
+}
+
+template <int BITS, int G>
+void launch_pack_t(const CacheView& v, const uint16_t* kn, const uint16_t* vn, int64_t t_old,
+                   int32_t n_new, int64_t g0, int64_t ng, hipStream_t s) {
+    const size_t lds = 2 * (size_t)G * D * sizeof(uint16_t);
+    static bool attr = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(pack_kernel<BITS, G>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * G * D * 2);
+        return true;
+    }();
+    (void)attr;
+    hipLaunchKernelGGL((pack_kernel<BITS, G>), dim3((unsigned)ng, v.units), dim3(256), lds, s, v,
+                       kn, vn, t_old, n_new, g0);
+}
+
+}  // namespace
+
+int launch_init(const CacheView& v, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t n = (int64_t)v.units * 4 + (int64_t)v.units * v.chunks;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(init_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0,
+                       s, v);
+    return (int)hipGetLastError();
+}
+
+int launch_append(const CacheView& v, const uint16_t* kn, const uint16_t* vn, int64_t t_old,
+                  int32_t n_new, int64_t nq_old, int64_t nq_new, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int G = v.group;
+    const int64_t g0 = nq_old / G, g1 = nq_new / G, ng = g1 - g0;
+    if (ng > 0) {
+        if (v.pool > 0) {
+            const int64_t ntok = ng * G;
+            hipLaunchKernelGGL(ott_score_kernel, dim3((unsigned)((ntok + 15) / 16), v.units),
+                               dim3(256), 0, s, v, kn, t_old, n_new, nq_old, ntok);
+            hipLaunchKernelGGL(ott_scan_kernel, dim3(v.units), dim3(64), 0, s, v, kn, vn, t_old,
+                               n_new, g0, g1);
+        }
+#define KVQ_PACK(B_, G_)                                                         \
+    if (v.bits == B_ && G == G_) launch_pack_t<B_, G_>(v, kn, vn, t_old, n_new, g0, ng, s);
+        KVQ_PACK(2, 32) KVQ_PACK(2, 64) KVQ_PACK(2, 128)
+        KVQ_PACK(4, 32) KVQ_PACK(4, 64) KVQ_PACK(4, 128)
+#undef KVQ_PACK
+    }
+    const int64_t ts = t_old > nq_new ? t_old : nq_new, te = t_old + n_new;
+    if (te > ts) {
+        const int64_t ntok = te - ts;
+        hipLaunchKernelGGL(ring_store_kernel, dim3((unsigned)((ntok * 16 + 255) / 256), v.units),
+                           dim3(256), 0, s, v, kn, vn, t_old, n_new, ts, ntok);
+    }
+    return (int)hipGetLastError();
+}
+
+int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t total = (int64_t)v.units * n_q * D;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, v, n_q, kc, vc);
+    return (int)hipGetLastError();
+}
+
+}  // namespace kvq

@@ -260,28 +260,69 @@ class UnitCache:
     def __init__(self, p: CacheParams):
         self.p = p
         d = p.head_dim
-        self.k16 = np.zeros((0, d), dtype=np.float16)  # every appended row, original
-        self.v16 = np.zeros((0, d), dtype=np.float16)
+        self._k16 = [np.zeros((0, d), dtype=np.float16)]  # every appended row, original
+        self._v16 = [np.zeros((0, d), dtype=np.float16)]
         self.n_q = 0
-        self.kcodes = np.zeros((0, d), dtype=np.uint8)
-        self.kscale = np.zeros((0, d), dtype=np.float16)  # per group
-        self.kzero = np.zeros((0, d), dtype=np.float16)
-        self.vcodes = np.zeros((0, d), dtype=np.uint8)
-        self.vscale = np.zeros((0, d // p.gv), dtype=np.float16)  # per token
-        self.vzero = np.zeros((0, d // p.gv), dtype=np.float16)
-        self.replaced = np.zeros(0, dtype=bool)  # token was admitted to the pool
+        # one entry per quantized group; read through the concatenating properties below
+        self._kcodes, self._kscale, self._kzero = [], [], []
+        self._vcodes, self._vscale, self._vzero, self._replaced = [], [], [], []
         self.tracer = OutlierTracer(p.pool, p.evict_cap)
+
+    @staticmethod
+    def _cat(parts, shape, dtype):
+        return np.concatenate(parts) if parts else np.zeros(shape, dtype=dtype)
+
+    @property
+    def k16(self) -> np.ndarray:
+        if len(self._k16) > 1:
+            self._k16 = [np.concatenate(self._k16)]
+        return self._k16[0]
+
+    @property
+    def v16(self) -> np.ndarray:
+        if len(self._v16) > 1:
+            self._v16 = [np.concatenate(self._v16)]
+        return self._v16[0]
+
+    @property
+    def kcodes(self):
+        return self._cat(self._kcodes, (0, self.p.head_dim), np.uint8)
+
+    @property
+    def kscale(self):  # per group [n_q/G][d]
+        return self._cat(self._kscale, (0, self.p.head_dim), np.float16)
+
+    @property
+    def kzero(self):
+        return self._cat(self._kzero, (0, self.p.head_dim), np.float16)
+
+    @property
+    def vcodes(self):
+        return self._cat(self._vcodes, (0, self.p.head_dim), np.uint8)
+
+    @property
+    def vscale(self):  # per token [n_q][d/gv]
+        return self._cat(self._vscale, (0, self.p.head_dim // self.p.gv), np.float16)
+
+    @property
+    def vzero(self):
+        return self._cat(self._vzero, (0, self.p.head_dim // self.p.gv), np.float16)
+
+    @property
+    def replaced(self):  # token was admitted to the pool
+        return self._cat(self._replaced, (0,), bool)
 
     @property
     def T(self) -> int:
-        return self.k16.shape[0]
+        return sum(x.shape[0] for x in self._k16)
 
     def append(self, k16: np.ndarray, v16: np.ndarray) -> None:
         """Append fp16 rows; quantize every group that leaves the residual window."""
-        self.k16 = np.concatenate([self.k16, np.asarray(k16, dtype=np.float16)])
-        self.v16 = np.concatenate([self.v16, np.asarray(v16, dtype=np.float16)])
+        self._k16.append(np.asarray(k16, dtype=np.float16))
+        self._v16.append(np.asarray(v16, dtype=np.float16))
         G = self.p.group
-        while self.n_q < n_quantized(self.T, self.p.residual, G):
+        T = self.T
+        while self.n_q < n_quantized(T, self.p.residual, G):
             self._quantize_group(self.n_q)
             self.n_q += G
 
@@ -299,13 +340,13 @@ class UnitCache:
                 replaced[i] = True
         kc, ks, kz = quantize_key_group(kg, self.p.bits)
         vc, vs, vz = quantize_value_rows(vg, self.p.bits, self.p.gv)
-        self.kcodes = np.concatenate([self.kcodes, kc])
-        self.kscale = np.concatenate([self.kscale, ks[None]])
-        self.kzero = np.concatenate([self.kzero, kz[None]])
-        self.vcodes = np.concatenate([self.vcodes, vc])
-        self.vscale = np.concatenate([self.vscale, vs])
-        self.vzero = np.concatenate([self.vzero, vz])
-        self.replaced = np.concatenate([self.replaced, replaced])
+        self._kcodes.append(kc)
+        self._kscale.append(ks[None])
+        self._kzero.append(kz[None])
+        self._vcodes.append(vc)
+        self._vscale.append(vs)
+        self._vzero.append(vz)
+        self._replaced.append(replaced)
 
     def dequantized_kv(self):
         """K_hat, V_hat [T][d] in fp64, each cached token exactly once (R8)."""

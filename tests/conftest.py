@@ -18,3 +18,14 @@ def golden():
     import json
     with open(os.path.join(ROOT, "tests", "golden", "page_values.json")) as f:
         return json.load(f)
+
+
+@pytest.fixture(scope="session")
+def kvq():
+    """The ABI binding with libkvq.so loaded (built first only if it is missing)."""
+    from kv_cache_compression_kvq_amd import abi
+    if not os.path.exists(abi.LIB_PATH):
+        from kv_cache_compression_kvq_amd import build
+        build.build()
+    abi.lib()
+    return abi
