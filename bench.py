@@ -1,0 +1,373 @@
+#!/usr/bin/env python3
+"""Benchmark: decode steps over a 2/4-bit compressed KV cache on one MI355X.
+
+A step is one decode step of one attention layer at the chosen workload, every
+row of the hot path it touches included:
+  * append the step's new token to every (batch, KV head) unit (residual ring;
+    when a group leaves the window: OTT scoring / pool scan if the workload has
+    a pool, quantize + pack);
+  * attention over the compressed cache (fused dequant + split-K kernel, merge);
+  * for workloads with H2O scores (minikv): accumulate the scores instead of
+    appending, then select heavy hitters (top-k + recent window).
+
+Inputs are seeded synthetic tensors of the workload's shapes, resident in HBM
+before timing. The cache is replicated past the 256 MB Infinity Cache and the
+steps rotate over the replicas, as the layers of a model would, so that no step
+reads data left cached by the previous one. The timed steps are captured once
+in a HIP graph and replayed (the loop is launch-bound otherwise).
+
+value = algorithmic bytes of all timed steps / their time (GB/s). The roofline
+entry times the fused attention kernel alone through HIP events attached to its
+dispatch. The CPU baseline times the oracle on a bounded sample of units.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "compressed-KV decode attention GB/s and % of MI355X HBM peak; tokens·heads/s"
+HBM_PEAK_GBS = 8000.0
+REPLICA_BYTES = 600e6  # total cache bytes the rotation spans (> 256 MB Infinity Cache)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="llama8b")
+    p.add_argument("--no-graph", action="store_true", help="launch the timed steps eagerly")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="timed CPU work for the oracle baseline (0 disables it)")
+    p.add_argument("--kernel-reps", type=int, default=4,
+                   help="event-timed attention launches per replica for the roofline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 256 MiB device copy (counter calibration runs)")
+    return p.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t helpers on the HIP runtime torch has loaded (same soname)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        f = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(f), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value
+
+    def destroy(self, e: int) -> None:
+        self.lib.hipEventDestroy(e)
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("kvq_decode.hip", "kvq_internal.h"):
+        with open(os.path.join(ROOT, "kv_cache_compression_kvq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_entry(workload: str, kernel_alg_bytes: float):
+    """HBM traffic of the attention kernel from the committed rocprofv3 counter
+    summary, when it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha") != source_sha():
+        return None
+    return {"fetch_bytes": t["fetch_bytes"], "write_bytes": t["write_bytes"],
+            "total_bytes": t["fetch_bytes"] + t["write_bytes"],
+            "vs_algorithmic": (t["fetch_bytes"] + t["write_bytes"]) / kernel_alg_bytes,
+            "copy_scale": t["copy_scale"], "source": os.path.relpath(path, ROOT)}
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle (numpy, fp64 attention, one thread) on a bounded sample of
+    units: per sampled unit, repeated decode steps of the same kind the GPU
+    times. Setup (quantizing the prefix) is not timed."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from kv_cache_compression_kvq_amd import bytes_model as BM, synth
+    from oracle import kvq_oracle as O
+
+    p = O.CacheParams(bits=w.bits, group=w.group, residual=w.residual, pool=w.pool,
+                      evict_cap=w.evict_cap, head_dim=w.head_dim)
+    units = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
+    rng = np.random.default_rng(1)
+    pick = [units[i] for i in rng.permutation(len(units))[: min(4, len(units))]]
+    r = w.gqa
+    total_t, total_bytes, steps, used = 0.0, 0, 0, set()
+    with threadpool_limits(limits=1):
+        caches = {}
+        for (b, h) in pick:
+            k, v = synth.unit_kv(w, b, h)
+            uc = O.UnitCache(p)
+            uc.append(k, v)
+            caches[(b, h)] = uc
+        q = synth.queries(w)
+        n_max = 4000
+        new_tok = {} if w.h2o else {
+            u: synth.unit_kv(w, u[0], u[1], n=n_max, start=w.tokens + 1) for u in pick}
+        i = 0
+        while total_t < seconds and steps < n_max:
+            b, h = pick[i % len(pick)]
+            uc = caches[(b, h)]
+            t0 = time.perf_counter()
+            if not w.h2o:
+                j = i // len(pick)
+                uc.append(new_tok[(b, h)][0][j:j + 1], new_tok[(b, h)][1][j:j + 1])
+            K, V = uc.dequantized_kv()
+            _, pr = O.unit_attention(K, V, q[b, h * r:(h + 1) * r])
+            if w.h2o:
+                acc = O.h2o_increment(pr).astype(np.float32)[None]
+                O.topk_keep(acc, w.topk_k, w.recent)
+            total_t += time.perf_counter() - t0
+            pools = len(uc.tracer.pool) + len(uc.tracer.evicted)
+            total_bytes += BM.decode_step_bytes(
+                units=1, gqa=r, head_dim=w.head_dim, tokens=uc.T, bits=w.bits, group=w.group,
+                residual=w.residual, pool_tokens=pools, h2o=w.h2o).total
+            steps += 1
+            used.add((b, h))
+            i += 1
+    return {"value": total_bytes / total_t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} single-unit decode steps over {len(used)} of {len(units)} "
+                      f"(batch, KV head) units of the same workload, "
+                      f"{'H2O scores + top-k' if w.h2o else 'append one token + attention'}, "
+                      f"numpy fp64, BLAS limited to 1 thread, {total_t:.1f} s"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the attention units shard with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from kv_cache_compression_kvq_amd import abi, bytes_model as BM, synth
+
+    if not os.path.exists(abi.LIB_PATH):
+        from kv_cache_compression_kvq_amd import build as B
+        B.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    U, r, d = w.units, w.gqa, w.head_dim
+    hip = HipEvents()
+
+    # ---- inputs, resident in HBM before timing -----------------------------
+    K, V = synth.all_kv(w)
+    Kd = torch.from_numpy(K).to(dev)
+    Vd = torch.from_numpy(V).to(dev)
+    del K, V
+    append_mode = not w.h2o
+    n_total = args.warmup + args.steps
+    cfg0 = abi.make_config(bits=w.bits, group=w.group, residual=w.residual, pool=w.pool,
+                           evict_cap=w.evict_cap, head_dim=d, n_q_heads=w.n_q_heads,
+                           n_kv_heads=w.n_kv_heads, batch=w.batch, max_tokens=w.tokens)
+    cache_bytes0 = abi.cache_bytes(cfg0)
+    n_rep = max(2, math.ceil(REPLICA_BYTES / cache_bytes0))
+    per_rep = math.ceil(n_total / n_rep) if append_mode else 0
+    max_tokens = w.tokens + per_rep
+    reps = []
+    for _ in range(n_rep):
+        cfg = abi.make_config(bits=w.bits, group=w.group, residual=w.residual, pool=w.pool,
+                              evict_cap=w.evict_cap, head_dim=d, n_q_heads=w.n_q_heads,
+                              n_kv_heads=w.n_kv_heads, batch=w.batch, max_tokens=max_tokens)
+        arena = torch.empty(abi.cache_bytes(cfg), dtype=torch.uint8, device=dev)
+        h = abi.cache_init(cfg, arena)
+        abi.quantize_append(h, Kd, Vd, w.tokens)
+        acc = torch.zeros((w.batch, w.n_kv_heads, w.tokens), device=dev) if w.h2o else None
+        reps.append({"arena": arena, "h": h, "acc": acc})
+    del Kd, Vd
+    if append_mode:
+        ks = torch.empty((n_total, w.batch, w.n_kv_heads, 1, d), dtype=torch.float16)
+        vs = torch.empty_like(ks)
+        for i in range(n_total):
+            a, b = synth.step_kv(w, i)
+            ks[i], vs[i] = torch.from_numpy(a), torch.from_numpy(b)
+        ks, vs = ks.to(dev), vs.to(dev)
+    n_q_rot = 8
+    qs = torch.stack([torch.from_numpy(synth.queries(w, i)) for i in range(n_q_rot)]).to(dev)
+    out = torch.empty((w.batch, w.n_q_heads, d), device=dev)
+    # workspace for the largest T any replica reaches
+    hmax = abi.Cache()
+    ctypes.memmove(ctypes.byref(hmax), ctypes.byref(reps[0]["h"]), ctypes.sizeof(hmax))
+    hmax.tokens = max_tokens
+    hmax.n_quant = max(0, (max_tokens - w.residual) // w.group * w.group)
+    ws = torch.empty(abi.decode_workspace(hmax, w.h2o), dtype=torch.uint8, device=dev)
+    k_hh = w.topk_k
+    idx = torch.empty((U, k_hh + w.recent), dtype=torch.int32, device=dev) if w.h2o else None
+    torch.cuda.synchronize()
+
+    step_bytes = []   # algorithmic bytes of each executed step (host bookkeeping)
+    step_tokens = []  # cached token x KV-head entries read by each step
+
+    def pool_tokens(rep):
+        if w.pool == 0:
+            return 0
+        cnt = rep["arena"][rep["h"].off_counters:rep["h"].off_counters + 16 * U]
+        c = cnt.view(torch.int32).view(U, 4).cpu()
+        return int(c[:, 0].sum() + c[:, 1].sum())
+
+    pools_now = [pool_tokens(rp) for rp in reps]
+
+    def decode_bytes(h, pools):
+        return BM.decode_step_bytes(units=U, gqa=r, head_dim=d, tokens=h.tokens, bits=w.bits,
+                                    group=w.group, residual=w.residual, pool_tokens=pools,
+                                    h2o=w.h2o).total
+
+    def step(i, ev=(None, None)):
+        rep = reps[i % n_rep]
+        h = rep["h"]
+        nb = 0
+        if append_mode:
+            nq0 = h.n_quant
+            abi.quantize_append(h, ks[i], vs[i], 1)
+            nb += BM.append_bytes(units=U, head_dim=d, n_new=1, bits=w.bits, group=w.group,
+                                  groups_packed=(h.n_quant - nq0) // w.group)
+        q = qs[i % n_q_rot]
+        if ev[0] is not None:
+            abi.decode_attention_timed(rep["h"], q, out, rep["acc"], ws, ev[0], ev[1])
+        else:
+            abi.decode_attention(rep["h"], q, out, rep["acc"], ws)
+        nb += decode_bytes(h, pools_now[i % n_rep])
+        if w.h2o:
+            abi.topk_evict(rep["acc"], U, w.tokens, k_hh, w.recent, idx)
+            nb += BM.topk_bytes(rows=U, tokens=w.tokens, k=k_hh, w=w.recent)
+        step_bytes.append(nb)
+        step_tokens.append(U * h.tokens)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    step_bytes.clear()
+    step_tokens.clear()
+
+    use_graph = not args.no_graph
+    if use_graph:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=cap):
+            for j in range(args.steps):
+                step(args.warmup + j)
+        torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    if use_graph:
+        g.replay()
+    else:
+        for j in range(args.steps):
+            step(args.warmup + j)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    if use_graph:
+        # the replayed steps must give what an eager launch gives on the same state
+        last = reps[(args.warmup + args.steps - 1) % n_rep]
+        ref = torch.empty_like(out)
+        got = out.clone()
+        acc_copy = last["acc"].clone() if w.h2o else None
+        abi.decode_attention(last["h"], qs[(args.warmup + args.steps - 1) % n_q_rot], ref,
+                             acc_copy, ws)
+        torch.cuda.synchronize()
+        if not torch.equal(got, ref):
+            raise RuntimeError("graph replay result differs from an eager launch")
+
+    # ---- the fused attention kernel alone, timed by events on its dispatch ----
+    evs = [(hip.create(), hip.create()) for _ in range(args.kernel_reps * n_rep)]
+    kbytes = []
+    for i, ev in enumerate(evs):
+        rep = reps[i % n_rep]
+        abi.decode_attention_timed(rep["h"], qs[i % n_q_rot], out, rep["acc"], ws, ev[0], ev[1])
+        kbytes.append(decode_bytes(rep["h"], pools_now[i % n_rep]))
+    torch.cuda.synchronize()
+    kms = [hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    kernel_us = 1e3 * sum(kms) / len(kms)
+    kernel_bytes = sum(kbytes) / len(kbytes)
+    achieved = kernel_bytes / (kernel_us * 1e-6) / 1e9
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    value = sum(step_bytes) / (total_ms * 1e-3) / 1e9
+    tok_heads = sum(step_tokens) / (total_ms * 1e-3)
+    h0 = reps[0]["h"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": d, "tokens": w.tokens,
+                   "bits": w.bits, "group": w.group, "residual": w.residual, "pool": w.pool,
+                   "h2o": w.h2o, "replicas": n_rep, "hip_graph": use_graph,
+                   "step": "append 1 token + attention" if append_mode
+                   else "attention with H2O scores + top-k"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_heads_per_s": round(tok_heads, 1),
+        "query_head_scores_per_s": round(tok_heads * r, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_entry(w.name, kernel_bytes),
+                     "kernel": "decode_kernel", "kernel_us": round(kernel_us, 3),
+                     "kernel_alg_bytes": int(kernel_bytes), "source_sha": source_sha()},
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -197,6 +197,16 @@ kvq_status kvq_decode_attention(const kvq_cache* h, const void* d_q, float* d_ou
                                 float* d_acc, void* d_ws, size_t ws_bytes, void* stream);
 
 /*
+ * kvq_decode_attention, additionally recording ev_start and ev_stop (hipEvent_t
+ * handles created by the caller, or NULL) at the start and end of the fused
+ * attention kernel's own execution, so that it can be timed without the merge
+ * kernel and launch gaps. Same arguments, results and errors otherwise.
+ */
+kvq_status kvq_decode_attention_timed(const kvq_cache* h, const void* d_q, float* d_out,
+                                      float* d_acc, void* d_ws, size_t ws_bytes,
+                                      void* ev_start, void* ev_stop, void* stream);
+
+/*
  * Heavy-hitter selection on fp32 scores (device [rows][T]): for each row keep
  * the k largest scores among indices [0, T - w), ties broken toward the
  * larger index, plus the w most recent indices [T - w, T). Writes device

@@ -24,7 +24,8 @@ KVQ_ELAUNCH = -5
 
 # Entry points declared in include/kvq.h.
 EXPORTS = ("kvq_status_string", "kvq_cache_bytes", "kvq_cache_init", "kvq_quantize_append",
-           "kvq_decode_workspace", "kvq_decode_attention", "kvq_topk_evict", "kvq_unpack_codes")
+           "kvq_decode_workspace", "kvq_decode_attention", "kvq_decode_attention_timed",
+           "kvq_topk_evict", "kvq_unpack_codes")
 
 
 class Config(ctypes.Structure):
@@ -56,6 +57,9 @@ def lib() -> ctypes.CDLL:
     """The loaded libkvq.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        # torch first: libkvq then binds to the HIP runtime torch already loaded
+        # (same soname), so tensors, streams and events are shared with it.
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"libkvq.so not built ({LIB_PATH}); run __graft_entry__.build()")
         L = ctypes.CDLL(LIB_PATH)
@@ -68,6 +72,7 @@ def lib() -> ctypes.CDLL:
             "kvq_quantize_append": [ctypes.POINTER(Cache), P, P, I32, P],
             "kvq_decode_workspace": [ctypes.POINTER(Cache), I32, ctypes.POINTER(SZ)],
             "kvq_decode_attention": [ctypes.POINTER(Cache), P, P, P, P, SZ, P],
+            "kvq_decode_attention_timed": [ctypes.POINTER(Cache), P, P, P, P, SZ, P, P, P],
             "kvq_topk_evict": [P, I32, I32, I32, I32, P, P],
             "kvq_unpack_codes": [ctypes.POINTER(Cache), P, P, P],
         }
@@ -142,6 +147,14 @@ def decode_attention(h: Cache, q, out, acc, ws, ws_bytes: int | None = None, str
     nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
     _check("kvq_decode_attention", lib().kvq_decode_attention(
         ctypes.byref(h), _ptr(q), _ptr(out), _ptr(acc), _ptr(ws), nbytes, _stream(stream)))
+
+
+def decode_attention_timed(h: Cache, q, out, acc, ws, ev_start: int, ev_stop: int,
+                           ws_bytes: int | None = None, stream=None) -> None:
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check("kvq_decode_attention_timed", lib().kvq_decode_attention_timed(
+        ctypes.byref(h), _ptr(q), _ptr(out), _ptr(acc), _ptr(ws), nbytes, ev_start, ev_stop,
+        _stream(stream)))
 
 
 def topk_evict(scores, rows: int, T: int, k: int, w: int, idx, stream=None) -> None:

@@ -23,6 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -146,8 +146,11 @@ DecodePlan plan_decode(const kvq_cache* h, bool want_scores) {
         if (s > kMaxQuantSplits) s = kMaxQuantSplits;
         if (s < 1) s = 1;
     }
+    const int64_t fp16_rows = (h->tokens - h->n_quant) +
+                              (h->cfg.pool > 0 ? h->cfg.pool + h->cfg.evict_cap : 0);
     p.splits_q = (int32_t)s;
-    p.splits = (int32_t)s + 1;
+    p.fp16_tiles = (int32_t)(fp16_rows > 0 ? (fp16_rows + 63) / 64 : 1);
+    p.splits = p.splits_q + p.fp16_tiles;
     p.part_floats = U * p.splits * r * (kHeadDim + 2);
     p.logit_floats = want_scores ? U * r * h->tokens : 0;
     p.ws_bytes = align_up((uint64_t)p.part_floats * 4) + (uint64_t)p.logit_floats * 4;
@@ -230,15 +233,22 @@ kvq_status kvq_decode_workspace(const kvq_cache* h, int32_t want_scores, size_t*
     return KVQ_OK;
 }
 
-kvq_status kvq_decode_attention(const kvq_cache* h, const void* d_q, float* d_out, float* d_acc,
-                                void* d_ws, size_t ws_bytes, void* stream) {
+kvq_status kvq_decode_attention_timed(const kvq_cache* h, const void* d_q, float* d_out,
+                                      float* d_acc, void* d_ws, size_t ws_bytes, void* ev_start,
+                                      void* ev_stop, void* stream) {
     if (!valid_handle(h) || !d_q || !d_out || !d_ws) return KVQ_EINVAL;
     if (h->tokens < 1) return KVQ_EINVAL;
     const DecodePlan p = plan_decode(h, d_acc != nullptr);
     if (ws_bytes < p.ws_bytes) return KVQ_EWORKSPACE;
     return launch_status(launch_decode(view_of(h), h->tokens, h->n_quant, p,
                                        static_cast<const uint16_t*>(d_q), d_out, d_acc, d_ws,
-                                       stream));
+                                       ev_start, ev_stop, stream));
+}
+
+kvq_status kvq_decode_attention(const kvq_cache* h, const void* d_q, float* d_out, float* d_acc,
+                                void* d_ws, size_t ws_bytes, void* stream) {
+    return kvq_decode_attention_timed(h, d_q, d_out, d_acc, d_ws, ws_bytes, nullptr, nullptr,
+                                      stream);
 }
 
 kvq_status kvq_topk_evict(const float* d_scores, int32_t rows, int32_t T, int32_t k, int32_t w,

@@ -47,7 +47,8 @@ CacheView view_of(const kvq_cache* h);
 // Split plan of one decode call.
 struct DecodePlan {
     int32_t splits_q;    // quantized-partition splits per unit (0 when n_q == 0)
-    int32_t splits;      // splits_q + 1 (the last one is the fp16 partition)
+    int32_t fp16_tiles;  // 64-row tiles of the fp16 partition (ring + pools)
+    int32_t splits;      // splits_q + fp16_tiles partial records per unit
     int64_t part_floats; // partial records: U * splits * r * (d + 2)
     int64_t logit_floats;// U * r * T when scores are wanted
     size_t ws_bytes;
@@ -60,7 +61,8 @@ int launch_init(const CacheView& v, void* stream);
 int launch_append(const CacheView& v, const uint16_t* k_new, const uint16_t* v_new,
                   int64_t t_old, int32_t n_new, int64_t nq_old, int64_t nq_new, void* stream);
 int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& plan,
-                  const uint16_t* q, float* out, float* acc, void* ws, void* stream);
+                  const uint16_t* q, float* out, float* acc, void* ws, void* ev_start,
+                  void* ev_stop, void* stream);
 int launch_topk(const float* scores, int32_t rows, int32_t T, int32_t k, int32_t w,
                 int32_t* idx, void* stream);
 int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, void* stream);
