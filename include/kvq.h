@@ -86,7 +86,7 @@ const char* kvq_status_string(kvq_status status);
  *   head_dim    d, must be 128
  *   n_q_heads   Hq, n_kv_heads Hkv: Hq / Hkv = r in {1, 2, 4}
  *   batch       B >= 1
- *   max_tokens  capacity in tokens per unit, >= 1
+ *   max_tokens  capacity in tokens per unit, in [1, 2^24]
  */
 typedef struct kvq_config {
     int32_t bits;

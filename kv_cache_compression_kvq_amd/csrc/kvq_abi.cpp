@@ -33,6 +33,7 @@ kvq_status check_config(const kvq_config* c) {
     if (c->head_dim != kHeadDim) return KVQ_EUNSUPPORTED;
     if (r != 1 && r != 2 && r != 4) return KVQ_EUNSUPPORTED;
     if (c->pool > kMaxPool || c->evict_cap > kMaxEvict) return KVQ_EUNSUPPORTED;
+    if (c->max_tokens > kMaxTokens) return KVQ_EUNSUPPORTED;
     if ((int64_t)c->residual + c->group + c->pool + c->evict_cap > kMaxFp16Rows)
         return KVQ_EUNSUPPORTED;
     return KVQ_OK;
@@ -126,26 +127,16 @@ CacheView view_of(const kvq_cache* h) {
 }
 
 DecodePlan plan_decode(const kvq_cache* h, bool want_scores) {
-    // Split-K over the quantized tokens: about kTargetBlocks workgroups of four
-    // wavefronts in total, each wavefront taking whole key groups, so that a
-    // step fills the 256 compute units even for a single long sequence.
-    static const int64_t kTargetBlocks = [] {
-        const char* s = std::getenv("KVQ_DECODE_BLOCKS");
-        long v = s ? std::strtol(s, nullptr, 10) : 0;
-        return (int64_t)(v > 0 ? v : 1024);
-    }();
+    // Split-K over the quantized tokens. Every wavefront of a split takes
+    // whole key groups, four wavefronts per block, so a unit has at most
+    // ceil(groups / 4) useful splits; the launch picks how many it uses (one
+    // resident round of blocks), and the workspace covers the largest choice.
     DecodePlan p{};
     const int64_t U = (int64_t)h->cfg.batch * h->cfg.n_kv_heads;
     const int64_t r = h->cfg.n_q_heads / h->cfg.n_kv_heads;
     const int64_t groups = h->n_quant / h->cfg.group;
-    int64_t s = 0;
-    if (groups > 0) {
-        s = (kTargetBlocks + U - 1) / U;
-        const int64_t by_work = (groups + 3) / 4;
-        if (s > by_work) s = by_work;
-        if (s > kMaxQuantSplits) s = kMaxQuantSplits;
-        if (s < 1) s = 1;
-    }
+    int64_t s = groups > 0 ? (groups + 3) / 4 : 0;
+    if (s > kMaxQuantSplits) s = kMaxQuantSplits;
     const int64_t fp16_rows = (h->tokens - h->n_quant) +
                               (h->cfg.pool > 0 ? h->cfg.pool + h->cfg.evict_cap : 0);
     p.splits_q = (int32_t)s;

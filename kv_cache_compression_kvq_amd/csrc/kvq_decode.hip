@@ -27,6 +27,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -41,11 +43,62 @@ constexpr int D = kHeadDim;
 constexpr int kRec = D + 2;  // partial record: o[d], m, l
 constexpr int kMaxSplits = 1056;
 constexpr int kH2OChunk = 2048;
-constexpr int kWaveFloats = 1024;  // per-wavefront LDS of the quantized path (4 KB)
-// LDS of one block: the fp16 partition's K/V tiles, queries and probabilities
-// (64 rows x 2 x 256 B + 4 x 256 B + 4 x 256 B), or 4 wavefronts x 4 KB.
-constexpr int kSmemFloats = (64 * D * 2 * 2 + 4 * D * 2 + 4 * 64 * 4) / 4;
-static_assert(kSmemFloats >= 4 * kWaveFloats, "LDS layout");
+// LDS of the fp16 partition: K/V tiles, queries and probabilities
+// (64 rows x 2 x 256 B + 4 x 256 B + 4 x 256 B).
+constexpr int kFp16Bytes = 64 * D * 2 * 2 + 4 * D * 2 + 4 * 64 * 4;
+
+// Per-wavefront LDS of the quantized path: a ring of kStages chunk stages
+// filled by direct global->LDS loads (codes, value scales, key scales, pool
+// mask word); after the loop the same bytes hold the output accumulators. The
+// folded-query table and the probability exchange live in LDS objects of their
+// own, so that writing them never waits on the ring's copies in flight.
+template <int BITS>
+struct Ring {
+    static constexpr int kStages = 3;
+    static constexpr int kCodes = 128 * BITS * 4;          // packed codes of one chunk
+    static constexpr int kMeta = 1024;                      // value (<= 512 B) + key (512 B) scales
+    static constexpr int kStage = 2 * kCodes + kMeta + 16;  // + pool mask word
+    static constexpr int kLoads = 2 * (kCodes / 1024) + 2;  // loads issued per stage
+    static constexpr int kWave = kStages * kStage;          // ring bytes per wavefront
+    static constexpr int kBlock = 4 * kWave > kFp16Bytes ? 4 * kWave : kFp16Bytes;
+    static_assert(kWave >= (2048 + 48) * 4, "epilogue fits the wavefront's ring");
+};
+
+__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
+    // lane i's 16 bytes land at lds + 16 * i
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)g,
+        (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)g,
+        (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+// Wait until at most N of this wavefront's vector memory operations are in
+// flight (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// LDS address of a pointer into a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Reads of a ring stage. They are issued as inline assembly, after the
+// stage's explicit vmcnt wait, because the compiler cannot tell which ring
+// slot a global->LDS copy in flight targets and would otherwise wait for all
+// of them; ring_done() then waits for the reads and ties their results.
+__device__ __forceinline__ u32x4 ring_read(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+__device__ __forceinline__ uint32_t ring_read32(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
 
 struct DecodeArgs {
     const uint32_t* kq;
@@ -100,6 +153,24 @@ __device__ __forceinline__ float dpp(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
                                                                  CTRL, 0xF, 0xF, false));
 }
+// x at lanes l and l ^ 32 (swap32) or l and l ^ 16 (swap16), returned as the
+// pair (a, b) in either order: the gfx950 permlane swaps exchange rows of two
+// registers on the VALU, with no LDS round trip. Written as inline asm because
+// the compiler's builtin for these drops the second result.
+__device__ __forceinline__ void swap32(float x, float& a, float& b) {
+    a = x;
+    b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap16(float x, float& a, float& b) {
+    a = x;
+    b = x;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_x32(float x) { float a, b; swap32(x, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float max_x16(float x) { float a, b; swap16(x, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float sum_x32(float x) { float a, b; swap32(x, a, b); return a + b; }
+__device__ __forceinline__ float sum_x16(float x) { float a, b; swap16(x, a, b); return a + b; }
 __device__ __forceinline__ float readlane(float x, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
@@ -167,18 +238,29 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
     const int N = a.pool, E = a.evict_cap, RB = a.ring_slots;
     const int64_t base = (int64_t)tile * 64;
     const int cnt = (int)(ntot - base < 0 ? 0 : ntot - base < 64 ? ntot - base : 64);
-    auto row_of = [&](int64_t li, const uint16_t* ring, const uint16_t* pool,
+    // Row li of the partition: ring slot (n_q + li) % RB, or a pool / extra-pool row.
+    const int64_t slot0 = (a.n_q + base) % RB;
+    auto row_of = [&](int i, const uint16_t* ring, const uint16_t* pool,
                       const uint16_t* ev) -> const uint16_t* {
-        if (li < nres) return ring + ((int64_t)u * RB + (a.n_q + li) % RB) * D;
+        const int64_t li = base + i;
+        if (li < nres) {
+            int64_t sl = slot0 + i;
+            if (sl >= RB) sl -= RB;
+            return ring + ((int64_t)u * RB + sl) * D;
+        }
         if (li < nres + pc) return pool + ((int64_t)u * N + (li - nres)) * D;
         return ev + ((int64_t)u * E + (li - nres - pc)) * D;
     };
-    for (int e = tid; e < cnt * 16; e += 256) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int e = tid + 256 * r;
         const int i = e / 16, part = e % 16;
-        reinterpret_cast<uint4*>(kt)[e] =
-            reinterpret_cast<const uint4*>(row_of(base + i, a.kring, a.pool_k, a.ev_k))[part];
-        reinterpret_cast<uint4*>(vt)[e] =
-            reinterpret_cast<const uint4*>(row_of(base + i, a.vring, a.pool_v, a.ev_v))[part];
+        if (i < cnt) {
+            reinterpret_cast<uint4*>(kt)[e] =
+                reinterpret_cast<const uint4*>(row_of(i, a.kring, a.pool_k, a.ev_k))[part];
+            reinterpret_cast<uint4*>(vt)[e] =
+                reinterpret_cast<const uint4*>(row_of(i, a.vring, a.pool_v, a.ev_v))[part];
+        }
     }
     __syncthreads();
     if (h >= R) return;
@@ -215,13 +297,22 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
     const float l = wave_sum(p);
     ps[h * 64 + lane] = p;
     wave_lds_fence();
+    // Outputs: lane owns channels 2*lane, 2*lane+1; p is 0 for rows past cnt.
     float o0 = 0.f, o1 = 0.f;
     const uint32_t* vw = reinterpret_cast<const uint32_t*>(vt) + lane;
-    for (int i = 0; i < cnt; ++i) {
-        const uint32_t w = vw[i * (D / 2)];
-        const float pi = ps[h * 64 + i];
-        o0 += pi * h2f(w & 0xFFFF);
-        o1 += pi * h2f(w >> 16);
+    const float* ph = ps + h * 64;
+    for (int i0 = 0; i0 < cnt; i0 += 8) {
+        const floatx4 pa = *reinterpret_cast<const floatx4*>(ph + i0);
+        const floatx4 pb = *reinterpret_cast<const floatx4*>(ph + i0 + 4);
+        const float pv[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+        uint32_t wv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wv[i] = i0 + i < cnt ? vw[(i0 + i) * (D / 2)] : 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            o0 += pv[i] * h2f(wv[i] & 0xFFFF);
+            o1 += pv[i] * h2f(wv[i] >> 16);
+        }
     }
     float* rec = a.part + (((int64_t)u * a.splits + a.splits_q + tile) * R + h) * kRec;
     rec[2 * lane] = o0;
@@ -232,28 +323,25 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
     }
 }
 
-// Per-lane data of one 32-token chunk (and, at the first chunk of a key
-// group, the lane's eight key scale/zero pairs), loaded one chunk ahead.
-struct Chunk {
-    u32x4 km0, km1;  // key (scale, zero) of channels cb0 .. cb0+7
-    u32x4 wk0, wk1;  // packed key codes (second half only for 4-bit)
-    u32x4 wv0, wv1;  // packed value codes
-    u32x4 vm0, vm1;  // value (scale, zero) of the lane's 8 token slots
-    uint32_t mw;     // pool mask of the chunk (wave-uniform)
-};
-
 template <int BITS, int R, int G>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     constexpr int NG = D / G;        // value groups per token
     constexpr int CPG = G / 32;      // chunks per key group
     constexpr int WPC = 128 * BITS;  // words per chunk
     constexpr float F = (float)(1 << BITS);
+    // With r = 4 the 16 MFMA columns hold 4 copies of each head's logits;
+    // each copy then exponentiates a quarter of the tokens.
+    constexpr bool kSplitExp = R == 4;
     // Codes become fp16 operands F + code with two bit operations; the masks
     // live in VGPRs so that the pair becomes one v_and_or_b32.
     constexpr uint32_t kMagicC = BITS == 2 ? 0x44004400u : 0x4C004C00u;
     constexpr uint32_t kMaskC = BITS == 2 ? 0x03000300u : 0x03C003C0u;
-    __shared__ __align__(16) float smem[kSmemFloats];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    using RG = Ring<BITS>;
+    __shared__ __align__(16) float smem[RG::kBlock / 4];
+    __shared__ __align__(16) unsigned char s_btab[4][2048];
+    __shared__ __align__(16) float s_pbuf[4][128];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if ((int)blockIdx.x < a.units * a.fp16_tiles) {
         fp16_tile<R>(a, blockIdx.x / a.fp16_tiles, blockIdx.x % a.fp16_tiles, smem);
         return;
@@ -269,18 +357,29 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int idx = blockIdx.x - a.units * a.fp16_tiles;
     const int u = idx / a.splits_q, split = idx % a.splits_q;
     const int b = u / a.n_kv_heads, hk = u % a.n_kv_heads;
-    const int64_t groups = a.n_q / G;
-    const int64_t gs0 = split * groups / a.splits_q, gs1 = (split + 1) * groups / a.splits_q;
-    const int64_t my_groups = gs1 - gs0 > wave ? (gs1 - gs0 - wave + 3) / 4 : 0;
-    const int64_t n_items = my_groups * CPG;
+    const uint32_t groups = (uint32_t)(a.n_q / G);
+    const uint32_t gs0 = (uint32_t)((int64_t)split * groups / a.splits_q);
+    const uint32_t gs1 = (uint32_t)((int64_t)(split + 1) * groups / a.splits_q);
+    const uint32_t my_groups = gs1 - gs0 > (uint32_t)wave ? (gs1 - gs0 - wave + 3) / 4 : 0;
+    const uint32_t n_items = my_groups * CPG;
+
+    // Per-unit base pointers (wave-uniform); per-lane offsets stay 32-bit.
+    const uint32_t* kq_u = a.kq + (int64_t)u * a.chunks * WPC;
+    const uint32_t* vq_u = a.vq + (int64_t)u * a.chunks * WPC;
+    const uint32_t* km_u = a.kmeta + (int64_t)u * a.key_groups * D;
+    const uint32_t* vm_u = a.vmeta + (int64_t)u * a.chunks * NG * 32;
+    const uint32_t* mk_u = a.mask + (int64_t)u * a.chunks;
 
     // MFMA lane roles: j = column / row within a 16-lane row, kb = k-block.
     const int j = lane & 15, kb = lane >> 4;
     // Query-fold role: head hb, channels cb0 .. cb0+7 (k-step ksb, k-block kbb).
     const int hb = lane % R, kap = (lane >> 2) & 15, ksb = kap >> 2, kbb = kap & 3;
     const int cb0 = 32 * ksb + 8 * kbb;
-    // Softmax / value-operand role: row j = (head j % R, value group gs).
+    // Softmax / value-operand role: row j = (head j % R, value group gs); with
+    // kSplitExp, copy gr of the head owns token slots 2gr, 2gr+1.
     const int gs = (j / R) % NG;
+    const int gr = j >> 2;
+    const int own_tok = 16 * (gr >> 1) + 4 * kb + 2 * (gr & 1);  // first owned token
 
     float qv[8];
     {
@@ -294,49 +393,61 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         }
     }
 
-    auto load = [&](int64_t k, Chunk& c) {
-        const int64_t gi = gs0 + wave + 4 * (k / CPG);
-        const int cc = (int)(k % CPG);
-        const int64_t ch = gi * CPG + cc;
-        if (cc == 0) {
-            const uint32_t* km = a.kmeta + ((int64_t)u * a.key_groups + gi) * D + cb0;
-            c.km0 = *reinterpret_cast<const u32x4*>(km);
-            c.km1 = *reinterpret_cast<const u32x4*>(km + 4);
-        }
-        const uint32_t* kc = a.kq + ((int64_t)u * a.chunks + ch) * WPC;
-        const uint32_t* vc = a.vq + ((int64_t)u * a.chunks + ch) * WPC;
-        c.wk0 = *reinterpret_cast<const u32x4*>(kc + lane * 4);
-        c.wv0 = *reinterpret_cast<const u32x4*>(vc + lane * 4);
-        if (BITS == 4) {
-            c.wk1 = *reinterpret_cast<const u32x4*>(kc + 256 + lane * 4);
-            c.wv1 = *reinterpret_cast<const u32x4*>(vc + 256 + lane * 4);
-        }
-        const uint32_t* vm = a.vmeta + (((int64_t)u * a.chunks + ch) * NG + gs) * 32 + 4 * kb;
-        c.vm0 = *reinterpret_cast<const u32x4*>(vm);
-        c.vm1 = *reinterpret_cast<const u32x4*>(vm + 16);
-        c.mw = a.pool > 0 ? a.mask[(int64_t)u * a.chunks + ch] : 0u;
+    // Stage k (chunk k of this wavefront) lands in ring slot k % kStages.
+    char* wlds = reinterpret_cast<char*>(smem) + wave * RG::kWave;
+    auto issue = [&](uint32_t k) {
+        const uint32_t gi = gs0 + wave + 4 * (k / CPG), cc = k % CPG, ch = gi * CPG + cc;
+        char* st = wlds + (k % RG::kStages) * RG::kStage;
+        lds_load16(kq_u + ch * WPC + lane * 4, st);
+        if (BITS == 4) lds_load16(kq_u + ch * WPC + 256 + lane * 4, st + 1024);
+        lds_load16(vq_u + ch * WPC + lane * 4, st + RG::kCodes);
+        if (BITS == 4) lds_load16(vq_u + ch * WPC + 256 + lane * 4, st + RG::kCodes + 1024);
+        // value scales (lanes < 8 NG) and, at a key group's first chunk, key scales (lanes >= 32)
+        const uint32_t* src = lane < 32 ? vm_u + ch * NG * 32 + lane * 4 : km_u + gi * D + (lane - 32) * 4;
+        if (lane < 8 * NG || (lane >= 32 && cc == 0)) lds_load16(src, st + 2 * RG::kCodes);
+        if (lane == 0) lds_load4(mk_u + ch, st + 2 * RG::kCodes + RG::kMeta);
     };
-
-    unsigned char* btab = reinterpret_cast<unsigned char*>(smem + wave * kWaveFloats);
+    float* wsm = reinterpret_cast<float*>(wlds);
+    unsigned char* btab = s_btab[wave];  // folded query, 2 KB
+    float* pbuf = s_pbuf[wave];          // [4][32] probabilities
     float m_run = -INFINITY, lsum = 0.f, zc = 0.f, beta = 0.f;
-    floatx4 O[8];
+    floatx4 O[8], Oone = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const half8 ones = as_half8(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
 
-    Chunk cur, nxt;
-    if (n_items > 0) load(0, nxt);
-    for (int64_t k = 0; k < n_items; ++k) {
-        cur = nxt;
-        if (k + 1 < n_items) load(k + 1, nxt);
-        const int64_t gi = gs0 + wave + 4 * (k / CPG);
-        const int cc = (int)(k % CPG);
-        const int64_t tb = (gi * CPG + cc) * 32;
+    auto step = [&](uint32_t k, uint32_t later) {
+        const uint32_t gi = gs0 + wave + 4 * (k / CPG), cc = k % CPG;
+        const int64_t tb = (int64_t)(gi * CPG + cc) * 32;
+        const uint32_t st = lds_addr(wlds + (k % RG::kStages) * RG::kStage);
+        const uint32_t meta = st + 2 * RG::kCodes;
+        if (later >= 2) wait_vm<2 * RG::kLoads>();
+        else if (later == 1) wait_vm<RG::kLoads>();
+        else wait_vm<0>();
+        u32x4 wk0 = ring_read(st + lane * 16), wk1 = wk0;
+        u32x4 wv0 = ring_read(st + RG::kCodes + lane * 16), wv1 = wv0;
+        if (BITS == 4) {
+            wk1 = ring_read(st + 1024 + lane * 16);
+            wv1 = ring_read(st + RG::kCodes + 1024 + lane * 16);
+        }
+        u32x4 vm0 = ring_read(meta + (gs * 32 + 4 * kb) * 4);
+        u32x4 vm1 = ring_read(meta + (gs * 32 + 16 + 4 * kb) * 4);
+        u32x4 km0 = vm0, km1 = vm1;
+        if (cc == 0) {
+            km0 = ring_read(meta + 512 + cb0 * 4);
+            km1 = ring_read(meta + 512 + cb0 * 4 + 16);
+        }
+        uint32_t mwv = ring_read32(meta + RG::kMeta);
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(wk0), "+v"(wk1), "+v"(wv0), "+v"(wv1), "+v"(vm0), "+v"(vm1),
+                       "+v"(km0), "+v"(km1), "+v"(mwv)
+                     :
+                     : "memory");
         if (cc == 0) {
             // Fold the key scale into the query: B = hi/lo of q~_c * s_c, and
             // the zero point into beta_h = sum_c q~_c (z_c - 2^b s_c).
             wave_lds_fence();  // previous group's B reads are done
-            const uint32_t kmw[8] = {cur.km0.x, cur.km0.y, cur.km0.z, cur.km0.w,
-                                     cur.km1.x, cur.km1.y, cur.km1.z, cur.km1.w};
+            const uint32_t kmw[8] = {km0.x, km0.y, km0.z, km0.w, km1.x, km1.y, km1.z, km1.w};
             uint32_t hiw[4], low[4];
             float bp = 0.f;
 #pragma unroll
@@ -354,17 +465,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             *reinterpret_cast<u32x4*>(e0 + 4 * 16) = u32x4{low[0], low[1], low[2], low[3]};
             bp += row_ror<8>(bp);
             bp += row_ror<4>(bp);
-            bp += __shfl_xor(bp, 16);
-            bp += __shfl_xor(bp, 32);
-            beta = bp;
+            beta = sum_x32(sum_x16(bp));
             wave_lds_fence();
         }
 
         // Logits S^T[token][(head, g)] on the matrix cores: two 16-token tiles,
         // K = 128 channels x {hi, lo}.
-        const uint32_t wk[8] = {cur.wk0.x, cur.wk0.y, cur.wk0.z, cur.wk0.w,
-                                cur.wk1.x, cur.wk1.y, cur.wk1.z, cur.wk1.w};
-        floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+        const uint32_t wk[8] = {wk0.x, wk0.y, wk0.z, wk0.w, wk1.x, wk1.y, wk1.z, wk1.w};
+        floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc0l = acc0, acc1l = acc0;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             half8 A0, A1;
@@ -380,80 +488,122 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                 A0 = as_half8(cvt(w0, 6), cvt(w0, 2), cvt(w0, -2), cvt(w0, -6));
                 A1 = as_half8(cvt(w1, 6), cvt(w1, 2), cvt(w1, -2), cvt(w1, -6));
             }
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const half8 B = *reinterpret_cast<const half8*>(
-                    btab + ((((ks * 4 + kb) * 2 + x) * 4) + (j % R)) * 16);
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, B, acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, B, acc1, 0, 0, 0);
+            const half8 Bh = *reinterpret_cast<const half8*>(
+                btab + ((((ks * 4 + kb) * 2 + 0) * 4) + (j % R)) * 16);
+            const half8 Bl = *reinterpret_cast<const half8*>(
+                btab + ((((ks * 4 + kb) * 2 + 1) * 4) + (j % R)) * 16);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bh, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh, acc1, 0, 0, 0);
+            acc0l = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bl, acc0l, 0, 0, 0);
+            acc1l = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, acc1l, 0, 0, 0);
+        }
+        acc0 += acc0l;
+        acc1 += acc1l;
+        const uint32_t mw = __builtin_amdgcn_readfirstlane(mwv);  // same word in every lane
+        float p[8];
+        float mnew;
+        if constexpr (kSplitExp) {
+            // This lane's two tokens (slots 2gr, 2gr+1 of its k-block).
+            const float a0 = gr & 1 ? acc0[2] : acc0[0], b0 = gr & 1 ? acc1[2] : acc1[0];
+            const float a1 = gr & 1 ? acc0[3] : acc0[1], b1 = gr & 1 ? acc1[3] : acc1[1];
+            float s0 = (gr < 2 ? a0 : b0) + beta, s1 = (gr < 2 ? a1 : b1) + beta;
+            if (mw) {
+                if ((mw >> own_tok) & 1u) s0 = -INFINITY;
+                if ((mw >> (own_tok + 1)) & 1u) s1 = -INFINITY;
             }
-        }
-        float s[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            s[i] = acc0[i] + beta;
-            s[4 + i] = acc1[i] + beta;
-        }
-        const uint32_t mw = __builtin_amdgcn_readfirstlane(cur.mw);  // same word in every lane
-        if (mw) {
-#pragma unroll
-            for (int sl = 0; sl < 8; ++sl) {
-                const int tok = 16 * (sl / 4) + 4 * kb + sl % 4;
-                if ((mw >> tok) & 1u) s[sl] = -INFINITY;
+            if (a.logits) {
+                float* lg = a.logits + ((int64_t)u * R + hb) * a.T + tb + own_tok;
+                if (s0 != -INFINITY) lg[0] = s0;
+                if (s1 != -INFINITY) lg[1] = s1;
             }
-        }
-        if (a.logits && j < R) {
-            float* lg = a.logits + ((int64_t)u * R + j) * a.T + tb + 4 * kb;
-            if (!mw) {
-                *reinterpret_cast<floatx4*>(lg) = floatx4{s[0], s[1], s[2], s[3]};
-                *reinterpret_cast<floatx4*>(lg + 16) = floatx4{s[4], s[5], s[6], s[7]};
-            } else {
+            float cm = fmaxf(s0, s1);
+            cm = fmaxf(cm, row_ror<8>(cm));
+            cm = fmaxf(cm, row_ror<4>(cm));
+            cm = max_x32(max_x16(cm));
+            mnew = fmaxf(m_run, cm);
+            if (__any(mnew > m_run)) {
+                const float alpha =
+                    m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
+                lsum *= alpha;
+                zc *= alpha;
+                const float ah[4] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha),
+                                     quad_bcast<2>(alpha), quad_bcast<3>(alpha)};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) O[nt][i] *= ah[i];
+                    Oone[i] *= ah[i];
+                }
+                m_run = mnew;
+            }
+            const float mu = m_run == -INFINITY ? 0.f : m_run;
+            const float p0 = __builtin_amdgcn_exp2f(s0 - mu), p1 = __builtin_amdgcn_exp2f(s1 - mu);
+            lsum += p0 + p1;
+            float* ph = pbuf + hb * 32;
+            *reinterpret_cast<float2*>(ph + own_tok) = float2{p0, p1};
+            wave_lds_fence();
+            const floatx4 pa = *reinterpret_cast<const floatx4*>(ph + 4 * kb);
+            const floatx4 pb = *reinterpret_cast<const floatx4*>(ph + 16 + 4 * kb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = pa[i];
+                p[4 + i] = pb[i];
+            }
+        } else {
+            float s[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s[i] = acc0[i] + beta;
+                s[4 + i] = acc1[i] + beta;
+            }
+            if (mw) {
 #pragma unroll
                 for (int sl = 0; sl < 8; ++sl) {
                     const int tok = 16 * (sl / 4) + 4 * kb + sl % 4;
-                    if (!((mw >> tok) & 1u)) lg[16 * (sl / 4) + sl % 4] = s[sl];
+                    if ((mw >> tok) & 1u) s[sl] = -INFINITY;
                 }
             }
-        }
-
-        // Online softmax (log2 units); rescale only when the running max grows.
-        float cm = s[0];
+            if (a.logits && j < R) {
+                float* lg = a.logits + ((int64_t)u * R + j) * a.T + tb + 4 * kb;
 #pragma unroll
-        for (int sl = 1; sl < 8; ++sl) cm = fmaxf(cm, s[sl]);
-        cm = fmaxf(cm, __shfl_xor(cm, 16));
-        cm = fmaxf(cm, __shfl_xor(cm, 32));
-        const float mnew = fmaxf(m_run, cm);
-        if (__any(mnew > m_run)) {
-            const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
-            lsum *= alpha;
-            zc *= alpha;
-            float ah[4];
-            ah[0] = quad_bcast<0>(alpha);
-            if (R > 1) ah[1] = quad_bcast<1>(alpha);
-            if (R > 2) {
-                ah[2] = quad_bcast<2>(alpha);
-                ah[3] = quad_bcast<3>(alpha);
+                for (int sl = 0; sl < 8; ++sl)
+                    if (s[sl] != -INFINITY) lg[16 * (sl / 4) + sl % 4] = s[sl];
             }
+            float cm = s[0];
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt)
+            for (int sl = 1; sl < 8; ++sl) cm = fmaxf(cm, s[sl]);
+            cm = max_x32(max_x16(cm));
+            mnew = fmaxf(m_run, cm);
+            if (__any(mnew > m_run)) {
+                const float alpha =
+                    m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
+                lsum *= alpha;
+                zc *= alpha;
+                float ah[4];
+                ah[0] = quad_bcast<0>(alpha);
+                if (R > 1) ah[1] = quad_bcast<1>(alpha);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) O[nt][i] *= ah[i % R];
-            m_run = mnew;
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) O[nt][i] *= ah[i % R];
+                    Oone[i] *= ah[i % R];
+                }
+                m_run = mnew;
+            }
+            const float mu = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+            for (int sl = 0; sl < 8; ++sl) {
+                p[sl] = __builtin_amdgcn_exp2f(s[sl] - mu);
+                lsum += p[sl];
+            }
         }
-        const float mu = m_run == -INFINITY ? 0.f : m_run;
 
-        // Value operand rows (head, value group): hi/lo of p_t * s^V_t; the
-        // offsets go to zc = sum_t p_t (z^V_t - 2^b s^V_t).
-        const uint32_t vmw[8] = {cur.vm0.x, cur.vm0.y, cur.vm0.z, cur.vm0.w,
-                                 cur.vm1.x, cur.vm1.y, cur.vm1.z, cur.vm1.w};
-        float p[8];
+        // Value operand rows (head, value group): hi/lo of p_t * s^V_t. The
+        // zero points go to zc = sum_t p_t z^V_t; the 2^b offset of the code
+        // operands is taken out exactly through the ones column (Oone).
+        const uint32_t vmw[8] = {vm0.x, vm0.y, vm0.z, vm0.w, vm1.x, vm1.y, vm1.z, vm1.w};
 #pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-            p[sl] = __builtin_amdgcn_exp2f(s[sl] - mu);
-            lsum += p[sl];
-            const float sv = h2f(vmw[sl] & 0xFFFF), zv = h2f(vmw[sl] >> 16);
-            zc += p[sl] * (zv - F * sv);
-        }
+        for (int sl = 0; sl < 8; ++sl) zc += p[sl] * h2f(vmw[sl] >> 16);
         uint32_t ahw[4], alw[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -462,8 +612,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         }
         const half8 Ahi = as_half8(ahw[0], ahw[1], ahw[2], ahw[3]);
         const half8 Alo = as_half8(alw[0], alw[1], alw[2], alw[3]);
-        const uint32_t wv[8] = {cur.wv0.x, cur.wv0.y, cur.wv0.z, cur.wv0.w,
-                                cur.wv1.x, cur.wv1.y, cur.wv1.z, cur.wv1.w};
+        const uint32_t wv[8] = {wv0.x, wv0.y, wv0.z, wv0.w, wv1.x, wv1.y, wv1.z, wv1.w};
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
             half8 Bv;
@@ -479,20 +628,34 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bv, O[nt], 0, 0, 0);
             O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, O[nt], 0, 0, 0);
         }
+        Oone = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, ones, Oone, 0, 0, 0);
+        Oone = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, ones, Oone, 0, 0, 0);
+    };
+
+    // Pipeline: stages k+1 and k+2 are in flight while stage k computes.
+    for (uint32_t k = 0; k < 2 && k < n_items; ++k) issue(k);
+    for (uint32_t k = 0; k < n_items; ++k) {
+        if (k + 2 < n_items) issue(k + 2);
+        step(k, n_items - 1 - k);  // stages issued after k: min(2, n_items - 1 - k)
     }
     wave_lds_fence();
 
-    // Wavefront epilogue: l per head, value corrections per row, outputs to LDS.
+    // Wavefront epilogue: per-head l, per-row zero-point totals, outputs to LDS
+    // as they sit in the accumulators; the block combine picks the valid rows.
     float lt = lsum;
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    float zt = zc;
-    zt += __shfl_xor(zt, 16);
-    zt += __shfl_xor(zt, 32);
-    float* ws = smem + wave * kWaveFloats;  // [R][D] outputs, then Z[16], m[4], l[4]
-    float* Zs = ws + R * D;
-    float* ms = Zs + 16;
-    float* ls = ms + 4;
+    if (kSplitExp) {
+        lt += row_ror<8>(lt);
+        lt += row_ror<4>(lt);
+    }
+    lt = sum_x32(sum_x16(lt));
+    const float zt = sum_x32(sum_x16(zc));
+    float* obuf = wsm;               // [8][64][4] (reuses the ring)
+    float* Zs = wsm + 2048;          // [16] sum_t p z^V per row
+    float* Zo = Zs + 16;             // [16] ones-column totals per row
+    float* ms = Zo + 16;             // [4]
+    float* ls = ms + 4;              // [4]
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) *reinterpret_cast<floatx4*>(obuf + (nt * 64 + lane) * 4) = O[nt];
     if (kb == 0) {
         Zs[j] = zt;
         if (j < R) {
@@ -500,32 +663,27 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             ls[j] = lt;
         }
     }
-    wave_lds_fence();
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ir = 4 * kb + i;
-            const int c = 16 * nt + j;
-            if (ir / R == c / G) ws[(ir % R) * D + c] = O[nt][i] + Zs[ir];
-        }
+    if (j == 0) *reinterpret_cast<floatx4*>(Zo + 4 * kb) = Oone;
     __syncthreads();
     // Block combine of the four wavefronts.
     for (int e = threadIdx.x; e < R * D; e += 256) {
         const int h = e / D, c = e % D;
+        const int ir = h + R * (c / G);  // accumulator row (head, value group)
+        const int src = ((c / 16) * 64 + (c % 16) + 16 * (ir / 4)) * 4 + ir % 4;
         float mw[4], M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            mw[w] = smem[w * kWaveFloats + R * D + 16 + h];
+            mw[w] = smem[w * (RG::kWave / 4) + 2048 + 32 + h];
             M = fmaxf(M, mw[w]);
         }
         float o = 0.f, l = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
+                const float* wb = smem + w * (RG::kWave / 4);
                 const float f = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
-                o += smem[w * kWaveFloats + h * D + c] * f;
-                l += smem[w * kWaveFloats + R * D + 20 + h] * f;
+                o += (wb[src] + wb[2048 + ir] - F * wb[2048 + 16 + ir]) * f;
+                l += wb[2048 + 36 + h] * f;
             }
         }
         float* rec = a.part + (((int64_t)u * a.splits + split) * R + h) * kRec;
@@ -585,8 +743,42 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     }
 }
 
+// Blocks of decode_kernel<BITS, R, G> resident on the current device at once
+// (occupancy x compute units), cached per device. KVQ_DECODE_BLOCKS overrides
+// it, for launch-shape sweeps.
 template <int BITS, int R, int G>
-void launch_decode_t(const DecodeArgs& a, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
+int resident_blocks() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (const char* env = std::getenv("KVQ_DECODE_BLOCKS")) n = std::atoi(env);
+        if (n <= 0) {
+            int cus = 0, per = 0;
+            if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                    hipSuccess ||
+                hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &per, reinterpret_cast<const void*>(decode_kernel<BITS, R, G>), 256, 0) !=
+                    hipSuccess)
+                cus = per = 0;
+            n = cus * per > 0 ? cus * per : 512;
+        }
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <int BITS, int R, int G>
+void launch_decode_t(DecodeArgs a, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
+    if (a.splits_q > 0) {
+        // one resident round: the fp16 tiles plus as many splits per unit as fit
+        int64_t q = ((int64_t)resident_blocks<BITS, R, G>() - (int64_t)a.units * a.fp16_tiles) /
+                    a.units;
+        if (q < 1) q = 1;
+        if (q < a.splits_q) a.splits_q = (int32_t)q;
+    }
+    a.splits = a.splits_q + a.fp16_tiles;
     const unsigned blocks = (unsigned)(a.units * a.fp16_tiles + a.units * a.splits_q);
     if (e0 || e1)
         hipExtLaunchKernelGGL((decode_kernel<BITS, R, G>), dim3(blocks), dim3(256), 0, s, e0, e1, 0,

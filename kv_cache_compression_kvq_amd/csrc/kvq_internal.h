@@ -14,6 +14,7 @@ constexpr int kChunk = 32;         // tokens per packed chunk
 constexpr int kMaxPool = 64;       // N limit
 constexpr int kMaxEvict = 1024;    // E limit
 constexpr int kMaxFp16Rows = 2048; // R + G + N + E limit (fp16 partition kept in LDS)
+constexpr int kMaxTokens = 1 << 24; // per-unit capacity: keeps per-unit offsets in 32 bits
 
 // Device pointers of one cache, resolved from the arena and the handle's offsets.
 struct CacheView {
@@ -46,7 +47,8 @@ CacheView view_of(const kvq_cache* h);
 
 // Split plan of one decode call.
 struct DecodePlan {
-    int32_t splits_q;    // quantized-partition splits per unit (0 when n_q == 0)
+    int32_t splits_q;    // upper bound on quantized-partition splits per unit (0 when
+                         // n_q == 0); the launch picks the count that fills the GPU once
     int32_t fp16_tiles;  // 64-row tiles of the fp16 partition (ring + pools)
     int32_t splits;      // splits_q + fp16_tiles partial records per unit
     int64_t part_floats; // partial records: U * splits * r * (d + 2)
