@@ -346,7 +346,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16-mfma/f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": d, "tokens": w.tokens,
