@@ -124,15 +124,20 @@ typedef struct kvq_config {
  *   pool_k    fp16 [U][N][d] original key row;  pool_v likewise
  *   ev_idx    int32 [U][E]; ev_k, ev_v fp16 [U][E][d] (extra pool, in the
  *             order members were displaced)
- *   counters  int32 [U][4]: pool count, extra-pool count, frozen flag, 0
+ *   counters  int32 [U][4]: pool count, extra-pool count, frozen flag, and the
+ *             largest value scale held by the unit (fp16 bits; 0 while
+ *             nothing is quantized), which bounds the decoder's lazy rescale
  *   scores    uint64 [U][Qcap] scratch for key L1 norms during an append
  * Slots of pool_idx / ev_idx beyond the counters are unspecified.
  *
  * Packed code layout. Codes of 32 consecutive quantized tokens form a chunk
  * laid out for the matrix-core operands of the decode kernel: 64 lanes own
  * 2b 32-bit words each; word w of lane l is stored at word offset
- * (w / 4) * 256 + l * 4 + (w % 4) of the chunk. kvq_unpack_codes returns the
- * canonical view (one byte per code, [token][channel]) for inspection.
+ * (w / 4) * 256 + l * 4 + (w % 4) of the chunk. Inside a word the two 16-bit
+ * halves hold the two codes of one operand pair at the same bit position;
+ * which pair sits at which position is chosen so that the decoder needs at
+ * most one shift or rotate per word position (see kvq_unpack_codes, which
+ * returns the canonical view, one byte per code, [token][channel]).
  */
 typedef struct kvq_cache {
     kvq_config cfg;

@@ -328,14 +328,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     constexpr int NG = D / G;        // value groups per token
     constexpr int CPG = G / 32;      // chunks per key group
     constexpr int WPC = 128 * BITS;  // words per chunk
-    constexpr float F = (float)(1 << BITS);
     // With r = 4 the 16 MFMA columns hold 4 copies of each head's logits;
     // each copy then exponentiates a quarter of the tokens.
     constexpr bool kSplitExp = R == 4;
-    // Codes become fp16 operands F + code with two bit operations; the masks
-    // live in VGPRs so that the pair becomes one v_and_or_b32.
-    constexpr uint32_t kMagicC = BITS == 2 ? 0x44004400u : 0x4C004C00u;
-    constexpr uint32_t kMaskC = BITS == 2 ? 0x03000300u : 0x03C003C0u;
+    // Code operands. A code masked in place at bits [p, p + b) of both 16-bit
+    // halves is the pair of fp16 subnormals code * 2^(p - 24): exact, one AND.
+    // The matrix cores align products by the encoded exponent, so codes are
+    // kept at bits 6-9 (at most two leading zero bits; lower positions cost
+    // precision): at b = 2 every pair is rotated to bits 6-7 or 8-9, at b = 4
+    // value nibbles are shifted to bits 4-7. Each matrix-core operand takes all
+    // its pairs from one position, so the weight 2^(p - 24) is common to the
+    // operand and is taken out elsewhere (keys: in the folded query; values:
+    // in the epilogue). At b = 4 keys are shifted to bits 6-9 and become
+    // 16 + code (v_and_or_b32 with the exponent of 16).
+    constexpr float kAccW = BITS == 2 ? 65536.f : 1.f;  // keys: 2^16 removes the operand weight
+    constexpr uint32_t kMaskA = 0x03C003C0u;
+    constexpr uint32_t kMagicA = 0x4C004C00u;
     using RG = Ring<BITS>;
     __shared__ __align__(16) float smem[RG::kBlock / 4];
     __shared__ __align__(16) unsigned char s_btab[4][2048];
@@ -346,12 +354,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         fp16_tile<R>(a, blockIdx.x / a.fp16_tiles, blockIdx.x % a.fp16_tiles, smem);
         return;
     }
-    uint32_t vmask, vmagic;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(vmask) : "i"(kMaskC));
-    asm volatile("v_mov_b32 %0, %1" : "=v"(vmagic) : "i"(kMagicC));
-    auto cvt = [&](uint32_t w, int sh) -> uint32_t {  // sh > 0: left shift
+    uint32_t vmaskA, vmagicA;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(vmaskA) : "i"(kMaskA));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(vmagicA) : "i"(kMagicA));
+    auto cvt4 = [&](uint32_t w, int sh) -> uint32_t {  // b = 4 keys; sh > 0: left shift
         const uint32_t x = sh >= 0 ? (w << sh) : (w >> -sh);
-        return (x & vmask) | vmagic;
+        return (x & vmaskA) | vmagicA;
     };
 
     const int idx = blockIdx.x - a.units * a.fp16_tiles;
@@ -386,10 +394,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const uint16_t* qrow = a.q + ((int64_t)b * a.n_kv_heads * R + hk * R + hb) * D + cb0;
         const uint4 x = *reinterpret_cast<const uint4*>(qrow);
         const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        // b = 2: this lane's channels (k-step ksb) sit at bits 6-7 (even ksb,
+        // weight 2^-18) or 8-9 (odd ksb, 2^-16); the folded query takes 2^2 or
+        // 2^0 so that every key product carries 2^-16
+        const float wq = BITS == 2 && ksb % 2 == 0 ? 4.f * a.qscale : a.qscale;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            qv[2 * i] = h2f(w[i] & 0xFFFF) * a.qscale;
-            qv[2 * i + 1] = h2f(w[i] >> 16) * a.qscale;
+            qv[2 * i] = h2f(w[i] & 0xFFFF) * wq;
+            qv[2 * i + 1] = h2f(w[i] >> 16) * wq;
         }
     }
 
@@ -411,10 +423,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     unsigned char* btab = s_btab[wave];  // folded query, 2 KB
     float* pbuf = s_pbuf[wave];          // [4][32] probabilities
     float m_run = -INFINITY, lsum = 0.f, zc = 0.f, beta = 0.f;
-    floatx4 O[8], Oone = {0.f, 0.f, 0.f, 0.f};
+    floatx4 O[8];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const half8 ones = as_half8(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+    // Lazy rescale: the running max m_run only moves when a logit exceeds it
+    // by more than tau (log2 units), so probabilities stay below 2^tau; tau is
+    // bounded so that p * s^V, s^V below the unit's largest value scale, stays
+    // far inside fp16 (< 2^15).
+    float m_thr = -INFINITY;
+    float tau = 8.f;
+    {
+        const uint32_t smax = (uint32_t)a.counters[(int64_t)u * 4 + 3] & 0x7FFFu;
+        if (smax >= 0x0400u) {  // normal: s < 2^(e+1)
+            const int e = (int)(smax >> 10) - 15;
+            tau = (float)min(8, max(0, 14 - e));
+        }
+    }
 
     auto step = [&](uint32_t k, uint32_t later) {
         const uint32_t gi = gs0 + wave + 4 * (k / CPG), cc = k % CPG;
@@ -457,9 +481,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float sk = h2f(kmw[i] & 0xFFFF), zk = h2f(kmw[i] >> 16);
-                bp += qv[i] * (zk - F * sk);
+                const float zk = h2f(kmw[i] >> 16);
+                if (BITS == 2) {
+                    bp += qv[i] * zk;
+                } else {
+                    const float sk = h2f(kmw[i] & 0xFFFF);
+                    bp += qv[i] * (zk - 16.f * sk);
+                }
             }
+            if (BITS == 2 && ksb % 2 == 0) bp *= 0.25f;  // undo the query weight
             unsigned char* e0 = btab + ((((ksb * 4 + kbb) * 2) * 4) + hb) * 16;
             *reinterpret_cast<u32x4*>(e0) = u32x4{hiw[0], hiw[1], hiw[2], hiw[3]};
             *reinterpret_cast<u32x4*>(e0 + 4 * 16) = u32x4{low[0], low[1], low[2], low[3]};
@@ -472,21 +502,29 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         // Logits S^T[token][(head, g)] on the matrix cores: two 16-token tiles,
         // K = 128 channels x {hi, lo}.
         const uint32_t wk[8] = {wk0.x, wk0.y, wk0.z, wk0.w, wk1.x, wk1.y, wk1.z, wk1.w};
+        uint32_t wkL4[4], wkR4[4], wkL8[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            wkL4[m] = __builtin_amdgcn_alignbit(wk[m], wk[m], 28);
+            wkR4[m] = __builtin_amdgcn_alignbit(wk[m], wk[m], 4);
+            wkL8[m] = __builtin_amdgcn_alignbit(wk[m], wk[m], 24);
+        }
         floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc0l = acc0, acc1l = acc0;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             half8 A0, A1;
             if (BITS == 2) {
-                const uint32_t w0 = wk[ks / 2], w1 = wk[2 + ks / 2];
-                const int q0 = (ks % 2) * 4;
-                A0 = as_half8(cvt(w0, 8 - 2 * q0), cvt(w0, 6 - 2 * q0), cvt(w0, 4 - 2 * q0),
-                              cvt(w0, 2 - 2 * q0));
-                A1 = as_half8(cvt(w1, 8 - 2 * q0), cvt(w1, 6 - 2 * q0), cvt(w1, 4 - 2 * q0),
-                              cvt(w1, 2 - 2 * q0));
+                // pair m from word m: tile 0 at positions 3, 4, 1, 2 (k-steps
+                // 0..3), tile 1 at 5, 6, 7, 0; even k-steps end at bits 6-7
+                const uint32_t mk = ks % 2 == 0 ? 0x00C000C0u : 0x03000300u;
+                const uint32_t* x0 = ks < 2 ? wk : wkL4;
+                const uint32_t* x1 = ks < 2 ? wkR4 : wkL8;
+                A0 = as_half8(x0[0] & mk, x0[1] & mk, x0[2] & mk, x0[3] & mk);
+                A1 = as_half8(x1[0] & mk, x1[1] & mk, x1[2] & mk, x1[3] & mk);
             } else {
                 const uint32_t w0 = wk[ks], w1 = wk[4 + ks];
-                A0 = as_half8(cvt(w0, 6), cvt(w0, 2), cvt(w0, -2), cvt(w0, -6));
-                A1 = as_half8(cvt(w1, 6), cvt(w1, 2), cvt(w1, -2), cvt(w1, -6));
+                A0 = as_half8(cvt4(w0, 6), cvt4(w0, 2), cvt4(w0, -2), cvt4(w0, -6));
+                A1 = as_half8(cvt4(w1, 6), cvt4(w1, 2), cvt4(w1, -2), cvt4(w1, -6));
             }
             const half8 Bh = *reinterpret_cast<const half8*>(
                 btab + ((((ks * 4 + kb) * 2 + 0) * 4) + (j % R)) * 16);
@@ -506,7 +544,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             // This lane's two tokens (slots 2gr, 2gr+1 of its k-block).
             const float a0 = gr & 1 ? acc0[2] : acc0[0], b0 = gr & 1 ? acc1[2] : acc1[0];
             const float a1 = gr & 1 ? acc0[3] : acc0[1], b1 = gr & 1 ? acc1[3] : acc1[1];
-            float s0 = (gr < 2 ? a0 : b0) + beta, s1 = (gr < 2 ? a1 : b1) + beta;
+            float s0 = fmaf(gr < 2 ? a0 : b0, kAccW, beta), s1 = fmaf(gr < 2 ? a1 : b1, kAccW, beta);
             if (mw) {
                 if ((mw >> own_tok) & 1u) s0 = -INFINITY;
                 if ((mw >> (own_tok + 1)) & 1u) s1 = -INFINITY;
@@ -521,20 +559,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             cm = fmaxf(cm, row_ror<4>(cm));
             cm = max_x32(max_x16(cm));
             mnew = fmaxf(m_run, cm);
-            if (__any(mnew > m_run)) {
-                const float alpha =
-                    m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
-                lsum *= alpha;
-                zc *= alpha;
-                const float ah[4] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha),
-                                     quad_bcast<2>(alpha), quad_bcast<3>(alpha)};
+            if (__any(mnew > m_thr)) {
+                if (__builtin_amdgcn_readfirstlane(m_run != -INFINITY)) {
+                    const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+                    lsum *= alpha;
+                    zc *= alpha;
+                    const float ah[4] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha),
+                                         quad_bcast<2>(alpha), quad_bcast<3>(alpha)};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                    for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int nt = 0; nt < 8; ++nt) O[nt][i] *= ah[i];
-                    Oone[i] *= ah[i];
+                        for (int nt = 0; nt < 8; ++nt) O[nt][i] *= ah[i];
                 }
                 m_run = mnew;
+                m_thr = mnew + tau;
             }
             const float mu = m_run == -INFINITY ? 0.f : m_run;
             const float p0 = __builtin_amdgcn_exp2f(s0 - mu), p1 = __builtin_amdgcn_exp2f(s1 - mu);
@@ -553,8 +591,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             float s[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                s[i] = acc0[i] + beta;
-                s[4 + i] = acc1[i] + beta;
+                s[i] = fmaf(acc0[i], kAccW, beta);
+                s[4 + i] = fmaf(acc1[i], kAccW, beta);
             }
             if (mw) {
 #pragma unroll
@@ -574,21 +612,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             for (int sl = 1; sl < 8; ++sl) cm = fmaxf(cm, s[sl]);
             cm = max_x32(max_x16(cm));
             mnew = fmaxf(m_run, cm);
-            if (__any(mnew > m_run)) {
-                const float alpha =
-                    m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
-                lsum *= alpha;
-                zc *= alpha;
-                float ah[4];
-                ah[0] = quad_bcast<0>(alpha);
-                if (R > 1) ah[1] = quad_bcast<1>(alpha);
+            if (__any(mnew > m_thr)) {
+                if (__builtin_amdgcn_readfirstlane(m_run != -INFINITY)) {
+                    const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+                    lsum *= alpha;
+                    zc *= alpha;
+                    float ah[4];
+                    ah[0] = quad_bcast<0>(alpha);
+                    if (R > 1) ah[1] = quad_bcast<1>(alpha);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                    for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int nt = 0; nt < 8; ++nt) O[nt][i] *= ah[i % R];
-                    Oone[i] *= ah[i % R];
+                        for (int nt = 0; nt < 8; ++nt) O[nt][i] *= ah[i % R];
                 }
                 m_run = mnew;
+                m_thr = mnew + tau;
             }
             const float mu = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
@@ -599,8 +637,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         }
 
         // Value operand rows (head, value group): hi/lo of p_t * s^V_t. The
-        // zero points go to zc = sum_t p_t z^V_t; the 2^b offset of the code
-        // operands is taken out exactly through the ones column (Oone).
+        // zero points go to zc = sum_t p_t z^V_t. Value codes enter as fp16
+        // subnormals code * 2^(pos - 24), masked in place: every operand of
+        // tile nt has the same position, so the tile's sum carries one exact
+        // power-of-two weight that the epilogue removes.
         const uint32_t vmw[8] = {vm0.x, vm0.y, vm0.z, vm0.w, vm1.x, vm1.y, vm1.z, vm1.w};
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) zc += p[sl] * h2f(vmw[sl] >> 16);
@@ -615,21 +655,28 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const uint32_t wv[8] = {wv0.x, wv0.y, wv0.z, wv0.w, wv1.x, wv1.y, wv1.z, wv1.w};
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
-            half8 Bv;
-            if (BITS == 2) {
-                const uint32_t w = wv[nt / 2];
-                const int q0 = (nt % 2) * 4;
-                Bv = as_half8(cvt(w, 8 - 2 * q0), cvt(w, 6 - 2 * q0), cvt(w, 4 - 2 * q0),
-                              cvt(w, 2 - 2 * q0));
-            } else {
-                const uint32_t w = wv[nt];
-                Bv = as_half8(cvt(w, 6), cvt(w, 2), cvt(w, -2), cvt(w, -6));
+            uint32_t x[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if (BITS == 2) {
+                    // tile nt at position 3, 4, 1, 2, 5, 6, 7, 0 of word m
+                    const uint32_t w = wv[m];
+                    const uint32_t r = nt < 2 ? w : nt < 4 ? __builtin_amdgcn_alignbit(w, w, 28)
+                                     : nt < 6 ? __builtin_amdgcn_alignbit(w, w, 4)
+                                              : __builtin_amdgcn_alignbit(w, w, 24);
+                    x[m] = r & (nt % 2 == 0 ? 0x00C000C0u : 0x03000300u);
+                } else {
+                    // nibble j of word 4*(nt/4) + m, moved to bits 4-7
+                    const uint32_t w = wv[4 * (nt / 4) + m];
+                    const int j = nt % 4;
+                    const uint32_t r = j == 0 ? w << 4 : j == 1 ? w : j == 2 ? w >> 4 : w >> 8;
+                    x[m] = r & 0x00F000F0u;
+                }
             }
+            const half8 Bv = as_half8(x[0], x[1], x[2], x[3]);
             O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bv, O[nt], 0, 0, 0);
             O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, O[nt], 0, 0, 0);
         }
-        Oone = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, ones, Oone, 0, 0, 0);
-        Oone = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, ones, Oone, 0, 0, 0);
     };
 
     // Pipeline: stages k+1 and k+2 are in flight while stage k computes.
@@ -651,8 +698,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const float zt = sum_x32(sum_x16(zc));
     float* obuf = wsm;               // [8][64][4] (reuses the ring)
     float* Zs = wsm + 2048;          // [16] sum_t p z^V per row
-    float* Zo = Zs + 16;             // [16] ones-column totals per row
-    float* ms = Zo + 16;             // [4]
+    float* ms = Zs + 16;             // [4]
     float* ls = ms + 4;              // [4]
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) *reinterpret_cast<floatx4*>(obuf + (nt * 64 + lane) * 4) = O[nt];
@@ -663,17 +709,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             ls[j] = lt;
         }
     }
-    if (j == 0) *reinterpret_cast<floatx4*>(Zo + 4 * kb) = Oone;
     __syncthreads();
     // Block combine of the four wavefronts.
     for (int e = threadIdx.x; e < R * D; e += 256) {
         const int h = e / D, c = e % D;
         const int ir = h + R * (c / G);  // accumulator row (head, value group)
         const int src = ((c / 16) * 64 + (c % 16) + 16 * (ir / 4)) * 4 + ir % 4;
+        // weight of tile c / 16's code operands: 2^(pos - 24)
+        const int nt = c / 16;
+        const int pos = BITS == 2 ? (nt % 2 == 0 ? 6 : 8) : 4;
         float mw[4], M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            mw[w] = smem[w * (RG::kWave / 4) + 2048 + 32 + h];
+            mw[w] = smem[w * (RG::kWave / 4) + 2048 + 16 + h];
             M = fmaxf(M, mw[w]);
         }
         float o = 0.f, l = 0.f;
@@ -682,8 +730,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             for (int w = 0; w < 4; ++w) {
                 const float* wb = smem + w * (RG::kWave / 4);
                 const float f = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
-                o += (wb[src] + wb[2048 + ir] - F * wb[2048 + 16 + ir]) * f;
-                l += wb[2048 + 36 + h] * f;
+                o += (ldexpf(wb[src], 24 - pos) + wb[2048 + ir]) * f;
+                l += wb[2048 + 20 + h] * f;
             }
         }
         float* rec = a.part + (((int64_t)u * a.splits + split) * R + h) * kRec;

@@ -205,6 +205,13 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
     }
 }
 
+// 2-bit position of operand pair j (0..7) inside a packed word: the decoder
+// brings positions 3 and 4 (bits 6-9 of each half) into place directly,
+// 1-2 by a 4-bit left rotate, 5-6 by a 4-bit right rotate and 7, 0 by an
+// 8-bit left rotate, which also swaps the halves of position 7 (stored
+// swapped for that reason). Even j ends at bits 6-7, odd j at bits 8-9.
+__device__ constexpr int kPos2[8] = {3, 4, 1, 2, 5, 6, 7, 0};
+
 // Quantize and pack one key group (G tokens) of one unit; 256 threads.
 // Pool members' rows are first replaced, for keys and values alike, by the
 // per-channel mean of all G rows of the group, computed exactly and rounded
@@ -284,8 +291,14 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
         }
         const float q = fmaxf(mx - mn, range_floor()) / levels;
         const int64_t t = t0 + i;
+        const uint16_t qh = f2h(q);
         v.vmeta[(((int64_t)u * v.chunks + t / kChunk) * NG + gq) * kChunk + t % kChunk] =
-            (uint32_t)f2h(q) | ((uint32_t)f2h(mn) << 16);
+            (uint32_t)qh | ((uint32_t)f2h(mn) << 16);
+        // Largest value scale of the unit (fp16 bits of a positive number order
+        // like the numbers): bounds the lazy softmax rescale of the decoder.
+        uint32_t mq = qh;
+        for (int off = 32; off > 0; off >>= 1) mq = max(mq, (uint32_t)__shfl_xor((int)mq, off));
+        if ((tid & 63) == 0) atomicMax(reinterpret_cast<uint32_t*>(v.counters) + (int64_t)u * 4 + 3, mq);
         for (int c = 0; c < G; ++c) row[c] = (uint16_t)quant_code(h2f(row[c]), mn, q, levels);
     }
     __syncthreads();
@@ -302,14 +315,20 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
             // lane (token row n of tile tau, channel block kb): codes of channels
             // 32*ks + 8*kb + {2m, 2m+1} in the low/high halves of the word
             if (BITS == 2) {
-                const int tau = w / 2;
-                const int tok = cc * kChunk + 16 * tau + n;
+                // Word m holds pair m of every (tile tau, k-step ks) at 2-bit
+                // position kPos2[4 tau + ks]: one matrix-core operand takes its
+                // four pairs from one position of the four words.
+                const int m = w;
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int ks = (w % 2) * 2 + q / 4, m = q % 4;
-                    const int ch = 32 * ks + 8 * kb + 2 * m;
-                    word |= (uint32_t)kx[tok * D + ch] << (2 * q);
-                    word |= (uint32_t)kx[tok * D + ch + 1] << (16 + 2 * q);
+                for (int tau = 0; tau < 2; ++tau) {
+                    const int tok = cc * kChunk + 16 * tau + n;
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const int ch = 32 * ks + 8 * kb + 2 * m, q = kPos2[4 * tau + ks];
+                        const int sw = q == 7 ? 1 : 0;
+                        word |= (uint32_t)kx[tok * D + ch + sw] << (2 * q);
+                        word |= (uint32_t)kx[tok * D + ch + 1 - sw] << (16 + 2 * q);
+                    }
                 }
             } else {
                 const int tau = w / 4, ks = w % 4;
@@ -323,27 +342,28 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
             }
         } else {
             // lane (channel n of each 16-channel tile nt, token block kb): slot s
-            // holds token 16*(s/4) + 4*kb + s%4; slots {2m, 2m+1} share a word
+            // holds token 16*(s/4) + 4*kb + s%4; slots {2m, 2m+1} share a word.
+            // The position inside the word depends on the tile only (b = 2: word
+            // m, position kPos2[nt]; b = 4: word 4*(nt/4) + m, nibble nt%4), so
+            // that every operand of one tile carries the same power-of-two weight.
+            const int m = w % 4;
+            const int sa = 2 * m, sb = 2 * m + 1;
+            const int ta = cc * kChunk + 16 * (sa / 4) + 4 * kb + sa % 4;
+            const int tb = cc * kChunk + 16 * (sb / 4) + 4 * kb + sb % 4;
             if (BITS == 2) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int nt = 2 * w + q / 4, m = q % 4;
-                    const int c = 16 * nt + n;
-                    const int sa = 2 * m, sb = 2 * m + 1;
-                    const int ta = cc * kChunk + 16 * (sa / 4) + 4 * kb + sa % 4;
-                    const int tb = cc * kChunk + 16 * (sb / 4) + 4 * kb + sb % 4;
-                    word |= (uint32_t)vx[ta * D + c] << (2 * q);
-                    word |= (uint32_t)vx[tb * D + c] << (16 + 2 * q);
+                for (int nt = 0; nt < 8; ++nt) {
+                    const int c = 16 * nt + n, q = kPos2[nt];
+                    const int xa = q == 7 ? tb : ta, xb = q == 7 ? ta : tb;
+                    word |= (uint32_t)vx[xa * D + c] << (2 * q);
+                    word |= (uint32_t)vx[xb * D + c] << (16 + 2 * q);
                 }
             } else {
-                const int c = 16 * w + n;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int sa = 2 * m, sb = 2 * m + 1;
-                    const int ta = cc * kChunk + 16 * (sa / 4) + 4 * kb + sa % 4;
-                    const int tb = cc * kChunk + 16 * (sb / 4) + 4 * kb + sb % 4;
-                    word |= (uint32_t)vx[ta * D + c] << (4 * m);
-                    word |= (uint32_t)vx[tb * D + c] << (16 + 4 * m);
+                for (int j = 0; j < 4; ++j) {
+                    const int c = 16 * (4 * (w / 4) + j) + n;
+                    word |= (uint32_t)vx[ta * D + c] << (4 * j);
+                    word |= (uint32_t)vx[tb * D + c] << (16 + 4 * j);
                 }
             }
         }
@@ -388,8 +408,14 @@ __global__ __launch_bounds__(256) void unpack_kernel(CacheView v, int64_t n_q, u
             const int ks = c / 32, kb = (c % 32) / 8, s = c % 8, m = s / 2, hi = s % 2;
             const int l = row + 16 * kb;
             int w, bit;
-            if (b == 2) { w = 2 * tau + ks / 2; bit = 2 * ((ks % 2) * 4 + m) + 16 * hi; }
-            else { w = 4 * tau + ks; bit = 4 * m + 16 * hi; }
+            if (b == 2) {
+                const int q = kPos2[4 * tau + ks];
+                w = m;
+                bit = 2 * q + 16 * (q == 7 ? 1 - hi : hi);
+            } else {
+                w = 4 * tau + ks;
+                bit = 4 * m + 16 * hi;
+            }
             kc[e] = (uint8_t)((kbase[(w / 4) * 256 + l * 4 + w % 4] >> bit) & mask);
         }
         {   // value code
@@ -397,8 +423,12 @@ __global__ __launch_bounds__(256) void unpack_kernel(CacheView v, int64_t n_q, u
             const int m = s / 2, hi = s % 2, nt = c / 16, n = c % 16;
             const int l = n + 16 * kb;
             int w, bit;
-            if (b == 2) { w = nt / 2; bit = 2 * ((nt % 2) * 4 + m) + 16 * hi; }
-            else { w = nt; bit = 4 * m + 16 * hi; }
+            if (b == 2) {
+                const int q = kPos2[nt];
+                w = m;
+                bit = 2 * q + 16 * (q == 7 ? 1 - hi : hi);
+            }
+            else { w = 4 * (nt / 4) + m; bit = 4 * (nt % 4) + 16 * hi; }
             vc[e] = (uint8_t)((vbase[(w / 4) * 256 + l * 4 + w % 4] >> bit) & mask);
         }
     }

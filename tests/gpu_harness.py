@@ -114,6 +114,9 @@ def check_unit_state(st: dict, u: int, uc: O.UnitCache) -> None:
     vm = st["vmeta"][u, : nq // 32].transpose(0, 2, 1, 3).reshape(-1, d // p.gv, 2)[:nq]
     assert np.array_equal(vm[..., 0].view(np.uint16), uc.vscale.view(np.uint16))
     assert np.array_equal(vm[..., 1], uc.vzero)
+    # counters[3]: largest value scale of the unit, as fp16 bits
+    vmax = int(uc.vscale.view(np.uint16).max()) if nq else 0
+    assert int(st["counters"][u, 3]) == vmax, (int(st["counters"][u, 3]), vmax)
     RB = st["kring"].shape[1]
     for t in range(nq, T):
         assert np.array_equal(st["kring"][u, t % RB].view(np.uint16), uc.k16[t].view(np.uint16))
