@@ -43,25 +43,34 @@ constexpr int D = kHeadDim;
 constexpr int kRec = D + 2;  // partial record: o[d], m, l
 constexpr int kMaxSplits = 1056;
 constexpr int kH2OChunk = 2048;
-// LDS of the fp16 partition: K/V tiles, queries and probabilities
-// (64 rows x 2 x 256 B + 4 x 256 B + 4 x 256 B).
-constexpr int kFp16Bytes = 64 * D * 2 * 2 + 4 * D * 2 + 4 * 64 * 4;
+// LDS of the fp16 partition: queries and probabilities (4 x 256 B + 4 x 256 B).
+constexpr int kFp16Bytes = 4 * D * 2 + 4 * 64 * 4;
 
 // Per-wavefront LDS of the quantized path: a ring of kStages chunk stages
 // filled by direct global->LDS loads (codes, value scales, key scales, pool
 // mask word); after the loop the same bytes hold the output accumulators. The
 // folded-query table and the probability exchange live in LDS objects of their
 // own, so that writing them never waits on the ring's copies in flight.
+#ifndef KVQ_RING_STAGES
+#define KVQ_RING_STAGES 2
+#endif
+#ifndef KVQ_SPLIT_EXP
+#define KVQ_SPLIT_EXP 1
+#endif
+#ifndef KVQ_MIN_WAVES
+#define KVQ_MIN_WAVES 4
+#endif
 template <int BITS>
 struct Ring {
-    static constexpr int kStages = 3;
+    static constexpr int kStages = KVQ_RING_STAGES;
     static constexpr int kCodes = 128 * BITS * 4;          // packed codes of one chunk
     static constexpr int kMeta = 1024;                      // value (<= 512 B) + key (512 B) scales
     static constexpr int kStage = 2 * kCodes + kMeta + 16;  // + pool mask word
     static constexpr int kLoads = 2 * (kCodes / 1024) + 2;  // loads issued per stage
     static constexpr int kWave = kStages * kStage;          // ring bytes per wavefront
     static constexpr int kBlock = 4 * kWave > kFp16Bytes ? 4 * kWave : kFp16Bytes;
-    static_assert(kWave >= (2048 + 48) * 4, "epilogue fits the wavefront's ring");
+    // epilogue: accumulators of tiles 0-5 in the ring, 6-7 in the query table
+    static_assert(kWave >= 6 * 64 * 4 * 4, "epilogue fits the wavefront's ring");
 };
 
 __device__ __forceinline__ void lds_load16(const void* g, void* lds) {
@@ -210,6 +219,18 @@ __device__ __forceinline__ uint32_t mul_pk_res(float a0, uint32_t s0, float a1, 
     return d;
 }
 
+// Words 0-3 shifted left by 4, right by 4 and rotated left by 8 bits: the
+// three moves that bring every 2-bit code position to bits 6-9 (positions 3, 4).
+__device__ __forceinline__ void moved4(const uint32_t* w, uint32_t* l4, uint32_t* r4,
+                                       uint32_t* o8) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        l4[m] = w[m] << 4;
+        r4[m] = w[m] >> 4;
+        o8[m] = __builtin_amdgcn_alignbit(w[m], w[m], 24);
+    }
+}
+
 __device__ __forceinline__ void wave_lds_fence() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
@@ -217,16 +238,16 @@ __device__ __forceinline__ void wave_lds_fence() {
 
 // One 64-row tile of the fp16 partition of unit u: rows are the residual
 // ring tokens [n_q, T), then the pool members, then the extra-pool members.
-// The block stages the tile's K and V rows in LDS; wavefront h < r then takes
-// query head h (one token per lane for the logits, two channels per lane for
-// the outputs) and writes one partial record.
+// Wavefront h < r takes query head h. Logits: one row per lane, the row read
+// straight from memory and dotted with the query (fp16 x fp16 products are
+// exact in the fp32 dot2 accumulation). Outputs: lane (row phase l / 16,
+// channel block l % 16) accumulates 8 channels over every fourth row, then the
+// four row phases are summed across lanes.
 template <int R>
 __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
     const int tid = threadIdx.x, lane = tid & 63, h = tid >> 6;
-    uint16_t* kt = reinterpret_cast<uint16_t*>(smem);  // [64][D] fp16
-    uint16_t* vt = kt + 64 * D;                         // [64][D] fp16
-    uint32_t* qh = reinterpret_cast<uint32_t*>(vt + 64 * D);  // [R][D/2] fp16 pairs
-    float* ps = reinterpret_cast<float*>(qh + R * D / 2);     // [R][64]
+    uint32_t* qh = reinterpret_cast<uint32_t*>(smem);      // [R][D/2] fp16 pairs
+    float* ps = reinterpret_cast<float*>(qh + R * D / 2);  // [R][64]
     const int b = u / a.n_kv_heads, hk = u % a.n_kv_heads;
     const uint32_t* qsrc =
         reinterpret_cast<const uint32_t*>(a.q + ((int64_t)b * a.n_kv_heads * R + hk * R) * D);
@@ -238,49 +259,46 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
     const int N = a.pool, E = a.evict_cap, RB = a.ring_slots;
     const int64_t base = (int64_t)tile * 64;
     const int cnt = (int)(ntot - base < 0 ? 0 : ntot - base < 64 ? ntot - base : 64);
-    // Row li of the partition: ring slot (n_q + li) % RB, or a pool / extra-pool row.
+    // Row i of the tile: ring slot (n_q + base + i) % RB, or a pool / extra-pool row.
     const int64_t slot0 = (a.n_q + base) % RB;
-    auto row_of = [&](int i, const uint16_t* ring, const uint16_t* pool,
-                      const uint16_t* ev) -> const uint16_t* {
+    auto row_off = [&](int i, bool& in_ring) -> int64_t {
         const int64_t li = base + i;
+        in_ring = li < nres;
         if (li < nres) {
             int64_t sl = slot0 + i;
             if (sl >= RB) sl -= RB;
-            return ring + ((int64_t)u * RB + sl) * D;
+            return ((int64_t)u * RB + sl) * D;
         }
-        if (li < nres + pc) return pool + ((int64_t)u * N + (li - nres)) * D;
-        return ev + ((int64_t)u * E + (li - nres - pc)) * D;
+        if (li < nres + pc) return ((int64_t)u * N + (li - nres)) * D;
+        return -1 - ((int64_t)u * E + (li - nres - pc)) * D;  // extra pool: encoded negative
     };
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int e = tid + 256 * r;
-        const int i = e / 16, part = e % 16;
-        if (i < cnt) {
-            reinterpret_cast<uint4*>(kt)[e] =
-                reinterpret_cast<const uint4*>(row_of(i, a.kring, a.pool_k, a.ev_k))[part];
-            reinterpret_cast<uint4*>(vt)[e] =
-                reinterpret_cast<const uint4*>(row_of(i, a.vring, a.pool_v, a.ev_v))[part];
-        }
-    }
+    auto row_ptr = [&](int i, const uint16_t* ring, const uint16_t* pool,
+                       const uint16_t* ev) -> const uint16_t* {
+        bool in_ring;
+        const int64_t o = row_off(i, in_ring);
+        if (in_ring) return ring + o;
+        return o >= 0 ? pool + o : ev + (-1 - o);
+    };
     __syncthreads();
     if (h >= R) return;
     float s = -INFINITY;
     if (lane < cnt) {
-        // fp16 x fp16 products are exact in the fp32 dot2 accumulation
-        float acc = 0.f;
-        const uint32_t* qr = qh + h * (D / 2);
+        const uint4* kr = reinterpret_cast<const uint4*>(row_ptr(lane, a.kring, a.pool_k, a.ev_k));
+        uint4 x[16];
 #pragma unroll
-        for (int c8 = 0; c8 < D / 8; ++c8) {
-            const int cx = (c8 + lane) & 15;  // rotate to spread LDS banks
-            const uint4 x = reinterpret_cast<const uint4*>(kt + lane * D)[cx];
-            const uint4 y = reinterpret_cast<const uint4*>(qr)[cx];
-            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, x.x),
+        for (int c8 = 0; c8 < 16; ++c8) x[c8] = kr[c8];
+        const uint4* qr = reinterpret_cast<const uint4*>(qh + h * (D / 2));
+        float acc = 0.f;
+#pragma unroll
+        for (int c8 = 0; c8 < 16; ++c8) {
+            const uint4 y = qr[c8];
+            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, x[c8].x),
                                          __builtin_bit_cast(half2_t, y.x), acc, false);
-            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, x.y),
+            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, x[c8].y),
                                          __builtin_bit_cast(half2_t, y.y), acc, false);
-            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, x.z),
+            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, x[c8].z),
                                          __builtin_bit_cast(half2_t, y.z), acc, false);
-            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, x.w),
+            acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, x[c8].w),
                                          __builtin_bit_cast(half2_t, y.w), acc, false);
         }
         s = acc * a.qscale;
@@ -297,26 +315,39 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
     const float l = wave_sum(p);
     ps[h * 64 + lane] = p;
     wave_lds_fence();
-    // Outputs: lane owns channels 2*lane, 2*lane+1; p is 0 for rows past cnt.
-    float o0 = 0.f, o1 = 0.f;
-    const uint32_t* vw = reinterpret_cast<const uint32_t*>(vt) + lane;
+    // Outputs: lane (phase rp, block cb) takes channels 8 cb .. 8 cb + 7 of rows
+    // rp, rp + 4, ...; p is 0 past cnt.
+    const int rp = lane >> 4, cb = lane & 15;
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const float* ph = ps + h * 64;
-    for (int i0 = 0; i0 < cnt; i0 += 8) {
-        const floatx4 pa = *reinterpret_cast<const floatx4*>(ph + i0);
-        const floatx4 pb = *reinterpret_cast<const floatx4*>(ph + i0 + 4);
-        const float pv[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
-        uint32_t wv[8];
+    for (int i0 = 0; i0 < cnt; i0 += 16) {
+        uint4 w[4];
+        float pv[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) wv[i] = i0 + i < cnt ? vw[(i0 + i) * (D / 2)] : 0u;
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 4 * r + rp;
+            pv[r] = ph[i < 64 ? i : 63];
+            w[r] = i < cnt ? reinterpret_cast<const uint4*>(
+                                 row_ptr(i, a.vring, a.pool_v, a.ev_v))[cb]
+                           : make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            o0 += pv[i] * h2f(wv[i] & 0xFFFF);
-            o1 += pv[i] * h2f(wv[i] >> 16);
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t ww[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                o[2 * c] += pv[r] * h2f(ww[c] & 0xFFFF);
+                o[2 * c + 1] += pv[r] * h2f(ww[c] >> 16);
+            }
         }
     }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = sum_x32(sum_x16(o[c]));
     float* rec = a.part + (((int64_t)u * a.splits + a.splits_q + tile) * R + h) * kRec;
-    rec[2 * lane] = o0;
-    rec[2 * lane + 1] = o1;
+    if (rp == 0) {
+        *reinterpret_cast<floatx4*>(rec + 8 * cb) = floatx4{o[0], o[1], o[2], o[3]};
+        *reinterpret_cast<floatx4*>(rec + 8 * cb + 4) = floatx4{o[4], o[5], o[6], o[7]};
+    }
     if (lane == 0) {
         rec[D] = m;
         rec[D + 1] = l;
@@ -324,18 +355,19 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
 }
 
 template <int BITS, int R, int G>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAVES))) void decode_kernel(DecodeArgs a) {
     constexpr int NG = D / G;        // value groups per token
     constexpr int CPG = G / 32;      // chunks per key group
     constexpr int WPC = 128 * BITS;  // words per chunk
     // With r = 4 the 16 MFMA columns hold 4 copies of each head's logits;
     // each copy then exponentiates a quarter of the tokens.
-    constexpr bool kSplitExp = R == 4;
+    constexpr bool kSplitExp = R == 4 && KVQ_SPLIT_EXP;
+    constexpr bool kMirror = kSplitExp;
     // Code operands. A code masked in place at bits [p, p + b) of both 16-bit
     // halves is the pair of fp16 subnormals code * 2^(p - 24): exact, one AND.
     // The matrix cores align products by the encoded exponent, so codes are
     // kept at bits 6-9 (at most two leading zero bits; lower positions cost
-    // precision): at b = 2 every pair is rotated to bits 6-7 or 8-9, at b = 4
+    // precision): at b = 2 every pair is moved to bits 6-7 or 8-9, at b = 4
     // value nibbles are shifted to bits 4-7. Each matrix-core operand takes all
     // its pairs from one position, so the weight 2^(p - 24) is common to the
     // operand and is taken out elsewhere (keys: in the folded query; values:
@@ -379,15 +411,24 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const uint32_t* mk_u = a.mask + (int64_t)u * a.chunks;
 
     // MFMA lane roles: j = column / row within a 16-lane row, kb = k-block.
-    const int j = lane & 15, kb = lane >> 4;
-    // Query-fold role: head hb, channels cb0 .. cb0+7 (k-step ksb, k-block kbb).
-    const int hb = lane % R, kap = (lane >> 2) & 15, ksb = kap >> 2, kbb = kap & 3;
+    const int j = lane & 15, kb = lane >> 4, jj = j & 7;
+    // Logit columns. With r = 4 (kMirror) column j holds head hq, the hi
+    // (pq = 0) or lo (pq = 1) half of the folded query, copy cq: within each
+    // half-row of 8 lanes, the lo column of a head mirrors its hi column, so
+    // one row_half_mirror add gives both lanes the full logit. Otherwise the
+    // columns repeat head j % r and hi/lo are two k-steps.
+    const int hq = kMirror ? (jj < 4 ? jj : 7 - jj) : j % R;
+    const int pq = jj < 4 ? 0 : 1;
+    const int cq = kMirror ? pq + 2 * (j >> 3) : j >> 2;
+    // Query-fold role: head hb, channels cb0 .. cb0+7 (k-step ksb, k-block kbb);
+    // with kMirror the lanes of one head in a row are its four logit columns.
+    const int hb = kMirror ? hq : lane % R, kap = (lane >> 2) & 15, ksb = kap >> 2, kbb = kap & 3;
     const int cb0 = 32 * ksb + 8 * kbb;
-    // Softmax / value-operand role: row j = (head j % R, value group gs); with
-    // kSplitExp, copy gr of the head owns token slots 2gr, 2gr+1.
+    // Value-operand role: row j = (head ha = j % r, value group gs); with
+    // kSplitExp, copy cq of head hq owns token slots 2cq, 2cq+1.
+    const int ha = j % R;
     const int gs = (j / R) % NG;
-    const int gr = j >> 2;
-    const int own_tok = 16 * (gr >> 1) + 4 * kb + 2 * (gr & 1);  // first owned token
+    const int own_tok = 16 * (cq >> 1) + 4 * kb + 2 * (cq & 1);  // first owned token
 
     float qv[8];
     {
@@ -445,8 +486,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const int64_t tb = (int64_t)(gi * CPG + cc) * 32;
         const uint32_t st = lds_addr(wlds + (k % RG::kStages) * RG::kStage);
         const uint32_t meta = st + 2 * RG::kCodes;
-        if (later >= 2) wait_vm<2 * RG::kLoads>();
-        else if (later == 1) wait_vm<RG::kLoads>();
+        // stages issued after this one: min(kStages - 1, later)
+        if (RG::kStages >= 3 && later >= 2) wait_vm<2 * RG::kLoads>();
+        else if (later >= 1) wait_vm<RG::kLoads>();
         else wait_vm<0>();
         u32x4 wk0 = ring_read(st + lane * 16), wk1 = wk0;
         u32x4 wv0 = ring_read(st + RG::kCodes + lane * 16), wv1 = wv0;
@@ -494,7 +536,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             *reinterpret_cast<u32x4*>(e0) = u32x4{hiw[0], hiw[1], hiw[2], hiw[3]};
             *reinterpret_cast<u32x4*>(e0 + 4 * 16) = u32x4{low[0], low[1], low[2], low[3]};
             bp += row_ror<8>(bp);
-            bp += row_ror<4>(bp);
+            bp += kMirror ? dpp<0x141>(bp) : row_ror<4>(bp);  // row_half_mirror
             beta = sum_x32(sum_x16(bp));
             wave_lds_fence();
         }
@@ -502,14 +544,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         // Logits S^T[token][(head, g)] on the matrix cores: two 16-token tiles,
         // K = 128 channels x {hi, lo}.
         const uint32_t wk[8] = {wk0.x, wk0.y, wk0.z, wk0.w, wk1.x, wk1.y, wk1.z, wk1.w};
-        uint32_t wkL4[4], wkR4[4], wkL8[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            wkL4[m] = __builtin_amdgcn_alignbit(wk[m], wk[m], 28);
-            wkR4[m] = __builtin_amdgcn_alignbit(wk[m], wk[m], 4);
-            wkL8[m] = __builtin_amdgcn_alignbit(wk[m], wk[m], 24);
-        }
-        floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc0l = acc0, acc1l = acc0;
+        uint32_t wkL4[4], wkR4[4], wkO8[4];
+        moved4(wk, wkL4, wkR4, wkO8);
+        floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             half8 A0, A1;
@@ -518,7 +555,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                 // 0..3), tile 1 at 5, 6, 7, 0; even k-steps end at bits 6-7
                 const uint32_t mk = ks % 2 == 0 ? 0x00C000C0u : 0x03000300u;
                 const uint32_t* x0 = ks < 2 ? wk : wkL4;
-                const uint32_t* x1 = ks < 2 ? wkR4 : wkL8;
+                const uint32_t* x1 = ks < 2 ? wkR4 : wkO8;
                 A0 = as_half8(x0[0] & mk, x0[1] & mk, x0[2] & mk, x0[3] & mk);
                 A1 = as_half8(x1[0] & mk, x1[1] & mk, x1[2] & mk, x1[3] & mk);
             } else {
@@ -526,46 +563,60 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                 A0 = as_half8(cvt4(w0, 6), cvt4(w0, 2), cvt4(w0, -2), cvt4(w0, -6));
                 A1 = as_half8(cvt4(w1, 6), cvt4(w1, 2), cvt4(w1, -2), cvt4(w1, -6));
             }
-            const half8 Bh = *reinterpret_cast<const half8*>(
-                btab + ((((ks * 4 + kb) * 2 + 0) * 4) + (j % R)) * 16);
-            const half8 Bl = *reinterpret_cast<const half8*>(
-                btab + ((((ks * 4 + kb) * 2 + 1) * 4) + (j % R)) * 16);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bh, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh, acc1, 0, 0, 0);
-            acc0l = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bl, acc0l, 0, 0, 0);
-            acc1l = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, acc1l, 0, 0, 0);
+            if (kMirror) {
+                const half8 B = *reinterpret_cast<const half8*>(
+                    btab + ((((ks * 4 + kb) * 2 + pq) * 4) + hq) * 16);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, B, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, B, acc1, 0, 0, 0);
+            } else {
+                const half8 Bh = *reinterpret_cast<const half8*>(
+                    btab + ((((ks * 4 + kb) * 2 + 0) * 4) + hq) * 16);
+                const half8 Bl = *reinterpret_cast<const half8*>(
+                    btab + ((((ks * 4 + kb) * 2 + 1) * 4) + hq) * 16);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bh, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh, acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bl, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, acc1, 0, 0, 0);
+            }
         }
-        acc0 += acc0l;
-        acc1 += acc1l;
+        if (kMirror) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc0[i] += dpp<0x141>(acc0[i]);  // hi + lo of the head
+                acc1[i] += dpp<0x141>(acc1[i]);
+            }
+        }
         const uint32_t mw = __builtin_amdgcn_readfirstlane(mwv);  // same word in every lane
         float p[8];
-        float mnew;
         if constexpr (kSplitExp) {
-            // This lane's two tokens (slots 2gr, 2gr+1 of its k-block).
-            const float a0 = gr & 1 ? acc0[2] : acc0[0], b0 = gr & 1 ? acc1[2] : acc1[0];
-            const float a1 = gr & 1 ? acc0[3] : acc0[1], b1 = gr & 1 ? acc1[3] : acc1[1];
-            float s0 = fmaf(gr < 2 ? a0 : b0, kAccW, beta), s1 = fmaf(gr < 2 ? a1 : b1, kAccW, beta);
+            // This lane's two tokens (slots 2cq, 2cq+1 of its k-block).
+            const float a0 = cq & 1 ? acc0[2] : acc0[0], b0 = cq & 1 ? acc1[2] : acc1[0];
+            const float a1 = cq & 1 ? acc0[3] : acc0[1], b1 = cq & 1 ? acc1[3] : acc1[1];
+            float s0 = fmaf(cq < 2 ? a0 : b0, kAccW, beta), s1 = fmaf(cq < 2 ? a1 : b1, kAccW, beta);
             if (mw) {
                 if ((mw >> own_tok) & 1u) s0 = -INFINITY;
                 if ((mw >> (own_tok + 1)) & 1u) s1 = -INFINITY;
             }
             if (a.logits) {
-                float* lg = a.logits + ((int64_t)u * R + hb) * a.T + tb + own_tok;
+                float* lg = a.logits + ((int64_t)u * R + hq) * a.T + tb + own_tok;
                 if (s0 != -INFINITY) lg[0] = s0;
                 if (s1 != -INFINITY) lg[1] = s1;
             }
-            float cm = fmaxf(s0, s1);
-            cm = fmaxf(cm, row_ror<8>(cm));
-            cm = fmaxf(cm, row_ror<4>(cm));
-            cm = max_x32(max_x16(cm));
-            mnew = fmaxf(m_run, cm);
-            if (__any(mnew > m_thr)) {
+            // The wavefront max is only needed when some logit passes the
+            // threshold (always on the first chunk, rarely afterwards).
+            const float lm = fmaxf(s0, s1);
+            if (__any(lm > m_thr)) {
+                float cm = fmaxf(lm, row_ror<8>(lm));
+                cm = fmaxf(cm, dpp<0x141>(cm));  // row_half_mirror: the head's four columns
+                cm = max_x32(max_x16(cm));
+                const float mnew = fmaxf(m_run, cm);
                 if (__builtin_amdgcn_readfirstlane(m_run != -INFINITY)) {
                     const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+                    // per head h, from lane h (whose logit head is h)
+                    const float ah[4] = {readlane(alpha, 0), readlane(alpha, 1), readlane(alpha, 2),
+                                         readlane(alpha, 3)};
                     lsum *= alpha;
-                    zc *= alpha;
-                    const float ah[4] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha),
-                                         quad_bcast<2>(alpha), quad_bcast<3>(alpha)};
+                    zc *= (lane & 3) == 0 ? ah[0] : (lane & 3) == 1 ? ah[1] : (lane & 3) == 2 ? ah[2] : ah[3];
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -577,9 +628,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             const float mu = m_run == -INFINITY ? 0.f : m_run;
             const float p0 = __builtin_amdgcn_exp2f(s0 - mu), p1 = __builtin_amdgcn_exp2f(s1 - mu);
             lsum += p0 + p1;
-            float* ph = pbuf + hb * 32;
-            *reinterpret_cast<float2*>(ph + own_tok) = float2{p0, p1};
+            *reinterpret_cast<float2*>(pbuf + hq * 32 + own_tok) = float2{p0, p1};
             wave_lds_fence();
+            const float* ph = pbuf + ha * 32;
             const floatx4 pa = *reinterpret_cast<const floatx4*>(ph + 4 * kb);
             const floatx4 pb = *reinterpret_cast<const floatx4*>(ph + 16 + 4 * kb);
 #pragma unroll
@@ -607,12 +658,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                 for (int sl = 0; sl < 8; ++sl)
                     if (s[sl] != -INFINITY) lg[16 * (sl / 4) + sl % 4] = s[sl];
             }
-            float cm = s[0];
+            float lm = s[0];
 #pragma unroll
-            for (int sl = 1; sl < 8; ++sl) cm = fmaxf(cm, s[sl]);
-            cm = max_x32(max_x16(cm));
-            mnew = fmaxf(m_run, cm);
-            if (__any(mnew > m_thr)) {
+            for (int sl = 1; sl < 8; ++sl) lm = fmaxf(lm, s[sl]);
+            if (__any(lm > m_thr)) {
+                const float cm = max_x32(max_x16(lm));
+                const float mnew = fmaxf(m_run, cm);
                 if (__builtin_amdgcn_readfirstlane(m_run != -INFINITY)) {
                     const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
                     lsum *= alpha;
@@ -653,6 +704,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const half8 Ahi = as_half8(ahw[0], ahw[1], ahw[2], ahw[3]);
         const half8 Alo = as_half8(alw[0], alw[1], alw[2], alw[3]);
         const uint32_t wv[8] = {wv0.x, wv0.y, wv0.z, wv0.w, wv1.x, wv1.y, wv1.z, wv1.w};
+        uint32_t wvL4[4], wvR4[4], wvO8[4];
+        if (BITS == 2) moved4(wv, wvL4, wvR4, wvO8);
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
             uint32_t x[4];
@@ -660,10 +713,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             for (int m = 0; m < 4; ++m) {
                 if (BITS == 2) {
                     // tile nt at position 3, 4, 1, 2, 5, 6, 7, 0 of word m
-                    const uint32_t w = wv[m];
-                    const uint32_t r = nt < 2 ? w : nt < 4 ? __builtin_amdgcn_alignbit(w, w, 28)
-                                     : nt < 6 ? __builtin_amdgcn_alignbit(w, w, 4)
-                                              : __builtin_amdgcn_alignbit(w, w, 24);
+                    const uint32_t r = nt < 2 ? wv[m] : nt < 4 ? wvL4[m] : nt < 6 ? wvR4[m] : wvO8[m];
                     x[m] = r & (nt % 2 == 0 ? 0x00C000C0u : 0x03000300u);
                 } else {
                     // nibble j of word 4*(nt/4) + m, moved to bits 4-7
@@ -680,9 +730,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     };
 
     // Pipeline: stages k+1 and k+2 are in flight while stage k computes.
-    for (uint32_t k = 0; k < 2 && k < n_items; ++k) issue(k);
+    constexpr uint32_t kAhead = RG::kStages - 1;
+    for (uint32_t k = 0; k < kAhead && k < n_items; ++k) issue(k);
     for (uint32_t k = 0; k < n_items; ++k) {
-        if (k + 2 < n_items) issue(k + 2);
+        if (k + kAhead < n_items) issue(k + kAhead);
         step(k, n_items - 1 - k);  // stages issued after k: min(2, n_items - 1 - k)
     }
     wave_lds_fence();
@@ -692,16 +743,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     float lt = lsum;
     if (kSplitExp) {
         lt += row_ror<8>(lt);
-        lt += row_ror<4>(lt);
+        lt += dpp<0x141>(lt);  // row_half_mirror
     }
     lt = sum_x32(sum_x16(lt));
     const float zt = sum_x32(sum_x16(zc));
-    float* obuf = wsm;               // [8][64][4] (reuses the ring)
-    float* Zs = wsm + 2048;          // [16] sum_t p z^V per row
-    float* ms = Zs + 16;             // [4]
-    float* ls = ms + 4;              // [4]
+    // Accumulators as they sit in the registers: tiles 0-5 in the ring, 6-7 in
+    // the query table; row totals in the probability buffer.
+    float* obuf = wsm;                               // [6][64][4]
+    float* obuf2 = reinterpret_cast<float*>(btab);   // [2][64][4]
+    float* Zs = pbuf;                                // [16] sum_t p z^V per row
+    float* ms = Zs + 16;                             // [4]
+    float* ls = ms + 4;                              // [4]
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) *reinterpret_cast<floatx4*>(obuf + (nt * 64 + lane) * 4) = O[nt];
+    for (int nt = 0; nt < 8; ++nt)
+        *reinterpret_cast<floatx4*>((nt < 6 ? obuf + nt * 256 : obuf2 + (nt - 6) * 256) + lane * 4) = O[nt];
     if (kb == 0) {
         Zs[j] = zt;
         if (j < R) {
@@ -714,24 +769,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     for (int e = threadIdx.x; e < R * D; e += 256) {
         const int h = e / D, c = e % D;
         const int ir = h + R * (c / G);  // accumulator row (head, value group)
-        const int src = ((c / 16) * 64 + (c % 16) + 16 * (ir / 4)) * 4 + ir % 4;
-        // weight of tile c / 16's code operands: 2^(pos - 24)
         const int nt = c / 16;
+        const int src = ((nt % 6) * 64 + (c % 16) + 16 * (ir / 4)) * 4 + ir % 4;
+        // weight of tile nt's code operands: 2^(pos - 24)
         const int pos = BITS == 2 ? (nt % 2 == 0 ? 6 : 8) : 4;
         float mw[4], M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            mw[w] = smem[w * (RG::kWave / 4) + 2048 + 16 + h];
+            mw[w] = s_pbuf[w][16 + h];
             M = fmaxf(M, mw[w]);
         }
         float o = 0.f, l = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const float* wb = smem + w * (RG::kWave / 4);
+                const float* ob = nt < 6 ? smem + w * (RG::kWave / 4)
+                                         : reinterpret_cast<const float*>(s_btab[w]);
                 const float f = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
-                o += (ldexpf(wb[src], 24 - pos) + wb[2048 + ir]) * f;
-                l += wb[2048 + 20 + h] * f;
+                o += (ldexpf(ob[src], 24 - pos) + s_pbuf[w][ir]) * f;
+                l += s_pbuf[w][20 + h] * f;
             }
         }
         float* rec = a.part + (((int64_t)u * a.splits + split) * R + h) * kRec;

@@ -206,10 +206,10 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
 }
 
 // 2-bit position of operand pair j (0..7) inside a packed word: the decoder
-// brings positions 3 and 4 (bits 6-9 of each half) into place directly,
-// 1-2 by a 4-bit left rotate, 5-6 by a 4-bit right rotate and 7, 0 by an
-// 8-bit left rotate, which also swaps the halves of position 7 (stored
-// swapped for that reason). Even j ends at bits 6-7, odd j at bits 8-9.
+// uses positions 3 and 4 (bits 6-9 of each half) in place, brings 1-2 there
+// by a 4-bit left shift, 5-6 by a 4-bit right shift, and 0 and 7 by one 8-bit
+// left rotate, which also swaps the two halves of position 7 (stored swapped
+// for that reason). Even j ends at bits 6-7, odd j at bits 8-9.
 __device__ constexpr int kPos2[8] = {3, 4, 1, 2, 5, 6, 7, 0};
 
 // Quantize and pack one key group (G tokens) of one unit; 256 threads.
