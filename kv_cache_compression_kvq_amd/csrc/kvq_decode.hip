@@ -810,6 +810,16 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     const float* base = a.part + (int64_t)u * S * R * kRec;
     if (wave < R) {
         const int h = wave;
+        // Outputs: lane owns channels 2 lane, 2 lane + 1. The first splits' rows
+        // are requested together with the (m, l) pairs.
+        constexpr int kPre = 16;
+        float2 xp[kPre];
+        if (blockIdx.y == 0) {
+#pragma unroll
+            for (int s = 0; s < kPre; ++s)
+                xp[s] = s < S ? *reinterpret_cast<const float2*>(base + (s * R + h) * kRec + 2 * lane)
+                              : make_float2(0.f, 0.f);
+        }
         float m = -INFINITY;
         for (int s = lane; s < S; s += 64) m = fmaxf(m, base[(s * R + h) * kRec + D]);
         m = wave_max(m);
@@ -821,29 +831,43 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
             l += base[(s * R + h) * kRec + D + 1] * f;
         }
         l = wave_sum(l);
+        const float linv = 1.0f / l;
+        if (blockIdx.y == 0) {
+            wave_lds_fence();  // this wave's split weights are in LDS
+            float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+            for (int s = 0; s < kPre; ++s) {
+                const float f = s < S ? wsp[h][s] : 0.f;
+                o0 += xp[s].x * f;
+                o1 += xp[s].y * f;
+            }
+            for (int s = kPre; s < S; ++s) {
+                const float2 x = *reinterpret_cast<const float2*>(base + (s * R + h) * kRec + 2 * lane);
+                const float f = wsp[h][s];
+                o0 += x.x * f;
+                o1 += x.y * f;
+            }
+            const int b = u / a.n_kv_heads, hk = u % a.n_kv_heads;
+            *reinterpret_cast<float2*>(a.out + ((int64_t)b * a.n_kv_heads * R + hk * R + h) * D + 2 * lane) =
+                make_float2(o0 * linv, o1 * linv);
+            return;
+        }
         if (lane == 0) {
             Ms[h] = m;
-            Linv[h] = 1.0f / l;
+            Linv[h] = linv;
         }
     }
+    if (blockIdx.y == 0) return;
     __syncthreads();
-    if (blockIdx.y == 0) {
-        const int b = u / a.n_kv_heads, hk = u % a.n_kv_heads;
-        for (int e = threadIdx.x; e < R * D; e += 256) {
-            const int h = e / D, c = e % D;
-            float o = 0.f;
-            for (int s = 0; s < S; ++s) o += base[(s * R + h) * kRec + c] * wsp[h][s];
-            a.out[((int64_t)b * a.n_kv_heads * R + hk * R + h) * D + c] = o * Linv[h];
-        }
-    } else {
-        const int64_t t0 = (int64_t)(blockIdx.y - 1) * kH2OChunk;
-        for (int64_t t = t0 + threadIdx.x; t < t0 + kH2OChunk && t < a.T; t += 256) {
-            float d = 0.f;
+    // H2O increments of a 2048-token slice: sum over the r query heads of the
+    // normalized probabilities.
+    const int64_t t0 = (int64_t)(blockIdx.y - 1) * kH2OChunk;
+    for (int64_t t = t0 + threadIdx.x; t < t0 + kH2OChunk && t < a.T; t += 256) {
+        float d = 0.f;
 #pragma unroll
-            for (int h = 0; h < R; ++h)
-                d += __builtin_amdgcn_exp2f(a.logits[((int64_t)u * R + h) * a.T + t] - Ms[h]) * Linv[h];
-            a.acc[(int64_t)u * a.T + t] += d;
-        }
+        for (int h = 0; h < R; ++h)
+            d += __builtin_amdgcn_exp2f(a.logits[((int64_t)u * R + h) * a.T + t] - Ms[h]) * Linv[h];
+        a.acc[(int64_t)u * a.T + t] += d;
     }
 }
 
