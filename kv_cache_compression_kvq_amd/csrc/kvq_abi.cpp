@@ -140,7 +140,12 @@ DecodePlan plan_decode(const kvq_cache* h, bool want_scores) {
     const int64_t fp16_rows = (h->tokens - h->n_quant) +
                               (h->cfg.pool > 0 ? h->cfg.pool + h->cfg.evict_cap : 0);
     p.splits_q = (int32_t)s;
-    p.fp16_tiles = (int32_t)(fp16_rows > 0 ? (fp16_rows + 63) / 64 : 1);
+    // fp16 tiles of 16 to 64 rows; the launch picks the count (about one tile
+    // block per compute unit), the workspace covers the largest choice
+    int64_t t = fp16_rows > 0 ? (fp16_rows + 15) / 16 : 1;
+    if (t > kMaxFp16Tiles) t = kMaxFp16Tiles;
+    if (t < (fp16_rows + 63) / 64) t = (fp16_rows + 63) / 64;
+    p.fp16_tiles = (int32_t)t;
     p.splits = p.splits_q + p.fp16_tiles;
     p.part_floats = U * p.splits * r * (kHeadDim + 2);
     p.logit_floats = want_scores ? U * r * h->tokens : 0;

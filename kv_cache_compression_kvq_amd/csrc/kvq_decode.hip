@@ -131,6 +131,7 @@ struct DecodeArgs {
     float* acc;
     int64_t T, n_q, chunks, key_groups;
     int32_t units, n_kv_heads, ring_slots, splits_q, splits, fp16_tiles, pool, evict_cap;
+    int32_t tile_rows;  // rows per fp16-partition tile (<= 64)
     float qscale;  // log2(e) / sqrt(d)
 };
 
@@ -257,8 +258,8 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
     const int ec = a.pool > 0 ? a.counters[(int64_t)u * 4 + 1] : 0;
     const int64_t ntot = nres + pc + ec;
     const int N = a.pool, E = a.evict_cap, RB = a.ring_slots;
-    const int64_t base = (int64_t)tile * 64;
-    const int cnt = (int)(ntot - base < 0 ? 0 : ntot - base < 64 ? ntot - base : 64);
+    const int64_t base = (int64_t)tile * a.tile_rows;
+    const int cnt = (int)(ntot - base < 0 ? 0 : ntot - base < a.tile_rows ? ntot - base : a.tile_rows);
     // Row i of the tile: ring slot (n_q + base + i) % RB, or a pool / extra-pool row.
     const int64_t slot0 = (a.n_q + base) % RB;
     auto row_off = [&](int i, bool& in_ring) -> int64_t {
@@ -897,8 +898,34 @@ int resident_blocks() {
     return cached[dev];
 }
 
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
 template <int BITS, int R, int G>
 void launch_decode_t(DecodeArgs a, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
+    // fp16 tiles: about one tile block per compute unit, so that every unit
+    // hosts the same mix of blocks; 16 to 64 rows each.
+    {
+        // rows of the partition at most: ring tokens plus full pools
+        const int64_t fp16_rows = (a.T - a.n_q) + (a.pool > 0 ? (int64_t)a.pool + a.evict_cap : 0);
+        int64_t t = ((int64_t)cu_count() + a.units - 1) / a.units;
+        const int64_t t_min = fp16_rows > 0 ? (fp16_rows + 63) / 64 : 1;
+        if (t > a.fp16_tiles) t = a.fp16_tiles;
+        if (t < t_min) t = t_min;
+        a.fp16_tiles = (int32_t)t;
+        a.tile_rows = fp16_rows > 0 ? (int32_t)((fp16_rows + t - 1) / t) : 1;
+    }
     if (a.splits_q > 0) {
         // one resident round: the fp16 tiles plus as many splits per unit as fit
         int64_t q = ((int64_t)resident_blocks<BITS, R, G>() - (int64_t)a.units * a.fp16_tiles) /

@@ -13,7 +13,8 @@ constexpr int kHeadDim = 128;      // d
 constexpr int kChunk = 32;         // tokens per packed chunk
 constexpr int kMaxPool = 64;       // N limit
 constexpr int kMaxEvict = 1024;    // E limit
-constexpr int kMaxFp16Rows = 2048; // R + G + N + E limit (fp16 partition kept in LDS)
+constexpr int kMaxFp16Rows = 2048; // R + G + N + E limit
+constexpr int kMaxFp16Tiles = 56;   // fp16-partition tiles per unit (each at most 64 rows)
 constexpr int kMaxTokens = 1 << 24; // per-unit capacity: keeps per-unit offsets in 32 bits
 
 // Device pointers of one cache, resolved from the arena and the handle's offsets.
@@ -49,7 +50,7 @@ CacheView view_of(const kvq_cache* h);
 struct DecodePlan {
     int32_t splits_q;    // upper bound on quantized-partition splits per unit (0 when
                          // n_q == 0); the launch picks the count that fills the GPU once
-    int32_t fp16_tiles;  // 64-row tiles of the fp16 partition (ring + pools)
+    int32_t fp16_tiles;  // upper bound on fp16-partition tiles (ring + pools), 16-64 rows each
     int32_t splits;      // splits_q + fp16_tiles partial records per unit
     int64_t part_floats; // partial records: U * splits * r * (d + 2)
     int64_t logit_floats;// U * r * T when scores are wanted
