@@ -57,6 +57,9 @@ constexpr int kFp16Bytes = 4 * D * 2 + 4 * 64 * 4;
 #ifndef KVQ_SPLIT_EXP
 #define KVQ_SPLIT_EXP 1
 #endif
+#ifndef KVQ_PRIO_HI
+#define KVQ_PRIO_HI 3
+#endif
 #ifndef KVQ_MIN_WAVES
 #define KVQ_MIN_WAVES 4
 #endif
@@ -734,9 +737,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAV
     constexpr uint32_t kAhead = RG::kStages - 1;
     for (uint32_t k = 0; k < kAhead && k < n_items; ++k) issue(k);
     for (uint32_t k = 0; k < n_items; ++k) {
+        // Issue priority from the work left: the arbiter otherwise favours the
+        // oldest wavefronts, and the youngest ones finish last, alone.
+        const uint32_t left = n_items - k;
+        if (left >= KVQ_PRIO_HI) __builtin_amdgcn_s_setprio(3);
+        else if (left >= KVQ_PRIO_HI - 1) __builtin_amdgcn_s_setprio(2);
+        else if (left >= KVQ_PRIO_HI - 2) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
         if (k + kAhead < n_items) issue(k + kAhead);
         step(k, n_items - 1 - k);  // stages issued after k: min(2, n_items - 1 - k)
     }
+    __builtin_amdgcn_s_setprio(0);
     wave_lds_fence();
 
     // Wavefront epilogue: per-head l, per-row zero-point totals, outputs to LDS
