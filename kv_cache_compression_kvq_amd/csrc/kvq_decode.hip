@@ -63,6 +63,16 @@ constexpr int kFp16Bytes = 4 * D * 2 + 4 * 64 * 4;
 #ifndef KVQ_MIN_WAVES
 #define KVQ_MIN_WAVES 4
 #endif
+// Ring refill: 0 = chunk k + kStages - 1 is requested at the top of iteration
+// k; 1 = chunk k + kStages is requested as soon as chunk k is in registers.
+#ifndef KVQ_DEEP_RING
+#define KVQ_DEEP_RING 0
+#endif
+// 1: every wavefront waits for its first chunk before requesting more, so
+// that the first chunks of all wavefronts lead the start-up burst.
+#ifndef KVQ_START_WAIT
+#define KVQ_START_WAIT 0
+#endif
 template <int BITS>
 struct Ring {
     static constexpr int kStages = KVQ_RING_STAGES;
@@ -96,6 +106,11 @@ __device__ __forceinline__ void wait_vm() {
 // LDS address of a pointer into a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Load of a wave-uniform word that no kernel writes while this one runs,
+// through the scalar data cache (read only).
+__device__ __forceinline__ uint32_t scalar_load(const void* p) {
+    return *(const __attribute__((address_space(4))) uint32_t*)p;
 }
 // Reads of a ring stage. They are issued as inline assembly, after the
 // stage's explicit vmcnt wait, because the compiler cannot tell which ring
@@ -434,21 +449,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAV
     const int gs = (j / R) % NG;
     const int own_tok = 16 * (cq >> 1) + 4 * kb + 2 * (cq & 1);  // first owned token
 
+    // The query row is requested first (inline assembly, so that the
+    // compiler's counter bookkeeping does not wait for every ring stage before
+    // it is used) and converted once the first ring stages are in flight.
+    u32x4 qraw;
+    asm volatile("global_load_dwordx4 %0, %1, off"
+                 : "=v"(qraw)
+                 : "v"(a.q + ((int64_t)b * a.n_kv_heads * R + hk * R + hb) * D + cb0)
+                 : "memory");
     float qv[8];
-    {
-        const uint16_t* qrow = a.q + ((int64_t)b * a.n_kv_heads * R + hk * R + hb) * D + cb0;
-        const uint4 x = *reinterpret_cast<const uint4*>(qrow);
-        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-        // b = 2: this lane's channels (k-step ksb) sit at bits 6-7 (even ksb,
-        // weight 2^-18) or 8-9 (odd ksb, 2^-16); the folded query takes 2^2 or
-        // 2^0 so that every key product carries 2^-16
-        const float wq = BITS == 2 && ksb % 2 == 0 ? 4.f * a.qscale : a.qscale;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            qv[2 * i] = h2f(w[i] & 0xFFFF) * wq;
-            qv[2 * i + 1] = h2f(w[i] >> 16) * wq;
-        }
-    }
 
     // Stage k (chunk k of this wavefront) lands in ring slot k % kStages.
     char* wlds = reinterpret_cast<char*>(smem) + wave * RG::kWave;
@@ -478,7 +487,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAV
     float m_thr = -INFINITY;
     float tau = 8.f;
     {
-        const uint32_t smax = (uint32_t)a.counters[(int64_t)u * 4 + 3] & 0x7FFFu;
+        // wave-uniform and constant during the kernel: a scalar load, so that it
+        // never waits on the ring's vector-memory counter
+        const uint32_t smax = scalar_load(a.counters + (int64_t)u * 4 + 3) & 0x7FFFu;
         if (smax >= 0x0400u) {  // normal: s < 2^(e+1)
             const int e = (int)(smax >> 10) - 15;
             tau = (float)min(8, max(0, 14 - e));
@@ -513,6 +524,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAV
                        "+v"(km0), "+v"(km1), "+v"(mwv)
                      :
                      : "memory");
+        if (KVQ_DEEP_RING) {
+            // The stage is in registers: refill its slot with chunk k + kStages,
+            // so that kStages chunks stay in flight while this one computes.
+            if (KVQ_START_WAIT && k == 0)
+                for (uint32_t j = 1; j < RG::kStages && j < n_items; ++j) issue(j);
+            if (k + RG::kStages < n_items) issue(k + RG::kStages);
+        }
         if (cc == 0) {
             // Fold the key scale into the query: B = hi/lo of q~_c * s_c, and
             // the zero point into beta_h = sum_c q~_c (z_c - 2^b s_c).
@@ -733,9 +751,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAV
         }
     };
 
-    // Pipeline: stages k+1 and k+2 are in flight while stage k computes.
-    constexpr uint32_t kAhead = RG::kStages - 1;
-    for (uint32_t k = 0; k < kAhead && k < n_items; ++k) issue(k);
+    // Pipeline start. The ring stages requested here, after the query row:
+    // the first one only (KVQ_START_WAIT), else kStages (deep refill) or
+    // kStages - 1.
+    constexpr uint32_t kFirst = KVQ_START_WAIT ? 1 : KVQ_DEEP_RING ? RG::kStages : RG::kStages - 1;
+    for (uint32_t k = 0; k < kFirst && k < n_items; ++k) issue(k);
+    if (KVQ_START_WAIT) {
+        wait_vm<0>();  // the query row and the first chunk
+    } else {
+        // the query row only: the stages requested after it may stay in flight
+        const uint32_t issued = n_items < kFirst ? n_items : kFirst;
+        if (issued >= 3) wait_vm<3 * RG::kLoads>();
+        else if (issued == 2) wait_vm<2 * RG::kLoads>();
+        else if (issued == 1) wait_vm<RG::kLoads>();
+        else wait_vm<0>();
+    }
+    asm volatile("" : "+v"(qraw));
+    {
+        // b = 2: this lane's channels (k-step ksb) sit at bits 6-7 (even ksb,
+        // weight 2^-18) or 8-9 (odd ksb, 2^-16); the folded query takes 2^2 or
+        // 2^0 so that every key product carries 2^-16
+        const uint32_t w[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
+        const float wq = BITS == 2 && ksb % 2 == 0 ? 4.f * a.qscale : a.qscale;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            qv[2 * i] = h2f(w[i] & 0xFFFF) * wq;
+            qv[2 * i + 1] = h2f(w[i] >> 16) * wq;
+        }
+    }
     for (uint32_t k = 0; k < n_items; ++k) {
         // Issue priority from the work left: the arbiter otherwise favours the
         // oldest wavefronts, and the youngest ones finish last, alone.
@@ -744,8 +787,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAV
         else if (left >= KVQ_PRIO_HI - 1) __builtin_amdgcn_s_setprio(2);
         else if (left >= KVQ_PRIO_HI - 2) __builtin_amdgcn_s_setprio(1);
         else __builtin_amdgcn_s_setprio(0);
-        if (k + kAhead < n_items) issue(k + kAhead);
-        step(k, n_items - 1 - k);  // stages issued after k: min(2, n_items - 1 - k)
+        if (!KVQ_DEEP_RING) {
+            // chunks k + 1 .. k + kStages - 1 in flight while chunk k computes
+            const uint32_t kn = k + RG::kStages - 1;
+            if (kn < n_items && (KVQ_START_WAIT || kn >= kFirst)) {
+                if (KVQ_START_WAIT && k == 0)
+                    for (uint32_t j = 1; j < kn; ++j) issue(j);
+                issue(kn);
+            }
+        }
+        step(k, n_items - 1 - k);  // stages issued after k: min(kStages - 1, n_items - 1 - k)
     }
     __builtin_amdgcn_s_setprio(0);
     wave_lds_fence();
