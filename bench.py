@@ -254,13 +254,18 @@ def main():
         rep = reps[i % n_rep]
         h = rep["h"]
         nb = 0
+        q = qs[i % n_q_rot]
         if append_mode:
+            # one decode step: append the token, then attend (the attention
+            # kernel stores the token into the fp16 ring)
             nq0 = h.n_quant
-            abi.quantize_append(h, ks[i], vs[i], 1)
+            if ev[0] is not None:
+                abi.decode_step_timed(h, ks[i], vs[i], q, out, rep["acc"], ws, ev[0], ev[1])
+            else:
+                abi.decode_step(h, ks[i], vs[i], q, out, rep["acc"], ws)
             nb += BM.append_bytes(units=U, head_dim=d, n_new=1, bits=w.bits, group=w.group,
                                   groups_packed=(h.n_quant - nq0) // w.group)
-        q = qs[i % n_q_rot]
-        if ev[0] is not None:
+        elif ev[0] is not None:
             abi.decode_attention_timed(rep["h"], q, out, rep["acc"], ws, ev[0], ev[1])
         else:
             abi.decode_attention(rep["h"], q, out, rep["acc"], ws)

@@ -212,6 +212,38 @@ kvq_status kvq_decode_attention_timed(const kvq_cache* h, const void* d_q, float
                                       void* ev_start, void* ev_stop, void* stream);
 
 /*
+/*
+ * One decode step: append one token to every unit, then attend with the
+ * updated cache. Results and cache state are those of
+ *   kvq_quantize_append(h, d_k, d_v, 1, stream);
+ *   kvq_decode_attention(h, d_q, d_out, d_acc, d_ws, ws_bytes, stream);
+ * (MiniKV, Algorithm 1, one generation step; KIVI-style residual window:
+ * "Accurate KV Cache Quantization with Outlier Tokens Tracing", section
+ * "Method details", decoding stage). When the new token stays in the fp16
+ * window, the attention kernel reads it from d_k / d_v and stores it into the
+ * ring itself, so the step costs one kernel less than the two calls.
+ *   d_k, d_v  device fp16 [B][Hkv][1][d], the step's key and value
+ *   d_ws      ws_bytes >= kvq_decode_workspace of the cache after the append
+ *             (T + 1 tokens)
+ * Every argument is checked before anything is enqueued; an error leaves
+ * *h and the cache unchanged. Updates h->tokens and h->n_quant on success.
+ * Errors: KVQ_EINVAL (null pointer), KVQ_ECAPACITY (T + 1 > max_tokens),
+ * KVQ_EWORKSPACE, KVQ_ELAUNCH (then the cache contents are unspecified).
+ */
+kvq_status kvq_decode_step(kvq_cache* h, const void* d_k, const void* d_v, const void* d_q,
+                           float* d_out, float* d_acc, void* d_ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * kvq_decode_step, additionally recording ev_start and ev_stop (hipEvent_t or
+ * NULL) around the attention kernel's own execution, as
+ * kvq_decode_attention_timed does.
+ */
+kvq_status kvq_decode_step_timed(kvq_cache* h, const void* d_k, const void* d_v,
+                                 const void* d_q, float* d_out, float* d_acc, void* d_ws,
+                                 size_t ws_bytes, void* ev_start, void* ev_stop, void* stream);
+
+/*
  * Heavy-hitter selection on fp32 scores (device [rows][T]): for each row keep
  * the k largest scores among indices [0, T - w), ties broken toward the
  * larger index, plus the w most recent indices [T - w, T). Writes device

@@ -25,7 +25,7 @@ KVQ_ELAUNCH = -5
 # Entry points declared in include/kvq.h.
 EXPORTS = ("kvq_status_string", "kvq_cache_bytes", "kvq_cache_init", "kvq_quantize_append",
            "kvq_decode_workspace", "kvq_decode_attention", "kvq_decode_attention_timed",
-           "kvq_topk_evict", "kvq_unpack_codes")
+           "kvq_decode_step", "kvq_decode_step_timed", "kvq_topk_evict", "kvq_unpack_codes")
 
 
 class Config(ctypes.Structure):
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
             "kvq_decode_workspace": [ctypes.POINTER(Cache), I32, ctypes.POINTER(SZ)],
             "kvq_decode_attention": [ctypes.POINTER(Cache), P, P, P, P, SZ, P],
             "kvq_decode_attention_timed": [ctypes.POINTER(Cache), P, P, P, P, SZ, P, P, P],
+            "kvq_decode_step": [ctypes.POINTER(Cache), P, P, P, P, P, P, SZ, P],
+            "kvq_decode_step_timed": [ctypes.POINTER(Cache), P, P, P, P, P, P, SZ, P, P, P],
             "kvq_topk_evict": [P, I32, I32, I32, I32, P, P],
             "kvq_unpack_codes": [ctypes.POINTER(Cache), P, P, P],
         }
@@ -155,6 +157,23 @@ def decode_attention_timed(h: Cache, q, out, acc, ws, ev_start: int, ev_stop: in
     _check("kvq_decode_attention_timed", lib().kvq_decode_attention_timed(
         ctypes.byref(h), _ptr(q), _ptr(out), _ptr(acc), _ptr(ws), nbytes, ev_start, ev_stop,
         _stream(stream)))
+
+
+def decode_step(h: Cache, k, v, q, out, acc, ws, ws_bytes: int | None = None,
+                stream=None) -> None:
+    """Append one token per unit (k, v: [B][Hkv][1][d] fp16) and attend."""
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check("kvq_decode_step", lib().kvq_decode_step(
+        ctypes.byref(h), _ptr(k), _ptr(v), _ptr(q), _ptr(out), _ptr(acc), _ptr(ws), nbytes,
+        _stream(stream)))
+
+
+def decode_step_timed(h: Cache, k, v, q, out, acc, ws, ev_start: int, ev_stop: int,
+                      ws_bytes: int | None = None, stream=None) -> None:
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check("kvq_decode_step_timed", lib().kvq_decode_step_timed(
+        ctypes.byref(h), _ptr(k), _ptr(v), _ptr(q), _ptr(out), _ptr(acc), _ptr(ws), nbytes,
+        ev_start, ev_stop, _stream(stream)))
 
 
 def topk_evict(scores, rows: int, T: int, k: int, w: int, idx, stream=None) -> None:

@@ -247,6 +247,39 @@ kvq_status kvq_decode_attention(const kvq_cache* h, const void* d_q, float* d_ou
                                       stream);
 }
 
+kvq_status kvq_decode_step_timed(kvq_cache* h, const void* d_k, const void* d_v,
+                                 const void* d_q, float* d_out, float* d_acc, void* d_ws,
+                                 size_t ws_bytes, void* ev_start, void* ev_stop, void* stream) {
+    if (!valid_handle(h) || !d_k || !d_v || !d_q || !d_out || !d_ws) return KVQ_EINVAL;
+    const int64_t t_old = h->tokens, t_new = t_old + 1;
+    if (t_new > h->cfg.max_tokens) return KVQ_ECAPACITY;
+    kvq_cache next = *h;
+    next.tokens = t_new;
+    next.n_quant = n_quantized(t_new, h->cfg.residual, h->cfg.group);
+    const DecodePlan p = plan_decode(&next, d_acc != nullptr);
+    if (ws_bytes < p.ws_bytes) return KVQ_EWORKSPACE;
+    const uint16_t* kn = static_cast<const uint16_t*>(d_k);
+    const uint16_t* vn = static_cast<const uint16_t*>(d_v);
+    const CacheView v = view_of(h);
+    kvq_status st = launch_status(
+        launch_append(v, kn, vn, t_old, 1, h->n_quant, next.n_quant, stream, false));
+    if (st != KVQ_OK) return st;
+    // the new token stays fp16 unless its own group was just quantized
+    const bool in_ring = t_old >= next.n_quant;
+    st = launch_status(launch_decode(v, t_new, next.n_quant, p, static_cast<const uint16_t*>(d_q),
+                                     d_out, d_acc, d_ws, ev_start, ev_stop, stream,
+                                     in_ring ? kn : nullptr, in_ring ? vn : nullptr));
+    if (st == KVQ_OK) *h = next;
+    return st;
+}
+
+kvq_status kvq_decode_step(kvq_cache* h, const void* d_k, const void* d_v, const void* d_q,
+                           float* d_out, float* d_acc, void* d_ws, size_t ws_bytes,
+                           void* stream) {
+    return kvq_decode_step_timed(h, d_k, d_v, d_q, d_out, d_acc, d_ws, ws_bytes, nullptr,
+                                 nullptr, stream);
+}
+
 kvq_status kvq_topk_evict(const float* d_scores, int32_t rows, int32_t T, int32_t k, int32_t w,
                           int32_t* d_idx, void* stream) {
     if (rows < 0 || T < 0 || k < 0 || w < 0 || (int64_t)k + w > T) return KVQ_EINVAL;

@@ -142,6 +142,8 @@ struct DecodeArgs {
     const uint16_t* ev_k;
     const uint16_t* ev_v;
     const int32_t* counters;
+    const uint16_t* k_new;  // decode step: the newest token's rows [U][d] (else null)
+    const uint16_t* v_new;
     const uint16_t* q;
     float* part;
     float* logits;
@@ -291,18 +293,31 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
         if (li < nres + pc) return ((int64_t)u * N + (li - nres)) * D;
         return -1 - ((int64_t)u * E + (li - nres - pc)) * D;  // extra pool: encoded negative
     };
-    auto row_ptr = [&](int i, const uint16_t* ring, const uint16_t* pool,
-                       const uint16_t* ev) -> const uint16_t* {
+    // With a decode step's input, the newest token (ring row nres - 1) is read
+    // from it; its ring slot is written below.
+    const bool new_row = a.k_new != nullptr;
+    auto row_ptr = [&](int i, const uint16_t* ring, const uint16_t* pool, const uint16_t* ev,
+                       const uint16_t* nw) -> const uint16_t* {
         bool in_ring;
         const int64_t o = row_off(i, in_ring);
-        if (in_ring) return ring + o;
+        if (in_ring) return new_row && base + i == nres - 1 ? nw + (int64_t)u * D : ring + o;
         return o >= 0 ? pool + o : ev + (-1 - o);
     };
+    if (new_row && h == 0 && lane < 32 && base <= nres - 1 && nres - 1 < base + cnt) {
+        // store the step's token into ring slot (T - 1) % RB: lanes 0-15 the
+        // key, 16-31 the value, 16 bytes each
+        const int64_t dst = ((int64_t)u * RB + (a.T - 1) % RB) * D;
+        const int part = lane & 15;
+        const uint16_t* src = (lane < 16 ? a.k_new : a.v_new) + (int64_t)u * D;
+        uint16_t* ring = const_cast<uint16_t*>(lane < 16 ? a.kring : a.vring);
+        reinterpret_cast<uint4*>(ring + dst)[part] = reinterpret_cast<const uint4*>(src)[part];
+    }
     __syncthreads();
     if (h >= R) return;
     float s = -INFINITY;
     if (lane < cnt) {
-        const uint4* kr = reinterpret_cast<const uint4*>(row_ptr(lane, a.kring, a.pool_k, a.ev_k));
+        const uint4* kr =
+            reinterpret_cast<const uint4*>(row_ptr(lane, a.kring, a.pool_k, a.ev_k, a.k_new));
         uint4 x[16];
 #pragma unroll
         for (int c8 = 0; c8 < 16; ++c8) x[c8] = kr[c8];
@@ -347,7 +362,7 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
             const int i = i0 + 4 * r + rp;
             pv[r] = ph[i < 64 ? i : 63];
             w[r] = i < cnt ? reinterpret_cast<const uint4*>(
-                                 row_ptr(i, a.vring, a.pool_v, a.ev_v))[cb]
+                                 row_ptr(i, a.vring, a.pool_v, a.ev_v, a.v_new))[cb]
                            : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
@@ -1024,7 +1039,7 @@ void dispatch_r(const DecodeArgs& a, int R, int G, hipEvent_t e0, hipEvent_t e1,
 
 int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& plan,
                   const uint16_t* q, float* out, float* acc, void* ws, void* ev_start,
-                  void* ev_stop, void* stream) {
+                  void* ev_stop, void* stream, const uint16_t* k_new, const uint16_t* v_new) {
     if (plan.splits > kMaxSplits) return (int)hipErrorInvalidValue;
     DecodeArgs a{};
     a.kq = v.kq;
@@ -1041,6 +1056,8 @@ int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& 
     a.ev_k = v.ev_k;
     a.ev_v = v.ev_v;
     a.counters = v.counters;
+    a.k_new = k_new;
+    a.v_new = v_new;
     a.q = q;
     a.part = static_cast<float*>(ws);
     a.logits = acc ? reinterpret_cast<float*>(static_cast<char*>(ws) +

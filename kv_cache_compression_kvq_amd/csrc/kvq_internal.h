@@ -61,11 +61,17 @@ DecodePlan plan_decode(const kvq_cache* h, bool want_scores);
 
 // Launchers (return hipError_t as int; 0 = success).
 int launch_init(const CacheView& v, void* stream);
+// ring_store = false leaves the appended tokens that stay fp16 out of the
+// ring (the decode step stores its one token itself).
 int launch_append(const CacheView& v, const uint16_t* k_new, const uint16_t* v_new,
-                  int64_t t_old, int32_t n_new, int64_t nq_old, int64_t nq_new, void* stream);
+                  int64_t t_old, int32_t n_new, int64_t nq_old, int64_t nq_new, void* stream,
+                  bool ring_store = true);
+// k_new / v_new (or null): the newest token (T - 1, fp16, [U][d]) is read
+// from there instead of the ring and stored into its ring slot.
 int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& plan,
                   const uint16_t* q, float* out, float* acc, void* ws, void* ev_start,
-                  void* ev_stop, void* stream);
+                  void* ev_stop, void* stream, const uint16_t* k_new = nullptr,
+                  const uint16_t* v_new = nullptr);
 int launch_topk(const float* scores, int32_t rows, int32_t T, int32_t k, int32_t w,
                 int32_t* idx, void* stream);
 int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, void* stream);

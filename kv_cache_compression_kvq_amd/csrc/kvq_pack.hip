@@ -460,7 +460,7 @@ int launch_init(const CacheView& v, void* stream) {
 }
 
 int launch_append(const CacheView& v, const uint16_t* kn, const uint16_t* vn, int64_t t_old,
-                  int32_t n_new, int64_t nq_old, int64_t nq_new, void* stream) {
+                  int32_t n_new, int64_t nq_old, int64_t nq_new, void* stream, bool ring_store) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int G = v.group;
     const int64_t g0 = nq_old / G, g1 = nq_new / G, ng = g1 - g0;
@@ -479,7 +479,7 @@ int launch_append(const CacheView& v, const uint16_t* kn, const uint16_t* vn, in
 #undef KVQ_PACK
     }
     const int64_t ts = t_old > nq_new ? t_old : nq_new, te = t_old + n_new;
-    if (te > ts) {
+    if (ring_store && te > ts) {
         const int64_t ntok = te - ts;
         hipLaunchKernelGGL(ring_store_kernel, dim3((unsigned)((ntok * 16 + 255) / 256), v.units),
                            dim3(256), 0, s, v, kn, vn, t_old, n_new, ts, ntok);

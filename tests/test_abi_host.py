@@ -106,6 +106,34 @@ def test_validation_paths_launch_nothing(kvq):
     assert L.kvq_topk_evict(None, 3, 100, 10, 20, P(1), None) == -1
 
 
+def test_decode_step_validation_launches_nothing(kvq):
+    """kvq_decode_step checks every argument before enqueuing anything and then
+    leaves the handle as it was; its workspace is that of the cache after the
+    append (T + 1 tokens)."""
+    L = kvq.lib()
+    P = ctypes.c_void_p
+    cfg = _cfg(kvq, max_tokens=4097)
+    h = _fake_handle(kvq, cfg, 4096)
+    nxt = _fake_handle(kvq, cfg, 4097)
+    need = kvq.decode_workspace(nxt, False)
+    before = bytes(h)
+    args = [P(1), P(1), P(1), P(1), None, P(1)]
+    for i in (0, 1, 2, 3, 5):  # k, v, q, out, ws
+        bad = list(args)
+        bad[i] = None
+        assert L.kvq_decode_step(ctypes.byref(h), *bad, need, None) == -1
+    assert L.kvq_decode_step(ctypes.byref(h), *args, need - 1, None) == -4
+    full = _fake_handle(kvq, cfg, 4097)
+    assert L.kvq_decode_step(ctypes.byref(full), *args, need, None) == -3
+    assert L.kvq_decode_step_timed(ctypes.byref(h), *args, need - 1, None, None, None) == -4
+    assert bytes(h) == before
+    # a group boundary: T = R + G - 1 -> T + 1 quantizes one group first
+    cfg2 = _cfg(kvq, max_tokens=1000)
+    h3 = _fake_handle(kvq, cfg2, 128 + 32 - 1)
+    assert h3.n_quant == 0 and _fake_handle(kvq, cfg2, 160).n_quant == 32
+    assert L.kvq_decode_step(ctypes.byref(h3), *args, 0, None) == -4
+
+
 def test_decode_plan_covers_partials_and_logits(kvq):
     """Workspace grows by exactly U * r * T floats when scores are wanted."""
     cfg = _cfg(kvq, batch=2, n_kv_heads=8, n_q_heads=32, max_tokens=40000)
