@@ -116,9 +116,10 @@ __device__ __forceinline__ uint32_t scalar_load(const void* p) {
 // stage's explicit vmcnt wait, because the compiler cannot tell which ring
 // slot a global->LDS copy in flight targets and would otherwise wait for all
 // of them; ring_done() then waits for the reads and ties their results.
+template <int OFF = 0>
 __device__ __forceinline__ u32x4 ring_read(uint32_t addr) {
     u32x4 v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
     return v;
 }
 __device__ __forceinline__ uint32_t ring_read32(uint32_t addr) {
@@ -511,6 +512,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAV
         }
     }
 
+    // per-lane parts of the ring-stage addresses: codes, value scales of this
+    // lane's value-operand row, key scales of its query-fold channels
+    const uint32_t lane_codes = lane * 16;
+    const uint32_t lane_vm = 2 * RG::kCodes + (gs * 32 + 4 * kb) * 4;
+    const uint32_t lane_km = 2 * RG::kCodes + 512 + cb0 * 4;
     auto step = [&](uint32_t k, uint32_t later) {
         const uint32_t gi = gs0 + wave + 4 * (k / CPG), cc = k % CPG;
         const int64_t tb = (int64_t)(gi * CPG + cc) * 32;
@@ -520,25 +526,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAV
         if (RG::kStages >= 3 && later >= 2) wait_vm<2 * RG::kLoads>();
         else if (later >= 1) wait_vm<RG::kLoads>();
         else wait_vm<0>();
-        u32x4 wk0 = ring_read(st + lane * 16), wk1 = wk0;
-        u32x4 wv0 = ring_read(st + RG::kCodes + lane * 16), wv1 = wv0;
+        // three per-lane bases, every other offset an immediate
+        const uint32_t a_codes = st + lane_codes, a_vm = st + lane_vm, a_km = st + lane_km;
+        u32x4 wk0 = ring_read<0>(a_codes), wk1;
+        u32x4 wv0 = ring_read<RG::kCodes>(a_codes), wv1;
         if (BITS == 4) {
-            wk1 = ring_read(st + 1024 + lane * 16);
-            wv1 = ring_read(st + RG::kCodes + 1024 + lane * 16);
+            wk1 = ring_read<1024>(a_codes);
+            wv1 = ring_read<RG::kCodes + 1024>(a_codes);
         }
-        u32x4 vm0 = ring_read(meta + (gs * 32 + 4 * kb) * 4);
-        u32x4 vm1 = ring_read(meta + (gs * 32 + 16 + 4 * kb) * 4);
+        u32x4 vm0 = ring_read<0>(a_vm);
+        u32x4 vm1 = ring_read<64>(a_vm);
         u32x4 km0 = vm0, km1 = vm1;
         if (cc == 0) {
-            km0 = ring_read(meta + 512 + cb0 * 4);
-            km1 = ring_read(meta + 512 + cb0 * 4 + 16);
+            km0 = ring_read<0>(a_km);
+            km1 = ring_read<16>(a_km);
         }
         uint32_t mwv = ring_read32(meta + RG::kMeta);
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(wk0), "+v"(wk1), "+v"(wv0), "+v"(wv1), "+v"(vm0), "+v"(vm1),
-                       "+v"(km0), "+v"(km1), "+v"(mwv)
-                     :
-                     : "memory");
+        if (BITS == 4) {
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(wk0), "+v"(wk1), "+v"(wv0), "+v"(wv1), "+v"(vm0), "+v"(vm1),
+                           "+v"(km0), "+v"(km1), "+v"(mwv)
+                         :
+                         : "memory");
+        } else {
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(wk0), "+v"(wv0), "+v"(vm0), "+v"(vm1), "+v"(km0), "+v"(km1),
+                           "+v"(mwv)
+                         :
+                         : "memory");
+            wk1 = wk0;  // one 16-byte word group per lane at b = 2
+            wv1 = wv0;
+        }
         if (KVQ_DEEP_RING) {
             // The stage is in registers: refill its slot with chunk k + kStages,
             // so that kStages chunks stay in flight while this one computes.
