@@ -53,6 +53,11 @@ def parse_args():
                    help="event-timed attention launches per replica for the roofline")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (counter calibration runs)")
+    p.add_argument("--rows", nargs="*", default=None, metavar="ROW",
+                   help="instead of the step line: time each row of the hot path on the "
+                        f"workload it is measured at, one JSON line per row ({', '.join(ROWS)}; "
+                        "no names = all)")
+    p.add_argument("--reps", type=int, default=20, help="timed calls per row (--rows)")
     return p.parse_args()
 
 
@@ -164,8 +169,168 @@ def cpu_baseline(w, seconds: float):
                       f"numpy fp64, BLAS limited to 1 thread, {total_t:.1f} s"}
 
 
+# Rows of the hot path timed by --rows: name -> (workload, what the timed call runs).
+ROWS = {
+    "append_llama8b": ("llama8b", "a4-a7: bulk quantize + pack of the whole prefix, ring store"),
+    "append_ott": ("ott", "a1-a7: OTT scores + pool scan, mean replacement, quantize + pack, ring"),
+    "decode_h2o_minikv": ("minikv", "a8-a10: fused decode + merge with H2O accumulation"),
+    "topk_minikv": ("minikv", "a11: heavy-hitter top-k + recent window"),
+    "decode_long_b2g32": ("long_b2g32", "a8-a10: fused decode + merge, split-K over context"),
+    "decode_long_b2g128": ("long_b2g128", "a8-a10: fused decode + merge, split-K over context"),
+    "decode_long_b4g32": ("long_b4g32", "a8-a10: fused decode + merge, split-K over context"),
+    "decode_long_b4g128": ("long_b4g128", "a8-a10: fused decode + merge, split-K over context"),
+}
+
+
+def rows_main(args):
+    """Time each row's ABI call with events on the stream it launches on.
+
+    Inputs are resident in HBM; caches and sources rotate over replicas that
+    together exceed the 256 MB Infinity Cache. One JSON line per row:
+    algorithmic bytes of one call (the byte model), mean call time, GB/s and
+    the fraction of the 8 TB/s HBM peak.
+    """
+    import torch
+
+    from kv_cache_compression_kvq_amd import abi, bytes_model as BM, synth
+
+    if not os.path.exists(abi.LIB_PATH):
+        from kv_cache_compression_kvq_amd import build as B
+        B.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    names = args.rows or list(ROWS)
+    for n in names:
+        if n not in ROWS:
+            print(f"unknown row {n}; rows: {', '.join(ROWS)}", file=sys.stderr)
+            sys.exit(2)
+
+    def cfg_of(w):
+        return abi.make_config(bits=w.bits, group=w.group, residual=w.residual, pool=w.pool,
+                               evict_cap=w.evict_cap, head_dim=w.head_dim, n_q_heads=w.n_q_heads,
+                               n_kv_heads=w.n_kv_heads, batch=w.batch, max_tokens=w.tokens)
+
+    def timed(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for i, (a, b) in enumerate(evs):
+            fn(i, a, b)
+        torch.cuda.synchronize()
+        return 1e3 * sum(a.elapsed_time(b) for a, b in evs) / reps  # us
+
+    def emit(name, w, us, nbytes, extra):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        line = {"row": name, "workload": w.name, "what": ROWS[name][1], "us_per_call": round(us, 3),
+                "alg_bytes": int(nbytes), "GB/s": round(gbs, 2),
+                "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+        line.update(extra)
+        print(json.dumps(line), flush=True)
+
+    loaded = {}
+
+    def source(w):
+        # fp16 K/V of the whole prefix, replicated past the Infinity Cache
+        if w.name not in loaded:
+            loaded.clear()
+            K, V = synth.all_kv(w)
+            src_bytes = 2 * K.nbytes
+            n_src = max(2, math.ceil(REPLICA_BYTES / src_bytes))
+            Kd = torch.from_numpy(K).to(dev)
+            Vd = torch.from_numpy(V).to(dev)
+            loaded[w.name] = [(Kd, Vd)] + [(Kd.clone(), Vd.clone()) for _ in range(n_src - 1)]
+        return loaded[w.name]
+
+    def caches(w, n_min=2):
+        cfg = cfg_of(w)
+        nb = abi.cache_bytes(cfg)
+        n_rep = max(n_min, math.ceil(REPLICA_BYTES / nb))
+        out = []
+        for _ in range(n_rep):
+            arena = torch.empty(nb, dtype=torch.uint8, device=dev)
+            out.append({"arena": arena, "h": abi.cache_init(cfg, arena)})
+        return cfg, out
+
+    for name in names:
+        w = synth.WORKLOADS[ROWS[name][0]]
+        U, d = w.units, w.head_dim
+        if name.startswith("append"):
+            srcs = source(w)
+            cfg, reps = caches(w)
+
+            def call(i, a, b):
+                rep = reps[i % len(reps)]
+                kd, vd = srcs[i % len(srcs)]
+                h = abi.cache_init(cfg, rep["arena"])
+                a.record()
+                abi.quantize_append(h, kd, vd, w.tokens)
+                b.record()
+                rep["h"] = h
+
+            timed(call, 2)  # warm-up
+            us = timed(call, args.reps)
+            nq = BM.n_quantized(w.tokens, w.residual, w.group)
+            nbytes = BM.bulk_append_bytes(units=U, head_dim=d, tokens=w.tokens, n_quant=nq,
+                                          bits=w.bits, group=w.group)
+            emit(name, w, us, nbytes, {"kernels": ["ott_score_kernel", "ott_scan_kernel",
+                                                   "pack_kernel", "ring_store_kernel"]
+                                       if w.pool else ["pack_kernel", "ring_store_kernel"]})
+            continue
+        srcs = source(w)
+        cfg, reps = caches(w)
+        for i, rep in enumerate(reps):
+            kd, vd = srcs[i % len(srcs)]
+            abi.quantize_append(rep["h"], kd, vd, w.tokens)
+            rep["acc"] = torch.zeros((w.batch, w.n_kv_heads, w.tokens), device=dev) \
+                if w.h2o else None
+        loaded.clear()
+        q = torch.from_numpy(synth.queries(w)).to(dev)
+        out = torch.empty((w.batch, w.n_q_heads, d), device=dev)
+        ws = torch.empty(abi.decode_workspace(reps[0]["h"], w.h2o), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        if name.startswith("decode"):
+            def call(i, a, b):
+                rep = reps[i % len(reps)]
+                a.record()
+                abi.decode_attention(rep["h"], q, out, rep["acc"], ws)
+                b.record()
+
+            timed(call, 2)
+            us = timed(call, args.reps)
+            nbytes = BM.decode_step_bytes(units=U, gqa=w.gqa, head_dim=d, tokens=w.tokens,
+                                          bits=w.bits, group=w.group, residual=w.residual,
+                                          h2o=w.h2o).total
+            emit(name, w, us, nbytes, {"kernels": ["decode_kernel", "merge_kernel"]})
+        else:  # top-k over the accumulated scores of a decode call
+            for rep in reps:
+                abi.decode_attention(rep["h"], q, out, rep["acc"], ws)
+            k, wr = w.topk_k, w.recent
+            idx = torch.empty((U, k + wr), dtype=torch.int32, device=dev)
+
+            def call(i, a, b):
+                rep = reps[i % len(reps)]
+                a.record()
+                abi.topk_evict(rep["acc"], U, w.tokens, k, wr, idx)
+                b.record()
+
+            timed(call, 2)
+            us = timed(call, args.reps)
+            emit(name, w, us, BM.topk_bytes(rows=U, tokens=w.tokens, k=k, w=wr),
+                 {"kernels": ["topk_kernel"], "k": k, "recent": wr})
+        del reps, ws, out
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse_args()
+    if args.rows is not None:
+        if args.gpus != 1:
+            print("bench.py: this build runs on one GPU", file=sys.stderr)
+            sys.exit(2)
+        rows_main(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the attention units shard with no exchange; see the design notes)",

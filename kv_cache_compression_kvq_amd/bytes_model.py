@@ -82,6 +82,20 @@ def append_bytes(*, units: int, head_dim: int, n_new: int, bits: int, group: int
     return ring + units * groups_packed * per_group
 
 
+def bulk_append_bytes(*, units: int, head_dim: int, tokens: int, n_quant: int, bits: int,
+                      group: int) -> int:
+    """Algorithmic bytes of appending a whole prefix of ``tokens`` to an empty cache.
+
+    fp16 K/V of every token are read once; the ``n_quant`` quantized tokens
+    write codes and scale/zero for keys and values, the rest are written to
+    the fp16 residual ring.
+    """
+    d, G = head_dim, group
+    gv = min(G, d)
+    per_q = d * bits // 4 + 4 * d // G + 4 * d // gv
+    return units * (tokens * 4 * d + n_quant * per_q + (tokens - n_quant) * 4 * d)
+
+
 def topk_bytes(*, rows: int, tokens: int, k: int, w: int) -> int:
     """fp32 scores read once, int32 kept indices written."""
     return rows * tokens * 4 + rows * (k + w) * 4

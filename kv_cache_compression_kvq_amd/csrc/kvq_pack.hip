@@ -19,6 +19,7 @@ namespace kvq {
 namespace {
 
 constexpr int D = kHeadDim;
+constexpr int kPackRow = D + 8;  // LDS row stride of the pack kernel, in fp16 elements
 
 __device__ __forceinline__ float h2f(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
@@ -60,9 +61,35 @@ __device__ uint16_t fixed_to_half(int64_t S, int sh) {
     return sign | (uint16_t)(e << 10) | (uint16_t)f;
 }
 
-__device__ __forceinline__ uint32_t quant_code(float x, float mn, float q, float levels) {
-    const float t = (x - mn) / q;
-    return (uint32_t)fminf(fmaxf(rintf(t), 0.0f), levels);
+// Codes of N elements of one group: clamp(rint(fl32(fl32(x - mn) / q)), 0,
+// levels), exactly. The quotient is first taken as fl32(d * rq) with
+// rq = fl32(1 / q): for quotients below 16 that lies within 2^-18.6 of the
+// correctly rounded quotient (two roundings of 2^-24 relative each, plus half
+// an ulp of the quotient), so whenever it is at least 2^-17 away from every
+// half-integer both round to the same integer. Closer than that (rare), the
+// correctly rounded division decides; that branch is taken by the whole
+// wavefront or not at all.
+__device__ __forceinline__ bool near_tie(float t) {
+    return fabsf(fabsf(t - rintf(t)) - 0.5f) < 0x1p-17f;
+}
+template <int N>
+__device__ __forceinline__ void quant_codes(const float (&x)[N], float mn, float q, float rq,
+                                            float levels, uint32_t (&c)[N]) {
+    float d[N], t[N];
+    bool near = false;
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+        d[m] = x[m] - mn;
+        t[m] = d[m] * rq;
+        near |= near_tie(t[m]);
+    }
+    if (__any(near)) {
+#pragma unroll
+        for (int m = 0; m < N; ++m)
+            if (near_tie(t[m])) t[m] = d[m] / q;
+    }
+#pragma unroll
+    for (int m = 0; m < N; ++m) c[m] = (uint32_t)fminf(fmaxf(rintf(t[m]), 0.0f), levels);
 }
 
 // Lower bound on the range before dividing (the reference quantizer clamps
@@ -127,7 +154,10 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
                                                       int32_t n_new, int64_t g0, int64_t g1) {
     const int u = blockIdx.x, lane = threadIdx.x;
     const int G = v.group, N = v.pool, E = v.evict_cap;
-    __shared__ uint64_t sc[128];
+    // scores of up to kScanBatch tokens are staged at once, so that the serial
+    // walk over the groups reads them from LDS
+    constexpr int kScanBatch = 2048;
+    __shared__ uint64_t sc_all[kScanBatch];
     __shared__ uint64_t psc[kMaxPool];
     __shared__ int32_t pidx[kMaxPool];
     __shared__ int32_t slot[kMaxPool];
@@ -139,9 +169,17 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
         psc[p] = v.pool_score[(int64_t)u * N + p];
     }
     __syncthreads();
+    int64_t gb = g0, gb_end = g0;
     for (int64_t g = g0; g < g1 && !frozen; ++g) {
         const int64_t t0 = g * G;
-        for (int i = lane; i < G; i += 64) sc[i] = v.scores[(int64_t)u * v.q_cap + t0 + i];
+        if (g == gb_end) {
+            gb = g;
+            gb_end = g + kScanBatch / G < g1 ? g + kScanBatch / G : g1;
+            __syncthreads();  // the previous batch is no longer read
+            for (int64_t i = lane; i < (gb_end - g) * G; i += 64)
+                sc_all[i] = v.scores[(int64_t)u * v.q_cap + t0 + i];
+        }
+        const uint64_t* sc = sc_all + (g - gb) * G;
         for (int p = lane; p < N; p += 64) slot[p] = -1;
         if (lane < 4) mwords[lane] = 0;
         __syncthreads();
@@ -229,17 +267,28 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
     constexpr int LG = G == 32 ? 5 : G == 64 ? 6 : 7;
     const float levels = (float)((1 << BITS) - 1);
     extern __shared__ __align__(16) uint16_t smem[];
-    uint16_t* kx = smem;        // [G][D] fp16 rows, overwritten by their codes
-    uint16_t* vx = smem + G * D;
+    // [G][RS] fp16 rows, overwritten by their codes. The row stride of 272
+    // bytes puts the 16-byte value reads of a quarter wavefront (4 tokens x
+    // 4 value groups at G = 32) on disjoint LDS banks.
+    constexpr int RS = kPackRow;
+    uint16_t* kx = smem;
+    uint16_t* vx = smem + G * RS;
     __shared__ uint16_t meank[D], meanv[D];
-    const int u = blockIdx.y, tid = threadIdx.x;
-    const int64_t g = g0 + blockIdx.x, t0 = g * G;
+    __shared__ uint32_t vmax_w[2];
+    // Blocks walk the units fastest, so that the blocks resident at once
+    // spread over all units (and the units' counter words).
+    const int u = (int)(blockIdx.x % (uint32_t)v.units), tid = threadIdx.x;
+    const int64_t g = g0 + blockIdx.x / (uint32_t)v.units, t0 = g * G;
+    // The unit's largest value scale so far; a block only raises it with an
+    // atomic when its own maximum is larger (stale reads cost an atomic, no
+    // more).
+    const uint32_t vmax_seen = tid == 0 ? v.counters[(int64_t)u * 4 + 3] : 0u;
 
     for (int e = tid; e < G * 16; e += 256) {
         const int i = e / 16, part = e % 16;
-        reinterpret_cast<uint4*>(kx)[e] = reinterpret_cast<const uint4*>(
+        reinterpret_cast<uint4*>(kx + i * RS)[part] = reinterpret_cast<const uint4*>(
             src_row(v.kring, knew, v, u, t0 + i, t_old, n_new))[part];
-        reinterpret_cast<uint4*>(vx)[e] = reinterpret_cast<const uint4*>(
+        reinterpret_cast<uint4*>(vx + i * RS)[part] = reinterpret_cast<const uint4*>(
             src_row(v.vring, vnew, v, u, t0 + i, t_old, n_new))[part];
     }
     uint32_t mw[CPG];
@@ -254,15 +303,15 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
         if (tid < 2 * D) {
             const uint16_t* x = tid < D ? kx + tid : vx + (tid - D);
             int64_t s = 0;
-            for (int i = 0; i < G; ++i) s += half_fixed(x[i * D]);
+            for (int i = 0; i < G; ++i) s += half_fixed(x[i * RS]);
             (tid < D ? meank[tid] : meanv[tid - D]) = fixed_to_half(s, LG);
         }
         __syncthreads();
         for (int e = tid; e < G * D; e += 256) {
             const int i = e / D, c = e % D;
             if ((mw[i / kChunk] >> (i % kChunk)) & 1u) {
-                kx[e] = meank[c];
-                vx[e] = meanv[c];
+                kx[i * RS + c] = meank[c];
+                vx[i * RS + c] = meanv[c];
             }
         }
         __syncthreads();
@@ -272,24 +321,39 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
         const int c = tid;
         float mn = INFINITY, mx = -INFINITY;
         for (int i = 0; i < G; ++i) {
-            const float x = h2f(kx[i * D + c]);
+            const float x = h2f(kx[i * RS + c]);
             mn = fminf(mn, x);
             mx = fmaxf(mx, x);
         }
         const float q = fmaxf(mx - mn, range_floor()) / levels;
+        const float rq = 1.0f / q;
         v.kmeta[((int64_t)u * v.key_groups + g) * D + c] = (uint32_t)f2h(q) | ((uint32_t)f2h(mn) << 16);
-        for (int i = 0; i < G; ++i) kx[i * D + c] = (uint16_t)quant_code(h2f(kx[i * D + c]), mn, q, levels);
+        for (int i0 = 0; i0 < G; i0 += 8) {
+            float x[8];
+            uint32_t cd[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) x[m] = h2f(kx[(i0 + m) * RS + c]);
+            quant_codes(x, mn, q, rq, levels, cd);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) kx[(i0 + m) * RS + c] = (uint16_t)cd[m];
+        }
     } else {
-        // values: token i, channels [gq*G, gq*G + G)
+        // values: token i, channels [gq*G, gq*G + G), eight at a time
         const int j = tid - D, i = j / NG, gq = j % NG;
-        uint16_t* row = vx + i * D + gq * G;
+        uint4* row = reinterpret_cast<uint4*>(vx + i * RS + gq * G);
         float mn = INFINITY, mx = -INFINITY;
-        for (int c = 0; c < G; ++c) {
-            const float x = h2f(row[c]);
-            mn = fminf(mn, x);
-            mx = fmaxf(mx, x);
+        for (int c8 = 0; c8 < G / 8; ++c8) {
+            const uint4 x = row[c8];
+            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float a = h2f((uint16_t)(w[m] & 0xFFFF)), b = h2f((uint16_t)(w[m] >> 16));
+                mn = fminf(mn, fminf(a, b));
+                mx = fmaxf(mx, fmaxf(a, b));
+            }
         }
         const float q = fmaxf(mx - mn, range_floor()) / levels;
+        const float rq = 1.0f / q;
         const int64_t t = t0 + i;
         const uint16_t qh = f2h(q);
         v.vmeta[(((int64_t)u * v.chunks + t / kChunk) * NG + gq) * kChunk + t % kChunk] =
@@ -298,10 +362,27 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
         // like the numbers): bounds the lazy softmax rescale of the decoder.
         uint32_t mq = qh;
         for (int off = 32; off > 0; off >>= 1) mq = max(mq, (uint32_t)__shfl_xor((int)mq, off));
-        if ((tid & 63) == 0) atomicMax(reinterpret_cast<uint32_t*>(v.counters) + (int64_t)u * 4 + 3, mq);
-        for (int c = 0; c < G; ++c) row[c] = (uint16_t)quant_code(h2f(row[c]), mn, q, levels);
+        if ((tid & 63) == 0) vmax_w[(tid - D) >> 6] = mq;
+        for (int c8 = 0; c8 < G / 8; ++c8) {
+            const uint4 x = row[c8];
+            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+            float xf[8];
+            uint32_t cd[8];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                xf[2 * m] = h2f((uint16_t)(w[m] & 0xFFFF));
+                xf[2 * m + 1] = h2f((uint16_t)(w[m] >> 16));
+            }
+            quant_codes(xf, mn, q, rq, levels, cd);
+            row[c8] = make_uint4(cd[0] | cd[1] << 16, cd[2] | cd[3] << 16, cd[4] | cd[5] << 16,
+                                 cd[6] | cd[7] << 16);
+        }
     }
     __syncthreads();
+    if (tid == 0) {
+        const uint32_t mq = max(vmax_w[0], vmax_w[1]);
+        if (mq > vmax_seen) atomicMax(reinterpret_cast<uint32_t*>(v.counters) + (int64_t)u * 4 + 3, mq);
+    }
 
     // Pack. Word w of lane l sits at (w/4)*256 + l*4 + w%4 within its chunk.
     for (int e = tid; e < 2 * CPG * WPC; e += 256) {
@@ -326,8 +407,8 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
                     for (int ks = 0; ks < 4; ++ks) {
                         const int ch = 32 * ks + 8 * kb + 2 * m, q = kPos2[4 * tau + ks];
                         const int sw = q == 7 ? 1 : 0;
-                        word |= (uint32_t)kx[tok * D + ch + sw] << (2 * q);
-                        word |= (uint32_t)kx[tok * D + ch + 1 - sw] << (16 + 2 * q);
+                        word |= (uint32_t)kx[tok * RS + ch + sw] << (2 * q);
+                        word |= (uint32_t)kx[tok * RS + ch + 1 - sw] << (16 + 2 * q);
                     }
                 }
             } else {
@@ -336,8 +417,8 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int ch = 32 * ks + 8 * kb + 2 * m;
-                    word |= (uint32_t)kx[tok * D + ch] << (4 * m);
-                    word |= (uint32_t)kx[tok * D + ch + 1] << (16 + 4 * m);
+                    word |= (uint32_t)kx[tok * RS + ch] << (4 * m);
+                    word |= (uint32_t)kx[tok * RS + ch + 1] << (16 + 4 * m);
                 }
             }
         } else {
@@ -355,15 +436,15 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
                 for (int nt = 0; nt < 8; ++nt) {
                     const int c = 16 * nt + n, q = kPos2[nt];
                     const int xa = q == 7 ? tb : ta, xb = q == 7 ? ta : tb;
-                    word |= (uint32_t)vx[xa * D + c] << (2 * q);
-                    word |= (uint32_t)vx[xb * D + c] << (16 + 2 * q);
+                    word |= (uint32_t)vx[xa * RS + c] << (2 * q);
+                    word |= (uint32_t)vx[xb * RS + c] << (16 + 2 * q);
                 }
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int c = 16 * (4 * (w / 4) + j) + n;
-                    word |= (uint32_t)vx[ta * D + c] << (4 * j);
-                    word |= (uint32_t)vx[tb * D + c] << (16 + 4 * j);
+                    word |= (uint32_t)vx[ta * RS + c] << (4 * j);
+                    word |= (uint32_t)vx[tb * RS + c] << (16 + 4 * j);
                 }
             }
         }
@@ -437,15 +518,20 @@ __global__ __launch_bounds__(256) void unpack_kernel(CacheView v, int64_t n_q, u
 template <int BITS, int G>
 void launch_pack_t(const CacheView& v, const uint16_t* kn, const uint16_t* vn, int64_t t_old,
                    int32_t n_new, int64_t g0, int64_t ng, hipStream_t s) {
-    const size_t lds = 2 * (size_t)G * D * sizeof(uint16_t);
+    const size_t lds = 2 * (size_t)G * kPackRow * sizeof(uint16_t);
     static bool attr = [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(pack_kernel<BITS, G>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * G * D * 2);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * G * kPackRow * 2);
         return true;
     }();
     (void)attr;
-    hipLaunchKernelGGL((pack_kernel<BITS, G>), dim3((unsigned)ng, v.units), dim3(256), lds, s, v,
-                       kn, vn, t_old, n_new, g0);
+    // one block per (unit, group), units fastest; at most 2^22 blocks a launch
+    const int64_t step = (int64_t)1 << 22 >= v.units ? ((int64_t)1 << 22) / v.units : 1;
+    for (int64_t gs = 0; gs < ng; gs += step) {
+        const int64_t n = ng - gs < step ? ng - gs : step;
+        hipLaunchKernelGGL((pack_kernel<BITS, G>), dim3((unsigned)(n * v.units)), dim3(256), lds, s,
+                           v, kn, vn, t_old, n_new, g0 + gs);
+    }
 }
 
 }  // namespace
