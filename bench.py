@@ -529,11 +529,16 @@ def main():
         "query_head_scores_per_s": round(tok_heads * r, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_entry(w.name, kernel_bytes),
+                     "traffic": None,
                      "kernel": "decode_kernel", "kernel_us": round(kernel_us, 3),
                      "kernel_alg_bytes": int(kernel_bytes), "source_sha": source_sha()},
         "cpu_baseline": None,
     }
+    tr = traffic_entry(w.name, kernel_bytes)
+    if tr is not None:
+        # HBM bytes per launch from the rocprofv3 counter runs, calibrated by a copy
+        line["roofline"]["traffic"] = int(tr["total_bytes"])
+        line["roofline"]["traffic_detail"] = tr
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

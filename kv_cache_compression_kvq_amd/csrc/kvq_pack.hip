@@ -124,21 +124,24 @@ __global__ __launch_bounds__(256) void ott_score_kernel(CacheView v, const uint1
     const int u = blockIdx.y;
     const int64_t tl = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
     const int part = threadIdx.x % 16;
-    uint64_t s = 0;
+    // Every |x| is a multiple of 2^-24 below 2^16, so any partial sum of the
+    // 128 magnitudes is a multiple of 2^-24 below 2^23: at most 47 significant
+    // bits, exact in fp64 in any order. Scaled by 2^24 it is the integer score.
+    double s = 0.0;
     if (tl < ntok) {
         const uint16_t* row = src_row(v.kring, knew, v, u, t0 + tl, t_old, n_new);
         const uint4 x = reinterpret_cast<const uint4*>(row)[part];
         const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t a = half_fixed((uint16_t)(w[i] & 0xFFFF));
-            const int64_t b = half_fixed((uint16_t)(w[i] >> 16));
-            s += (uint64_t)(a < 0 ? -a : a) + (uint64_t)(b < 0 ? -b : b);
+            s += fabs((double)h2f((uint16_t)(w[i] & 0xFFFF)));
+            s += fabs((double)h2f((uint16_t)(w[i] >> 16)));
         }
     }
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off, 16);
-    if (part == 0 && tl < ntok) v.scores[(int64_t)u * v.q_cap + t0 + tl] = s;
+    if (part == 0 && tl < ntok)
+        v.scores[(int64_t)u * v.q_cap + t0 + tl] = (uint64_t)(s * 16777216.0);
 }
 
 // OTT pool competition, one wavefront per unit, groups in token order.
@@ -162,36 +165,84 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
     __shared__ int32_t pidx[kMaxPool];
     __shared__ int32_t slot[kMaxPool];
     __shared__ uint32_t mwords[4];
+    __shared__ uint32_t mbatch[kScanBatch / 32];  // chunk mask words of the staged groups
+    // members displaced in this call: token and the pool slot it left
+    __shared__ int32_t ev_tok[kMaxEvict], ev_from[kMaxEvict];
+    // The block is one wavefront: LDS ordering needs the LDS counter and a wave
+    // barrier only (no wait for global stores in flight).
+    auto wave_sync = [] {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+    };
     int32_t* cnt = v.counters + (int64_t)u * 4;
     int pc = cnt[0], ec = cnt[1], frozen = cnt[2];
+    const int ec0 = ec;
+    const int64_t t_first = g0 * G;  // tokens from here on are admitted in this call
     for (int p = lane; p < N; p += 64) {
         pidx[p] = v.pool_idx[(int64_t)u * N + p];
         psc[p] = v.pool_score[(int64_t)u * N + p];
     }
     __syncthreads();
-    int64_t gb = g0, gb_end = g0;
-    for (int64_t g = g0; g < g1 && !frozen; ++g) {
+    // The pool's worst member (largest (score, index)) once the pool is full:
+    // only tokens ordered before it can rank among the N best. Recomputed
+    // after admissions only.
+    uint64_t wsc = ~0ull;
+    int32_t widx = INT32_MAX;
+    auto find_worst = [&] {
+        if (pc < N) return;
+        uint64_t a = lane < N ? psc[lane] : 0ull;
+        int32_t b = lane < N ? pidx[lane] : -1;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const uint64_t a2 = __shfl_xor(a, off);
+            const int32_t b2 = __shfl_xor(b, off);
+            if (a2 > a || (a2 == a && b2 > b)) {
+                a = a2;
+                b = b2;
+            }
+        }
+        wsc = a;
+        widx = b;
+    };
+    find_worst();
+    int64_t gb = g0, gb_end = g0, g = g0;
+    // mask words of groups [gb, ge) to memory
+    auto flush = [&](int64_t ge) {
+        for (int64_t i = lane; i < (ge - gb) * (G / 32); i += 64)
+            v.mask[(int64_t)u * v.chunks + gb * (G / 32) + i] = mbatch[i];
+    };
+    for (; g < g1 && !frozen; ++g) {
         const int64_t t0 = g * G;
         if (g == gb_end) {
+            flush(g);
             gb = g;
             gb_end = g + kScanBatch / G < g1 ? g + kScanBatch / G : g1;
-            __syncthreads();  // the previous batch is no longer read
+            wave_sync();  // the previous batch is no longer read
             for (int64_t i = lane; i < (gb_end - g) * G; i += 64)
                 sc_all[i] = v.scores[(int64_t)u * v.q_cap + t0 + i];
+            wave_sync();
         }
         const uint64_t* sc = sc_all + (g - gb) * G;
+        bool cand = false;
+        for (int i = lane; i < G; i += 64)
+            cand |= pc < N || sc[i] < wsc || (sc[i] == wsc && t0 + i < widx);
+        if (!__any(cand)) {  // nothing enters the pool: the common case
+            if (lane < G / 32) mbatch[(g - gb) * (G / 32) + lane] = 0u;
+            continue;
+        }
         for (int p = lane; p < N; p += 64) slot[p] = -1;
         if (lane < 4) mwords[lane] = 0;
-        __syncthreads();
+        wave_sync();
         for (int i = lane; i < G; i += 64) {
             const uint64_t si = sc[i];
             const int64_t ti = t0 + i;
+            if (pc == N && !(si < wsc || (si == wsc && ti < widx))) continue;
             int rank = 0;
             for (int p = 0; p < pc; ++p) rank += (psc[p] < si) || (psc[p] == si && pidx[p] < ti);
             for (int q = 0; q < G; ++q) rank += (sc[q] < si) || (sc[q] == si && q < i);
             if (rank < N) slot[rank] = i;
         }
-        __syncthreads();
+        wave_sync();
         for (int rk = 0; rk < N; ++rk) {
             const int i = slot[rk];
             if (i < 0) continue;
@@ -205,32 +256,50 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
                     frozen = 1;
                     break;
                 }
-                const int64_t ps = (int64_t)u * N + w, es = (int64_t)u * E + ec;
-                if (lane == 0) v.ev_idx[es] = pidx[w];
-                reinterpret_cast<uint32_t*>(v.ev_k + es * D)[lane] =
-                    reinterpret_cast<const uint32_t*>(v.pool_k + ps * D)[lane];
-                reinterpret_cast<uint32_t*>(v.ev_v + es * D)[lane] =
-                    reinterpret_cast<const uint32_t*>(v.pool_v + ps * D)[lane];
+                if (lane == 0) {
+                    v.ev_idx[(int64_t)u * E + ec] = pidx[w];
+                    ev_tok[ec - ec0] = pidx[w];
+                    ev_from[ec - ec0] = w;
+                }
                 ++ec;
                 dst = w;
             } else {
                 dst = pc++;
             }
-            const int64_t pd = (int64_t)u * N + dst;
-            reinterpret_cast<uint32_t*>(v.pool_k + pd * D)[lane] = reinterpret_cast<const uint32_t*>(
-                src_row(v.kring, knew, v, u, t, t_old, n_new))[lane];
-            reinterpret_cast<uint32_t*>(v.pool_v + pd * D)[lane] = reinterpret_cast<const uint32_t*>(
-                src_row(v.vring, vnew, v, u, t, t_old, n_new))[lane];
-            __syncthreads();
+            wave_sync();  // the displaced member is recorded before its slot is reused
             if (lane == 0) {
                 pidx[dst] = (int32_t)t;
                 psc[dst] = sc[i];
                 mwords[i / 32] |= 1u << (i % 32);
             }
-            __syncthreads();
+            wave_sync();
         }
-        if (lane < G / 32) v.mask[(int64_t)u * v.chunks + t0 / 32 + lane] = mwords[lane];
-        __syncthreads();
+        if (lane < G / 32) mbatch[(g - gb) * (G / 32) + lane] = mwords[lane];
+        wave_sync();
+        find_worst();
+    }
+    flush(g);
+    wave_sync();
+    // Row copies, after the walk. Displaced members first: a member admitted
+    // in this call still has its rows in the input or the ring; an older one
+    // has them in the pool slot it left, which no copy below has overwritten yet.
+    for (int e = ec0; e < ec; ++e) {
+        const int64_t t = ev_tok[e - ec0];
+        const int64_t ps = (int64_t)u * N + ev_from[e - ec0], es = (int64_t)u * E + e;
+        const uint16_t* kr = t >= t_first ? src_row(v.kring, knew, v, u, t, t_old, n_new) : v.pool_k + ps * D;
+        const uint16_t* vr = t >= t_first ? src_row(v.vring, vnew, v, u, t, t_old, n_new) : v.pool_v + ps * D;
+        reinterpret_cast<uint32_t*>(v.ev_k + es * D)[lane] = reinterpret_cast<const uint32_t*>(kr)[lane];
+        reinterpret_cast<uint32_t*>(v.ev_v + es * D)[lane] = reinterpret_cast<const uint32_t*>(vr)[lane];
+    }
+    __syncthreads();  // every old pool row is read before the slots are rewritten
+    for (int p = 0; p < pc; ++p) {
+        const int64_t t = pidx[p];
+        if (t < t_first) continue;  // member from an earlier call, rows in place
+        const int64_t pd = (int64_t)u * N + p;
+        reinterpret_cast<uint32_t*>(v.pool_k + pd * D)[lane] = reinterpret_cast<const uint32_t*>(
+            src_row(v.kring, knew, v, u, t, t_old, n_new))[lane];
+        reinterpret_cast<uint32_t*>(v.pool_v + pd * D)[lane] = reinterpret_cast<const uint32_t*>(
+            src_row(v.vring, vnew, v, u, t, t_old, n_new))[lane];
     }
     for (int p = lane; p < N; p += 64) {
         v.pool_idx[(int64_t)u * N + p] = pidx[p];
@@ -279,10 +348,14 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
     // spread over all units (and the units' counter words).
     const int u = (int)(blockIdx.x % (uint32_t)v.units), tid = threadIdx.x;
     const int64_t g = g0 + blockIdx.x / (uint32_t)v.units, t0 = g * G;
-    // The unit's largest value scale so far; a block only raises it with an
-    // atomic when its own maximum is larger (stale reads cost an atomic, no
-    // more).
-    const uint32_t vmax_seen = tid == 0 ? v.counters[(int64_t)u * 4 + 3] : 0u;
+    // The unit's largest value scale so far, read at device scope (past this
+    // XCD's L2, where the atomics below do not land); a block only raises it
+    // with an atomic when its own maximum is larger. A stale value costs one
+    // atomic, no more.
+    const uint32_t vmax_seen =
+        tid == 0 ? __hip_atomic_load(reinterpret_cast<const uint32_t*>(v.counters) + (int64_t)u * 4 + 3,
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : 0u;
 
     for (int e = tid; e < G * 16; e += 256) {
         const int i = e / 16, part = e % 16;
