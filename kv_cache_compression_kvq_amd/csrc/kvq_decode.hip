@@ -895,70 +895,114 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAV
     }
 }
 
-// Merge the split partials of unit blockIdx.x: block y = 0 writes the
-// outputs, blocks y >= 1 add the H2O increments of a 2048-token slice.
+// Merge of the split partials. Block x serves unit x / r. Blocks y = 0 write
+// the outputs of head x % r: wavefront w sums a contiguous quarter of the
+// splits, and the four partial sums are added in order, so results do not
+// depend on timing. Blocks y >= 1 add the H2O increments of the
+// (x % r)-th part of a 2048-token slice.
 template <int R>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
-    __shared__ float wsp[R][kMaxSplits + 1];
+    constexpr int kML = 4;  // (m, l) pairs per lane kept in registers
+    __shared__ float wsp[kMaxSplits + 1];
+    __shared__ float opart[4][D];
     __shared__ float Ms[R], Linv[R];
-    const int u = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int u = blockIdx.x / R, hb = blockIdx.x % R;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int S = a.splits;
     const float* base = a.part + (int64_t)u * S * R * kRec;
-    if (wave < R) {
-        const int h = wave;
-        // Outputs: lane owns channels 2 lane, 2 lane + 1. The first splits' rows
-        // are requested together with the (m, l) pairs.
-        constexpr int kPre = 16;
-        float2 xp[kPre];
-        if (blockIdx.y == 0) {
+    // Global max and normaliser of head h over all splits; split weights of
+    // [s_lo, s_hi) go to wsp.
+    auto softmax_terms = [&](int h, int s_lo, int s_hi, float& m, float& l) {
+        float mr[kML], lr[kML];
+        m = -INFINITY;
 #pragma unroll
-            for (int s = 0; s < kPre; ++s)
-                xp[s] = s < S ? *reinterpret_cast<const float2*>(base + (s * R + h) * kRec + 2 * lane)
-                              : make_float2(0.f, 0.f);
+        for (int j = 0; j < kML; ++j) {
+            const int s = lane + 64 * j;
+            mr[j] = s < S ? base[(s * R + h) * kRec + D] : -INFINITY;
+            lr[j] = s < S ? base[(s * R + h) * kRec + D + 1] : 0.f;
+            m = fmaxf(m, mr[j]);
         }
-        float m = -INFINITY;
-        for (int s = lane; s < S; s += 64) m = fmaxf(m, base[(s * R + h) * kRec + D]);
+        for (int s = lane + 64 * kML; s < S; s += 64) m = fmaxf(m, base[(s * R + h) * kRec + D]);
         m = wave_max(m);
-        float l = 0.f;
-        for (int s = lane; s < S; s += 64) {
+        l = 0.f;
+#pragma unroll
+        for (int j = 0; j < kML; ++j) {
+            const int s = lane + 64 * j;
+            const float f = mr[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mr[j] - m);
+            if (s >= s_lo && s < s_hi) wsp[s] = f;
+            l += lr[j] * f;
+        }
+        for (int s = lane + 64 * kML; s < S; s += 64) {
             const float ms = base[(s * R + h) * kRec + D];
             const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - m);
-            wsp[h][s] = f;
+            if (s >= s_lo && s < s_hi) wsp[s] = f;
             l += base[(s * R + h) * kRec + D + 1] * f;
         }
         l = wave_sum(l);
-        const float linv = 1.0f / l;
-        if (blockIdx.y == 0) {
-            wave_lds_fence();  // this wave's split weights are in LDS
-            float o0 = 0.f, o1 = 0.f;
+    };
+    if (blockIdx.y == 0) {
+        const int h = hb;
+        const int s_lo = S * wave / 4, s_hi = S * (wave + 1) / 4;
+        auto row = [&](int s) {
+            return *reinterpret_cast<const float2*>(base + (s * R + h) * kRec + 2 * lane);
+        };
+        // the range's first rows are requested together with the (m, l) pairs
+        constexpr int kPre = 16;
+        float2 xp[kPre];
 #pragma unroll
-            for (int s = 0; s < kPre; ++s) {
-                const float f = s < S ? wsp[h][s] : 0.f;
-                o0 += xp[s].x * f;
-                o1 += xp[s].y * f;
+        for (int j = 0; j < kPre; ++j) xp[j] = s_lo + j < s_hi ? row(s_lo + j) : make_float2(0.f, 0.f);
+        float m, l;
+        softmax_terms(h, s_lo, s_hi, m, l);
+        wave_lds_fence();  // this wavefront's split weights are in LDS
+        // lane owns channels 2 lane, 2 lane + 1
+        float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < kPre; ++j) {
+            const float f = s_lo + j < s_hi ? wsp[s_lo + j] : 0.f;
+            o0 += xp[j].x * f;
+            o1 += xp[j].y * f;
+        }
+        for (int s0 = s_lo + kPre; s0 < s_hi; s0 += 16) {
+            float2 x[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) x[j] = s0 + j < s_hi ? row(s0 + j) : make_float2(0.f, 0.f);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float f = s0 + j < s_hi ? wsp[s0 + j] : 0.f;
+                o0 += x[j].x * f;
+                o1 += x[j].y * f;
             }
-            for (int s = kPre; s < S; ++s) {
-                const float2 x = *reinterpret_cast<const float2*>(base + (s * R + h) * kRec + 2 * lane);
-                const float f = wsp[h][s];
-                o0 += x.x * f;
-                o1 += x.y * f;
+        }
+        *reinterpret_cast<float2*>(&opart[wave][2 * lane]) = make_float2(o0, o1);
+        __syncthreads();
+        if (wave == 0) {
+            float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                t0 += opart[w][2 * lane];
+                t1 += opart[w][2 * lane + 1];
             }
+            const float linv = 1.0f / l;
             const int b = u / a.n_kv_heads, hk = u % a.n_kv_heads;
             *reinterpret_cast<float2*>(a.out + ((int64_t)b * a.n_kv_heads * R + hk * R + h) * D + 2 * lane) =
-                make_float2(o0 * linv, o1 * linv);
-            return;
+                make_float2(t0 * linv, t1 * linv);
         }
+        return;
+    }
+    if (wave < R) {
+        float m, l;
+        softmax_terms(wave, 0, 0, m, l);
         if (lane == 0) {
-            Ms[h] = m;
-            Linv[h] = linv;
+            Ms[wave] = m;
+            Linv[wave] = 1.0f / l;
         }
     }
-    if (blockIdx.y == 0) return;
     __syncthreads();
-    // H2O increments of a 2048-token slice: sum over the r query heads of the
-    // normalized probabilities.
-    const int64_t t0 = (int64_t)(blockIdx.y - 1) * kH2OChunk;
-    for (int64_t t = t0 + threadIdx.x; t < t0 + kH2OChunk && t < a.T; t += 256) {
+    // H2O increments of this block's part of a 2048-token slice: sum over the
+    // r query heads of the normalized probabilities.
+    constexpr int kPart = kH2OChunk / R;
+    const int64_t t0 = (int64_t)(blockIdx.y - 1) * kH2OChunk + (int64_t)hb * kPart;
+    for (int64_t t = t0 + threadIdx.x; t < t0 + kPart && t < a.T; t += 256) {
         float d = 0.f;
 #pragma unroll
         for (int h = 0; h < R; ++h)
@@ -1036,7 +1080,7 @@ void launch_decode_t(DecodeArgs a, hipEvent_t e0, hipEvent_t e1, hipStream_t s) 
     else
         hipLaunchKernelGGL((decode_kernel<BITS, R, G>), dim3(blocks), dim3(256), 0, s, a);
     const unsigned ny = 1 + (a.acc ? (unsigned)((a.T + kH2OChunk - 1) / kH2OChunk) : 0u);
-    hipLaunchKernelGGL((merge_kernel<R>), dim3(a.units, ny), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((merge_kernel<R>), dim3(a.units * R, ny), dim3(256), 0, s, a);
 }
 
 template <int BITS, int R>

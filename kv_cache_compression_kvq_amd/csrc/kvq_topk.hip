@@ -7,8 +7,12 @@
 //
 // One 1024-thread workgroup per row. The row's order-preserving 32-bit keys
 // are staged once in LDS (rows longer than the LDS share are read from
-// memory in every pass instead). An 8-bit-digit radix select finds the k-th
-// largest key tau and how many of the keys equal to tau are kept; lanes of a
+// memory in every pass instead). A radix select with 11-, 11- and 10-bit
+// digits finds the k-th largest key tau and how many of the keys equal to
+// tau are kept: after the first digit's histogram, the keys sharing the
+// chosen first digit (usually a few percent of the row) are copied to a
+// candidate list, and the two remaining digits are resolved on that list (on
+// the whole row if it overflows). Lanes of a
 // wavefront that fall into the same histogram bin add once, by their count.
 // Each wavefront then owns a contiguous index range and writes its kept
 // indices in ascending order from ballot prefix counts.
@@ -21,7 +25,9 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kLdsKeys = 36864;  // keys staged in LDS (144 KB)
+constexpr int kLdsKeys = 33280;  // keys staged in LDS (130 KB)
+constexpr int kBins = 2048;      // histogram bins (11-bit digits)
+constexpr int kCand = 4096;      // candidate list after the first digit
 
 __device__ __forceinline__ uint32_t order_key(float x) {
     uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -54,12 +60,42 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
     if ((todo >> lane_id()) & 1ull) atomicAdd(&hist[bin], 1u);
 }
 
+// Digit of the k-th largest among the counted keys: the bin where the count
+// from the top reaches `need`; also the keys still needed inside that bin.
+// Wavefront 0 only: lane l holds bins 32 l .. 32 l + 31.
+__device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t need, uint32_t* sel) {
+    const int lane = threadIdx.x & 63;
+    uint32_t c = 0;
+    for (int j = 0; j < kBins / 64; ++j) c += hist[(kBins / 64) * lane + j];
+    uint32_t s = c;  // sum over lanes >= l
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_down(s, o);
+        if (lane + o < 64) s += y;
+    }
+    if (s >= need && s - c < need) {
+        uint32_t cum = s - c, d = (kBins / 64) * lane;
+        for (int j = kBins / 64 - 1; j >= 0; --j) {
+            const uint32_t b = hist[(kBins / 64) * lane + j];
+            if (cum + b >= need) {
+                d = (kBins / 64) * lane + j;
+                break;
+            }
+            cum += b;
+        }
+        sel[0] = d;
+        sel[1] = need - cum;
+    }
+}
+
 template <bool kLds>
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* scores, int32_t T, int32_t k,
                                                         int32_t w, int32_t* idx) {
     extern __shared__ uint32_t keys[];  // [n] when kLds
-    __shared__ uint32_t hist[256];
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t cand[kCand];
     __shared__ uint32_t sel[2];  // chosen digit, keys still needed
+    __shared__ uint32_t n_cand;
     __shared__ uint32_t cnt_gt[kWaves], cnt_eq[kWaves];
     const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = T - w;
@@ -71,53 +107,60 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* scores, int
         for (int i = tid; i < n; i += kThreads) out[i] = i;
         return;
     }
-    if (kLds)
-        for (int i = tid; i < n; i += kThreads) keys[i] = order_key(sc[i]);
     auto key_at = [&](int i) -> uint32_t { return kLds ? keys[i] : order_key(sc[i]); };
-
-    // Radix select: tau = the k-th largest key, need = keys equal to tau kept.
-    uint32_t prefix = 0, pmask = 0, need = (uint32_t)k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        if (tid < 256) hist[tid] = 0;
+    for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+    if (tid == 0) n_cand = 0;
+    __syncthreads();
+    // Staging first, in a loop of independent loads (the histogram's LDS
+    // atomics would otherwise sit between consecutive loads).
+    if (kLds) {
+        for (int i = tid; i < n; i += kThreads) keys[i] = order_key(sc[i]);
         __syncthreads();
-        // every wavefront runs the same trip count, so ballots see whole waves
-        for (int i0 = 0; i0 < n; i0 += kThreads) {
+    }
+    // First digit (bits 21-31). Every wavefront runs the same trip count, so
+    // ballots see whole waves.
+    for (int i0 = 0; i0 < n; i0 += kThreads) {
+        const int i = i0 + tid;
+        const uint32_t key = i < n ? key_at(i) : 0u;
+        hist_add(hist, key >> 21, i < n);
+    }
+    __syncthreads();
+    if (wave == 0) pick_digit(hist, (uint32_t)k, sel);
+    __syncthreads();
+    uint32_t prefix = sel[0] << 21, need = sel[1];
+    // Candidates: the keys with that first digit.
+    for (int i0 = 0; i0 < n; i0 += kThreads) {
+        const int i = i0 + tid;
+        const uint32_t key = i < n ? key_at(i) : 0u;
+        const bool c = i < n && (key >> 21) == (prefix >> 21);
+        const uint64_t m = __ballot(c);
+        uint32_t base = 0;
+        if (lane == 0 && m) base = atomicAdd(&n_cand, (uint32_t)__popcll(m));
+        base = __builtin_amdgcn_readfirstlane(base);
+        const uint32_t at = base + rank_in(m);
+        if (c && at < (uint32_t)kCand) cand[at] = key;
+    }
+    __syncthreads();
+    const uint32_t nc = n_cand;
+    const bool use_cand = nc <= (uint32_t)kCand;
+    // Remaining digits: bits 10-20, then 0-9.
+    uint32_t pmask = 0xFFE00000u;
+    for (int pass = 0; pass < 2; ++pass) {
+        const int shift = pass == 0 ? 10 : 0;
+        const uint32_t dmask = pass == 0 ? 0x7FFu : 0x3FFu;
+        for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+        __syncthreads();
+        const int m = use_cand ? (int)nc : n;
+        for (int i0 = 0; i0 < m; i0 += kThreads) {
             const int i = i0 + tid;
-            const uint32_t key = i < n ? key_at(i) : 0u;
-            hist_add(hist, (key >> shift) & 255u, i < n && (key & pmask) == prefix);
+            const uint32_t key = i < m ? (use_cand ? cand[i] : key_at(i)) : 0u;
+            hist_add(hist, (key >> shift) & dmask, i < m && (key & pmask) == prefix);
         }
         __syncthreads();
-        if (wave == 0) {
-            // lane l holds bins 4l .. 4l+3; suffix sums from the top bin down
-            uint32_t b[4], c = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                b[j] = hist[4 * lane + j];
-                c += b[j];
-            }
-            uint32_t s = c;  // sum over lanes >= l
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t y = __shfl_down(s, o);
-                if (lane + o < 64) s += y;
-            }
-            if (s >= need && s - c < need) {
-                uint32_t cum = s - c, d = 4 * lane;
-#pragma unroll
-                for (int j = 3; j >= 0; --j) {
-                    if (cum + b[j] >= need) {
-                        d = 4 * lane + j;
-                        break;
-                    }
-                    cum += b[j];
-                }
-                sel[0] = d;
-                sel[1] = need - cum;
-            }
-        }
+        if (wave == 0) pick_digit(hist, need, sel);
         __syncthreads();
         prefix |= sel[0] << shift;
-        pmask |= 255u << shift;
+        pmask |= dmask << shift;
         need = sel[1];
         __syncthreads();
     }

@@ -202,7 +202,8 @@ def test_snapshot_and_resume_match_unsplit_run():
 @pytest.mark.parametrize("rows,T,k,w,ties", [
     (5, 1000, 190, 64, False), (3, 4097, 800, 256, True), (2, 300, 0, 10, False),
     (2, 300, 290, 10, True), (4, 513, 100, 0, True), (1, 70000, 9000, 300, False),
-    (2, 37120, 7000, 256, True), (2, 500, 490, 10, False),
+    (2, 37120, 7000, 256, True), (2, 500, 490, 10, False), (2, 33536, 6000, 256, True),
+    (3, 33536, 6553, 256, False),
 ])
 def test_topk_exact(kvq, rows, T, k, w, ties):
     s = synth.score_rows(rows, T, seed=3, ties=ties)
