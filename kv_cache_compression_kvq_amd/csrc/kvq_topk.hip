@@ -64,9 +64,18 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
 // from the top reaches `need`; also the keys still needed inside that bin.
 // Wavefront 0 only: lane l holds bins 32 l .. 32 l + 31.
 __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t need, uint32_t* sel) {
+    constexpr int kPer = kBins / 64;
     const int lane = threadIdx.x & 63;
-    uint32_t c = 0;
-    for (int j = 0; j < kBins / 64; ++j) c += hist[(kBins / 64) * lane + j];
+    uint32_t b[kPer], c = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; j += 4) {
+        const uint4 x = *reinterpret_cast<const uint4*>(hist + kPer * lane + j);
+        b[j] = x.x;
+        b[j + 1] = x.y;
+        b[j + 2] = x.z;
+        b[j + 3] = x.w;
+        c += (x.x + x.y) + (x.z + x.w);
+    }
     uint32_t s = c;  // sum over lanes >= l
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -74,28 +83,31 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t need, 
         if (lane + o < 64) s += y;
     }
     if (s >= need && s - c < need) {
-        uint32_t cum = s - c, d = (kBins / 64) * lane;
-        for (int j = kBins / 64 - 1; j >= 0; --j) {
-            const uint32_t b = hist[(kBins / 64) * lane + j];
-            if (cum + b >= need) {
-                d = (kBins / 64) * lane + j;
-                break;
+        // walk this lane's bins from the top, in registers
+        uint32_t cum = s - c, d = kPer * lane, left = 0;
+        bool found = false;
+#pragma unroll
+        for (int j = kPer - 1; j >= 0; --j) {
+            const bool hit = !found && cum + b[j] >= need;
+            if (hit) {
+                d = kPer * lane + j;
+                left = need - cum;
             }
-            cum += b;
+            found |= hit;
+            if (!found) cum += b[j];
         }
         sel[0] = d;
-        sel[1] = need - cum;
+        sel[1] = left;
     }
 }
 
 template <bool kLds>
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* scores, int32_t T, int32_t k,
                                                         int32_t w, int32_t* idx) {
-    extern __shared__ uint32_t keys[];  // [n] when kLds
-    __shared__ uint32_t hist[kBins];
+    extern __shared__ __align__(16) uint32_t keys[];  // [n] when kLds
+    __shared__ __align__(16) uint32_t hist[kBins];
     __shared__ uint32_t cand[kCand];
     __shared__ uint32_t sel[2];  // chosen digit, keys still needed
-    __shared__ uint32_t n_cand;
     __shared__ uint32_t cnt_gt[kWaves], cnt_eq[kWaves];
     const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = T - w;
@@ -109,39 +121,73 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* scores, int
     }
     auto key_at = [&](int i) -> uint32_t { return kLds ? keys[i] : order_key(sc[i]); };
     for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
-    if (tid == 0) n_cand = 0;
     __syncthreads();
     // Staging first, in a loop of independent loads (the histogram's LDS
     // atomics would otherwise sit between consecutive loads).
     if (kLds) {
-        for (int i = tid; i < n; i += kThreads) keys[i] = order_key(sc[i]);
+        // 16-byte loads when the row is 16-byte aligned
+        int done = 0;
+        if ((reinterpret_cast<uintptr_t>(sc) & 15) == 0) {
+            const float4* s4 = reinterpret_cast<const float4*>(sc);
+            for (int i = tid; i < n / 4; i += kThreads) {
+                const float4 x = s4[i];
+                *reinterpret_cast<uint4*>(keys + 4 * i) =
+                    make_uint4(order_key(x.x), order_key(x.y), order_key(x.z), order_key(x.w));
+            }
+            done = n / 4 * 4;
+        }
+        for (int i = done + tid; i < n; i += kThreads) keys[i] = order_key(sc[i]);
         __syncthreads();
     }
+    // Keys i0 + j * stride (+ this thread's offset) for j < 4, read together
+    // before they are used; 0 past lim.
+    auto load4 = [&](int i0, int stride, int lim, uint32_t (&kk)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kk[j] = i0 + j * stride < lim ? key_at(i0 + j * stride) : 0u;
+    };
     // First digit (bits 21-31). Every wavefront runs the same trip count, so
     // ballots see whole waves.
-    for (int i0 = 0; i0 < n; i0 += kThreads) {
-        const int i = i0 + tid;
-        const uint32_t key = i < n ? key_at(i) : 0u;
-        hist_add(hist, key >> 21, i < n);
+    for (int i0 = 0; i0 < n; i0 += 4 * kThreads) {
+        uint32_t kk[4];
+        load4(i0 + tid, kThreads, n, kk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hist_add(hist, kk[j] >> 21, i0 + j * kThreads + tid < n);
     }
     __syncthreads();
     if (wave == 0) pick_digit(hist, (uint32_t)k, sel);
     __syncthreads();
     uint32_t prefix = sel[0] << 21, need = sel[1];
-    // Candidates: the keys with that first digit.
-    for (int i0 = 0; i0 < n; i0 += kThreads) {
-        const int i = i0 + tid;
-        const uint32_t key = i < n ? key_at(i) : 0u;
-        const bool c = i < n && (key >> 21) == (prefix >> 21);
-        const uint64_t m = __ballot(c);
-        uint32_t base = 0;
-        if (lane == 0 && m) base = atomicAdd(&n_cand, (uint32_t)__popcll(m));
-        base = __builtin_amdgcn_readfirstlane(base);
-        const uint32_t at = base + rank_in(m);
-        if (c && at < (uint32_t)kCand) cand[at] = key;
+    // Candidates: the keys with that first digit, counted per wavefront, then
+    // written at the wavefront's offset.
+    uint32_t mine = 0;
+    for (int i0 = 0; i0 < n; i0 += 4 * kThreads) {
+        uint32_t kk[4];
+        load4(i0 + tid, kThreads, n, kk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            mine += __popcll(__ballot(i0 + j * kThreads + tid < n && (kk[j] >> 21) == (prefix >> 21)));
+    }
+    if (lane == 0) cnt_gt[wave] = mine;
+    __syncthreads();
+    uint32_t at0 = 0, nc = 0;
+    for (int v = 0; v < kWaves; ++v) {
+        at0 += v < wave ? cnt_gt[v] : 0u;
+        nc += cnt_gt[v];
+    }
+    if (nc <= (uint32_t)kCand) {
+        for (int i0 = 0; i0 < n; i0 += 4 * kThreads) {
+            uint32_t kk[4];
+            load4(i0 + tid, kThreads, n, kk);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool c = i0 + j * kThreads + tid < n && (kk[j] >> 21) == (prefix >> 21);
+                const uint64_t m = __ballot(c);
+                if (c) cand[at0 + rank_in(m)] = kk[j];
+                at0 += __popcll(m);
+            }
+        }
     }
     __syncthreads();
-    const uint32_t nc = n_cand;
     const bool use_cand = nc <= (uint32_t)kCand;
     // Remaining digits: bits 10-20, then 0-9.
     uint32_t pmask = 0xFFE00000u;
@@ -171,11 +217,15 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* scores, int
     const int lo = wave * per < n ? wave * per : n;
     const int hi = lo + per < n ? lo + per : n;
     uint32_t gt = 0, eq = 0;
-    for (int i0 = lo; i0 < hi; i0 += 64) {
-        const int i = i0 + lane;
-        const uint32_t key = i < hi ? key_at(i) : 0u;
-        gt += __popcll(__ballot(i < hi && key > tau));
-        eq += __popcll(__ballot(i < hi && key == tau));
+    for (int i0 = lo; i0 < hi; i0 += 256) {
+        uint32_t kk[4];
+        load4(i0 + lane, 64, hi, kk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool in = i0 + 64 * j + lane < hi;
+            gt += __popcll(__ballot(in && kk[j] > tau));
+            eq += __popcll(__ballot(in && kk[j] == tau));
+        }
     }
     if (lane == 0) {
         cnt_gt[wave] = gt;
@@ -194,16 +244,20 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* scores, int
     const uint32_t eq_first_kept = eq_total - need;
     uint32_t pos = gt_before + (eq_before > eq_first_kept ? eq_before - eq_first_kept : 0u);
     uint32_t er = eq_before;
-    for (int i0 = lo; i0 < hi; i0 += 64) {
-        const int i = i0 + lane;
-        const uint32_t key = i < hi ? key_at(i) : 0u;
-        const bool is_eq = i < hi && key == tau;
-        const uint64_t me = __ballot(is_eq);
-        const bool keep = (i < hi && key > tau) || (is_eq && er + rank_in(me) >= eq_first_kept);
-        const uint64_t mk = __ballot(keep);
-        if (keep) out[pos + rank_in(mk)] = i;
-        pos += __popcll(mk);
-        er += __popcll(me);
+    for (int i0 = lo; i0 < hi; i0 += 256) {
+        uint32_t kk[4];
+        load4(i0 + lane, 64, hi, kk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = i0 + 64 * j + lane;
+            const bool is_eq = i < hi && kk[j] == tau;
+            const uint64_t me = __ballot(is_eq);
+            const bool keep = (i < hi && kk[j] > tau) || (is_eq && er + rank_in(me) >= eq_first_kept);
+            const uint64_t mk = __ballot(keep);
+            if (keep) out[pos + rank_in(mk)] = i;
+            pos += __popcll(mk);
+            er += __popcll(me);
+        }
     }
 }
 
