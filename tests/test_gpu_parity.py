@@ -79,6 +79,60 @@ def test_append_state_bit_exact_ragged(bits, group):
         H.check_unit_state(st, u, orc[key])
 
 
+def _tie_groups(bits, n_groups, d, G, seed):
+    """fp16 rows [n_groups * G][d] whose groups put many quotients (x - mn) / q
+    on or within a few fp32 ulps of a half-integer: ranges 2^e, 3*2^e, 5*2^e
+    (q inexact for 2^b - 1 = 3 or 15), values at the exact half points those
+    ranges allow, their fp16 neighbours, and random fill. Layout: the min and
+    max sit in the first two rows of each group (key groups run over tokens)."""
+    rng = np.random.default_rng(seed)
+    L = (1 << bits) - 1
+    out = np.empty((n_groups * G, d), dtype=np.float32)
+    for g in range(n_groups):
+        for c in range(d):
+            e = int(rng.integers(-6, 3))
+            mult = [1, 3, 5][int(rng.integers(0, 3))]
+            rng_w = mult * 2.0 ** e
+            mn = float(rng.integers(-8, 9)) * 2.0 ** (e - 1)
+            # half points (k + 1/2) * rng_w / L that are exact binary fractions
+            halves = [mn + (2 * k + 1) * rng_w / (2 * L) for k in range(L)
+                      if ((2 * k + 1) * mult) % L == 0]
+            halves = [h for h in halves if np.float16(h) == h] or [mn + rng_w / 2]
+            col = [mn, mn + rng_w]
+            while len(col) < G:
+                h = np.float16(halves[int(rng.integers(0, len(halves)))])
+                step = int(rng.integers(-1, 2))
+                x = h if step == 0 else np.nextafter(h, np.float16(np.inf * step))
+                if rng.random() < 0.25:
+                    x = np.float16(mn + rng.random() * rng_w)
+                col.append(float(min(max(float(x), mn), mn + rng_w)))
+            out[g * G:(g + 1) * G, c] = np.array(col, dtype=np.float32)
+    return out.astype(np.float16)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_append_quotient_ties_bit_exact(bits):
+    # Codes whose fp32 quotient sits on or next to a rounding boundary decide
+    # through the correctly rounded division, not the reciprocal product.
+    G, d, R, n_groups = 32, 128, 32, 6
+    w = small(bits=bits, group=G, residual=R, tokens=n_groups * G + R, batch=1, hkv=2)
+    K = np.empty((1, 2, w.tokens, d), dtype=np.float16)
+    V = np.empty_like(K)
+    for h in range(2):
+        kk = _tie_groups(bits, n_groups + 1, d, G, seed=10 + h)
+        # values: the same construction along channels (one 32-channel group
+        # per column block), transposed into token rows
+        vv = _tie_groups(bits, d // G, w.tokens, G, seed=20 + h)
+        K[0, h] = kk[: w.tokens]
+        V[0, h] = vv.reshape(d // G, G, w.tokens).transpose(2, 0, 1).reshape(w.tokens, d)
+    gc = H.GpuCache(w)
+    gc.append(K, V)
+    orc = H.oracle_units(w, all_units(w), K, V)
+    st = gc.state()
+    for u, key in enumerate(all_units(w)):
+        H.check_unit_state(st, u, orc[key])
+
+
 def test_append_tiny_workload_bit_exact():
     w = W["tiny"]
     gc, K, V = run_appends(w, [w.tokens])

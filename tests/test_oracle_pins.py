@@ -569,3 +569,19 @@ def test_topk_equals_repeated_argmin_eviction(ties):
 def test_topk_tie_order_prefers_newer():
     s = np.array([[1, 2, 2, 2, 0, 5]], dtype=np.float32)
     assert O.topk_keep(s, 2, 1).tolist() == [[2, 3, 5]]
+
+
+def test_bulk_append_bytes_closed_form():
+    """Bulk append moves every fp16 K/V row in once (2 * d * 2 bytes), writes
+    the quantized tokens' codes and fp16 scale/zero (d*b/4 + 4d/G + 4d/Gv
+    bytes) and the residual tokens' fp16 rows (4d bytes)."""
+    from kv_cache_compression_kvq_amd import bytes_model as BM
+    # 2-bit, G = 32, d = 128: 64 B of codes + 16 B key meta + 16 B value meta
+    per_q = 128 * 2 // 4 + 4 * 128 // 32 + 4 * 128 // 32
+    assert per_q == 96
+    # B8 x 8 KV heads, T = 8192, R = 128: n_q = 8064
+    got = BM.bulk_append_bytes(units=64, head_dim=128, tokens=8192, n_quant=8064, bits=2, group=32)
+    assert got == 64 * (8192 * 512 + 8064 * 96 + 128 * 512) == 322174976
+    # 4-bit, G = 128 (one value group per token): 128 + 4 + 4 bytes per quantized token
+    got4 = BM.bulk_append_bytes(units=1, head_dim=128, tokens=300, n_quant=128, bits=4, group=128)
+    assert got4 == 300 * 512 + 128 * 136 + 172 * 512
