@@ -113,10 +113,11 @@ def traffic_entry(workload: str, kernel_alg_bytes: float):
             "copy_scale": t["copy_scale"], "source": os.path.relpath(path, ROOT)}
 
 
-def cpu_baseline(w, seconds: float):
+def cpu_baseline(w, seconds: float, picks=None):
     """The oracle (numpy, fp64 attention, one thread) on a bounded sample of
     units: per sampled unit, repeated decode steps of the same kind the GPU
-    times. Setup (quantizing the prefix) is not timed."""
+    times. Setup (quantizing the prefix) is not timed. ``picks`` selects
+    units by position in a fixed seeded permutation (default: the first 4)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -127,7 +128,9 @@ def cpu_baseline(w, seconds: float):
                       evict_cap=w.evict_cap, head_dim=w.head_dim)
     units = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
     rng = np.random.default_rng(1)
-    pick = [units[i] for i in rng.permutation(len(units))[: min(4, len(units))]]
+    perm = rng.permutation(len(units))
+    pick = [units[perm[i % len(units)]] for i in (picks if picks is not None
+                                                  else range(min(4, len(units))))]
     r = w.gqa
     total_t, total_bytes, steps, used = 0.0, 0, 0, set()
     with threadpool_limits(limits=1):
@@ -166,7 +169,35 @@ def cpu_baseline(w, seconds: float):
             "sample": f"{steps} single-unit decode steps over {len(used)} of {len(units)} "
                       f"(batch, KV head) units of the same workload, "
                       f"{'H2O scores + top-k' if w.h2o else 'append one token + attention'}, "
-                      f"numpy fp64, BLAS limited to 1 thread, {total_t:.1f} s"}
+                      f"numpy fp64, BLAS limited to 1 thread, {total_t:.1f} s",
+            "bytes": total_bytes, "seconds": total_t, "steps": steps}
+
+
+def _cpu_worker(job):
+    name, i, seconds = job
+    from kv_cache_compression_kvq_amd import synth
+    return cpu_baseline(synth.WORKLOADS[name], seconds, picks=[i])
+
+
+def cpu_baselines(w, seconds: float):
+    """The oracle on one core, then on every core of this process's CPU set
+    (at most 16, the share of one GPU) at once, one unit per worker process.
+    Runs before anything touches the GPU: the workers are forked."""
+    import multiprocessing
+
+    single = cpu_baseline(w, seconds)
+    n = max(1, min(16, len(os.sched_getaffinity(0))))
+    with multiprocessing.get_context("fork").Pool(n) as pool:
+        res = pool.map(_cpu_worker, [(w.name, i, seconds) for i in range(n)])
+    value = sum(r["bytes"] / r["seconds"] for r in res) / 1e9
+    steps = sum(r["steps"] for r in res)
+    out = {"value": value, "unit": "GB/s", "cores": n, "kind": "oracle",
+           "sample": f"{n} worker processes, one (batch, KV head) unit each, running at once: "
+                     f"{steps} single-unit decode steps of the same workload, numpy fp64, "
+                     f"one BLAS thread per worker, about {seconds:.0f} s each; value = sum of "
+                     f"the workers' rates",
+           "single_thread": {k: single[k] for k in ("value", "unit", "cores", "sample")}}
+    return out
 
 
 # Rows of the hot path timed by --rows: name -> (workload, what the timed call runs).
@@ -325,6 +356,11 @@ def rows_main(args):
 
 def main():
     args = parse_args()
+    # CPU oracle baseline first, while no process has touched the GPU
+    cpu_line = None
+    if args.rows is None and args.cpu_seconds > 0 and args.gpus == 1:
+        from kv_cache_compression_kvq_amd import synth as _synth
+        cpu_line = cpu_baselines(_synth.WORKLOADS[args.workload], args.cpu_seconds)
     if args.rows is not None:
         if args.gpus != 1:
             print("bench.py: this build runs on one GPU", file=sys.stderr)
@@ -540,7 +576,7 @@ def main():
         line["roofline"]["traffic"] = int(tr["total_bytes"])
         line["roofline"]["traffic_detail"] = tr
     if args.cpu_seconds > 0:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_line
     print(json.dumps(line), flush=True)
 
 
