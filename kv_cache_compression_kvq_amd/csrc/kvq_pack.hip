@@ -161,10 +161,6 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
     // walk over the groups reads them from LDS
     constexpr int kScanBatch = 2048;
     __shared__ uint64_t sc_all[kScanBatch];
-    __shared__ uint64_t psc[kMaxPool];
-    __shared__ int32_t pidx[kMaxPool];
-    __shared__ int32_t slot[kMaxPool];
-    __shared__ uint32_t mwords[4];
     __shared__ uint32_t mbatch[kScanBatch / 32];  // chunk mask words of the staged groups
     // members displaced in this call: token and the pool slot it left
     __shared__ int32_t ev_tok[kMaxEvict], ev_from[kMaxEvict];
@@ -178,31 +174,36 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
     int pc = cnt[0], ec = cnt[1], frozen = cnt[2];
     const int ec0 = ec;
     const int64_t t_first = g0 * G;  // tokens from here on are admitted in this call
-    for (int p = lane; p < N; p += 64) {
-        pidx[p] = v.pool_idx[(int64_t)u * N + p];
-        psc[p] = v.pool_score[(int64_t)u * N + p];
-    }
-    __syncthreads();
-    // The pool's worst member (largest (score, index)) once the pool is full:
-    // only tokens ordered before it can rank among the N best. Recomputed
-    // after admissions only.
+    // Pool member p lives in lane p (N <= 64): its exact score and token index.
+    uint64_t psl = lane < N ? v.pool_score[(int64_t)u * N + lane] : 0ull;
+    int32_t pil = lane < N ? v.pool_idx[(int64_t)u * N + lane] : -1;
+    auto rl64 = [](uint64_t x, int l) -> uint64_t {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+        return (uint64_t)lo | ((uint64_t)hi << 32);
+    };
+    // The pool's worst member (largest (score, index)) and its slot once the
+    // pool is full: only tokens ordered before it can rank among the N best.
     uint64_t wsc = ~0ull;
     int32_t widx = INT32_MAX;
+    int wslot = 0;
     auto find_worst = [&] {
+        wsc = ~0ull;
+        widx = INT32_MAX;
         if (pc < N) return;
-        uint64_t a = lane < N ? psc[lane] : 0ull;
-        int32_t b = lane < N ? pidx[lane] : -1;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const uint64_t a2 = __shfl_xor(a, off);
-            const int32_t b2 = __shfl_xor(b, off);
-            if (a2 > a || (a2 == a && b2 > b)) {
-                a = a2;
-                b = b2;
+        uint64_t bs = 0;
+        int32_t bi = -1;
+        for (int p = 0; p < N; ++p) {
+            const uint64_t sp = rl64(psl, p);
+            const int32_t ip = __builtin_amdgcn_readlane(pil, p);
+            if (sp > bs || (sp == bs && ip > bi)) {
+                bs = sp;
+                bi = ip;
+                wslot = p;
             }
         }
-        wsc = a;
-        widx = b;
+        wsc = bs;
+        widx = bi;
     };
     find_worst();
     int64_t gb = g0, gb_end = g0, g = g0;
@@ -223,87 +224,182 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
             wave_sync();
         }
         const uint64_t* sc = sc_all + (g - gb) * G;
-        bool cand = false;
-        for (int i = lane; i < G; i += 64)
-            cand |= pc < N || sc[i] < wsc || (sc[i] == wsc && t0 + i < widx);
-        if (!__any(cand)) {  // nothing enters the pool: the common case
+        // this lane's tokens of the group: lane and lane + 64 (G = 128)
+        uint64_t sl[2];
+        bool cand[2], any = false;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int i = lane + 64 * j;
+            sl[j] = i < G ? sc[i] : ~0ull;
+            cand[j] = i < G && (pc < N || sl[j] < wsc || (sl[j] == wsc && t0 + i < widx));
+            any |= cand[j];
+        }
+        if (!__any(any)) {  // nothing enters the pool: the common case
             if (lane < G / 32) mbatch[(g - gb) * (G / 32) + lane] = 0u;
             continue;
         }
-        for (int p = lane; p < N; p += 64) slot[p] = -1;
-        if (lane < 4) mwords[lane] = 0;
-        wave_sync();
-        for (int i = lane; i < G; i += 64) {
-            const uint64_t si = sc[i];
-            const int64_t ti = t0 + i;
-            if (pc == N && !(si < wsc || (si == wsc && ti < widx))) continue;
-            int rank = 0;
-            for (int p = 0; p < pc; ++p) rank += (psc[p] < si) || (psc[p] == si && pidx[p] < ti);
-            for (int q = 0; q < G; ++q) rank += (sc[q] < si) || (sc[q] == si && q < i);
-            if (rank < N) slot[rank] = i;
-        }
-        wave_sync();
-        for (int rk = 0; rk < N; ++rk) {
-            const int i = slot[rk];
-            if (i < 0) continue;
-            const int64_t t = t0 + i;
-            int dst;
-            if (pc == N) {
-                int w = 0;
-                for (int p = 1; p < N; ++p)
-                    if (psc[p] > psc[w] || (psc[p] == psc[w] && pidx[p] > pidx[w])) w = p;
+        uint32_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
+        auto mark = [&](int i) {
+            const uint32_t bit = 1u << (i & 31);
+            if ((i >> 5) == 0) mw0 |= bit;
+            else if ((i >> 5) == 1) mw1 |= bit;
+            else if ((i >> 5) == 2) mw2 |= bit;
+            else mw3 |= bit;
+        };
+        if (pc == N) {
+            // Full pool: the candidates order before the worst member, hence
+            // before every other token of the group. Taking them in ascending
+            // (score, index) order, the k-th enters iff it still orders before
+            // the current worst member, i.e. iff (pool members before it) +
+            // k - 1 < N: the same admissions, in the same order, as by rank.
+            uint64_t m0 = __ballot(cand[0]), m1 = __ballot(cand[1]);
+            while (m0 | m1) {
+                uint64_t bs = ~0ull;
+                int64_t bt = INT64_MAX;
+                int bl = 0;
+                for (uint64_t m = m0; m; m &= m - 1) {
+                    const int l = __builtin_ctzll(m);
+                    const uint64_t sq = rl64(sl[0], l);
+                    if (sq < bs || (sq == bs && t0 + l < bt)) {
+                        bs = sq;
+                        bt = t0 + l;
+                        bl = l;
+                    }
+                }
+                for (uint64_t m = m1; m; m &= m - 1) {
+                    const int l = __builtin_ctzll(m);
+                    const uint64_t sq = rl64(sl[1], l);
+                    if (sq < bs || (sq == bs && t0 + 64 + l < bt)) {
+                        bs = sq;
+                        bt = t0 + 64 + l;
+                        bl = 64 + l;
+                    }
+                }
+                if (!(bs < wsc || (bs == wsc && bt < widx))) break;
                 if (ec == E) {
                     frozen = 1;
                     break;
                 }
                 if (lane == 0) {
-                    v.ev_idx[(int64_t)u * E + ec] = pidx[w];
-                    ev_tok[ec - ec0] = pidx[w];
-                    ev_from[ec - ec0] = w;
+                    v.ev_idx[(int64_t)u * E + ec] = widx;
+                    ev_tok[ec - ec0] = widx;
+                    ev_from[ec - ec0] = wslot;
                 }
                 ++ec;
-                dst = w;
+                if (lane == wslot) {
+                    psl = bs;
+                    pil = (int32_t)bt;
+                }
+                mark(bl);
+                if (bl < 64) m0 &= ~(1ull << bl);
+                else m1 &= ~(1ull << (bl - 64));
+                find_worst();
+            }
+            if (lane < G / 32)
+                mbatch[(g - gb) * (G / 32) + lane] = lane == 0 ? mw0 : lane == 1 ? mw1 : lane == 2 ? mw2 : mw3;
+            continue;
+        }
+        // Pool still filling: rank of each token among the pool members and
+        // the group, by (score, index).
+        int rank[2] = {0, 0};
+        for (int p = 0; p < pc; ++p) {
+            const uint64_t sp = rl64(psl, p);
+            const int64_t ip = __builtin_amdgcn_readlane(pil, p);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                rank[j] += (sp < sl[j]) || (sp == sl[j] && ip < t0 + lane + 64 * j);
+        }
+        for (int q = 0; q < G; ++q) {
+            const uint64_t sq = rl64(q < 64 ? sl[0] : sl[1], q & 63);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) rank[j] += (sq < sl[j]) || (sq == sl[j] && q < lane + 64 * j);
+        }
+        // Admissions in rank order; a full pool gives up its worst member.
+        for (int rk = 0; rk < N; ++rk) {
+            const uint64_t m0 = __ballot(cand[0] && rank[0] == rk);
+            const uint64_t m1 = __ballot(cand[1] && rank[1] == rk);
+            if (m0 == 0 && m1 == 0) continue;
+            const int i = m0 ? __builtin_ctzll(m0) : 64 + __builtin_ctzll(m1);
+            const int64_t t = t0 + i;
+            const uint64_t si = rl64(i < 64 ? sl[0] : sl[1], i & 63);
+            int dst;
+            if (pc == N) {
+                if (ec == E) {
+                    frozen = 1;
+                    break;
+                }
+                if (lane == 0) {
+                    v.ev_idx[(int64_t)u * E + ec] = widx;
+                    ev_tok[ec - ec0] = widx;
+                    ev_from[ec - ec0] = wslot;
+                }
+                ++ec;
+                dst = wslot;
             } else {
                 dst = pc++;
             }
-            wave_sync();  // the displaced member is recorded before its slot is reused
-            if (lane == 0) {
-                pidx[dst] = (int32_t)t;
-                psc[dst] = sc[i];
-                mwords[i / 32] |= 1u << (i % 32);
+            if (lane == dst) {
+                psl = si;
+                pil = (int32_t)t;
             }
-            wave_sync();
+            mark(i);
+            find_worst();
         }
-        if (lane < G / 32) mbatch[(g - gb) * (G / 32) + lane] = mwords[lane];
-        wave_sync();
-        find_worst();
+        if (lane < G / 32)
+            mbatch[(g - gb) * (G / 32) + lane] = lane == 0 ? mw0 : lane == 1 ? mw1 : lane == 2 ? mw2 : mw3;
     }
     flush(g);
     wave_sync();
     // Row copies, after the walk. Displaced members first: a member admitted
     // in this call still has its rows in the input or the ring; an older one
     // has them in the pool slot it left, which no copy below has overwritten yet.
-    for (int e = ec0; e < ec; ++e) {
-        const int64_t t = ev_tok[e - ec0];
-        const int64_t ps = (int64_t)u * N + ev_from[e - ec0], es = (int64_t)u * E + e;
-        const uint16_t* kr = t >= t_first ? src_row(v.kring, knew, v, u, t, t_old, n_new) : v.pool_k + ps * D;
-        const uint16_t* vr = t >= t_first ? src_row(v.vring, vnew, v, u, t, t_old, n_new) : v.pool_v + ps * D;
-        reinterpret_cast<uint32_t*>(v.ev_k + es * D)[lane] = reinterpret_cast<const uint32_t*>(kr)[lane];
-        reinterpret_cast<uint32_t*>(v.ev_v + es * D)[lane] = reinterpret_cast<const uint32_t*>(vr)[lane];
+    // Four rows at a time: all loads, then all stores.
+    for (int e0 = ec0; e0 < ec; e0 += 4) {
+        uint32_t kx[4], vx[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (e0 + j >= ec) break;
+            const int64_t t = ev_tok[e0 + j - ec0];
+            const int64_t ps = (int64_t)u * N + ev_from[e0 + j - ec0];
+            const uint16_t* kr = t >= t_first ? src_row(v.kring, knew, v, u, t, t_old, n_new) : v.pool_k + ps * D;
+            const uint16_t* vr = t >= t_first ? src_row(v.vring, vnew, v, u, t, t_old, n_new) : v.pool_v + ps * D;
+            kx[j] = reinterpret_cast<const uint32_t*>(kr)[lane];
+            vx[j] = reinterpret_cast<const uint32_t*>(vr)[lane];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (e0 + j >= ec) break;
+            const int64_t es = (int64_t)u * E + e0 + j;
+            reinterpret_cast<uint32_t*>(v.ev_k + es * D)[lane] = kx[j];
+            reinterpret_cast<uint32_t*>(v.ev_v + es * D)[lane] = vx[j];
+        }
     }
     __syncthreads();  // every old pool row is read before the slots are rewritten
-    for (int p = 0; p < pc; ++p) {
-        const int64_t t = pidx[p];
-        if (t < t_first) continue;  // member from an earlier call, rows in place
-        const int64_t pd = (int64_t)u * N + p;
-        reinterpret_cast<uint32_t*>(v.pool_k + pd * D)[lane] = reinterpret_cast<const uint32_t*>(
-            src_row(v.kring, knew, v, u, t, t_old, n_new))[lane];
-        reinterpret_cast<uint32_t*>(v.pool_v + pd * D)[lane] = reinterpret_cast<const uint32_t*>(
-            src_row(v.vring, vnew, v, u, t, t_old, n_new))[lane];
+    for (int p0 = 0; p0 < pc; p0 += 4) {
+        uint32_t kx[4], vx[4];
+        bool cp[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // members from an earlier call keep their rows in place
+            const int p = p0 + j;
+            const int64_t t = p < pc ? __builtin_amdgcn_readlane(pil, p) : -1;
+            cp[j] = p < pc && t >= t_first;
+            if (cp[j]) {
+                kx[j] = reinterpret_cast<const uint32_t*>(src_row(v.kring, knew, v, u, t, t_old, n_new))[lane];
+                vx[j] = reinterpret_cast<const uint32_t*>(src_row(v.vring, vnew, v, u, t, t_old, n_new))[lane];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (!cp[j]) continue;
+            const int64_t pd = (int64_t)u * N + p0 + j;
+            reinterpret_cast<uint32_t*>(v.pool_k + pd * D)[lane] = kx[j];
+            reinterpret_cast<uint32_t*>(v.pool_v + pd * D)[lane] = vx[j];
+        }
     }
-    for (int p = lane; p < N; p += 64) {
-        v.pool_idx[(int64_t)u * N + p] = pidx[p];
-        v.pool_score[(int64_t)u * N + p] = psc[p];
+    if (lane < N) {
+        v.pool_idx[(int64_t)u * N + lane] = pil;
+        v.pool_score[(int64_t)u * N + lane] = psl;
     }
     if (lane == 0) {
         cnt[0] = pc;
