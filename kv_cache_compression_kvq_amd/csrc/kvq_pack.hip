@@ -117,31 +117,41 @@ __global__ void init_kernel(CacheView v) {
 // OTT token score: S_t = sum_c |K_{t,c}|, exact, as a multiple of 2^-24
 // ("Accurate KV Cache Quantization with Outlier Tokens Tracing", sections
 // "Method details" and appendix E: the L1 norm of the key). Sixteen lanes per
-// token, 16 bytes each.
+// token, 16 bytes each; a block covers 64 tokens, each lane's four rows
+// requested together.
+constexpr int kScoreTokens = 64;
 __global__ __launch_bounds__(256) void ott_score_kernel(CacheView v, const uint16_t* knew,
                                                         int64_t t_old, int32_t n_new, int64_t t0,
                                                         int64_t ntok) {
     const int u = blockIdx.y;
-    const int64_t tl = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
     const int part = threadIdx.x % 16;
-    // Every |x| is a multiple of 2^-24 below 2^16, so any partial sum of the
-    // 128 magnitudes is a multiple of 2^-24 below 2^23: at most 47 significant
-    // bits, exact in fp64 in any order. Scaled by 2^24 it is the integer score.
-    double s = 0.0;
-    if (tl < ntok) {
-        const uint16_t* row = src_row(v.kring, knew, v, u, t0 + tl, t_old, n_new);
-        const uint4 x = reinterpret_cast<const uint4*>(row)[part];
-        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint4 x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t tl = (int64_t)blockIdx.x * kScoreTokens + 16 * j + threadIdx.x / 16;
+        x[j] = tl < ntok ? reinterpret_cast<const uint4*>(
+                               src_row(v.kring, knew, v, u, t0 + tl, t_old, n_new))[part]
+                         : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t tl = (int64_t)blockIdx.x * kScoreTokens + 16 * j + threadIdx.x / 16;
+        // Every |x| is a multiple of 2^-24 below 2^16, so any partial sum of
+        // the 128 magnitudes is a multiple of 2^-24 below 2^23: at most 47
+        // significant bits, exact in fp64 in any order. Scaled by 2^24 it is
+        // the integer score.
+        const uint32_t w[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
+        double s = 0.0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             s += fabs((double)h2f((uint16_t)(w[i] & 0xFFFF)));
             s += fabs((double)h2f((uint16_t)(w[i] >> 16)));
         }
-    }
 #pragma unroll
-    for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off, 16);
-    if (part == 0 && tl < ntok)
-        v.scores[(int64_t)u * v.q_cap + t0 + tl] = (uint64_t)(s * 16777216.0);
+        for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off, 16);
+        if (part == 0 && tl < ntok)
+            v.scores[(int64_t)u * v.q_cap + t0 + tl] = (uint64_t)(s * 16777216.0);
+    }
 }
 
 // OTT pool competition, one wavefront per unit, groups in token order.
@@ -722,7 +732,8 @@ int launch_append(const CacheView& v, const uint16_t* kn, const uint16_t* vn, in
     if (ng > 0) {
         if (v.pool > 0) {
             const int64_t ntok = ng * G;
-            hipLaunchKernelGGL(ott_score_kernel, dim3((unsigned)((ntok + 15) / 16), v.units),
+            hipLaunchKernelGGL(ott_score_kernel,
+                               dim3((unsigned)((ntok + kScoreTokens - 1) / kScoreTokens), v.units),
                                dim3(256), 0, s, v, kn, t_old, n_new, nq_old, ntok);
             hipLaunchKernelGGL(ott_scan_kernel, dim3(v.units), dim3(64), 0, s, v, kn, vn, t_old,
                                n_new, g0, g1);
