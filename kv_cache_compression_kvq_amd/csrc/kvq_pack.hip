@@ -463,12 +463,22 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                  : 0u;
 
-    for (int e = tid; e < G * 16; e += 256) {
-        const int i = e / 16, part = e % 16;
-        reinterpret_cast<uint4*>(kx + i * RS)[part] = reinterpret_cast<const uint4*>(
-            src_row(v.kring, knew, v, u, t0 + i, t_old, n_new))[part];
-        reinterpret_cast<uint4*>(vx + i * RS)[part] = reinterpret_cast<const uint4*>(
-            src_row(v.vring, vnew, v, u, t0 + i, t_old, n_new))[part];
+    {
+        // all of this thread's row pieces are requested before any is stored
+        constexpr int kPer = G * 16 / 256;  // 16-byte pieces per thread and tensor
+        uint4 kr[kPer], vr[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int e = tid + 256 * j, i = e / 16, part = e % 16;
+            kr[j] = reinterpret_cast<const uint4*>(src_row(v.kring, knew, v, u, t0 + i, t_old, n_new))[part];
+            vr[j] = reinterpret_cast<const uint4*>(src_row(v.vring, vnew, v, u, t0 + i, t_old, n_new))[part];
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int e = tid + 256 * j, i = e / 16, part = e % 16;
+            reinterpret_cast<uint4*>(kx + i * RS)[part] = kr[j];
+            reinterpret_cast<uint4*>(vx + i * RS)[part] = vr[j];
+        }
     }
     uint32_t mw[CPG];
     bool any = false;
