@@ -229,8 +229,21 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
             gb = g;
             gb_end = g + kScanBatch / G < g1 ? g + kScanBatch / G : g1;
             wave_sync();  // the previous batch is no longer read
-            for (int64_t i = lane; i < (gb_end - g) * G; i += 64)
-                sc_all[i] = v.scores[(int64_t)u * v.q_cap + t0 + i];
+            // eight loads in flight per lane before any is stored
+            const int64_t nb = (gb_end - g) * G;
+            for (int64_t i0 = 0; i0 < nb; i0 += 8 * 64) {
+                uint64_t x[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int64_t i = i0 + 64 * j + lane;
+                    x[j] = i < nb ? v.scores[(int64_t)u * v.q_cap + t0 + i] : 0ull;
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int64_t i = i0 + 64 * j + lane;
+                    if (i < nb) sc_all[i] = x[j];
+                }
+            }
             wave_sync();
         }
         const uint64_t* sc = sc_all + (g - gb) * G;

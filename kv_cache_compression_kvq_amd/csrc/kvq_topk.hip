@@ -128,13 +128,25 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* scores, int
         // 16-byte loads when the row is 16-byte aligned
         int done = 0;
         if ((reinterpret_cast<uintptr_t>(sc) & 15) == 0) {
+            // four 16-byte loads in flight per thread before any is stored
             const float4* s4 = reinterpret_cast<const float4*>(sc);
-            for (int i = tid; i < n / 4; i += kThreads) {
-                const float4 x = s4[i];
-                *reinterpret_cast<uint4*>(keys + 4 * i) =
-                    make_uint4(order_key(x.x), order_key(x.y), order_key(x.z), order_key(x.w));
+            const int n4 = n / 4;
+            for (int i0 = 0; i0 < n4; i0 += 4 * kThreads) {
+                float4 x[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = i0 + j * kThreads + tid;
+                    x[j] = i < n4 ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = i0 + j * kThreads + tid;
+                    if (i < n4)
+                        *reinterpret_cast<uint4*>(keys + 4 * i) = make_uint4(
+                            order_key(x[j].x), order_key(x[j].y), order_key(x[j].z), order_key(x[j].w));
+                }
             }
-            done = n / 4 * 4;
+            done = n4 * 4;
         }
         for (int i = done + tid; i < n; i += kThreads) keys[i] = order_key(sc[i]);
         __syncthreads();
