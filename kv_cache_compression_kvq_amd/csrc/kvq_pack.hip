@@ -75,21 +75,22 @@ __device__ __forceinline__ bool near_tie(float t) {
 template <int N>
 __device__ __forceinline__ void quant_codes(const float (&x)[N], float mn, float q, float rq,
                                             float levels, uint32_t (&c)[N]) {
-    float d[N], t[N];
-    bool near = false;
+    float d[N], t[N], r[N];
+    float dist = 1.0f;  // smallest distance of a quotient to a half-integer
 #pragma unroll
     for (int m = 0; m < N; ++m) {
         d[m] = x[m] - mn;
         t[m] = d[m] * rq;
-        near |= near_tie(t[m]);
+        r[m] = rintf(t[m]);
+        dist = fminf(dist, fabsf(fabsf(t[m] - r[m]) - 0.5f));
     }
-    if (__any(near)) {
+    if (__any(dist < 0x1p-17f)) {
 #pragma unroll
         for (int m = 0; m < N; ++m)
-            if (near_tie(t[m])) t[m] = d[m] / q;
+            if (near_tie(t[m])) r[m] = rintf(d[m] / q);
     }
 #pragma unroll
-    for (int m = 0; m < N; ++m) c[m] = (uint32_t)fminf(fmaxf(rintf(t[m]), 0.0f), levels);
+    for (int m = 0; m < N; ++m) c[m] = (uint32_t)fminf(fmaxf(r[m], 0.0f), levels);
 }
 
 // Lower bound on the range before dividing (the reference quantizer clamps
