@@ -191,6 +191,46 @@ def test_ott_freeze_with_descending_norms():
     check_decode(gc, w, orc, synth.queries(w))
 
 
+def test_ott_largest_pools_fill_and_freeze():
+    """N = 64, E = 1024 (the limits): with strictly decreasing key norms every
+    token is admitted, the extra pool fills and tracing freezes mid-sequence;
+    the decode then reads 1088 pool rows next to the ring."""
+    w = small(pool=64, evict_cap=1024, residual=32, tokens=1232, batch=1, hkv=1)
+    K, V = synth.all_kv(w)
+    # unit L1 norm per row, then a 0.2 % decrease per token: far above the
+    # fp16 rounding of the rows, so every token is a new minimum
+    Kf = K.astype(np.float32)
+    Kf /= np.abs(Kf).sum(-1, keepdims=True)
+    Kf *= (100.0 * 0.998 ** np.arange(w.tokens, dtype=np.float32))[None, None, :, None]
+    K = Kf.astype(np.float16)
+    splits = [600, 1, 631]
+    gc = H.GpuCache(w)
+    s0 = 0
+    for n in splits:
+        gc.append(K[:, :, s0:s0 + n], V[:, :, s0:s0 + n])
+        s0 += n
+    orc = H.oracle_units(w, all_units(w), K, V, splits)
+    tr = orc[(0, 0)].tracer
+    assert tr.frozen and len(tr.pool) == 64 and len(tr.evicted) == 1024
+    H.check_unit_state(gc.state(), 0, orc[(0, 0)])
+    check_decode(gc, w, orc, synth.queries(w),
+                 acc_in=np.zeros((w.batch, w.n_kv_heads, w.tokens), np.float32))
+
+
+def test_decode_residual_window_near_the_fp16_row_limit():
+    """R = 1536 with G = 128 (R + G close to the 2048 fp16-row limit): the
+    residual partition spans 25 fp16 tiles of one decode launch."""
+    w = small(bits=4, group=128, residual=1536, tokens=4000, batch=1, hkv=2)
+    splits = [1000, 1, 2999]
+    gc, K, V = run_appends(w, splits)
+    orc = H.oracle_units(w, all_units(w), K, V, splits)
+    st = gc.state()
+    for u, key in enumerate(all_units(w)):
+        H.check_unit_state(st, u, orc[key])
+    check_decode(gc, w, orc, synth.queries(w),
+                 acc_in=np.zeros((w.batch, w.n_kv_heads, w.tokens), np.float32))
+
+
 # ---------------------------------------------------------------------------
 # decode attention
 # ---------------------------------------------------------------------------
