@@ -352,6 +352,13 @@ def rows_main(args):
                  {"kernels": ["topk_kernel"], "k": k, "recent": wr})
         del reps, ws, out
         torch.cuda.empty_cache()
+    if args.copy_calibration:
+        # a plain 256 MiB device copy: the counter scale for the runs above
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 def main():
