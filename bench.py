@@ -349,7 +349,7 @@ def rows_main(args):
             timed(call, 2)
             us = timed(call, args.reps)
             emit(name, w, us, BM.topk_bytes(rows=U, tokens=w.tokens, k=k, w=wr),
-                 {"kernels": ["topk_kernel"], "k": k, "recent": wr})
+                 {"kernels": ["topk_reg_kernel"], "k": k, "recent": wr})
         del reps, ws, out
         torch.cuda.empty_cache()
     if args.copy_calibration:

@@ -247,9 +247,9 @@ kvq_status kvq_decode_step_timed(kvq_cache* h, const void* d_k, const void* d_v,
  * Heavy-hitter selection on fp32 scores (device [rows][T]): for each row keep
  * the k largest scores among indices [0, T - w), ties broken toward the
  * larger index, plus the w most recent indices [T - w, T). Writes device
- * int32 [rows][k + w], ascending. +0 and -0 compare equal; NaN scores are not
- * supported. Errors: KVQ_EINVAL (null pointer, rows < 0, k < 0, w < 0,
- * k + w > T).
+ * int32 [rows][k + w], ascending. +0 and -0 compare equal; a NaN score ranks
+ * below every number and all NaNs compare equal. Errors: KVQ_EINVAL (null
+ * pointer, rows < 0, k < 0, w < 0, k + w > T).
  */
 kvq_status kvq_topk_evict(const float* d_scores, int32_t rows, int32_t T, int32_t k,
                           int32_t w, int32_t* d_idx, void* stream);

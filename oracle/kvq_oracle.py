@@ -427,6 +427,8 @@ def topk_keep(scores: np.ndarray, k: int, w: int) -> np.ndarray:
     """Indices kept per row: top-k of [0, T-w) by (score desc, index desc) + [T-w, T).
 
     ``scores`` is fp32 [rows][T]; returns int32 [rows][k+w], ascending.
+    +0 and -0 compare equal; numpy's sort puts NaN after every number in the
+    descending order, so a NaN score ranks lowest and NaNs tie.
     """
     scores = np.asarray(scores, dtype=np.float32)
     rows, T = scores.shape

@@ -298,6 +298,10 @@ def test_snapshot_and_resume_match_unsplit_run():
     (2, 300, 290, 10, True), (4, 513, 100, 0, True), (1, 70000, 9000, 300, False),
     (2, 37120, 7000, 256, True), (2, 500, 490, 10, False), (2, 33536, 6000, 256, True),
     (3, 33536, 6553, 256, False),
+    # at and past the row lengths where the kernel switches register layout
+    (2, 16384 + 128, 3000, 128, False), (2, 16385 + 128, 3000, 128, True),
+    (2, 32768 + 256, 6553, 256, False), (2, 32769 + 256, 6553, 256, True),
+    (1, 65536 + 256, 13000, 256, False), (1, 65537 + 256, 13000, 256, True),
 ])
 def test_topk_exact(kvq, rows, T, k, w, ties):
     s = synth.score_rows(rows, T, seed=3, ties=ties)
@@ -306,6 +310,36 @@ def test_topk_exact(kvq, rows, T, k, w, ties):
     st = torch.from_numpy(s).cuda()
     idx = torch.full((rows, k + w), -1, dtype=torch.int32, device="cuda")
     kvq.topk_evict(st, rows, T, k, w, idx)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), O.topk_keep(s, k, w))
+
+
+def _special_rows(rows, T, seed):
+    """Score rows that stress the key range: signed values, +-inf, NaN, +-0,
+    a constant row, and a row of two values far apart."""
+    rng = np.random.default_rng([seed, rows, T])
+    s = rng.standard_normal((rows, T)).astype(np.float32)
+    pick = rng.integers(0, 12, size=(rows, T))
+    s[pick == 0] = np.inf
+    s[pick == 1] = -np.inf
+    s[pick == 2] = np.nan
+    s[pick == 3] = 0.0
+    s[pick == 4] = -0.0
+    s[pick == 5] *= np.float32(1e30)
+    s[pick == 6] *= np.float32(1e-30)
+    s[0] = np.float32(0.25)                                # every key equal
+    if rows > 1:
+        s[1] = np.where(pick[1] < 6, np.float32(-3e38), np.float32(3e38))
+    return s
+
+
+@pytest.mark.parametrize("T,k,w", [(1000, 300, 24), (20000, 4000, 128), (40000, 9000, 256),
+                                   (70000, 14000, 256)])
+def test_topk_special_values(kvq, T, k, w):
+    s = _special_rows(4, T, seed=11)
+    st = torch.from_numpy(s).cuda()
+    idx = torch.full((4, k + w), -1, dtype=torch.int32, device="cuda")
+    kvq.topk_evict(st, 4, T, k, w, idx)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(idx.cpu().numpy(), O.topk_keep(s, k, w))
 

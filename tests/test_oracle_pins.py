@@ -585,3 +585,21 @@ def test_bulk_append_bytes_closed_form():
     # 4-bit, G = 128 (one value group per token): 128 + 4 + 4 bytes per quantized token
     got4 = BM.bulk_append_bytes(units=1, head_dim=128, tokens=300, n_quant=128, bits=4, group=128)
     assert got4 == 300 * 512 + 128 * 136 + 172 * 512
+
+
+def test_topk_special_values_total_order():
+    # NaN ranks below every number and NaNs tie; -0 == +0; ties keep the
+    # larger index. Brute force over that total order on small rows.
+    rng = np.random.default_rng(23)
+    vals = np.array([np.nan, -np.inf, np.inf, 0.0, -0.0, 1.0, -1.0, 3e38, -3e38],
+                    dtype=np.float32)
+    for T, k, w in [(12, 5, 2), (9, 9, 0), (20, 7, 3), (15, 1, 0)]:
+        s = vals[rng.integers(0, len(vals), size=(4, T))]
+        got = O.topk_keep(s, k, w)
+        n = T - w
+        for r in range(4):
+            def rank(i):
+                x = float(s[r, i])
+                return (0, 0.0, i) if x != x else (1, x, i)
+            keep = sorted(sorted(range(n), key=rank, reverse=True)[:k])
+            assert got[r].tolist() == keep + list(range(n, T))
