@@ -212,7 +212,6 @@ kvq_status kvq_decode_attention_timed(const kvq_cache* h, const void* d_q, float
                                       void* ev_start, void* ev_stop, void* stream);
 
 /*
-/*
  * One decode step: append one token to every unit, then attend with the
  * updated cache. Results and cache state are those of
  *   kvq_quantize_append(h, d_k, d_v, 1, stream);
