@@ -118,24 +118,25 @@ __global__ void init_kernel(CacheView v) {
 // OTT token score: S_t = sum_c |K_{t,c}|, exact, as a multiple of 2^-24
 // ("Accurate KV Cache Quantization with Outlier Tokens Tracing", sections
 // "Method details" and appendix E: the L1 norm of the key). Sixteen lanes per
-// token, 16 bytes each; a block covers 64 tokens, each lane's four rows
-// requested together.
-constexpr int kScoreTokens = 64;
+// token, 16 bytes each; a block covers 32 tokens, each lane's two rows
+// requested together (smaller blocks than 64 or more tokens measured faster).
+constexpr int kScoreRows = 2;  // rows per lane
+constexpr int kScoreTokens = 16 * kScoreRows;
 __global__ __launch_bounds__(256) void ott_score_kernel(CacheView v, const uint16_t* knew,
                                                         int64_t t_old, int32_t n_new, int64_t t0,
                                                         int64_t ntok) {
     const int u = blockIdx.y;
     const int part = threadIdx.x % 16;
-    uint4 x[4];
+    uint4 x[kScoreRows];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kScoreRows; ++j) {
         const int64_t tl = (int64_t)blockIdx.x * kScoreTokens + 16 * j + threadIdx.x / 16;
         x[j] = tl < ntok ? reinterpret_cast<const uint4*>(
                                src_row(v.kring, knew, v, u, t0 + tl, t_old, n_new))[part]
                          : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kScoreRows; ++j) {
         const int64_t tl = (int64_t)blockIdx.x * kScoreTokens + 16 * j + threadIdx.x / 16;
         // Every |x| is a multiple of 2^-24 below 2^16, so any partial sum of
         // the 128 magnitudes is a multiple of 2^-24 below 2^23: at most 47
