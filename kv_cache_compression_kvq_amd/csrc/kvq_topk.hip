@@ -12,9 +12,11 @@
 // finds the k-th largest key tau and how many keys equal to tau are kept.
 // Taking digits from the row's own range spreads the first histogram over
 // more bins than the fixed top bits would and needs fewer passes when the
-// range is short; the bins spread well enough that plain LDS atomics beat
-// aggregating equal bins first. Each wavefront owns a contiguous index range
-// and writes its kept indices in ascending order from ballot prefix counts.
+// range is short. The first pass's bins spread well enough for plain LDS
+// atomics; the keys left for the later passes lie close together, and lanes
+// of a wavefront that share a bin there add once, by their count. Each
+// wavefront owns a contiguous index range and writes its kept indices in
+// ascending order from ballot prefix counts.
 // Longer rows are read from memory in every pass, with a candidate list after
 // the first digit.
 #include <hip/hip_runtime.h>
@@ -219,13 +221,26 @@ __global__ __launch_bounds__(kThreads) void topk_reg_kernel(const float* scores,
         const int lo = hi > 11 ? hi - 11 : 0;
         const uint32_t dmask = (1u << (hi - lo)) - 1u;
         uint32_t* h = hist[pass];
+        if (pass == 0) {
+            // every key counts; the bins spread over the row's range
 #pragma unroll
-        for (int j = 0; j < kJ; ++j)
+            for (int j = 0; j < kJ; ++j)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t v = key[j][c];
-                hist_add<0>(h, (v >> lo) & dmask, hi >= 32 || (v >> hi) == pref);
-            }
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t v = key[j][c];
+                    hist_add<0>(h, (v >> lo) & dmask, hi >= 32 || (v >> hi) == pref);
+                }
+        } else {
+            // only the keys of the chosen bin count (hi < 32 here); they lie
+            // close together, so equal bins are aggregated first
+#pragma unroll
+            for (int j = 0; j < kJ; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t v = key[j][c];
+                    hist_add<2>(h, (v >> lo) & dmask, (v >> hi) == pref);
+                }
+        }
         __syncthreads();
         if (wave == 0) pick_digit(h, need, sel, hi >= 32 ? (uint32_t)(kThreads * R - n) : 0u);
         __syncthreads();
