@@ -224,21 +224,26 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
         for (int64_t i = lane; i < (ge - gb) * (G / 32); i += 64)
             v.mask[(int64_t)u * v.chunks + gb * (G / 32) + i] = mbatch[i];
     };
+    // Lane l holds the smallest score of the staged batch's group gb + l. A
+    // group can admit a token only if the pool is not full or that minimum is
+    // at most the pool's worst score, so the walk goes from one such group to
+    // the next with a ballot (a tie on the score is checked in full there);
+    // the groups in between keep mask words of zero.
+    uint64_t gms = ~0ull;
     for (; g < g1 && !frozen; ++g) {
-        const int64_t t0 = g * G;
         if (g == gb_end) {
             flush(g);
             gb = g;
             gb_end = g + kScanBatch / G < g1 ? g + kScanBatch / G : g1;
             wave_sync();  // the previous batch is no longer read
             // eight loads in flight per lane before any is stored
-            const int64_t nb = (gb_end - g) * G;
+            const int64_t nb = (gb_end - g) * G, tb = g * G;
             for (int64_t i0 = 0; i0 < nb; i0 += 8 * 64) {
                 uint64_t x[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int64_t i = i0 + 64 * j + lane;
-                    x[j] = i < nb ? v.scores[(int64_t)u * v.q_cap + t0 + i] : 0ull;
+                    x[j] = i < nb ? v.scores[(int64_t)u * v.q_cap + tb + i] : 0ull;
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -246,8 +251,31 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
                     if (i < nb) sc_all[i] = x[j];
                 }
             }
+            for (int64_t i = lane; i < (gb_end - gb) * (G / 32); i += 64) mbatch[i] = 0u;
             wave_sync();
+            gms = ~0ull;
+            if (lane < gb_end - gb) {
+                // tokens visited from a lane-dependent start, so that the
+                // lanes' LDS reads fall into different banks
+                const uint64_t* sg = sc_all + (int64_t)lane * G;
+                for (int i0 = 0; i0 < G; i0 += 8) {  // G is a multiple of 8
+                    uint64_t x[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) x[j] = sg[(i0 + j + lane) & (G - 1)];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) gms = x[j] < gms ? x[j] : gms;
+                }
+            }
         }
+        {
+            const uint64_t m = __ballot(lane < gb_end - gb && lane >= g - gb && (pc < N || gms <= wsc));
+            if (m == 0) {  // no group left in the batch can admit a token
+                g = gb_end - 1;
+                continue;
+            }
+            g = gb + __builtin_ctzll(m);
+        }
+        const int64_t t0 = g * G;
         const uint64_t* sc = sc_all + (g - gb) * G;
         // this lane's tokens of the group: lane and lane + 64 (G = 128)
         uint64_t sl[2];

@@ -177,6 +177,30 @@ def test_ott_pool_bit_exact(E):
     check_decode(gc, w, orc, q, acc_in=np.zeros((w.batch, w.n_kv_heads, w.tokens), np.float32))
 
 
+@pytest.mark.parametrize("bits,group,dup", [(2, 64, False), (4, 128, False), (2, 32, True),
+                                            (4, 64, True)])
+def test_ott_pool_group_sizes_and_score_ties(bits, group, dup):
+    """OTT pools at G = 64 and 128 (the scan stages 2048 tokens, 32 or 16
+    groups, at a time), and keys duplicated in pairs so that equal scores,
+    also equal to the pool's worst member, are common."""
+    w = small(bits=bits, group=group, pool=3, evict_cap=8, residual=32, tokens=2300,
+              inject_frac=0.02, outlier_channels=6, outlier_scale=15.0)
+    K, V = synth.all_kv(w)
+    if dup:
+        K[:, :, 1::2] = K[:, :, 0::2][:, :, :K.shape[2] // 2]
+    splits = [1100, 1, 1199]
+    gc = H.GpuCache(w)
+    s0 = 0
+    for n in splits:
+        gc.append(K[:, :, s0:s0 + n], V[:, :, s0:s0 + n])
+        s0 += n
+    orc = H.oracle_units(w, all_units(w), K, V, splits)
+    st = gc.state()
+    for u, key in enumerate(all_units(w)):
+        H.check_unit_state(st, u, orc[key])
+    check_decode(gc, w, orc, synth.queries(w))
+
+
 def test_ott_freeze_with_descending_norms():
     """Keys with strictly decreasing L1 norm: every group displaces the pool."""
     w = small(pool=2, evict_cap=3, residual=32, tokens=320, batch=1, hkv=1)
