@@ -291,13 +291,11 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
             if (lane < G / 32) mbatch[(g - gb) * (G / 32) + lane] = 0u;
             continue;
         }
-        uint32_t mw0 = 0, mw1 = 0, mw2 = 0, mw3 = 0;
+        // Chunk mask word w of the group lives in lane w (G / 32 words), so
+        // marking a token is one masked OR in a register.
+        uint32_t mword = 0;
         auto mark = [&](int i) {
-            const uint32_t bit = 1u << (i & 31);
-            if ((i >> 5) == 0) mw0 |= bit;
-            else if ((i >> 5) == 1) mw1 |= bit;
-            else if ((i >> 5) == 2) mw2 |= bit;
-            else mw3 |= bit;
+            if (lane == (i >> 5)) mword |= 1u << (i & 31);
         };
         if (pc == N) {
             // Full pool: the candidates order before the worst member, hence
@@ -349,7 +347,7 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
                 find_worst();
             }
             if (lane < G / 32)
-                mbatch[(g - gb) * (G / 32) + lane] = lane == 0 ? mw0 : lane == 1 ? mw1 : lane == 2 ? mw2 : mw3;
+                mbatch[(g - gb) * (G / 32) + lane] = mword;
             continue;
         }
         // Pool still filling: rank of each token among the pool members and
@@ -399,7 +397,7 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
             find_worst();
         }
         if (lane < G / 32)
-            mbatch[(g - gb) * (G / 32) + lane] = lane == 0 ? mw0 : lane == 1 ? mw1 : lane == 2 ? mw2 : mw3;
+            mbatch[(g - gb) * (G / 32) + lane] = mword;
     }
     flush(g);
     wave_sync();
