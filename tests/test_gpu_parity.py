@@ -326,6 +326,8 @@ def test_snapshot_and_resume_match_unsplit_run():
     (2, 16384 + 128, 3000, 128, False), (2, 16385 + 128, 3000, 128, True),
     (2, 32768 + 256, 6553, 256, False), (2, 32769 + 256, 6553, 256, True),
     (1, 65536 + 256, 13000, 256, False), (1, 65537 + 256, 13000, 256, True),
+    # k = 1 over more rows than compute units; k = n - 1 with ties
+    (1000, 700, 1, 50, False), (3, 2000, 1949, 50, True),
 ])
 def test_topk_exact(kvq, rows, T, k, w, ties):
     s = synth.score_rows(rows, T, seed=3, ties=ties)
