@@ -283,34 +283,11 @@ __global__ __launch_bounds__(kThreads) void topk_reg_kernel(const float* scores,
     const uint32_t eq_first_kept = eq_total - need;
     uint32_t pos = gt_before + (eq_before > eq_first_kept ? eq_before - eq_first_kept : 0u);
     uint32_t er = eq_before;
-#pragma unroll
-    for (int j = 0; j < kJ; ++j) {
-        bool keep[4];
-        if (eq_first_kept == 0) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) keep[c] = key[j][c] - tk <= range - tk;
-        } else {
-            // rank of each equal key among the row's equal keys, in index order
-            bool is_eq[4];
-            uint64_t me[4];
-            uint32_t r = er;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                is_eq[c] = key[j][c] == tk;
-                me[c] = __ballot(is_eq[c]);
-                r += rank_in(me[c]);
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                keep[c] = key[j][c] - tk - 1u < range - tk || (is_eq[c] && r >= eq_first_kept);
-                r += is_eq[c];
-                er += __popcll(me[c]);
-            }
-        }
-        // position: kept keys of the lanes below (all four slots), then this
-        // lane's earlier slots
-        uint32_t p = pos;
+    // Writes this lane's kept slots of register row j: position = kept keys
+    // of the lanes below (all four slots), then this lane's earlier slots.
+    auto emit = [&](int j, const bool (&keep)[4]) {
         uint64_t mk[4];
+        uint32_t p = pos;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             mk[c] = __ballot(keep[c]);
@@ -321,6 +298,37 @@ __global__ __launch_bounds__(kThreads) void topk_reg_kernel(const float* scores,
             if (keep[c]) out[p] = base + 256 * j + c;
             p += keep[c];
             pos += __popcll(mk[c]);
+        }
+    };
+    if (eq_first_kept == 0) {
+        // every key equal to tau is kept: keep tau <= v <= range
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+            bool keep[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) keep[c] = key[j][c] - tk <= range - tk;
+            emit(j, keep);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) {
+            // rank of each equal key among the row's equal keys, in index order
+            bool is_eq[4], keep[4];
+            uint64_t me[4];
+            uint32_t r = er;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                is_eq[c] = key[j][c] == tk;
+                me[c] = __ballot(is_eq[c]);
+                r += rank_in(me[c]);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                keep[c] = (key[j][c] - tk - 1u < range - tk) | (is_eq[c] & (r >= eq_first_kept));
+                r += is_eq[c];
+                er += __popcll(me[c]);
+            }
+            emit(j, keep);
         }
     }
 }
