@@ -370,13 +370,13 @@ def main():
         cpu_line = cpu_baselines(_synth.WORKLOADS[args.workload], args.cpu_seconds)
     if args.rows is not None:
         if args.gpus != 1:
-            print("bench.py: this build runs on one GPU", file=sys.stderr)
+            print("bench.py: kvq runs on one GPU; --rows takes no --gpus above 1", file=sys.stderr)
             sys.exit(2)
         rows_main(args)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the attention units shard with no exchange; see the design notes)",
+        print(f"bench.py: kvq runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the (batch, KV head) units would shard across GPUs with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -65,7 +65,7 @@ typedef int32_t kvq_status;
 
 #define KVQ_OK            0
 #define KVQ_EINVAL       (-1) /* null pointer, negative or inconsistent size */
-#define KVQ_EUNSUPPORTED (-2) /* a configuration this build does not implement */
+#define KVQ_EUNSUPPORTED (-2) /* a configuration the library does not implement */
 #define KVQ_ECAPACITY    (-3) /* appending beyond max_tokens */
 #define KVQ_EWORKSPACE   (-4) /* arena or workspace smaller than required */
 #define KVQ_ELAUNCH      (-5) /* a HIP launch failed (hipGetLastError) */

@@ -26,8 +26,7 @@ Page citations name the page title and the section they come from:
 [POFE]    "KV cache quantization and eviction: FP8, INT4, H2O and attention
           sinks" (pofe.ai)
 
-Readings taken where the pages leave a step open (each is also listed with
-its reason in the design notes):
+Readings taken where the pages leave a step open:
 
 R1  Codes use round-half-to-even. [OTT] "Background" prints a floor, while
     [POFE] "Minimal implementation" rounds; rounding is what gives the

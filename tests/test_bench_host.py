@@ -1,0 +1,44 @@
+"""Host-side logic of the measurement: the byte model against the pages'
+storage formula, and bench.py's refusal of more than one GPU (CPU only)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from kv_cache_compression_kvq_amd import bytes_model as BM
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("bits,group,per_token", [(2, 32, 96), (2, 128, 72), (4, 32, 160),
+                                                  (4, 128, 136)])
+def test_quantized_bytes_per_token_follow_b_plus_32_over_g(bits, group, per_token):
+    # "KV cache quantization and eviction", section "The bottleneck in
+    # numbers": b + 32/g bits per element with an fp16 scale and zero per
+    # group; keys and values of d = 128 channels per token and KV head.
+    d = 128
+    assert per_token == 2 * d * BM.bits_per_element(bits, group) / 8
+    s = BM.decode_step_bytes(units=1, gqa=4, head_dim=d, tokens=64 * group, bits=bits,
+                             group=group, residual=0)
+    assert s.quantized == 64 * group * per_token
+    assert s.residual == 0 and s.query_out == 4 * d * 6
+
+
+def test_decode_step_bytes_split_the_window():
+    # T - n_q in [R, R + G): the window rows are fp16 K and V (4 d bytes)
+    s = BM.decode_step_bytes(units=64, gqa=4, head_dim=128, tokens=8192 + 20, bits=2,
+                             group=32, residual=128, h2o=True)
+    nq = BM.n_quantized(8212, 128, 32)
+    assert nq == 8064 and 8212 - nq == 148
+    assert s.quantized == 64 * 8064 * 96
+    assert s.residual == 64 * 148 * 512
+    assert s.h2o == 64 * 8212 * 8
+    assert s.total == s.quantized + s.residual + s.pools + s.query_out + s.h2o
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
