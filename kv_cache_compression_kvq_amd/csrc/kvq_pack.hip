@@ -185,7 +185,8 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
     int32_t* cnt = v.counters + (int64_t)u * 4;
     int pc = cnt[0], ec = cnt[1], frozen = cnt[2];
     const int ec0 = ec;
-    const int64_t t_first = g0 * G;  // tokens from here on are admitted in this call
+    // group and token indices fit in 32 bits (per-unit capacity below 2^24)
+    const int32_t t_first = (int32_t)g0 * G;  // tokens from here on are admitted in this call
     // Pool member p lives in lane p (N <= 64): its exact score and token index.
     uint64_t psl = lane < N ? v.pool_score[(int64_t)u * N + lane] : 0ull;
     int32_t pil = lane < N ? v.pool_idx[(int64_t)u * N + lane] : -1;
@@ -218,10 +219,11 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
         widx = bi;
     };
     find_worst();
-    int64_t gb = g0, gb_end = g0, g = g0;
+    const int32_t gend = (int32_t)g1;
+    int32_t gb = (int32_t)g0, gb_end = gb, g = gb;
     // mask words of groups [gb, ge) to memory
-    auto flush = [&](int64_t ge) {
-        for (int64_t i = lane; i < (ge - gb) * (G / 32); i += 64)
+    auto flush = [&](int32_t ge) {
+        for (int i = lane; i < (ge - gb) * (G / 32); i += 64)
             v.mask[(int64_t)u * v.chunks + gb * (G / 32) + i] = mbatch[i];
     };
     // Lane l holds the smallest score of the staged batch's group gb + l. A
@@ -230,28 +232,28 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
     // the next with a ballot (a tie on the score is checked in full there);
     // the groups in between keep mask words of zero.
     uint64_t gms = ~0ull;
-    for (; g < g1 && !frozen; ++g) {
+    for (; g < gend && !frozen; ++g) {
         if (g == gb_end) {
             flush(g);
             gb = g;
-            gb_end = g + kScanBatch / G < g1 ? g + kScanBatch / G : g1;
+            gb_end = g + kScanBatch / G < gend ? g + kScanBatch / G : gend;
             wave_sync();  // the previous batch is no longer read
             // eight loads in flight per lane before any is stored
-            const int64_t nb = (gb_end - g) * G, tb = g * G;
-            for (int64_t i0 = 0; i0 < nb; i0 += 8 * 64) {
+            const int32_t nb = (gb_end - g) * G, tb = g * G;
+            for (int i0 = 0; i0 < nb; i0 += 8 * 64) {
                 uint64_t x[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const int64_t i = i0 + 64 * j + lane;
+                    const int i = i0 + 64 * j + lane;
                     x[j] = i < nb ? v.scores[(int64_t)u * v.q_cap + tb + i] : 0ull;
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const int64_t i = i0 + 64 * j + lane;
+                    const int i = i0 + 64 * j + lane;
                     if (i < nb) sc_all[i] = x[j];
                 }
             }
-            for (int64_t i = lane; i < (gb_end - gb) * (G / 32); i += 64) mbatch[i] = 0u;
+            for (int i = lane; i < (gb_end - gb) * (G / 32); i += 64) mbatch[i] = 0u;
             wave_sync();
             gms = ~0ull;
             if (lane < gb_end - gb) {
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
             }
             g = gb + __builtin_ctzll(m);
         }
-        const int64_t t0 = g * G;
+        const int32_t t0 = g * G;
         const uint64_t* sc = sc_all + (g - gb) * G;
         // this lane's tokens of the group: lane and lane + 64 (G = 128)
         uint64_t sl[2];
@@ -306,7 +308,7 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
             uint64_t m0 = __ballot(cand[0]), m1 = __ballot(cand[1]);
             while (m0 | m1) {
                 uint64_t bs = ~0ull;
-                int64_t bt = INT64_MAX;
+                int32_t bt = INT32_MAX;
                 int bl = 0;
                 for (uint64_t m = m0; m; m &= m - 1) {
                     const int l = __builtin_ctzll(m);
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
         int rank[2] = {0, 0};
         for (int p = 0; p < pc; ++p) {
             const uint64_t sp = rl64(psl, p);
-            const int64_t ip = __builtin_amdgcn_readlane(pil, p);
+            const int32_t ip = __builtin_amdgcn_readlane(pil, p);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 rank[j] += (sp < sl[j]) || (sp == sl[j] && ip < t0 + lane + 64 * j);
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
             const uint64_t m1 = __ballot(cand[1] && rank[1] == rk);
             if (m0 == 0 && m1 == 0) continue;
             const int i = m0 ? __builtin_ctzll(m0) : 64 + __builtin_ctzll(m1);
-            const int64_t t = t0 + i;
+            const int32_t t = t0 + i;
             const uint64_t si = rl64(i < 64 ? sl[0] : sl[1], i & 63);
             int dst;
             if (pc == N) {
