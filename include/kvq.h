@@ -43,7 +43,12 @@
  *    addresses. Sizes are element counts unless named *_bytes.
  *  - Errors: every call validates its arguments on the host before launching
  *    anything. A call that returns an error has launched nothing and left the
- *    cache unchanged, except KVQ_ELAUNCH, which reports a failed launch.
+ *    cache unchanged, except KVQ_ELAUNCH, which reports a failed launch: some
+ *    of the call's kernels may then have run, so a call that updates a cache
+ *    handle marks it invalid (h->tokens = -1; every later call on it returns
+ *    KVQ_EINVAL) and the cache must be rebuilt or restored from a snapshot.
+ *    Errors left in the HIP runtime by unrelated earlier calls are cleared
+ *    before launching and never reported as this call's.
  *  - Threading: calls on distinct caches are independent. Calls on one cache
  *    must be ordered by the caller (same stream, or explicit events).
  *  - Shapes: batch B, query heads Hq, KV heads Hkv with Hq = r * Hkv (query
@@ -172,8 +177,9 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* d_arena, size_t arena_byt
  * with the group mean, then keys are quantized per channel and values per
  * token. Updates h->tokens and h->n_quant on the host. The inputs may be
  * reused as soon as the enqueued work has run.
- * Errors: KVQ_EINVAL (null pointer with n_new > 0, n_new < 0),
- * KVQ_ECAPACITY (T + n_new > max_tokens).
+ * Errors: KVQ_EINVAL (null pointer with n_new > 0, n_new < 0, invalid
+ * handle), KVQ_ECAPACITY (T + n_new > max_tokens), KVQ_ELAUNCH (the handle is
+ * then marked invalid).
  */
 kvq_status kvq_quantize_append(kvq_cache* h, const void* d_k, const void* d_v,
                                int32_t n_new, void* stream);
@@ -227,7 +233,7 @@ kvq_status kvq_decode_attention_timed(const kvq_cache* h, const void* d_q, float
  * Every argument is checked before anything is enqueued; an error leaves
  * *h and the cache unchanged. Updates h->tokens and h->n_quant on success.
  * Errors: KVQ_EINVAL (null pointer), KVQ_ECAPACITY (T + 1 > max_tokens),
- * KVQ_EWORKSPACE, KVQ_ELAUNCH (then the cache contents are unspecified).
+ * KVQ_EWORKSPACE, KVQ_ELAUNCH (the handle is then marked invalid).
  */
 kvq_status kvq_decode_step(kvq_cache* h, const void* d_k, const void* d_v, const void* d_q,
                            float* d_out, float* d_acc, void* d_ws, size_t ws_bytes,

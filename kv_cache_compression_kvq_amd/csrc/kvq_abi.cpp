@@ -89,6 +89,11 @@ bool valid_handle(const kvq_cache* h) {
 
 kvq_status launch_status(int e) { return e == 0 ? KVQ_OK : KVQ_ELAUNCH; }
 
+// After a failed launch some of a call's kernels may have run and changed the
+// arena, so the handle no longer describes it: it is marked invalid (every
+// later call on it returns KVQ_EINVAL) rather than left as it was.
+void invalidate(kvq_cache* h) { h->tokens = -1; }
+
 }  // namespace
 
 CacheView view_of(const kvq_cache* h) {
@@ -147,7 +152,7 @@ DecodePlan plan_decode(const kvq_cache* h, bool want_scores) {
     if (t < (fp16_rows + 63) / 64) t = (fp16_rows + 63) / 64;
     p.fp16_tiles = (int32_t)t;
     p.splits = p.splits_q + p.fp16_tiles;
-    p.part_floats = U * p.splits * r * (kHeadDim + 2);
+    p.part_floats = U * p.splits * r * kPartRec;
     p.logit_floats = want_scores ? U * r * h->tokens : 0;
     p.ws_bytes = align_up((uint64_t)p.part_floats * 4) + (uint64_t)p.logit_floats * 4;
     return p;
@@ -219,6 +224,8 @@ kvq_status kvq_quantize_append(kvq_cache* h, const void* d_k, const void* d_v, i
     if (st == KVQ_OK) {
         h->tokens = t_new;
         h->n_quant = nq_new;
+    } else {
+        invalidate(h);
     }
     return st;
 }
@@ -263,13 +270,17 @@ kvq_status kvq_decode_step_timed(kvq_cache* h, const void* d_k, const void* d_v,
     const CacheView v = view_of(h);
     kvq_status st = launch_status(
         launch_append(v, kn, vn, t_old, 1, h->n_quant, next.n_quant, stream, false));
-    if (st != KVQ_OK) return st;
+    if (st != KVQ_OK) {
+        invalidate(h);
+        return st;
+    }
     // the new token stays fp16 unless its own group was just quantized
     const bool in_ring = t_old >= next.n_quant;
     st = launch_status(launch_decode(v, t_new, next.n_quant, p, static_cast<const uint16_t*>(d_q),
                                      d_out, d_acc, d_ws, ev_start, ev_stop, stream,
                                      in_ring ? kn : nullptr, in_ring ? vn : nullptr));
     if (st == KVQ_OK) *h = next;
+    else invalidate(h);
     return st;
 }
 

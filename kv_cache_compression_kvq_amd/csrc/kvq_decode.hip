@@ -27,8 +27,6 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
-
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -40,42 +38,24 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 constexpr int D = kHeadDim;
-constexpr int kRec = D + 2;  // partial record: o[d], m, l
+// Partial record of one (unit, split, head): o[d], m, l, two pad floats, so
+// that every record starts 16-byte aligned for the vector stores into it.
+constexpr int kRec = kPartRec;
+static_assert(kRec % 4 == 0 && kRec >= D + 2, "record holds o, m, l, 16-byte aligned");
 constexpr int kMaxSplits = 1056;
 constexpr int kH2OChunk = 2048;
 // LDS of the fp16 partition: queries and probabilities (4 x 256 B + 4 x 256 B).
 constexpr int kFp16Bytes = 4 * D * 2 + 4 * 64 * 4;
 
-// Per-wavefront LDS of the quantized path: a ring of kStages chunk stages
-// filled by direct global->LDS loads (codes, value scales, key scales, pool
-// mask word); after the loop the same bytes hold the output accumulators. The
-// folded-query table and the probability exchange live in LDS objects of their
-// own, so that writing them never waits on the ring's copies in flight.
-#ifndef KVQ_RING_STAGES
-#define KVQ_RING_STAGES 2
-#endif
-#ifndef KVQ_SPLIT_EXP
-#define KVQ_SPLIT_EXP 1
-#endif
-#ifndef KVQ_PRIO_HI
-#define KVQ_PRIO_HI 3
-#endif
-#ifndef KVQ_MIN_WAVES
-#define KVQ_MIN_WAVES 4
-#endif
-// Ring refill: 0 = chunk k + kStages - 1 is requested at the top of iteration
-// k; 1 = chunk k + kStages is requested as soon as chunk k is in registers.
-#ifndef KVQ_DEEP_RING
-#define KVQ_DEEP_RING 0
-#endif
-// 1: every wavefront waits for its first chunk before requesting more, so
-// that the first chunks of all wavefronts lead the start-up burst.
-#ifndef KVQ_START_WAIT
-#define KVQ_START_WAIT 0
-#endif
+// Per-wavefront LDS of the quantized path: a ring of two chunk stages filled
+// by direct global->LDS loads (codes, value scales, key scales, pool mask
+// word); while chunk k computes, chunk k + 1 is in flight. After the loop the
+// same bytes hold the output accumulators. The folded-query table and the
+// probability exchange live in LDS objects of their own, so that writing them
+// never waits on the ring's copies in flight.
 template <int BITS>
 struct Ring {
-    static constexpr int kStages = KVQ_RING_STAGES;
+    static constexpr int kStages = 2;
     static constexpr int kCodes = 128 * BITS * 4;          // packed codes of one chunk
     static constexpr int kMeta = 1024;                      // value (<= 512 B) + key (512 B) scales
     static constexpr int kStage = 2 * kCodes + kMeta + 16;  // + pool mask word
@@ -390,13 +370,13 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
 }
 
 template <int BITS, int R, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAVES))) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(DecodeArgs a) {
     constexpr int NG = D / G;        // value groups per token
     constexpr int CPG = G / 32;      // chunks per key group
     constexpr int WPC = 128 * BITS;  // words per chunk
     // With r = 4 the 16 MFMA columns hold 4 copies of each head's logits;
     // each copy then exponentiates a quarter of the tokens.
-    constexpr bool kSplitExp = R == 4 && KVQ_SPLIT_EXP;
+    constexpr bool kSplitExp = R == 4;
     constexpr bool kMirror = kSplitExp;
     // Code operands. A code masked in place at bits [p, p + b) of both 16-bit
     // halves is the pair of fp16 subnormals code * 2^(p - 24): exact, one AND.
@@ -522,9 +502,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAV
         const int64_t tb = (int64_t)(gi * CPG + cc) * 32;
         const uint32_t st = lds_addr(wlds + (k % RG::kStages) * RG::kStage);
         const uint32_t meta = st + 2 * RG::kCodes;
-        // stages issued after this one: min(kStages - 1, later)
-        if (RG::kStages >= 3 && later >= 2) wait_vm<2 * RG::kLoads>();
-        else if (later >= 1) wait_vm<RG::kLoads>();
+        // the stage issued after this one (if any) may stay in flight
+        if (later >= 1) wait_vm<RG::kLoads>();
         else wait_vm<0>();
         // three per-lane bases, every other offset an immediate
         const uint32_t a_codes = st + lane_codes, a_vm = st + lane_vm, a_km = st + lane_km;
@@ -556,13 +535,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAV
                          : "memory");
             wk1 = wk0;  // one 16-byte word group per lane at b = 2
             wv1 = wv0;
-        }
-        if (KVQ_DEEP_RING) {
-            // The stage is in registers: refill its slot with chunk k + kStages,
-            // so that kStages chunks stay in flight while this one computes.
-            if (KVQ_START_WAIT && k == 0)
-                for (uint32_t j = 1; j < RG::kStages && j < n_items; ++j) issue(j);
-            if (k + RG::kStages < n_items) issue(k + RG::kStages);
         }
         if (cc == 0) {
             // Fold the key scale into the query: B = hi/lo of q~_c * s_c, and
@@ -784,20 +756,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAV
         }
     };
 
-    // Pipeline start. The ring stages requested here, after the query row:
-    // the first one only (KVQ_START_WAIT), else kStages (deep refill) or
-    // kStages - 1.
-    constexpr uint32_t kFirst = KVQ_START_WAIT ? 1 : KVQ_DEEP_RING ? RG::kStages : RG::kStages - 1;
-    for (uint32_t k = 0; k < kFirst && k < n_items; ++k) issue(k);
-    if (KVQ_START_WAIT) {
-        wait_vm<0>();  // the query row and the first chunk
+    // Pipeline start: the first chunk is requested right after the query row;
+    // the wait below is for the query row only, the chunk stays in flight.
+    if (n_items > 0) {
+        issue(0);
+        wait_vm<RG::kLoads>();
     } else {
-        // the query row only: the stages requested after it may stay in flight
-        const uint32_t issued = n_items < kFirst ? n_items : kFirst;
-        if (issued >= 3) wait_vm<3 * RG::kLoads>();
-        else if (issued == 2) wait_vm<2 * RG::kLoads>();
-        else if (issued == 1) wait_vm<RG::kLoads>();
-        else wait_vm<0>();
+        wait_vm<0>();
     }
     asm volatile("" : "+v"(qraw));
     {
@@ -816,20 +781,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVQ_MIN_WAV
         // Issue priority from the work left: the arbiter otherwise favours the
         // oldest wavefronts, and the youngest ones finish last, alone.
         const uint32_t left = n_items - k;
-        if (left >= KVQ_PRIO_HI) __builtin_amdgcn_s_setprio(3);
-        else if (left >= KVQ_PRIO_HI - 1) __builtin_amdgcn_s_setprio(2);
-        else if (left >= KVQ_PRIO_HI - 2) __builtin_amdgcn_s_setprio(1);
-        else __builtin_amdgcn_s_setprio(0);
-        if (!KVQ_DEEP_RING) {
-            // chunks k + 1 .. k + kStages - 1 in flight while chunk k computes
-            const uint32_t kn = k + RG::kStages - 1;
-            if (kn < n_items && (KVQ_START_WAIT || kn >= kFirst)) {
-                if (KVQ_START_WAIT && k == 0)
-                    for (uint32_t j = 1; j < kn; ++j) issue(j);
-                issue(kn);
-            }
-        }
-        step(k, n_items - 1 - k);  // stages issued after k: min(kStages - 1, n_items - 1 - k)
+        if (left >= 3) __builtin_amdgcn_s_setprio(3);
+        else if (left >= 2) __builtin_amdgcn_s_setprio(2);
+        else __builtin_amdgcn_s_setprio(1);
+        // chunk k + 1 in flight while chunk k computes
+        if (k + 1 < n_items) issue(k + 1);
+        step(k, n_items - 1 - k);  // stages issued after k: min(1, n_items - 1 - k)
     }
     __builtin_amdgcn_s_setprio(0);
     wave_lds_fence();
@@ -1012,27 +969,21 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
 }
 
 // Blocks of decode_kernel<BITS, R, G> resident on the current device at once
-// (occupancy x compute units), cached per device. KVQ_DECODE_BLOCKS overrides
-// it, for launch-shape sweeps.
+// (occupancy x compute units), cached per device.
 template <int BITS, int R, int G>
 int resident_blocks() {
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
     if (cached[dev] == 0) {
-        int n = 0;
-        if (const char* env = std::getenv("KVQ_DECODE_BLOCKS")) n = std::atoi(env);
-        if (n <= 0) {
-            int cus = 0, per = 0;
-            if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                    hipSuccess ||
-                hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                    &per, reinterpret_cast<const void*>(decode_kernel<BITS, R, G>), 256, 0) !=
-                    hipSuccess)
-                cus = per = 0;
-            n = cus * per > 0 ? cus * per : 512;
-        }
-        cached[dev] = n;
+        int cus = 0, per = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per, reinterpret_cast<const void*>(decode_kernel<BITS, R, G>), 256, 0) !=
+                hipSuccess)
+            cus = per = 0;
+        cached[dev] = cus * per > 0 ? cus * per : 512;
     }
     return cached[dev];
 }
@@ -1074,6 +1025,8 @@ void launch_decode_t(DecodeArgs a, hipEvent_t e0, hipEvent_t e1, hipStream_t s) 
     }
     a.splits = a.splits_q + a.fp16_tiles;
     const unsigned blocks = (unsigned)(a.units * a.fp16_tiles + a.units * a.splits_q);
+    // the device queries above may have left an error that is not a launch's
+    (void)hipGetLastError();
     if (e0 || e1)
         hipExtLaunchKernelGGL((decode_kernel<BITS, R, G>), dim3(blocks), dim3(256), 0, s, e0, e1, 0,
                               a);

@@ -16,6 +16,7 @@ constexpr int kMaxEvict = 1024;    // E limit
 constexpr int kMaxFp16Rows = 2048; // R + G + N + E limit
 constexpr int kMaxFp16Tiles = 56;   // fp16-partition tiles per unit (each at most 64 rows)
 constexpr int kMaxTokens = 1 << 24; // per-unit capacity: keeps per-unit offsets in 32 bits
+constexpr int kPartRec = kHeadDim + 4; // floats per decode partial record: o[d], m, l, 2 pad
 
 // Device pointers of one cache, resolved from the arena and the handle's offsets.
 struct CacheView {
@@ -52,7 +53,7 @@ struct DecodePlan {
                          // n_q == 0); the launch picks the count that fills the GPU once
     int32_t fp16_tiles;  // upper bound on fp16-partition tiles (ring + pools), 16-64 rows each
     int32_t splits;      // splits_q + fp16_tiles partial records per unit
-    int64_t part_floats; // partial records: U * splits * r * (d + 2)
+    int64_t part_floats; // partial records: U * splits * r * kPartRec
     int64_t logit_floats;// U * r * T when scores are wanted
     size_t ws_bytes;
 };

@@ -748,15 +748,14 @@ __global__ __launch_bounds__(256) void unpack_kernel(CacheView v, int64_t n_q, u
 }
 
 template <int BITS, int G>
-void launch_pack_t(const CacheView& v, const uint16_t* kn, const uint16_t* vn, int64_t t_old,
-                   int32_t n_new, int64_t g0, int64_t ng, hipStream_t s) {
+hipError_t launch_pack_t(const CacheView& v, const uint16_t* kn, const uint16_t* vn, int64_t t_old,
+                         int32_t n_new, int64_t g0, int64_t ng, hipStream_t s) {
     const size_t lds = 2 * (size_t)G * kPackRow * sizeof(uint16_t);
-    static bool attr = [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(pack_kernel<BITS, G>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * G * kPackRow * 2);
-        return true;
-    }();
-    (void)attr;
+    // the dynamic LDS limit is raised once per process; a failure is reported
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(pack_kernel<BITS, G>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
     // one block per (unit, group), units fastest; at most 2^22 blocks a launch
     const int64_t step = (int64_t)1 << 22 >= v.units ? ((int64_t)1 << 22) / v.units : 1;
     for (int64_t gs = 0; gs < ng; gs += step) {
@@ -764,11 +763,13 @@ void launch_pack_t(const CacheView& v, const uint16_t* kn, const uint16_t* vn, i
         hipLaunchKernelGGL((pack_kernel<BITS, G>), dim3((unsigned)(n * v.units)), dim3(256), lds, s,
                            v, kn, vn, t_old, n_new, g0 + gs);
     }
+    return hipSuccess;
 }
 
 }  // namespace
 
 int launch_init(const CacheView& v, void* stream) {
+    (void)hipGetLastError();  // an error left by an earlier call is not this call's
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t n = (int64_t)v.units * 4 + (int64_t)v.units * v.chunks;
     const int64_t blocks = (n + 255) / 256;
@@ -779,6 +780,7 @@ int launch_init(const CacheView& v, void* stream) {
 
 int launch_append(const CacheView& v, const uint16_t* kn, const uint16_t* vn, int64_t t_old,
                   int32_t n_new, int64_t nq_old, int64_t nq_new, void* stream, bool ring_store) {
+    (void)hipGetLastError();  // an error left by an earlier call is not this call's
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int G = v.group;
     const int64_t g0 = nq_old / G, g1 = nq_new / G, ng = g1 - g0;
@@ -791,11 +793,13 @@ int launch_append(const CacheView& v, const uint16_t* kn, const uint16_t* vn, in
             hipLaunchKernelGGL(ott_scan_kernel, dim3(v.units), dim3(64), 0, s, v, kn, vn, t_old,
                                n_new, g0, g1);
         }
+        hipError_t e = hipErrorInvalidValue;
 #define KVQ_PACK(B_, G_)                                                         \
-    if (v.bits == B_ && G == G_) launch_pack_t<B_, G_>(v, kn, vn, t_old, n_new, g0, ng, s);
+    if (v.bits == B_ && G == G_) e = launch_pack_t<B_, G_>(v, kn, vn, t_old, n_new, g0, ng, s);
         KVQ_PACK(2, 32) KVQ_PACK(2, 64) KVQ_PACK(2, 128)
         KVQ_PACK(4, 32) KVQ_PACK(4, 64) KVQ_PACK(4, 128)
 #undef KVQ_PACK
+        if (e != hipSuccess) return (int)e;
     }
     const int64_t ts = t_old > nq_new ? t_old : nq_new, te = t_old + n_new;
     if (ring_store && te > ts) {
@@ -807,6 +811,7 @@ int launch_append(const CacheView& v, const uint16_t* kn, const uint16_t* vn, in
 }
 
 int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, void* stream) {
+    (void)hipGetLastError();  // an error left by an earlier call is not this call's
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t total = (int64_t)v.units * n_q * D;
     int64_t blocks = (total + 255) / 256;

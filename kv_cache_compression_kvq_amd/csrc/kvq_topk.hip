@@ -482,6 +482,7 @@ __global__ __launch_bounds__(kThreads) void topk_global_kernel(const float* scor
 
 int launch_topk(const float* scores, int32_t rows, int32_t T, int32_t k, int32_t w, int32_t* idx,
                 void* stream) {
+    (void)hipGetLastError();  // an error left by an earlier call is not this call's
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int n = T - w;
     const dim3 grid(rows), block(kThreads);

@@ -29,3 +29,17 @@ def kvq():
         build.build()
     abi.lib()
     return abi
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Largest parity errors seen per workload tag (GPU runs), for the record."""
+    import sys as _sys
+    H = _sys.modules.get("tests.gpu_harness")
+    if H is None or not getattr(H, "ERRORS", None):
+        return
+    tr = terminalreporter
+    tr.section("largest errors against the oracle")
+    tr.write_line(f"{'tag':<24}{'out max-abs':>14}{'out rel-L2':>14}{'H2O rel':>14}")
+    for tag, e in sorted(H.ERRORS.items()):
+        cols = [f"{e[k]:.3e}" if k in e else "-" for k in ("out_abs", "out_rel_l2", "h2o_rel")]
+        tr.write_line(f"{tag:<24}{cols[0]:>14}{cols[1]:>14}{cols[2]:>14}")

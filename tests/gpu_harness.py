@@ -8,8 +8,13 @@ Bars (the oracle is the reference):
   compared as values, so +0 and -0 agree);
 * attention outputs: max |out - ref| <= 2e-3 and, per (batch, query head),
   ||out - ref||_2 <= 1e-3 * ||ref||_2;
-* H2O increments: |d_gpu - d_ref| <= 1e-4 * |d_ref| + 1e-7 (1e-7 is below one
-  fp32 ulp of the per-step total r = 4 the increments sum to).
+* H2O scores: |acc_gpu - (acc_in + d_ref)| <= 1e-4 * |d_ref| + ulp(acc_gpu) / 2,
+  element by element: relative 1e-4 on the increment, plus the rounding of the
+  fp32 accumulator's own stored value (the sum acc_in + d is held in fp32). With
+  acc_in = 0 that term is 2^-24 relative, so the check is relative 1e-4.
+
+Every check records the largest error it saw under its tag in ERRORS, which
+the test session prints at its end.
 """
 from __future__ import annotations
 
@@ -20,7 +25,16 @@ from kv_cache_compression_kvq_amd import abi, synth
 from oracle import kvq_oracle as O
 
 OUT_ABS, OUT_REL = 2e-3, 1e-3
-H2O_REL, H2O_ABS = 1e-4, 1e-7
+H2O_REL = 1e-4
+
+# tag -> {"out_abs": .., "out_rel_l2": .., "h2o_rel": ..}: the largest errors seen
+ERRORS: dict = {}
+
+
+def _record(tag: str, key: str, value: float) -> None:
+    tag = tag.split(" unit")[0] or "misc"
+    e = ERRORS.setdefault(tag, {})
+    e[key] = max(e.get(key, 0.0), float(value))
 
 
 def config_of(w: synth.Workload, max_tokens: int | None = None) -> abi.Config:
@@ -146,16 +160,26 @@ def check_outputs(out: np.ndarray, ref: np.ndarray, what: str = "") -> None:
     ref = ref.reshape(-1, ref.shape[-1])
     assert np.all(np.isfinite(out)), f"{what}: non-finite output"
     err = np.abs(out - ref)
-    assert err.max() <= OUT_ABS, f"{what}: max abs err {err.max():.3g}"
     rel = np.linalg.norm(out - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    _record(what, "out_abs", err.max())
+    _record(what, "out_rel_l2", rel.max())
+    assert err.max() <= OUT_ABS, f"{what}: max abs err {err.max():.3g}"
     assert rel.max() <= OUT_REL, f"{what}: max rel L2 err {rel.max():.3g}"
 
 
-def check_h2o(got: np.ndarray, ref: np.ndarray, what: str = "") -> None:
-    got = got.astype(np.float64)
-    bad = np.abs(got - ref) > H2O_REL * np.abs(ref) + H2O_ABS
-    assert not bad.any(), (f"{what}: {bad.sum()} H2O scores out of tolerance, worst "
-                           f"{np.max(np.abs(got - ref) - H2O_REL * np.abs(ref)):.3g}")
+def check_h2o(acc_out: np.ndarray, acc_in, ref: np.ndarray, what: str = "") -> None:
+    """acc_out: the fp32 scores after the call; acc_in: before it (array or 0);
+    ref: the oracle's fp64 increments."""
+    out = np.asarray(acc_out, dtype=np.float32)
+    want = np.asarray(acc_in, dtype=np.float64) + ref
+    half_ulp = np.spacing(np.abs(out)).astype(np.float64) / 2
+    dev = np.abs(out.astype(np.float64) - want)
+    nz = ref > 0
+    rel = np.max(np.maximum(dev - half_ulp, 0.0)[nz] / ref[nz]) if nz.any() else 0.0
+    _record(what, "h2o_rel", rel)
+    bad = dev > H2O_REL * np.abs(ref) + half_ulp
+    assert not bad.any(), (f"{what}: {bad.sum()} H2O scores out of tolerance, worst relative "
+                           f"{rel:.3g}")
 
 
 def oracle_units(w: synth.Workload, units, K: np.ndarray, V: np.ndarray, splits=None):

@@ -47,19 +47,22 @@ def all_units(w):
     return [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
 
 
-def check_decode(gc, w, orc, q, acc_in=None):
+def check_decode(gc, w, orc, q, acc_in=None, tag=None):
+    """Attention outputs (and H2O scores when acc_in is given) of every oracle
+    unit; errors are recorded under ``tag`` (default: the workload's name)."""
+    tag = tag or w.name
     acc = None
     if acc_in is not None:
         acc = torch.from_numpy(acc_in.copy()).cuda()
     out = gc.decode(q, acc).cpu().numpy()
     r = w.gqa
+    accn = acc.cpu().numpy() if acc is not None else None
     for (b, h), uc in orc.items():
         K, Vd = uc.dequantized_kv()
         ref, p = O.unit_attention(K, Vd, q[b, h * r:(h + 1) * r])
-        H.check_outputs(out[b, h * r:(h + 1) * r], ref, f"unit {(b, h)}")
+        H.check_outputs(out[b, h * r:(h + 1) * r], ref, f"{tag} unit {(b, h)}")
         if acc is not None:
-            got = acc.cpu().numpy()[b, h] - acc_in[b, h]
-            H.check_h2o(got, O.h2o_increment(p), f"unit {(b, h)}")
+            H.check_h2o(accn[b, h], acc_in[b, h], O.h2o_increment(p), f"{tag} unit {(b, h)}")
     return out
 
 
@@ -437,8 +440,8 @@ def test_workload_minikv_h2o_and_topk():
     for (b, h), uc in orc.items():
         Kd, Vd = uc.dequantized_kv()
         ref, p = O.unit_attention(Kd, Vd, q[b, h * r:(h + 1) * r])
-        H.check_outputs(out[b, h * r:(h + 1) * r], ref, f"unit {(b, h)}")
-        H.check_h2o(accn[b, h], O.h2o_increment(p), f"unit {(b, h)}")
+        H.check_outputs(out[b, h * r:(h + 1) * r], ref, f"minikv unit {(b, h)}")
+        H.check_h2o(accn[b, h], 0.0, O.h2o_increment(p), f"minikv unit {(b, h)}")
     # heavy hitters on the GPU-accumulated scores, all 128 rows
     rows = w.batch * w.n_kv_heads
     k, wr = w.topk_k, w.recent

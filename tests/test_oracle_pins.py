@@ -281,6 +281,95 @@ def test_incremental_and_bulk_appends_agree():
 
 
 # ---------------------------------------------------------------------------
+# The dequantized cache every attention check reads ("MiniKV", section 4.4:
+# one fp16 zero point and scale per group; "KV cache quantization and
+# eviction", Minimal implementation: x_hat = code * scale + zero).
+# ---------------------------------------------------------------------------
+
+def _mixed_unit(bits, G, N, E, T=300, R=40, seed=31):
+    """A unit with outlier key channels, low-norm tokens (pool admissions when
+    N > 0) and two appends; returns the oracle unit and the raw fp16 rows."""
+    rng = np.random.default_rng([seed, bits, G, N])
+    k = rng.standard_normal((T, 128)).astype(np.float32)
+    k[:, [3, 40, 77]] *= 15.0
+    low = rng.choice(T, size=T // 12, replace=False)
+    k[low] *= 0.02
+    v = rng.standard_normal((T, 128)).astype(np.float32) * rng.uniform(0.2, 3.0, size=(T, 1))
+    k16, v16 = k.astype(np.float16), v.astype(np.float16)
+    u = O.UnitCache(O.CacheParams(bits=bits, group=G, residual=R, pool=N, evict_cap=E))
+    u.append(k16[:137], v16[:137])
+    u.append(k16[137:], v16[137:])
+    return u, k16, v16
+
+
+@pytest.mark.parametrize("bits,G,N,E", [(2, 32, 0, 0), (4, 64, 3, 4), (2, 128, 3, 1),
+                                        (4, 16, 2, 8), (2, 16, 3, 32)])
+def test_dequantized_rows_rebuilt_token_by_token(bits, G, N, E):
+    """dequantized_kv() against a plain per-token loop: a quantized token takes,
+    channel by channel, the (scale, zero) of its own key group and channel and of
+    its own value channel group; pool and extra-pool tokens their original fp16
+    rows; tokens at n_q and later the fp16 rows. Then, from the raw rows alone
+    (pool members replaced by the exact group mean, rounded once to fp16), every
+    zero point is the group minimum and every dequantized element is within half
+    a step of the data: |x_hat - x| <= q/2 + L*|s16 - q| (+ fp32 slack), with q
+    the exact (max - min) / L of the group."""
+    u, k16, v16 = _mixed_unit(bits, G, N, E)
+    T, d, L, gv = u.T, 128, 2 ** bits - 1, min(G, 128)
+    n_q = u.n_q
+    assert n_q >= 2 * G
+    Kd, Vd = u.dequantized_kv()
+    members = {m.idx for m in u.tracer.pool + u.tracer.evicted}
+    if N:
+        assert members, "construction should admit pool members"
+    assert set(np.nonzero(u.replaced)[0].tolist()) == members
+    kc, ks, kz = u.kcodes, u.kscale, u.kzero
+    vc, vs, vz = u.vcodes, u.vscale, u.vzero
+    for t in range(T):
+        if t in members or t >= n_q:
+            assert np.array_equal(Kd[t], k16[t].astype(np.float64)), t
+            assert np.array_equal(Vd[t], v16[t].astype(np.float64)), t
+            continue
+        g = t // G
+        for c in range(d):
+            kw = float(kc[t, c]) * float(ks[g, c]) + float(kz[g, c])
+            vw = float(vc[t, c]) * float(vs[t, c // gv]) + float(vz[t, c // gv])
+            assert Kd[t, c] == kw and Vd[t, c] == vw, (t, c)
+
+    def bound_ok(x, xh, lo, hi, s16):
+        Q = max(hi - lo, Fraction(1, 10 ** 8)) / L
+        S = half_to_fraction(s16)
+        slack = Fraction(1, 2 ** 20) * (abs(x - lo) + Q)
+        return abs(Fraction(float(xh)) - x) <= Q / 2 + L * abs(S - Q) + slack
+
+    for g in range(n_q // G):
+        rows = list(range(g * G, (g + 1) * G))
+        krows = [[half_to_fraction(k16[t, c]) for c in range(d)] for t in rows]
+        vrows = [[half_to_fraction(v16[t, c]) for c in range(d)] for t in rows]
+        rep = [i for i, t in enumerate(rows) if t in members]
+        if rep:
+            mk = [half_to_fraction(round_to_half(sum(r[c] for r in krows) / G)) for c in range(d)]
+            mv = [half_to_fraction(round_to_half(sum(r[c] for r in vrows) / G)) for c in range(d)]
+            for i in rep:
+                krows[i], vrows[i] = list(mk), list(mv)
+        for c in range(d):
+            col = [r[c] for r in krows]
+            lo, hi = min(col), max(col)
+            assert half_to_fraction(kz[g, c]) == lo, (g, c)
+            for i, t in enumerate(rows):
+                if t not in members:
+                    assert bound_ok(col[i], Kd[t, c], lo, hi, ks[g, c]), (t, c)
+        for i, t in enumerate(rows):
+            if t in members:
+                continue
+            for j in range(d // gv):
+                seg = vrows[i][j * gv:(j + 1) * gv]
+                lo, hi = min(seg), max(seg)
+                assert half_to_fraction(vz[t, j]) == lo, (t, j)
+                for cc in range(gv):
+                    assert bound_ok(seg[cc], Vd[t, j * gv + cc], lo, hi, vs[t, j]), (t, j, cc)
+
+
+# ---------------------------------------------------------------------------
 # OTT: score, mean replacement, pool competition ("Accurate KV Cache
 # Quantization with Outlier Tokens Tracing", Method details and appendix E).
 # ---------------------------------------------------------------------------
@@ -308,18 +397,25 @@ def test_group_mean_rounds_once_to_fp16():
         for c in range(64):
             exact = sum(half_to_fraction(v) for v in x[:, c]) / G
             assert m[c].view(np.uint16) == round_to_half_bits(exact)
-    # constructed: (1 + 2^-11) + 2^-24 * 2^-? ... exact mean = 1 + 2^-11 + 2^-29
     G = 32
     col = np.full(G, 1.0, dtype=np.float16)
     col[0] = np.float16(1.0 + 2 ** -10)     # contributes 2^-10 / 32
     col[1] = np.float16(1.0 + 2 ** -10)
     # mean = 1 + 2^-10 * 2/32 = 1 + 2^-14: far below half an fp16 ulp (2^-11)
     assert O.group_mean_fp16(col[:, None])[0] == np.float16(1.0)
-    col = np.full(G, 1.0 + 2 ** -10, dtype=np.float16)
-    col[:16] = np.float16(1.0)
-    col[16] = np.float16(1.0 + 2 * 2 ** -10)
-    exact = sum(half_to_fraction(v) for v in col) / G      # 1 + 2^-11 + 2^-15: above half-way
-    assert O.group_mean_fp16(col[:, None])[0].view(np.uint16) == round_to_half_bits(exact)
+    # Constructed so that one rounding and two roundings disagree: 30 ones,
+    # 2 + 2^-6 and the subnormal 2^-24 have the exact mean 1 + 2^-11 + 2^-29,
+    # just above the fp16 half-way point 1 + 2^-11 by less than half an fp32 ulp
+    # (2^-24). Rounded once it goes up to 1 + 2^-10; rounded to fp32 first it
+    # lands on the half-way point and then ties to even, down to 1.0.
+    col = np.full(G, 1.0, dtype=np.float16)
+    col[7] = np.float16(2.0 + 2 ** -6)
+    col[19] = np.float16(2.0 ** -24)
+    exact = sum(half_to_fraction(v) for v in col) / G
+    assert exact == 1 + Fraction(1, 2 ** 11) + Fraction(1, 2 ** 29)
+    assert np.float32(float(exact)) == np.float32(1 + 2 ** -11)        # fp32 hits the tie
+    assert round_to_half_bits(Fraction(1 + 2 ** -11)) == 0x3C00        # which ties down
+    assert round_to_half_bits(exact) == np.float16(1 + 2 ** -10).view(np.uint16)
     assert O.group_mean_fp16(col[:, None])[0] == np.float16(1.0 + 2 ** -10)
 
 
