@@ -132,25 +132,37 @@ CacheView view_of(const kvq_cache* h) {
 }
 
 DecodePlan plan_decode(const kvq_cache* h, bool want_scores) {
-    // Split-K over the quantized tokens. Every wavefront of a split takes
-    // whole key groups, four wavefronts per block, so a unit has at most
-    // ceil(groups / 4) useful splits; the launch picks how many it uses (one
-    // resident round of blocks), and the workspace covers the largest choice.
+    // One resident round of blocks on the current GPU. The fp16 partition
+    // (ring + pools) takes about one tile block per compute unit, 16 to 64 rows
+    // each; the quantized tokens of each unit are split over the remaining
+    // resident blocks, every wavefront of a split taking whole key groups
+    // (four wavefronts per block, so at most ceil(groups / 4) useful splits).
     DecodePlan p{};
     const int64_t U = (int64_t)h->cfg.batch * h->cfg.n_kv_heads;
     const int64_t r = h->cfg.n_q_heads / h->cfg.n_kv_heads;
+    int cus = 0, resident = 0;
+    decode_launch_shape(h->cfg.bits, (int)r, h->cfg.group, &cus, &resident);
+    if (cus < 1) cus = 1;
+    if (resident < 1) resident = 1;
+    const int64_t fp16_rows = (h->tokens - h->n_quant) +
+                              (h->cfg.pool > 0 ? h->cfg.pool + h->cfg.evict_cap : 0);
+    const int64_t t_min = fp16_rows > 0 ? (fp16_rows + 63) / 64 : 1;
+    int64_t t_max = fp16_rows > 0 ? (fp16_rows + 15) / 16 : 1;
+    if (t_max > kMaxFp16Tiles) t_max = kMaxFp16Tiles;
+    if (t_max < t_min) t_max = t_min;
+    int64_t t = (cus + U - 1) / U;
+    if (t > t_max) t = t_max;
+    if (t < t_min) t = t_min;
+    p.fp16_tiles = (int32_t)t;
     const int64_t groups = h->n_quant / h->cfg.group;
     int64_t s = groups > 0 ? (groups + 3) / 4 : 0;
     if (s > kMaxQuantSplits) s = kMaxQuantSplits;
-    const int64_t fp16_rows = (h->tokens - h->n_quant) +
-                              (h->cfg.pool > 0 ? h->cfg.pool + h->cfg.evict_cap : 0);
+    if (s > 0) {
+        int64_t q = (resident - U * t) / U;
+        if (q < 1) q = 1;
+        if (q < s) s = q;
+    }
     p.splits_q = (int32_t)s;
-    // fp16 tiles of 16 to 64 rows; the launch picks the count (about one tile
-    // block per compute unit), the workspace covers the largest choice
-    int64_t t = fp16_rows > 0 ? (fp16_rows + 15) / 16 : 1;
-    if (t > kMaxFp16Tiles) t = kMaxFp16Tiles;
-    if (t < (fp16_rows + 63) / 64) t = (fp16_rows + 63) / 64;
-    p.fp16_tiles = (int32_t)t;
     p.splits = p.splits_q + p.fp16_tiles;
     p.part_floats = U * p.splits * r * kPartRec;
     p.logit_floats = want_scores ? U * r * h->tokens : 0;

@@ -27,6 +27,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -1004,28 +1005,12 @@ int cu_count() {
 
 template <int BITS, int R, int G>
 void launch_decode_t(DecodeArgs a, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
-    // fp16 tiles: about one tile block per compute unit, so that every unit
-    // hosts the same mix of blocks; 16 to 64 rows each.
-    {
-        // rows of the partition at most: ring tokens plus full pools
-        const int64_t fp16_rows = (a.T - a.n_q) + (a.pool > 0 ? (int64_t)a.pool + a.evict_cap : 0);
-        int64_t t = ((int64_t)cu_count() + a.units - 1) / a.units;
-        const int64_t t_min = fp16_rows > 0 ? (fp16_rows + 63) / 64 : 1;
-        if (t > a.fp16_tiles) t = a.fp16_tiles;
-        if (t < t_min) t = t_min;
-        a.fp16_tiles = (int32_t)t;
-        a.tile_rows = fp16_rows > 0 ? (int32_t)((fp16_rows + t - 1) / t) : 1;
-    }
-    if (a.splits_q > 0) {
-        // one resident round: the fp16 tiles plus as many splits per unit as fit
-        int64_t q = ((int64_t)resident_blocks<BITS, R, G>() - (int64_t)a.units * a.fp16_tiles) /
-                    a.units;
-        if (q < 1) q = 1;
-        if (q < a.splits_q) a.splits_q = (int32_t)q;
-    }
-    a.splits = a.splits_q + a.fp16_tiles;
+    // fp16 tile rows: the partition's rows (ring tokens plus full pools) over
+    // the plan's tile count
+    const int64_t fp16_rows = (a.T - a.n_q) + (a.pool > 0 ? (int64_t)a.pool + a.evict_cap : 0);
+    a.tile_rows = fp16_rows > 0 ? (int32_t)((fp16_rows + a.fp16_tiles - 1) / a.fp16_tiles) : 1;
     const unsigned blocks = (unsigned)(a.units * a.fp16_tiles + a.units * a.splits_q);
-    // the device queries above may have left an error that is not a launch's
+    // the device queries of the plan may have left an error that is not a launch's
     (void)hipGetLastError();
     if (e0 || e1)
         hipExtLaunchKernelGGL((decode_kernel<BITS, R, G>), dim3(blocks), dim3(256), 0, s, e0, e1, 0,
@@ -1050,7 +1035,23 @@ void dispatch_r(const DecodeArgs& a, int R, int G, hipEvent_t e0, hipEvent_t e1,
     else dispatch_g<BITS, 4>(a, G, e0, e1, s);
 }
 
+template <int BITS, int R>
+int resident_g(int G) {
+    return G == 32 ? resident_blocks<BITS, R, 32>()
+                   : G == 64 ? resident_blocks<BITS, R, 64>() : resident_blocks<BITS, R, 128>();
+}
+
 }  // namespace
+
+void decode_launch_shape(int bits, int r, int group, int* cus, int* resident) {
+    *cus = cu_count();
+    if (bits == 2)
+        *resident = r == 1 ? resident_g<2, 1>(group) : r == 2 ? resident_g<2, 2>(group)
+                                                              : resident_g<2, 4>(group);
+    else
+        *resident = r == 1 ? resident_g<4, 1>(group) : r == 2 ? resident_g<4, 2>(group)
+                                                              : resident_g<4, 4>(group);
+}
 
 int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& plan,
                   const uint16_t* q, float* out, float* acc, void* ws, void* ev_start,

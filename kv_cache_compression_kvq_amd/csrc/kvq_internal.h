@@ -49,9 +49,9 @@ CacheView view_of(const kvq_cache* h);
 
 // Split plan of one decode call.
 struct DecodePlan {
-    int32_t splits_q;    // upper bound on quantized-partition splits per unit (0 when
-                         // n_q == 0); the launch picks the count that fills the GPU once
-    int32_t fp16_tiles;  // upper bound on fp16-partition tiles (ring + pools), 16-64 rows each
+    int32_t splits_q;    // quantized-partition splits per unit (0 when n_q == 0): as
+                         // many as one resident round of blocks holds
+    int32_t fp16_tiles;  // fp16-partition tiles (ring + pools) per unit, 16-64 rows each
     int32_t splits;      // splits_q + fp16_tiles partial records per unit
     int64_t part_floats; // partial records: U * splits * r * kPartRec
     int64_t logit_floats;// U * r * T when scores are wanted
@@ -76,5 +76,8 @@ int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& 
 int launch_topk(const float* scores, int32_t rows, int32_t T, int32_t k, int32_t w,
                 int32_t* idx, void* stream);
 int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, void* stream);
+// Launch shape of the decode kernel on the current GPU: compute units and the
+// blocks of decode_kernel<bits, r, group> resident at once (cached per GPU).
+void decode_launch_shape(int bits, int r, int group, int* cus, int* resident);
 
 }  // namespace kvq
