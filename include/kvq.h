@@ -74,6 +74,11 @@ typedef int32_t kvq_status;
 #define KVQ_ECAPACITY    (-3) /* appending beyond max_tokens */
 #define KVQ_EWORKSPACE   (-4) /* arena or workspace smaller than required */
 #define KVQ_ELAUNCH      (-5) /* a HIP launch failed (hipGetLastError) */
+#define KVQ_ESCRATCH     (-6) /* the no-allocation decode needs more than its static scratch */
+
+/* Bytes of the library's static device scratch used by
+ * kvq_decode_attention_noalloc (one copy per GPU, held until the process ends). */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /* Static description of a status code. Never returns NULL. */
 const char* kvq_status_string(kvq_status status);
@@ -206,6 +211,26 @@ kvq_status kvq_decode_workspace(const kvq_cache* h, int32_t want_scores, size_t*
  */
 kvq_status kvq_decode_attention(const kvq_cache* h, const void* d_q, float* d_out,
                                 float* d_acc, void* d_ws, size_t ws_bytes, void* stream);
+
+/*
+ * kvq_decode_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the workspace taken from a
+ * static device array of KVQ_NOALLOC_SCRATCH_BYTES inside the library instead
+ * of a caller buffer. The call allocates and frees nothing. The array's device
+ * address is looked up once per GPU, on the first call made with that GPU
+ * current.
+ *   d_q, d_out, d_acc as for kvq_decode_attention (the caller still owns them)
+ * Every call on one GPU shares that GPU's array and overwrites what an earlier
+ * call left there; calls that overlap in time on one GPU (different streams
+ * without ordering) race and give undefined results. Nothing in the array has
+ * to start at zero: each call writes every scratch word before reading it.
+ * Errors: KVQ_EINVAL (null pointer, T == 0), KVQ_ESCRATCH (the call needs more
+ * than KVQ_NOALLOC_SCRATCH_BYTES: kvq_decode_workspace tells how much),
+ * KVQ_ELAUNCH (including a failed lookup of the array's address).
+ */
+kvq_status kvq_decode_attention_noalloc(const kvq_cache* h, const void* d_q, float* d_out,
+                                        float* d_acc, void* stream);
 
 /*
  * kvq_decode_attention, additionally recording ev_start and ev_stop (hipEvent_t

@@ -21,11 +21,14 @@ KVQ_EUNSUPPORTED = -2
 KVQ_ECAPACITY = -3
 KVQ_EWORKSPACE = -4
 KVQ_ELAUNCH = -5
+KVQ_ESCRATCH = -6
+NOALLOC_SCRATCH_BYTES = 32 << 20  # KVQ_NOALLOC_SCRATCH_BYTES
 
 # Entry points declared in include/kvq.h.
 EXPORTS = ("kvq_status_string", "kvq_cache_bytes", "kvq_cache_init", "kvq_quantize_append",
            "kvq_decode_workspace", "kvq_decode_attention", "kvq_decode_attention_timed",
-           "kvq_decode_step", "kvq_decode_step_timed", "kvq_topk_evict", "kvq_unpack_codes")
+           "kvq_decode_step", "kvq_decode_step_timed", "kvq_topk_evict", "kvq_unpack_codes",
+           "kvq_decode_attention_noalloc")
 
 
 class Config(ctypes.Structure):
@@ -73,6 +76,7 @@ def lib() -> ctypes.CDLL:
             "kvq_decode_workspace": [ctypes.POINTER(Cache), I32, ctypes.POINTER(SZ)],
             "kvq_decode_attention": [ctypes.POINTER(Cache), P, P, P, P, SZ, P],
             "kvq_decode_attention_timed": [ctypes.POINTER(Cache), P, P, P, P, SZ, P, P, P],
+            "kvq_decode_attention_noalloc": [ctypes.POINTER(Cache), P, P, P, P],
             "kvq_decode_step": [ctypes.POINTER(Cache), P, P, P, P, P, P, SZ, P],
             "kvq_decode_step_timed": [ctypes.POINTER(Cache), P, P, P, P, P, P, SZ, P, P, P],
             "kvq_topk_evict": [P, I32, I32, I32, I32, P, P],
@@ -149,6 +153,12 @@ def decode_attention(h: Cache, q, out, acc, ws, ws_bytes: int | None = None, str
     nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
     _check("kvq_decode_attention", lib().kvq_decode_attention(
         ctypes.byref(h), _ptr(q), _ptr(out), _ptr(acc), _ptr(ws), nbytes, _stream(stream)))
+
+
+def decode_attention_noalloc(h: Cache, q, out, acc, stream=None) -> None:
+    """kvq_decode_attention with the library's static scratch (no workspace)."""
+    _check("kvq_decode_attention_noalloc", lib().kvq_decode_attention_noalloc(
+        ctypes.byref(h), _ptr(q), _ptr(out), _ptr(acc), _stream(stream)))
 
 
 def decode_attention_timed(h: Cache, q, out, acc, ws, ev_start: int, ev_stop: int,

@@ -184,6 +184,9 @@ const char* kvq_status_string(kvq_status s) {
         case KVQ_ECAPACITY: return "cache capacity exceeded";
         case KVQ_EWORKSPACE: return "arena or workspace too small";
         case KVQ_ELAUNCH: return "HIP launch failed";
+        case KVQ_ESCRATCH:
+            return "decode needs more scratch than the library's static buffer "
+                   "(KVQ_NOALLOC_SCRATCH_BYTES) holds; use kvq_decode_attention with a workspace";
         default: return "unknown status";
     }
 }
@@ -264,6 +267,20 @@ kvq_status kvq_decode_attention(const kvq_cache* h, const void* d_q, float* d_ou
                                 void* d_ws, size_t ws_bytes, void* stream) {
     return kvq_decode_attention_timed(h, d_q, d_out, d_acc, d_ws, ws_bytes, nullptr, nullptr,
                                       stream);
+}
+
+kvq_status kvq_decode_attention_noalloc(const kvq_cache* h, const void* d_q, float* d_out,
+                                        float* d_acc, void* stream) {
+    if (!valid_handle(h) || !d_q || !d_out) return KVQ_EINVAL;
+    if (h->tokens < 1) return KVQ_EINVAL;
+    const DecodePlan p = plan_decode(h, d_acc != nullptr);
+    if (p.ws_bytes > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ESCRATCH;
+    int err = 0;
+    void* ws = noalloc_scratch(&err);
+    if (!ws) return KVQ_ELAUNCH;
+    return launch_status(launch_decode(view_of(h), h->tokens, h->n_quant, p,
+                                       static_cast<const uint16_t*>(d_q), d_out, d_acc, ws,
+                                       nullptr, nullptr, stream));
 }
 
 kvq_status kvq_decode_step_timed(kvq_cache* h, const void* d_k, const void* d_v,

@@ -27,6 +27,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 
 #include "kvq_internal.h"
 
@@ -1051,6 +1052,35 @@ void decode_launch_shape(int bits, int r, int group, int* cus, int* resident) {
     else
         *resident = r == 1 ? resident_g<4, 1>(group) : r == 2 ? resident_g<4, 2>(group)
                                                               : resident_g<4, 4>(group);
+}
+
+// Workspace of kvq_decode_attention_noalloc: a file-scope device array, one
+// copy per GPU. Host code never uses this name as an address (on the host it
+// is only a stand-in); it uses the device address hipGetSymbolAddress returns
+// for the current GPU.
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+void* noalloc_scratch(int* err) {
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64) {
+        *err = e != hipSuccess ? (int)e : (int)hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            *err = e != hipSuccess ? (int)e : (int)hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    *err = 0;
+    return addr[dev];
 }
 
 int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& plan,

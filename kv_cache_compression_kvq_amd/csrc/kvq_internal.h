@@ -79,5 +79,8 @@ int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, voi
 // Launch shape of the decode kernel on the current GPU: compute units and the
 // blocks of decode_kernel<bits, r, group> resident at once (cached per GPU).
 void decode_launch_shape(int bits, int r, int group, int* cus, int* resident);
+// Device address of the static decode scratch (KVQ_NOALLOC_SCRATCH_BYTES) on the
+// current GPU, looked up once per GPU; null with *err set when the lookup fails.
+void* noalloc_scratch(int* err);
 
 }  // namespace kvq

@@ -55,7 +55,10 @@ void decode_launch_shape(int, int, int, int* cus, int* resident) {
     *cus = 256;
     *resident = 1024;
 }
-
+void* noalloc_scratch(int* err) {
+    *err = 0;
+    return reinterpret_cast<void*>(uintptr_t(1) << 41);
+}
 }  // namespace kvq
 
 static kvq_config cfg(int bits, int group, int R, int pool, int E, int hq, int hkv, int B,
@@ -177,6 +180,28 @@ int main() {
                     CHECK(kvq_decode_workspace(&h, 0, &ws) == KVQ_EINVAL);
                     CHECK(kvq_unpack_codes(&h, nullptr, nullptr, nullptr) == KVQ_EINVAL);
                 }
+
+    // the no-allocation decode: fits, or KVQ_ESCRATCH with nothing launched
+    {
+        kvq_config k = cfg(2, 32, 128, 0, 32, 32, 8, 16, 32768);
+        size_t bytes = 0;
+        CHECK(kvq_cache_bytes(&k, &bytes) == KVQ_OK);
+        kvq_cache h{};
+        CHECK(kvq_cache_init(&k, reinterpret_cast<void*>(uintptr_t(1) << 40), bytes, &h,
+                             nullptr) == KVQ_OK);
+        const int16_t dummy = 0;
+        CHECK(kvq_quantize_append(&h, &dummy, &dummy, 32768, nullptr) == KVQ_OK);
+        size_t ws = 0, ws_h2o = 0;
+        CHECK(kvq_decode_workspace(&h, 0, &ws) == KVQ_OK && ws <= KVQ_NOALLOC_SCRATCH_BYTES);
+        CHECK(kvq_decode_workspace(&h, 1, &ws_h2o) == KVQ_OK && ws_h2o > KVQ_NOALLOC_SCRATCH_BYTES);
+        float out = 0.f, acc = 0.f;
+        const int before = g_launches;
+        CHECK(kvq_decode_attention_noalloc(&h, &dummy, &out, &acc, nullptr) == KVQ_ESCRATCH);
+        CHECK(g_launches == before);
+        CHECK(kvq_decode_attention_noalloc(&h, &dummy, &out, nullptr, nullptr) == KVQ_OK);
+        CHECK(g_launches == before + 1);
+        CHECK(kvq_decode_attention_noalloc(&h, nullptr, &out, nullptr, nullptr) == KVQ_EINVAL);
+    }
 
     // top-k argument checks
     float s = 0.f;

@@ -24,7 +24,7 @@ def test_library_exports_every_header_function(kvq):
 
 
 def test_status_strings(kvq):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert kvq.status_string(code) and "unknown" not in kvq.status_string(code)
     assert "unknown" in kvq.status_string(7)
 
