@@ -206,6 +206,7 @@ ROWS = {
     "append_ott": ("ott", "a1-a7: OTT scores + pool scan, mean replacement, quantize + pack, ring"),
     "decode_h2o_minikv": ("minikv", "a8-a10: fused decode + merge with H2O accumulation"),
     "topk_minikv": ("minikv", "a11: heavy-hitter top-k + recent window"),
+    "decode_llama8b_g16": ("llama8b_g16", "a8-a10: fused decode + merge at group size 16"),
     "decode_long_b2g32": ("long_b2g32", "a8-a10: fused decode + merge, split-K over context"),
     "decode_long_b2g128": ("long_b2g128", "a8-a10: fused decode + merge, split-K over context"),
     "decode_long_b4g32": ("long_b4g32", "a8-a10: fused decode + merge, split-K over context"),

@@ -291,6 +291,50 @@ kvq_status kvq_topk_evict(const float* d_scores, int32_t rows, int32_t T, int32_
 kvq_status kvq_unpack_codes(const kvq_cache* h, uint8_t* d_kcodes, uint8_t* d_vcodes,
                             void* stream);
 
+/*
+ * Canonical view of everything a cache stores, independent of the arena's
+ * internal layout (for parity checks and debugging). Every field is a device
+ * buffer owned by the caller, or NULL to skip it. With n_q, T the handle's
+ * counts, KG = n_q / G key groups and NG = d / min(G, d) value groups:
+ *   kcodes, vcodes  uint8 [U][n_q][d]: one code per element
+ *   kscale, kzero   fp16 [U][KG][d]: key scale and zero point per group and
+ *                   channel (MiniKV, section 4.4: both kept in FP16)
+ *   vscale, vzero   fp16 [U][n_q][NG]: value scale and zero point per token
+ *                   and channel group
+ *   pooled          uint8 [U][n_q]: 1 when the token was admitted to the
+ *                   outlier pool (its quantized slot holds the group mean)
+ *   kres, vres      fp16 [U][T - n_q][d]: the fp16 residual rows, token order
+ *   counters        int32 [U][4]: pool count, extra-pool count, frozen flag,
+ *                   largest value scale (fp16 bits)
+ *   pool_idx        int32 [U][N], pool_score uint64 [U][N] (key L1 norm in
+ *                   units of 2^-24), pool_k, pool_v fp16 [U][N][d]
+ *   ev_idx          int32 [U][E], ev_k, ev_v fp16 [U][E][d] (extra pool)
+ * Pool slots beyond the counters are unspecified.
+ */
+typedef struct kvq_debug_view {
+    uint8_t* kcodes;
+    uint8_t* vcodes;
+    uint16_t* kscale;
+    uint16_t* kzero;
+    uint16_t* vscale;
+    uint16_t* vzero;
+    uint8_t* pooled;
+    uint16_t* kres;
+    uint16_t* vres;
+    int32_t* counters;
+    int32_t* pool_idx;
+    uint64_t* pool_score;
+    uint16_t* pool_k;
+    uint16_t* pool_v;
+    int32_t* ev_idx;
+    uint16_t* ev_k;
+    uint16_t* ev_v;
+} kvq_debug_view;
+
+/* Fill the non-NULL fields of *view (host struct of device pointers) on
+ * `stream`. Errors: KVQ_EINVAL (invalid handle or null view). */
+kvq_status kvq_debug_unpack(const kvq_cache* h, const kvq_debug_view* view, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

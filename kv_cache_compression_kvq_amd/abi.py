@@ -28,7 +28,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20  # KVQ_NOALLOC_SCRATCH_BYTES
 EXPORTS = ("kvq_status_string", "kvq_cache_bytes", "kvq_cache_init", "kvq_quantize_append",
            "kvq_decode_workspace", "kvq_decode_attention", "kvq_decode_attention_timed",
            "kvq_decode_step", "kvq_decode_step_timed", "kvq_topk_evict", "kvq_unpack_codes",
-           "kvq_decode_attention_noalloc")
+           "kvq_decode_attention_noalloc", "kvq_debug_unpack")
 
 
 class Config(ctypes.Structure):
@@ -45,6 +45,13 @@ class Cache(ctypes.Structure):
             "off_kq", "off_vq", "off_kmeta", "off_vmeta", "off_mask", "off_kring", "off_vring",
             "off_pool_idx", "off_pool_score", "off_pool_k", "off_pool_v", "off_ev_idx",
             "off_ev_k", "off_ev_v", "off_counters", "off_scores")]
+
+
+class DebugView(ctypes.Structure):
+    """kvq_debug_view: device pointers (0 = skip) of the canonical cache view."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "kcodes", "vcodes", "kscale", "kzero", "vscale", "vzero", "pooled", "kres", "vres",
+        "counters", "pool_idx", "pool_score", "pool_k", "pool_v", "ev_idx", "ev_k", "ev_v")]
 
 
 class KvqError(RuntimeError):
@@ -81,6 +88,7 @@ def lib() -> ctypes.CDLL:
             "kvq_decode_step_timed": [ctypes.POINTER(Cache), P, P, P, P, P, P, SZ, P, P, P],
             "kvq_topk_evict": [P, I32, I32, I32, I32, P, P],
             "kvq_unpack_codes": [ctypes.POINTER(Cache), P, P, P],
+            "kvq_debug_unpack": [ctypes.POINTER(Cache), ctypes.POINTER(DebugView), P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -194,3 +202,10 @@ def topk_evict(scores, rows: int, T: int, k: int, w: int, idx, stream=None) -> N
 def unpack_codes(h: Cache, kcodes, vcodes, stream=None) -> None:
     _check("kvq_unpack_codes", lib().kvq_unpack_codes(ctypes.byref(h), _ptr(kcodes),
                                                       _ptr(vcodes), _stream(stream)))
+
+
+def debug_unpack(h: Cache, stream=None, **bufs) -> None:
+    """kvq_debug_unpack: fill the named fields (tensors) of the canonical view."""
+    view = DebugView(**{k: _ptr(v) for k, v in bufs.items()})
+    _check("kvq_debug_unpack", lib().kvq_debug_unpack(ctypes.byref(h), ctypes.byref(view),
+                                                      _stream(stream)))

@@ -14,6 +14,10 @@ constexpr int64_t kMaxQuantSplits = 1000;  // merge keeps per-split weights in L
 
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Key groups the kmeta region holds for C chunks: G = 16 keeps both groups of
+// every chunk, so that a half-used last chunk still has a (zeroed) second entry.
+uint64_t key_groups_of(uint64_t G, uint64_t C) { return G == 16 ? 2 * C : C * kChunk / G; }
+
 int64_t n_quantized(int64_t T, int64_t R, int64_t G) {
     // Tokens held quantized after T appends: the residual window keeps the
     // last R tokens plus any incomplete group in fp16 ("KV cache quantization
@@ -29,7 +33,8 @@ kvq_status check_config(const kvq_config* c) {
     if (c->n_q_heads % c->n_kv_heads != 0) return KVQ_EINVAL;
     const int r = c->n_q_heads / c->n_kv_heads;
     if (c->bits != 2 && c->bits != 4) return KVQ_EUNSUPPORTED;
-    if (c->group != 32 && c->group != 64 && c->group != 128) return KVQ_EUNSUPPORTED;
+    if (c->group != 16 && c->group != 32 && c->group != 64 && c->group != 128)
+        return KVQ_EUNSUPPORTED;
     if (c->head_dim != kHeadDim) return KVQ_EUNSUPPORTED;
     if (r != 1 && r != 2 && r != 4) return KVQ_EUNSUPPORTED;
     if (c->pool > kMaxPool || c->evict_cap > kMaxEvict) return KVQ_EUNSUPPORTED;
@@ -51,13 +56,13 @@ Layout layout_of(const kvq_config* c) {
     const uint64_t d = kHeadDim;
     const uint64_t G = c->group, b = c->bits, N = c->pool, E = c->evict_cap;
     L.q_cap = n_quantized(c->max_tokens, c->residual, c->group);
-    L.chunks = L.q_cap / kChunk;
+    L.chunks = (L.q_cap + kChunk - 1) / kChunk;  // G = 16: the last chunk may be half used
     L.ring = (int64_t)c->residual + c->group;
     const uint64_t C = L.chunks, NG = d / G;
     const uint64_t sizes[16] = {
         U * C * 128 * b * 4,          // kq
         U * C * 128 * b * 4,          // vq
-        U * (L.q_cap / G) * d * 4,    // kmeta
+        U * key_groups_of(G, C) * d * 4,  // kmeta
         U * C * NG * kChunk * 4,      // vmeta
         U * C * 4,                    // mask
         U * L.ring * d * 2,           // kring
@@ -126,8 +131,8 @@ CacheView view_of(const kvq_cache* h) {
     v.units = h->cfg.batch * h->cfg.n_kv_heads;
     v.ring_slots = (int32_t)h->ring_slots;
     v.q_cap = h->q_cap;
-    v.chunks = h->q_cap / kChunk;
-    v.key_groups = h->q_cap / h->cfg.group;
+    v.chunks = (h->q_cap + kChunk - 1) / kChunk;
+    v.key_groups = (int64_t)key_groups_of(h->cfg.group, v.chunks);
     return v;
 }
 
@@ -154,7 +159,9 @@ DecodePlan plan_decode(const kvq_cache* h, bool want_scores) {
     if (t > t_max) t = t_max;
     if (t < t_min) t = t_min;
     p.fp16_tiles = (int32_t)t;
-    const int64_t groups = h->n_quant / h->cfg.group;
+    // work items: key groups, or with G = 16 chunks (two groups each)
+    const int64_t groups = h->cfg.group == 16 ? (h->n_quant + kChunk - 1) / kChunk
+                                              : h->n_quant / h->cfg.group;
     int64_t s = groups > 0 ? (groups + 3) / 4 : 0;
     if (s > kMaxQuantSplits) s = kMaxQuantSplits;
     if (s > 0) {
@@ -334,6 +341,11 @@ kvq_status kvq_unpack_codes(const kvq_cache* h, uint8_t* d_kcodes, uint8_t* d_vc
     if (h->n_quant == 0) return KVQ_OK;
     if (!d_kcodes || !d_vcodes) return KVQ_EINVAL;
     return launch_status(launch_unpack(view_of(h), h->n_quant, d_kcodes, d_vcodes, stream));
+}
+
+kvq_status kvq_debug_unpack(const kvq_cache* h, const kvq_debug_view* view, void* stream) {
+    if (!valid_handle(h) || !view) return KVQ_EINVAL;
+    return launch_status(launch_debug_unpack(view_of(h), h->tokens, h->n_quant, *view, stream));
 }
 
 }  // extern "C"

@@ -55,13 +55,16 @@ constexpr int kFp16Bytes = 4 * D * 2 + 4 * 64 * 4;
 // same bytes hold the output accumulators. The folded-query table and the
 // probability exchange live in LDS objects of their own, so that writing them
 // never waits on the ring's copies in flight.
-template <int BITS>
+template <int BITS, int G>
 struct Ring {
     static constexpr int kStages = 2;
     static constexpr int kCodes = 128 * BITS * 4;          // packed codes of one chunk
-    static constexpr int kMeta = 1024;                      // value (<= 512 B) + key (512 B) scales
+    // value scales (32 tokens x d/G groups x 4 B: <= 512 B, 1 KB at G = 16),
+    // then key scales (512 B per key group; G = 16: both groups of the chunk)
+    static constexpr int kKmOff = G == 16 ? 1024 : 512;
+    static constexpr int kMeta = kKmOff + (G == 16 ? 1024 : 512);
     static constexpr int kStage = 2 * kCodes + kMeta + 16;  // + pool mask word
-    static constexpr int kLoads = 2 * (kCodes / 1024) + 2;  // loads issued per stage
+    static constexpr int kLoads = 2 * (kCodes / 1024) + (G == 16 ? 3 : 2);  // loads per stage
     static constexpr int kWave = kStages * kStage;          // ring bytes per wavefront
     static constexpr int kBlock = 4 * kWave > kFp16Bytes ? 4 * kWave : kFp16Bytes;
     // epilogue: accumulators of tiles 0-5 in the ring, 6-7 in the query table
@@ -373,8 +376,18 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
 
 template <int BITS, int R, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(DecodeArgs a) {
+    constexpr bool kG16 = G == 16;   // two key groups per 32-token chunk
     constexpr int NG = D / G;        // value groups per token
-    constexpr int CPG = G / 32;      // chunks per key group
+    // A wavefront's work item is a key group of CPG chunks, or with G = 16 one
+    // chunk holding KPC = 2 key groups (16-token tiles 0 and 1).
+    constexpr int CPG = kG16 ? 1 : G / 32;
+    constexpr int KPC = kG16 ? 2 : 1;
+    // Value-operand rows are (head, value group) pairs: 16 per matrix-core
+    // operand, so r = 4 with 8 value groups (G = 16) needs two row sets, set s
+    // holding groups 4s .. 4s + 3 for the channel tiles 4s .. 4s + 3.
+    constexpr int GPS = 16 / R < NG ? 16 / R : NG;  // value groups per row set
+    constexpr int VSETS = NG / GPS;
+    static_assert(VSETS == 1 || VSETS == 2, "at most two value row sets");
     constexpr int WPC = 128 * BITS;  // words per chunk
     // With r = 4 the 16 MFMA columns hold 4 copies of each head's logits;
     // each copy then exponentiates a quarter of the tokens.
@@ -393,9 +406,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     constexpr float kAccW = BITS == 2 ? 65536.f : 1.f;  // keys: 2^16 removes the operand weight
     constexpr uint32_t kMaskA = 0x03C003C0u;
     constexpr uint32_t kMagicA = 0x4C004C00u;
-    using RG = Ring<BITS>;
+    using RG = Ring<BITS, G>;
     __shared__ __align__(16) float smem[RG::kBlock / 4];
-    __shared__ __align__(16) unsigned char s_btab[4][2048];
+    __shared__ __align__(16) unsigned char s_btab[4][2048 * KPC];
     __shared__ __align__(16) float s_pbuf[4][128];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -414,7 +427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     const int idx = blockIdx.x - a.units * a.fp16_tiles;
     const int u = idx / a.splits_q, split = idx % a.splits_q;
     const int b = u / a.n_kv_heads, hk = u % a.n_kv_heads;
-    const uint32_t groups = (uint32_t)(a.n_q / G);
+    const uint32_t groups = (uint32_t)(kG16 ? (a.n_q + 31) / 32 : a.n_q / G);  // work items
     const uint32_t gs0 = (uint32_t)((int64_t)split * groups / a.splits_q);
     const uint32_t gs1 = (uint32_t)((int64_t)(split + 1) * groups / a.splits_q);
     const uint32_t my_groups = gs1 - gs0 > (uint32_t)wave ? (gs1 - gs0 - wave + 3) / 4 : 0;
@@ -466,15 +479,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
         if (BITS == 4) lds_load16(kq_u + ch * WPC + 256 + lane * 4, st + 1024);
         lds_load16(vq_u + ch * WPC + lane * 4, st + RG::kCodes);
         if (BITS == 4) lds_load16(vq_u + ch * WPC + 256 + lane * 4, st + RG::kCodes + 1024);
-        // value scales (lanes < 8 NG) and, at a key group's first chunk, key scales (lanes >= 32)
-        const uint32_t* src = lane < 32 ? vm_u + ch * NG * 32 + lane * 4 : km_u + gi * D + (lane - 32) * 4;
-        if (lane < 8 * NG || (lane >= 32 && cc == 0)) lds_load16(src, st + 2 * RG::kCodes);
+        if (kG16) {
+            // value scales (1 KB), then the key scales of both groups (1 KB)
+            lds_load16(vm_u + ch * NG * 32 + lane * 4, st + 2 * RG::kCodes);
+            lds_load16(km_u + 2 * ch * D + lane * 4, st + 2 * RG::kCodes + RG::kKmOff);
+        } else {
+            // value scales (lanes < 8 NG) and, at a key group's first chunk, key
+            // scales (lanes >= 32)
+            const uint32_t* src =
+                lane < 32 ? vm_u + ch * NG * 32 + lane * 4 : km_u + gi * D + (lane - 32) * 4;
+            if (lane < 8 * NG || (lane >= 32 && cc == 0)) lds_load16(src, st + 2 * RG::kCodes);
+        }
         if (lane == 0) lds_load4(mk_u + ch, st + 2 * RG::kCodes + RG::kMeta);
     };
     float* wsm = reinterpret_cast<float*>(wlds);
-    unsigned char* btab = s_btab[wave];  // folded query, 2 KB
+    unsigned char* btab = s_btab[wave];  // folded query, 2 KB per key group of a chunk
     float* pbuf = s_pbuf[wave];          // [4][32] probabilities
-    float m_run = -INFINITY, lsum = 0.f, zc = 0.f, beta = 0.f;
+    // beta0 / beta1: zero-point terms of the chunk's key groups (tiles 0 / 1);
+    // zc / zc2: sum_t p_t z^V_t of the lane's value rows in row set 0 / 1
+    float m_run = -INFINITY, lsum = 0.f, zc = 0.f, zc2 = 0.f, beta0 = 0.f, beta1 = 0.f;
     floatx4 O[8];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -498,7 +521,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     // lane's value-operand row, key scales of its query-fold channels
     const uint32_t lane_codes = lane * 16;
     const uint32_t lane_vm = 2 * RG::kCodes + (gs * 32 + 4 * kb) * 4;
-    const uint32_t lane_km = 2 * RG::kCodes + 512 + cb0 * 4;
+    const uint32_t lane_km = 2 * RG::kCodes + RG::kKmOff + cb0 * 4;
     auto step = [&](uint32_t k, uint32_t later) {
         const uint32_t gi = gs0 + wave + 4 * (k / CPG), cc = k % CPG;
         const int64_t tb = (int64_t)(gi * CPG + cc) * 32;
@@ -517,13 +540,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
         }
         u32x4 vm0 = ring_read<0>(a_vm);
         u32x4 vm1 = ring_read<64>(a_vm);
-        u32x4 km0 = vm0, km1 = vm1;
+        u32x4 km0 = vm0, km1 = vm1, km2 = vm0, km3 = vm1, vm2 = vm0, vm3 = vm1;
         if (cc == 0) {
             km0 = ring_read<0>(a_km);
             km1 = ring_read<16>(a_km);
         }
+        if (kG16) {
+            // the second key group's scales, and the value rows of set 1
+            km2 = ring_read<512>(a_km);
+            km3 = ring_read<528>(a_km);
+            vm2 = ring_read<GPS * 128>(a_vm);
+            vm3 = ring_read<GPS * 128 + 64>(a_vm);
+        }
         uint32_t mwv = ring_read32(meta + RG::kMeta);
-        if (BITS == 4) {
+        if (kG16 && BITS == 4) {
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(wk0), "+v"(wk1), "+v"(wv0), "+v"(wv1), "+v"(vm0), "+v"(vm1),
+                           "+v"(km0), "+v"(km1), "+v"(mwv), "+v"(km2), "+v"(km3), "+v"(vm2),
+                           "+v"(vm3)
+                         :
+                         : "memory");
+        } else if (kG16) {
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(wk0), "+v"(wv0), "+v"(vm0), "+v"(vm1), "+v"(km0), "+v"(km1),
+                           "+v"(mwv), "+v"(km2), "+v"(km3), "+v"(vm2), "+v"(vm3)
+                         :
+                         : "memory");
+            wk1 = wk0;
+            wv1 = wv0;
+        } else if (BITS == 4) {
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(wk0), "+v"(wk1), "+v"(wv0), "+v"(wv1), "+v"(vm0), "+v"(vm1),
                            "+v"(km0), "+v"(km1), "+v"(mwv)
@@ -540,33 +585,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
         }
         if (cc == 0) {
             // Fold the key scale into the query: B = hi/lo of q~_c * s_c, and
-            // the zero point into beta_h = sum_c q~_c (z_c - 2^b s_c).
+            // the zero point into beta_h = sum_c q~_c (z_c - 2^b s_c); with
+            // G = 16 once per key group of the chunk.
             wave_lds_fence();  // previous group's B reads are done
-            const uint32_t kmw[8] = {km0.x, km0.y, km0.z, km0.w, km1.x, km1.y, km1.z, km1.w};
-            uint32_t hiw[4], low[4];
-            float bp = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                hiw[i] = mul_pk(qv[2 * i], kmw[2 * i], qv[2 * i + 1], kmw[2 * i + 1]);
-                low[i] = mul_pk_res(qv[2 * i], kmw[2 * i], qv[2 * i + 1], kmw[2 * i + 1], hiw[i]);
-            }
+            for (int kg = 0; kg < KPC; ++kg) {
+                const u32x4 ka = kg == 0 ? km0 : km2, kc = kg == 0 ? km1 : km3;
+                const uint32_t kmw[8] = {ka.x, ka.y, ka.z, ka.w, kc.x, kc.y, kc.z, kc.w};
+                uint32_t hiw[4], low[4];
+                float bp = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float zk = h2f(kmw[i] >> 16);
-                if (BITS == 2) {
-                    bp += qv[i] * zk;
-                } else {
-                    const float sk = h2f(kmw[i] & 0xFFFF);
-                    bp += qv[i] * (zk - 16.f * sk);
+                for (int i = 0; i < 4; ++i) {
+                    hiw[i] = mul_pk(qv[2 * i], kmw[2 * i], qv[2 * i + 1], kmw[2 * i + 1]);
+                    low[i] = mul_pk_res(qv[2 * i], kmw[2 * i], qv[2 * i + 1], kmw[2 * i + 1], hiw[i]);
                 }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float zk = h2f(kmw[i] >> 16);
+                    if (BITS == 2) {
+                        bp += qv[i] * zk;
+                    } else {
+                        const float sk = h2f(kmw[i] & 0xFFFF);
+                        bp += qv[i] * (zk - 16.f * sk);
+                    }
+                }
+                if (BITS == 2 && ksb % 2 == 0) bp *= 0.25f;  // undo the query weight
+                unsigned char* e0 = btab + kg * 2048 + ((((ksb * 4 + kbb) * 2) * 4) + hb) * 16;
+                *reinterpret_cast<u32x4*>(e0) = u32x4{hiw[0], hiw[1], hiw[2], hiw[3]};
+                *reinterpret_cast<u32x4*>(e0 + 4 * 16) = u32x4{low[0], low[1], low[2], low[3]};
+                bp += row_ror<8>(bp);
+                bp += kMirror ? dpp<0x141>(bp) : row_ror<4>(bp);  // row_half_mirror
+                (kg == 0 ? beta0 : beta1) = sum_x32(sum_x16(bp));
             }
-            if (BITS == 2 && ksb % 2 == 0) bp *= 0.25f;  // undo the query weight
-            unsigned char* e0 = btab + ((((ksb * 4 + kbb) * 2) * 4) + hb) * 16;
-            *reinterpret_cast<u32x4*>(e0) = u32x4{hiw[0], hiw[1], hiw[2], hiw[3]};
-            *reinterpret_cast<u32x4*>(e0 + 4 * 16) = u32x4{low[0], low[1], low[2], low[3]};
-            bp += row_ror<8>(bp);
-            bp += kMirror ? dpp<0x141>(bp) : row_ror<4>(bp);  // row_half_mirror
-            beta = sum_x32(sum_x16(bp));
+            if (!kG16) beta1 = beta0;
             wave_lds_fence();
         }
 
@@ -592,20 +643,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
                 A0 = as_half8(cvt4(w0, 6), cvt4(w0, 2), cvt4(w0, -2), cvt4(w0, -6));
                 A1 = as_half8(cvt4(w1, 6), cvt4(w1, 2), cvt4(w1, -2), cvt4(w1, -6));
             }
+            // tile 1 takes the folded query of the chunk's second key group (G = 16)
+            constexpr int kT1 = (KPC - 1) * 2048;
             if (kMirror) {
-                const half8 B = *reinterpret_cast<const half8*>(
-                    btab + ((((ks * 4 + kb) * 2 + pq) * 4) + hq) * 16);
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, B, acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, B, acc1, 0, 0, 0);
+                const int ob = ((((ks * 4 + kb) * 2 + pq) * 4) + hq) * 16;
+                const half8 B0 = *reinterpret_cast<const half8*>(btab + ob);
+                const half8 B1 = *reinterpret_cast<const half8*>(btab + kT1 + ob);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, B0, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, B1, acc1, 0, 0, 0);
             } else {
-                const half8 Bh = *reinterpret_cast<const half8*>(
-                    btab + ((((ks * 4 + kb) * 2 + 0) * 4) + hq) * 16);
-                const half8 Bl = *reinterpret_cast<const half8*>(
-                    btab + ((((ks * 4 + kb) * 2 + 1) * 4) + hq) * 16);
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bh, acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh, acc1, 0, 0, 0);
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bl, acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl, acc1, 0, 0, 0);
+                const int oh = ((((ks * 4 + kb) * 2 + 0) * 4) + hq) * 16;
+                const int ol = ((((ks * 4 + kb) * 2 + 1) * 4) + hq) * 16;
+                const half8 Bh0 = *reinterpret_cast<const half8*>(btab + oh);
+                const half8 Bl0 = *reinterpret_cast<const half8*>(btab + ol);
+                const half8 Bh1 = *reinterpret_cast<const half8*>(btab + kT1 + oh);
+                const half8 Bl1 = *reinterpret_cast<const half8*>(btab + kT1 + ol);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bh0, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh1, acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bl0, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl1, acc1, 0, 0, 0);
             }
         }
         if (kMirror) {
@@ -615,13 +671,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
                 acc1[i] += dpp<0x141>(acc1[i]);
             }
         }
-        const uint32_t mw = __builtin_amdgcn_readfirstlane(mwv);  // same word in every lane
+        uint32_t mw = __builtin_amdgcn_readfirstlane(mwv);  // same word in every lane
+        // G = 16: a last chunk whose second group is not quantized yet (its
+        // tokens are in the fp16 ring) has that half masked out
+        if (kG16 && tb + 32 > a.n_q) mw |= 0xFFFF0000u;
         float p[8];
         if constexpr (kSplitExp) {
             // This lane's two tokens (slots 2cq, 2cq+1 of its k-block).
             const float a0 = cq & 1 ? acc0[2] : acc0[0], b0 = cq & 1 ? acc1[2] : acc1[0];
             const float a1 = cq & 1 ? acc0[3] : acc0[1], b1 = cq & 1 ? acc1[3] : acc1[1];
-            float s0 = fmaf(cq < 2 ? a0 : b0, kAccW, beta), s1 = fmaf(cq < 2 ? a1 : b1, kAccW, beta);
+            const float bt = cq < 2 ? beta0 : beta1;  // tile 0 or 1
+            float s0 = fmaf(cq < 2 ? a0 : b0, kAccW, bt), s1 = fmaf(cq < 2 ? a1 : b1, kAccW, bt);
             if (mw) {
                 if ((mw >> own_tok) & 1u) s0 = -INFINITY;
                 if ((mw >> (own_tok + 1)) & 1u) s1 = -INFINITY;
@@ -645,7 +705,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
                     const float ah[4] = {readlane(alpha, 0), readlane(alpha, 1), readlane(alpha, 2),
                                          readlane(alpha, 3)};
                     lsum *= alpha;
-                    zc *= (lane & 3) == 0 ? ah[0] : (lane & 3) == 1 ? ah[1] : (lane & 3) == 2 ? ah[2] : ah[3];
+                    const float az = (lane & 3) == 0   ? ah[0]
+                                     : (lane & 3) == 1 ? ah[1]
+                                     : (lane & 3) == 2 ? ah[2]
+                                                       : ah[3];
+                    zc *= az;  // rows j of both value row sets belong to head j % 4
+                    zc2 *= az;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -671,8 +736,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
             float s[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                s[i] = fmaf(acc0[i], kAccW, beta);
-                s[4 + i] = fmaf(acc1[i], kAccW, beta);
+                s[i] = fmaf(acc0[i], kAccW, beta0);
+                s[4 + i] = fmaf(acc1[i], kAccW, beta1);
             }
             if (mw) {
 #pragma unroll
@@ -697,6 +762,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
                     const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
                     lsum *= alpha;
                     zc *= alpha;
+                    zc2 *= alpha;
                     float ah[4];
                     ah[0] = quad_bcast<0>(alpha);
                     if (R > 1) ah[1] = quad_bcast<1>(alpha);
@@ -721,17 +787,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
         // subnormals code * 2^(pos - 24), masked in place: every operand of
         // tile nt has the same position, so the tile's sum carries one exact
         // power-of-two weight that the epilogue removes.
-        const uint32_t vmw[8] = {vm0.x, vm0.y, vm0.z, vm0.w, vm1.x, vm1.y, vm1.z, vm1.w};
+        half8 Ahi, Alo, Ahi2, Alo2;
 #pragma unroll
-        for (int sl = 0; sl < 8; ++sl) zc += p[sl] * h2f(vmw[sl] >> 16);
-        uint32_t ahw[4], alw[4];
+        for (int vs = 0; vs < VSETS; ++vs) {
+            const u32x4 va = vs == 0 ? vm0 : vm2, vc = vs == 0 ? vm1 : vm3;
+            const uint32_t vmw[8] = {va.x, va.y, va.z, va.w, vc.x, vc.y, vc.z, vc.w};
+            float z = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ahw[i] = mul_pk(p[2 * i], vmw[2 * i], p[2 * i + 1], vmw[2 * i + 1]);
-            alw[i] = mul_pk_res(p[2 * i], vmw[2 * i], p[2 * i + 1], vmw[2 * i + 1], ahw[i]);
+            for (int sl = 0; sl < 8; ++sl) z += p[sl] * h2f(vmw[sl] >> 16);
+            (vs == 0 ? zc : zc2) += z;
+            uint32_t ahw[4], alw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ahw[i] = mul_pk(p[2 * i], vmw[2 * i], p[2 * i + 1], vmw[2 * i + 1]);
+                alw[i] = mul_pk_res(p[2 * i], vmw[2 * i], p[2 * i + 1], vmw[2 * i + 1], ahw[i]);
+            }
+            (vs == 0 ? Ahi : Ahi2) = as_half8(ahw[0], ahw[1], ahw[2], ahw[3]);
+            (vs == 0 ? Alo : Alo2) = as_half8(alw[0], alw[1], alw[2], alw[3]);
         }
-        const half8 Ahi = as_half8(ahw[0], ahw[1], ahw[2], ahw[3]);
-        const half8 Alo = as_half8(alw[0], alw[1], alw[2], alw[3]);
         const uint32_t wv[8] = {wv0.x, wv0.y, wv0.z, wv0.w, wv1.x, wv1.y, wv1.z, wv1.w};
         uint32_t wvL4[4], wvR4[4], wvO8[4];
         if (BITS == 2) moved4(wv, wvL4, wvR4, wvO8);
@@ -753,8 +826,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
                 }
             }
             const half8 Bv = as_half8(x[0], x[1], x[2], x[3]);
-            O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bv, O[nt], 0, 0, 0);
-            O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, O[nt], 0, 0, 0);
+            // tile nt's channels belong to value group nt * 16 / G, in row set
+            // (nt * 16 / G) / GPS
+            const bool set1 = VSETS == 2 && (nt * 16 / G) / GPS == 1;
+            O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(set1 ? Ahi2 : Ahi, Bv, O[nt], 0, 0, 0);
+            O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(set1 ? Alo2 : Alo, Bv, O[nt], 0, 0, 0);
         }
     };
 
@@ -802,18 +878,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     }
     lt = sum_x32(sum_x16(lt));
     const float zt = sum_x32(sum_x16(zc));
+    const float zt2 = VSETS == 2 ? sum_x32(sum_x16(zc2)) : 0.f;
     // Accumulators as they sit in the registers: tiles 0-5 in the ring, 6-7 in
     // the query table; row totals in the probability buffer.
     float* obuf = wsm;                               // [6][64][4]
     float* obuf2 = reinterpret_cast<float*>(btab);   // [2][64][4]
-    float* Zs = pbuf;                                // [16] sum_t p z^V per row
-    float* ms = Zs + 16;                             // [4]
+    float* Zs = pbuf;                                // [2][16] sum_t p z^V per row and set
+    float* ms = Zs + 32;                             // [4]
     float* ls = ms + 4;                              // [4]
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
         *reinterpret_cast<floatx4*>((nt < 6 ? obuf + nt * 256 : obuf2 + (nt - 6) * 256) + lane * 4) = O[nt];
     if (kb == 0) {
         Zs[j] = zt;
+        Zs[16 + j] = zt2;
         if (j < R) {
             ms[j] = m_run;
             ls[j] = lt;
@@ -823,7 +901,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     // Block combine of the four wavefronts.
     for (int e = threadIdx.x; e < R * D; e += 256) {
         const int h = e / D, c = e % D;
-        const int ir = h + R * (c / G);  // accumulator row (head, value group)
+        const int gv = c / G;                       // value group of channel c
+        const int ir = h + R * (gv % GPS);          // accumulator row (head, value group)
+        const int zi = 16 * (gv / GPS) + ir;        // its zero-point total (row set)
         const int nt = c / 16;
         const int src = ((nt % 6) * 64 + (c % 16) + 16 * (ir / 4)) * 4 + ir % 4;
         // weight of tile nt's code operands: 2^(pos - 24)
@@ -831,7 +911,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
         float mw[4], M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            mw[w] = s_pbuf[w][16 + h];
+            mw[w] = s_pbuf[w][32 + h];
             M = fmaxf(M, mw[w]);
         }
         float o = 0.f, l = 0.f;
@@ -841,8 +921,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
                 const float* ob = nt < 6 ? smem + w * (RG::kWave / 4)
                                          : reinterpret_cast<const float*>(s_btab[w]);
                 const float f = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
-                o += (ldexpf(ob[src], 24 - pos) + s_pbuf[w][ir]) * f;
-                l += s_pbuf[w][20 + h] * f;
+                o += (ldexpf(ob[src], 24 - pos) + s_pbuf[w][zi]) * f;
+                l += s_pbuf[w][36 + h] * f;
             }
         }
         float* rec = a.part + (((int64_t)u * a.splits + split) * R + h) * kRec;
@@ -1024,7 +1104,8 @@ void launch_decode_t(DecodeArgs a, hipEvent_t e0, hipEvent_t e1, hipStream_t s) 
 
 template <int BITS, int R>
 void dispatch_g(const DecodeArgs& a, int G, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
-    if (G == 32) launch_decode_t<BITS, R, 32>(a, e0, e1, s);
+    if (G == 16) launch_decode_t<BITS, R, 16>(a, e0, e1, s);
+    else if (G == 32) launch_decode_t<BITS, R, 32>(a, e0, e1, s);
     else if (G == 64) launch_decode_t<BITS, R, 64>(a, e0, e1, s);
     else launch_decode_t<BITS, R, 128>(a, e0, e1, s);
 }
@@ -1038,8 +1119,10 @@ void dispatch_r(const DecodeArgs& a, int R, int G, hipEvent_t e0, hipEvent_t e1,
 
 template <int BITS, int R>
 int resident_g(int G) {
-    return G == 32 ? resident_blocks<BITS, R, 32>()
-                   : G == 64 ? resident_blocks<BITS, R, 64>() : resident_blocks<BITS, R, 128>();
+    return G == 16   ? resident_blocks<BITS, R, 16>()
+           : G == 32 ? resident_blocks<BITS, R, 32>()
+           : G == 64 ? resident_blocks<BITS, R, 64>()
+                     : resident_blocks<BITS, R, 128>();
 }
 
 }  // namespace

@@ -76,6 +76,8 @@ int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& 
 int launch_topk(const float* scores, int32_t rows, int32_t T, int32_t k, int32_t w,
                 int32_t* idx, void* stream);
 int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, void* stream);
+int launch_debug_unpack(const CacheView& v, int64_t T, int64_t n_q, const kvq_debug_view& out,
+                        void* stream);
 // Launch shape of the decode kernel on the current GPU: compute units and the
 // blocks of decode_kernel<bits, r, group> resident at once (cached per GPU).
 void decode_launch_shape(int bits, int r, int group, int* cus, int* resident);

@@ -106,12 +106,20 @@ __device__ __forceinline__ const uint16_t* src_row(const uint16_t* ring, const u
                      : fresh + ((int64_t)u * n_new + (t - t_old)) * D;
 }
 
+// Counters and pool masks start at zero. With G = 16 the key and value
+// scale/zero words are zeroed too: a chunk whose second group is not yet
+// quantized is read by the decoder with that half masked out, and its
+// parameters must then be finite.
 __global__ void init_kernel(CacheView v) {
     const int64_t nc = (int64_t)v.units * 4, nm = (int64_t)v.units * v.chunks;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nc + nm;
+    const int64_t nk = v.group == 16 ? (int64_t)v.units * v.key_groups * D : 0;
+    const int64_t nv = v.group == 16 ? (int64_t)v.units * v.chunks * (D / 16) * kChunk : 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nc + nm + nk + nv;
          i += (int64_t)gridDim.x * blockDim.x) {
         if (i < nc) v.counters[i] = 0;
-        else v.mask[i - nc] = 0;
+        else if (i < nc + nm) v.mask[i - nc] = 0;
+        else if (i < nc + nm + nk) v.kmeta[i - nc - nm] = 0;
+        else v.vmeta[i - nc - nm - nk] = 0;
     }
 }
 
@@ -221,10 +229,24 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
     find_worst();
     const int32_t gend = (int32_t)g1;
     int32_t gb = (int32_t)g0, gb_end = gb, g = gb;
-    // mask words of groups [gb, ge) to memory
+    // Chunk-mask words: group g's bits start at bit g*G of the unit's mask.
+    // With G = 16 two groups share a word (the odd group in the high half).
+    auto wfirst = [&](int32_t gg) { return (int32_t)(((int64_t)gg * G) >> 5); };
+    auto wend = [&](int32_t gg) { return (int32_t)(((int64_t)gg * G + 31) >> 5); };
+    // mask words of groups [gb, ge) to memory (none for an empty range: with
+    // G = 16 and an odd gb, wend(gb) - wfirst(gb) would otherwise be 1)
     auto flush = [&](int32_t ge) {
-        for (int i = lane; i < (ge - gb) * (G / 32); i += 64)
-            v.mask[(int64_t)u * v.chunks + gb * (G / 32) + i] = mbatch[i];
+        if (ge <= gb) return;
+        for (int i = lane; i < wend(ge) - wfirst(gb); i += 64)
+            v.mask[(int64_t)u * v.chunks + wfirst(gb) + i] = mbatch[i];
+    };
+    // the group's mask bits (mword holds group word w in lane w; G = 16: lane 0)
+    auto put_mask = [&](int32_t gg, uint32_t mword) {
+        if (G >= 32) {
+            if (lane < G / 32) mbatch[wfirst(gg) - wfirst(gb) + lane] = mword;
+        } else if (lane == 0 && mword) {
+            mbatch[wfirst(gg) - wfirst(gb)] |= mword << (16 * (gg & 1));
+        }
     };
     // Lane l holds the smallest score of the staged batch's group gb + l. A
     // group can admit a token only if the pool is not full or that minimum is
@@ -236,7 +258,12 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
         if (g == gb_end) {
             flush(g);
             gb = g;
-            gb_end = g + kScanBatch / G < gend ? g + kScanBatch / G : gend;
+            // At most 64 groups (lane l holds the minimum score of group
+            // gb + l). G = 16: batches after the first start at an even group,
+            // so that no mask word is shared by two batches of this launch.
+            const int32_t bmax = kScanBatch / G < 64 ? kScanBatch / G : 64;
+            gb_end = g + bmax < gend ? g + bmax : gend;
+            if (G < 32 && gb_end < gend && (gb_end & 1)) --gb_end;
             wave_sync();  // the previous batch is no longer read
             // eight loads in flight per lane before any is stored
             const int32_t nb = (gb_end - g) * G, tb = g * G;
@@ -253,7 +280,11 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
                     if (i < nb) sc_all[i] = x[j];
                 }
             }
-            for (int i = lane; i < (gb_end - gb) * (G / 32); i += 64) mbatch[i] = 0u;
+            for (int i = lane; i < wend(gb_end) - wfirst(gb); i += 64) mbatch[i] = 0u;
+            // G = 16, odd first group: the low half of its word belongs to the
+            // group before, quantized by an earlier call
+            if (G < 32 && (gb & 1) && lane == 0)
+                mbatch[0] = v.mask[(int64_t)u * v.chunks + wfirst(gb)];
             wave_sync();
             gms = ~0ull;
             if (lane < gb_end - gb) {
@@ -289,10 +320,7 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
             cand[j] = i < G && (pc < N || sl[j] < wsc || (sl[j] == wsc && t0 + i < widx));
             any |= cand[j];
         }
-        if (!__any(any)) {  // nothing enters the pool: the common case
-            if (lane < G / 32) mbatch[(g - gb) * (G / 32) + lane] = 0u;
-            continue;
-        }
+        if (!__any(any)) continue;  // nothing enters the pool: the common case
         // Chunk mask word w of the group lives in lane w (G / 32 words), so
         // marking a token is one masked OR in a register.
         uint32_t mword = 0;
@@ -348,8 +376,7 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
                 else m1 &= ~(1ull << (bl - 64));
                 find_worst();
             }
-            if (lane < G / 32)
-                mbatch[(g - gb) * (G / 32) + lane] = mword;
+            put_mask(g, mword);
             continue;
         }
         // Pool still filling: rank of each token among the pool members and
@@ -398,8 +425,7 @@ __global__ __launch_bounds__(64) void ott_scan_kernel(CacheView v, const uint16_
             mark(i);
             find_worst();
         }
-        if (lane < G / 32)
-            mbatch[(g - gb) * (G / 32) + lane] = mword;
+        put_mask(g, mword);
     }
     flush(g);
     wave_sync();
@@ -475,14 +501,19 @@ __device__ constexpr int kPos2[8] = {3, 4, 1, 2, 5, 6, 7, 0};
 // section "Method details"). Keys are then quantized per channel over the G
 // tokens, values per token over runs of G channels (KIVI grouping; MiniKV,
 // section 4.4), and the codes written in the chunk layout of kvq.h.
+// Block x takes group g0 + gstride * (x / U). With G = 16 a 32-token chunk
+// holds two groups: the even and the odd groups of an append run as two
+// launches (gstride 2), and a 2-bit key word, which holds codes of both
+// halves of its chunk, is rewritten keeping the other half's bits.
 template <int BITS, int G>
 __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* knew,
                                                    const uint16_t* vnew, int64_t t_old,
-                                                   int32_t n_new, int64_t g0) {
+                                                   int32_t n_new, int64_t g0, int32_t gstride) {
     constexpr int NG = D / G;          // value groups per token
-    constexpr int CPG = G / kChunk;    // chunks per key group
+    constexpr bool kHalf = G == 16;    // the group is half a chunk
+    constexpr int CPG = kHalf ? 1 : G / kChunk;  // chunks the group touches
     constexpr int WPC = 128 * BITS;    // 32-bit words per chunk
-    constexpr int LG = G == 32 ? 5 : G == 64 ? 6 : 7;
+    constexpr int LG = G == 16 ? 4 : G == 32 ? 5 : G == 64 ? 6 : 7;
     const float levels = (float)((1 << BITS) - 1);
     extern __shared__ __align__(16) uint16_t smem[];
     // [G][RS] fp16 rows, overwritten by their codes. The row stride of 272
@@ -496,7 +527,8 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
     // Blocks walk the units fastest, so that the blocks resident at once
     // spread over all units (and the units' counter words).
     const int u = (int)(blockIdx.x % (uint32_t)v.units), tid = threadIdx.x;
-    const int64_t g = g0 + blockIdx.x / (uint32_t)v.units, t0 = g * G;
+    const int64_t g = g0 + (int64_t)gstride * (blockIdx.x / (uint32_t)v.units), t0 = g * G;
+    const int hf = kHalf ? (int)(g & 1) : 0;  // G = 16: which half of its chunk
     // The unit's largest value scale so far, read at device scope (past this
     // XCD's L2, where the atomics below do not land); a block only raises it
     // with an atomic when its own maximum is larger. A stale value costs one
@@ -528,6 +560,7 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
 #pragma unroll
     for (int c = 0; c < CPG; ++c) {
         mw[c] = v.pool > 0 ? v.mask[(int64_t)u * v.chunks + t0 / kChunk + c] : 0u;
+        if (kHalf) mw[c] = (mw[c] >> (16 * hf)) & 0xFFFFu;
         any |= mw[c] != 0;
     }
     __syncthreads();
@@ -617,12 +650,21 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
     }
 
     // Pack. Word w of lane l sits at (w/4)*256 + l*4 + w%4 within its chunk.
+    // LDS row of the token at position tc of chunk cc (with G = 16 only the
+    // block's own half of the chunk is in LDS).
+    auto row_of = [&](int cc, int tc) { return kHalf ? tc - 16 * hf : cc * kChunk + tc; };
     for (int e = tid; e < 2 * CPG * WPC; e += 256) {
         const bool isv = e >= CPG * WPC;
         const int r = isv ? e - CPG * WPC : e;
         const int cc = r / WPC, o = r % WPC;
         const int w = (o / 256) * 4 + (o % 4), l = (o % 256) / 4;
         const int kb = l / 16, n = l % 16;
+        // With G = 16, the half (16-token tile) a word's codes belong to: 2-bit
+        // key words hold both halves (merged below), the others one half.
+        if (kHalf && !(BITS == 2 && !isv)) {
+            const int tau = isv ? (w % 4) / 2 : w / 4;
+            if (tau != hf) continue;
+        }
         uint32_t word = 0;
         if (!isv) {
             // lane (token row n of tile tau, channel block kb): codes of channels
@@ -634,7 +676,8 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
                 const int m = w;
 #pragma unroll
                 for (int tau = 0; tau < 2; ++tau) {
-                    const int tok = cc * kChunk + 16 * tau + n;
+                    if (kHalf && tau != hf) continue;
+                    const int tok = row_of(cc, 16 * tau + n);
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) {
                         const int ch = 32 * ks + 8 * kb + 2 * m, q = kPos2[4 * tau + ks];
@@ -645,7 +688,7 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
                 }
             } else {
                 const int tau = w / 4, ks = w % 4;
-                const int tok = cc * kChunk + 16 * tau + n;
+                const int tok = row_of(cc, 16 * tau + n);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int ch = 32 * ks + 8 * kb + 2 * m;
@@ -661,8 +704,8 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
             // that every operand of one tile carries the same power-of-two weight.
             const int m = w % 4;
             const int sa = 2 * m, sb = 2 * m + 1;
-            const int ta = cc * kChunk + 16 * (sa / 4) + 4 * kb + sa % 4;
-            const int tb = cc * kChunk + 16 * (sb / 4) + 4 * kb + sb % 4;
+            const int ta = row_of(cc, 16 * (sa / 4) + 4 * kb + sa % 4);
+            const int tb = row_of(cc, 16 * (sb / 4) + 4 * kb + sb % 4);
             if (BITS == 2) {
 #pragma unroll
                 for (int nt = 0; nt < 8; ++nt) {
@@ -680,7 +723,19 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
                 }
             }
         }
-        const int64_t base = ((int64_t)u * v.chunks + g * CPG + cc) * WPC;
+        const int64_t chunk = kHalf ? g / 2 : g * CPG + cc;
+        const int64_t base = ((int64_t)u * v.chunks + chunk) * WPC;
+        if (kHalf && BITS == 2 && !isv) {
+            // keep the other half's codes: tile 1 - hf sits at the 2-bit
+            // positions kPos2[4 (1 - hf) + ks] of both 16-bit halves
+            uint32_t keep = 0;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int q = kPos2[4 * (1 - hf) + ks];
+                keep |= (3u << (2 * q)) | (3u << (16 + 2 * q));
+            }
+            word |= v.kq[base + o] & keep;
+        }
         (isv ? v.vq : v.kq)[base + o] = word;
     }
 }
@@ -700,7 +755,7 @@ __global__ __launch_bounds__(256) void ring_store_kernel(CacheView v, const uint
     reinterpret_cast<uint4*>(v.vring + dst)[part] = reinterpret_cast<const uint4*>(vnew + src)[part];
 }
 
-// Canonical view: one byte per code, [unit][token][channel].
+// Canonical view: one byte per code, [unit][token][channel] (a null output is skipped).
 __global__ __launch_bounds__(256) void unpack_kernel(CacheView v, int64_t n_q, uint8_t* kc,
                                                      uint8_t* vc) {
     const int64_t total = (int64_t)v.units * n_q * D;
@@ -729,7 +784,7 @@ __global__ __launch_bounds__(256) void unpack_kernel(CacheView v, int64_t n_q, u
                 w = 4 * tau + ks;
                 bit = 4 * m + 16 * hi;
             }
-            kc[e] = (uint8_t)((kbase[(w / 4) * 256 + l * 4 + w % 4] >> bit) & mask);
+            if (kc) kc[e] = (uint8_t)((kbase[(w / 4) * 256 + l * 4 + w % 4] >> bit) & mask);
         }
         {   // value code
             const int tau = tt / 16, r16 = tt % 16, kb = r16 / 4, s = 4 * tau + r16 % 4;
@@ -742,26 +797,66 @@ __global__ __launch_bounds__(256) void unpack_kernel(CacheView v, int64_t n_q, u
                 bit = 2 * q + 16 * (q == 7 ? 1 - hi : hi);
             }
             else { w = 4 * (nt / 4) + m; bit = 4 * (nt % 4) + 16 * hi; }
-            vc[e] = (uint8_t)((vbase[(w / 4) * 256 + l * 4 + w % 4] >> bit) & mask);
+            if (vc) vc[e] = (uint8_t)((vbase[(w / 4) * 256 + l * 4 + w % 4] >> bit) & mask);
+        }
+    }
+}
+
+// The rest of the canonical view: scale/zero words split into fp16 arrays,
+// pool marks as bytes, residual rows in token order. One thread per output
+// element of the largest array it serves.
+__global__ __launch_bounds__(256) void debug_view_kernel(CacheView v, int64_t T, int64_t n_q,
+                                                         kvq_debug_view o) {
+    const int G = v.group, NG = D / (G < D ? G : D);
+    const int64_t KG = n_q / G, nres = T - n_q;
+    const int64_t nk = (int64_t)v.units * KG * D, nv = (int64_t)v.units * n_q * NG;
+    const int64_t np = (int64_t)v.units * n_q, nr = (int64_t)v.units * nres * D;
+    const int64_t n = nk > nv ? nk : nv;
+    const int64_t m = (np > nr ? np : nr) > n ? (np > nr ? np : nr) : n;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < m;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        if (e < nk && (o.kscale || o.kzero)) {
+            const int64_t u = e / (KG * D), r = e % (KG * D);
+            const uint32_t w = v.kmeta[u * v.key_groups * D + r];
+            if (o.kscale) o.kscale[e] = (uint16_t)(w & 0xFFFF);
+            if (o.kzero) o.kzero[e] = (uint16_t)(w >> 16);
+        }
+        if (e < nv && (o.vscale || o.vzero)) {
+            const int64_t u = e / (n_q * NG), t = (e / NG) % n_q, gq = e % NG;
+            const uint32_t w =
+                v.vmeta[((u * v.chunks + t / kChunk) * NG + gq) * kChunk + t % kChunk];
+            if (o.vscale) o.vscale[e] = (uint16_t)(w & 0xFFFF);
+            if (o.vzero) o.vzero[e] = (uint16_t)(w >> 16);
+        }
+        if (e < np && o.pooled) {
+            const int64_t u = e / n_q, t = e % n_q;
+            o.pooled[e] = (uint8_t)((v.mask[u * v.chunks + t / kChunk] >> (t % kChunk)) & 1u);
+        }
+        if (e < nr && (o.kres || o.vres)) {
+            const int64_t u = e / (nres * D), i = (e / D) % nres, c = e % D;
+            const int64_t src = (u * v.ring_slots + (n_q + i) % v.ring_slots) * D + c;
+            if (o.kres) o.kres[e] = v.kring[src];
+            if (o.vres) o.vres[e] = v.vring[src];
         }
     }
 }
 
 template <int BITS, int G>
 hipError_t launch_pack_t(const CacheView& v, const uint16_t* kn, const uint16_t* vn, int64_t t_old,
-                         int32_t n_new, int64_t g0, int64_t ng, hipStream_t s) {
+                         int32_t n_new, int64_t g0, int64_t ng, hipStream_t s, int32_t gstride) {
     const size_t lds = 2 * (size_t)G * kPackRow * sizeof(uint16_t);
     // the dynamic LDS limit is raised once per process; a failure is reported
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(pack_kernel<BITS, G>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
-    // one block per (unit, group), units fastest; at most 2^22 blocks a launch
+    // one block per (unit, group), units fastest; at most 2^22 blocks a launch.
+    // ng groups g0, g0 + gstride, ...
     const int64_t step = (int64_t)1 << 22 >= v.units ? ((int64_t)1 << 22) / v.units : 1;
     for (int64_t gs = 0; gs < ng; gs += step) {
         const int64_t n = ng - gs < step ? ng - gs : step;
         hipLaunchKernelGGL((pack_kernel<BITS, G>), dim3((unsigned)(n * v.units)), dim3(256), lds, s,
-                           v, kn, vn, t_old, n_new, g0 + gs);
+                           v, kn, vn, t_old, n_new, g0 + gs * gstride, gstride);
     }
     return hipSuccess;
 }
@@ -794,8 +889,21 @@ int launch_append(const CacheView& v, const uint16_t* kn, const uint16_t* vn, in
                                n_new, g0, g1);
         }
         hipError_t e = hipErrorInvalidValue;
+        if (G == 16) {
+            // even groups, then odd groups: the two halves of a chunk are never
+            // written by one launch
+            const int64_t ge = g0 + (g0 & 1), go = g0 + 1 - (g0 & 1);
+            const int64_t ne = ge < g1 ? (g1 - ge + 1) / 2 : 0, no = go < g1 ? (g1 - go + 1) / 2 : 0;
+            e = hipSuccess;
+            for (int pass = 0; pass < 2 && e == hipSuccess; ++pass) {
+                const int64_t gp = pass == 0 ? ge : go, np = pass == 0 ? ne : no;
+                if (np == 0) continue;
+                e = v.bits == 2 ? launch_pack_t<2, 16>(v, kn, vn, t_old, n_new, gp, np, s, 2)
+                                : launch_pack_t<4, 16>(v, kn, vn, t_old, n_new, gp, np, s, 2);
+            }
+        }
 #define KVQ_PACK(B_, G_)                                                         \
-    if (v.bits == B_ && G == G_) e = launch_pack_t<B_, G_>(v, kn, vn, t_old, n_new, g0, ng, s);
+    if (v.bits == B_ && G == G_) e = launch_pack_t<B_, G_>(v, kn, vn, t_old, n_new, g0, ng, s, 1);
         KVQ_PACK(2, 32) KVQ_PACK(2, 64) KVQ_PACK(2, 128)
         KVQ_PACK(4, 32) KVQ_PACK(4, 64) KVQ_PACK(4, 128)
 #undef KVQ_PACK
@@ -817,6 +925,49 @@ int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, voi
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, v, n_q, kc, vc);
+    return (int)hipGetLastError();
+}
+
+int launch_debug_unpack(const CacheView& v, int64_t T, int64_t n_q, const kvq_debug_view& o,
+                        void* stream) {
+    (void)hipGetLastError();  // an error left by an earlier call is not this call's
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (n_q > 0 && (o.kcodes || o.vcodes)) {
+        const int64_t total = (int64_t)v.units * n_q * D;
+        int64_t blocks = (total + 255) / 256;
+        if (blocks > 65536) blocks = 65536;
+        hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, v, n_q,
+                           o.kcodes, o.vcodes);
+    }
+    {
+        const int64_t KG = n_q / v.group, NG = D / (v.group < D ? v.group : D);
+        int64_t m = (int64_t)v.units * KG * D;
+        const int64_t m2 = (int64_t)v.units * n_q * NG, m3 = (int64_t)v.units * (T - n_q) * D;
+        if (m2 > m) m = m2;
+        if (m3 > m) m = m3;
+        if (m > 0 && (o.kscale || o.kzero || o.vscale || o.vzero || o.pooled || o.kres || o.vres)) {
+            int64_t blocks = (m + 255) / 256;
+            if (blocks > 65536) blocks = 65536;
+            hipLaunchKernelGGL(debug_view_kernel, dim3((unsigned)blocks), dim3(256), 0, s, v, T, n_q,
+                               o);
+        }
+    }
+    const size_t U = (size_t)v.units, N = (size_t)v.pool, E = (size_t)v.evict_cap;
+    struct {
+        void* dst;
+        const void* src;
+        size_t bytes;
+    } cp[] = {
+        {o.counters, v.counters, U * 4 * 4},     {o.pool_idx, v.pool_idx, U * N * 4},
+        {o.pool_score, v.pool_score, U * N * 8}, {o.pool_k, v.pool_k, U * N * D * 2},
+        {o.pool_v, v.pool_v, U * N * D * 2},     {o.ev_idx, v.ev_idx, U * E * 4},
+        {o.ev_k, v.ev_k, U * E * D * 2},         {o.ev_v, v.ev_v, U * E * D * 2},
+    };
+    for (const auto& c : cp) {
+        if (!c.dst || c.bytes == 0) continue;
+        const hipError_t e = hipMemcpyAsync(c.dst, c.src, c.bytes, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return (int)e;
+    }
     return (int)hipGetLastError();
 }
 

@@ -67,7 +67,7 @@ class Workload:
         return replace(self, **kw)
 
 
-# The five workloads. cfg_id only feeds the seed tuple.
+# The workloads. cfg_id only feeds the seed tuple.
 WORKLOADS = {
     "tiny": Workload("tiny", 0, batch=1, n_q_heads=1, n_kv_heads=1, head_dim=128,
                      tokens=1024, bits=2, group=32, residual=32,
@@ -75,6 +75,11 @@ WORKLOADS = {
     "llama8b": Workload("llama8b", 1, batch=8, n_q_heads=32, n_kv_heads=8, head_dim=128,
                         tokens=8192, bits=2, group=32, residual=128,
                         outlier_channels=6, outlier_scale=15.0),
+    # MiniKV's own group size (16 values share a scale and zero point) on the
+    # same layer shape; not one of the five headline workloads
+    "llama8b_g16": Workload("llama8b_g16", 8, batch=8, n_q_heads=32, n_kv_heads=8,
+                            head_dim=128, tokens=8192, bits=2, group=16, residual=128,
+                            outlier_channels=6, outlier_scale=15.0),
     "long_b2g32": Workload("long_b2g32", 2, batch=1, n_q_heads=32, n_kv_heads=8,
                            head_dim=128, tokens=131072, bits=2, group=32, residual=128,
                            outlier_channels=6, outlier_scale=15.0),

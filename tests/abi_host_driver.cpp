@@ -51,6 +51,10 @@ int launch_unpack(const CacheView&, int64_t n_q, uint8_t*, uint8_t*, void*) {
     CHECK(n_q > 0);
     return stub();
 }
+int launch_debug_unpack(const CacheView&, int64_t T, int64_t n_q, const kvq_debug_view&, void*) {
+    CHECK(n_q <= T);
+    return stub();
+}
 void decode_launch_shape(int, int, int, int* cus, int* resident) {
     *cus = 256;
     *resident = 1024;
@@ -179,6 +183,8 @@ int main() {
                     CHECK(kvq_quantize_append(&h, kp, kp, 1, nullptr) == KVQ_EINVAL);
                     CHECK(kvq_decode_workspace(&h, 0, &ws) == KVQ_EINVAL);
                     CHECK(kvq_unpack_codes(&h, nullptr, nullptr, nullptr) == KVQ_EINVAL);
+                    kvq_debug_view dv{};
+                    CHECK(kvq_debug_unpack(&h, &dv, nullptr) == KVQ_EINVAL);
                 }
 
     // the no-allocation decode: fits, or KVQ_ESCRATCH with nothing launched

@@ -76,65 +76,58 @@ class GpuCache:
         return out
 
     def state(self) -> dict:
-        """Host copy of every arena region, in the shapes include/kvq.h documents."""
+        """Host copy of the cache's canonical view (kvq_debug_unpack), in the
+        shapes include/kvq.h documents: no knowledge of the arena layout."""
         torch.cuda.synchronize()
         h, cfg = self.h, self.cfg
-        a = self.arena.cpu().numpy()
         U, d, G = cfg.batch * cfg.n_kv_heads, cfg.head_dim, cfg.group
-        C, KG, NG, RB = h.q_cap // 32, h.q_cap // G, d // G, h.ring_slots
-        N, E = cfg.pool, cfg.evict_cap
-
-        def arr(off, dt, shape):
-            n = int(np.prod(shape)) * np.dtype(dt).itemsize
-            return a[off:off + n].view(dt).reshape(shape)
-
-        st = dict(
-            kmeta=arr(h.off_kmeta, np.float16, (U, KG, d, 2)),
-            vmeta=arr(h.off_vmeta, np.float16, (U, C, NG, 32, 2)),
-            mask=arr(h.off_mask, np.uint32, (U, C)),
-            kring=arr(h.off_kring, np.float16, (U, RB, d)),
-            vring=arr(h.off_vring, np.float16, (U, RB, d)),
-            pool_idx=arr(h.off_pool_idx, np.int32, (U, N)),
-            pool_score=arr(h.off_pool_score, np.uint64, (U, N)),
-            pool_k=arr(h.off_pool_k, np.float16, (U, N, d)),
-            pool_v=arr(h.off_pool_v, np.float16, (U, N, d)),
-            ev_idx=arr(h.off_ev_idx, np.int32, (U, E)),
-            ev_k=arr(h.off_ev_k, np.float16, (U, E, d)),
-            ev_v=arr(h.off_ev_v, np.float16, (U, E, d)),
-            counters=arr(h.off_counters, np.int32, (U, 4)),
-            T=h.tokens, n_q=h.n_quant,
+        nq, T = h.n_quant, h.tokens
+        NG, N, E = d // min(G, d), cfg.pool, cfg.evict_cap
+        dev = "cuda"
+        bufs = dict(
+            kcodes=torch.empty((U, nq, d), dtype=torch.uint8, device=dev),
+            vcodes=torch.empty((U, nq, d), dtype=torch.uint8, device=dev),
+            kscale=torch.empty((U, nq // G, d), dtype=torch.float16, device=dev),
+            kzero=torch.empty((U, nq // G, d), dtype=torch.float16, device=dev),
+            vscale=torch.empty((U, nq, NG), dtype=torch.float16, device=dev),
+            vzero=torch.empty((U, nq, NG), dtype=torch.float16, device=dev),
+            pooled=torch.empty((U, nq), dtype=torch.uint8, device=dev),
+            kres=torch.empty((U, T - nq, d), dtype=torch.float16, device=dev),
+            vres=torch.empty((U, T - nq, d), dtype=torch.float16, device=dev),
+            counters=torch.empty((U, 4), dtype=torch.int32, device=dev),
+            pool_idx=torch.empty((U, N), dtype=torch.int32, device=dev),
+            pool_score=torch.empty((U, N), dtype=torch.int64, device=dev),
+            pool_k=torch.empty((U, N, d), dtype=torch.float16, device=dev),
+            pool_v=torch.empty((U, N, d), dtype=torch.float16, device=dev),
+            ev_idx=torch.empty((U, E), dtype=torch.int32, device=dev),
+            ev_k=torch.empty((U, E, d), dtype=torch.float16, device=dev),
+            ev_v=torch.empty((U, E, d), dtype=torch.float16, device=dev),
         )
-        nq = h.n_quant
-        kc = torch.empty((U, nq, d), dtype=torch.uint8, device="cuda")
-        vc = torch.empty((U, nq, d), dtype=torch.uint8, device="cuda")
-        if nq:
-            abi.unpack_codes(h, kc, vc)
-            torch.cuda.synchronize()
-        st["kcodes"], st["vcodes"] = kc.cpu().numpy(), vc.cpu().numpy()
+        abi.debug_unpack(h, **{k: (v if v.numel() else None) for k, v in bufs.items()})
+        torch.cuda.synchronize()
+        st = {k: v.cpu().numpy() for k, v in bufs.items()}
+        st["pool_score"] = st["pool_score"].view(np.uint64)
+        st["T"], st["n_q"] = T, nq
         return st
 
 
 def check_unit_state(st: dict, u: int, uc: O.UnitCache) -> None:
     """Bit-exact comparison of unit u of a GPU cache with the oracle's unit."""
     p = uc.p
-    G, d = p.group, p.head_dim
     nq, T = st["n_q"], st["T"]
     assert nq == uc.n_q and T == uc.T
     np.testing.assert_array_equal(st["kcodes"][u], uc.kcodes)
     np.testing.assert_array_equal(st["vcodes"][u], uc.vcodes)
-    km = st["kmeta"][u, : nq // G]
-    assert np.array_equal(km[..., 0].view(np.uint16), uc.kscale.view(np.uint16))
-    assert np.array_equal(km[..., 1], uc.kzero)
-    vm = st["vmeta"][u, : nq // 32].transpose(0, 2, 1, 3).reshape(-1, d // p.gv, 2)[:nq]
-    assert np.array_equal(vm[..., 0].view(np.uint16), uc.vscale.view(np.uint16))
-    assert np.array_equal(vm[..., 1], uc.vzero)
+    assert np.array_equal(st["kscale"][u].view(np.uint16), uc.kscale.view(np.uint16))
+    assert np.array_equal(st["kzero"][u], uc.kzero)  # as values: +0 and -0 agree
+    assert np.array_equal(st["vscale"][u].view(np.uint16), uc.vscale.view(np.uint16))
+    assert np.array_equal(st["vzero"][u], uc.vzero)
     # counters[3]: largest value scale of the unit, as fp16 bits
     vmax = int(uc.vscale.view(np.uint16).max()) if nq else 0
     assert int(st["counters"][u, 3]) == vmax, (int(st["counters"][u, 3]), vmax)
-    RB = st["kring"].shape[1]
-    for t in range(nq, T):
-        assert np.array_equal(st["kring"][u, t % RB].view(np.uint16), uc.k16[t].view(np.uint16))
-        assert np.array_equal(st["vring"][u, t % RB].view(np.uint16), uc.v16[t].view(np.uint16))
+    assert np.array_equal(st["kres"][u].view(np.uint16), uc.k16[nq:T].view(np.uint16))
+    assert np.array_equal(st["vres"][u].view(np.uint16), uc.v16[nq:T].view(np.uint16))
+    np.testing.assert_array_equal(st["pooled"][u].astype(bool), uc.replaced)
     tr = uc.tracer
     if p.pool > 0:
         pc, ec, frozen = (int(x) for x in st["counters"][u, :3])
@@ -150,8 +143,6 @@ def check_unit_state(st: dict, u: int, uc: O.UnitCache) -> None:
         for e, m in enumerate(tr.evicted):
             assert np.array_equal(st["ev_k"][u, e].view(np.uint16), m.k.view(np.uint16))
             assert np.array_equal(st["ev_v"][u, e].view(np.uint16), m.v.view(np.uint16))
-        bits = np.unpackbits(st["mask"][u, : nq // 32].view(np.uint8), bitorder="little")
-        np.testing.assert_array_equal(bits.astype(bool), uc.replaced)
 
 
 def check_outputs(out: np.ndarray, ref: np.ndarray, what: str = "") -> None:

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 @pytest.mark.parametrize("bits,group,per_token", [(2, 32, 96), (2, 128, 72), (4, 32, 160),
-                                                  (4, 128, 136)])
+                                                  (4, 128, 136), (2, 16, 128), (4, 16, 192)])
 def test_quantized_bytes_per_token_follow_b_plus_32_over_g(bits, group, per_token):
     # "KV cache quantization and eviction", section "The bottleneck in
     # numbers": b + 32/g bits per element with an fp16 scale and zero per

@@ -71,7 +71,7 @@ def check_decode(gc, w, orc, q, acc_in=None, tag=None):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("bits", [2, 4])
-@pytest.mark.parametrize("group", [32, 64, 128])
+@pytest.mark.parametrize("group", [16, 32, 64, 128])
 def test_append_state_bit_exact_ragged(bits, group):
     w = small(bits=bits, group=group, residual=40, tokens=801)
     splits = [1, 37, 300, 5, 64, 394]
@@ -143,8 +143,9 @@ def test_append_tiny_workload_bit_exact():
     H.check_unit_state(gc.state(), 0, orc[(0, 0)])
 
 
-def test_append_token_by_token_matches_oracle():
-    w = small(tokens=200, residual=16, batch=1, hkv=2)
+@pytest.mark.parametrize("group", [16, 32])
+def test_append_token_by_token_matches_oracle(group):
+    w = small(tokens=200, residual=16, batch=1, hkv=2, group=group)
     gc, K, V = run_appends(w, [100] + [1] * 100)
     orc = H.oracle_units(w, all_units(w), K, V, [100] + [1] * 100)
     st = gc.state()
@@ -181,7 +182,7 @@ def test_ott_pool_bit_exact(E):
 
 
 @pytest.mark.parametrize("bits,group,dup", [(2, 64, False), (4, 128, False), (2, 32, True),
-                                            (4, 64, True)])
+                                            (4, 64, True), (2, 16, False), (4, 16, True)])
 def test_ott_pool_group_sizes_and_score_ties(bits, group, dup):
     """OTT pools at G = 64 and 128 (the scan stages 2048 tokens, 32 or 16
     groups, at a time), and keys duplicated in pairs so that equal scores,
@@ -263,13 +264,61 @@ def test_decode_residual_window_near_the_fp16_row_limit():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("bits,group,r", [(2, 32, 4), (4, 32, 4), (2, 64, 4), (2, 128, 4),
-                                          (4, 128, 4), (2, 32, 1), (4, 64, 2), (2, 128, 1)])
+                                          (4, 128, 4), (2, 32, 1), (4, 64, 2), (2, 128, 1),
+                                          (2, 16, 4), (4, 16, 4), (2, 16, 2), (4, 16, 1)])
 def test_decode_small_all_units(bits, group, r):
     w = small(bits=bits, group=group, r=r, residual=50, tokens=1234)
     gc, K, V = run_appends(w, [1000, 234])
     orc = H.oracle_units(w, all_units(w), K, V, [1000, 234])
     acc0 = np.random.default_rng(5).random((w.batch, w.n_kv_heads, w.tokens)).astype(np.float32)
     check_decode(gc, w, orc, synth.queries(w), acc_in=acc0)
+
+
+@pytest.mark.parametrize("bits,group,r", [(4, 16, 4), (2, 16, 2), (4, 16, 1), (4, 32, 4)])
+def test_decode_several_chunks_per_wavefront(bits, group, r):
+    """128 units of 3000 tokens: few splits per unit, so every wavefront walks
+    several chunks and the running maximum moves after the first one (the
+    lazy rescale of outputs, normaliser and zero-point totals)."""
+    w = small(bits=bits, group=group, r=r, residual=64, tokens=3000, batch=32, hkv=4)
+    gc, K, V = run_appends(w, [2500, 500])
+    units = [(0, 0), (13, 2), (31, 3)]
+    orc = H.oracle_units(w, units, K, V, [2500, 500])
+    st = gc.state()
+    for (bb, hh) in units:
+        H.check_unit_state(st, bb * w.n_kv_heads + hh, orc[(bb, hh)])
+    check_decode(gc, w, orc, synth.queries(w),
+                 acc_in=np.zeros((w.batch, w.n_kv_heads, w.tokens), np.float32),
+                 tag=f"multi_b{bits}g{group}r{r}")
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_g16_half_chunks_through_appends_and_decodes(bits):
+    """G = 16: a 32-token chunk holds two key groups. Appends that stop after
+    the first group of a chunk leave a half-quantized last chunk (its second
+    half still in the fp16 ring); the next append quantizes the second half
+    next to the first. State and attention (with H2O scores) are checked at
+    every stop, half chunks included, on every unit, with OTT pools on."""
+    w = small(bits=bits, group=16, residual=40, tokens=420, pool=3, evict_cap=6,
+              inject_frac=0.03, outlier_channels=6, outlier_scale=15.0)
+    K, V = synth.all_kv(w)
+    gc = H.GpuCache(w)
+    splits = [40, 16, 15, 1, 17, 31, 16, 1, 47, 97, 2, 14, 16, 107]
+    assert sum(splits) == w.tokens
+    s0, half_seen = 0, 0
+    q = synth.queries(w)
+    for n in splits:
+        gc.append(K[:, :, s0:s0 + n], V[:, :, s0:s0 + n])
+        s0 += n
+        wt = w.with_(tokens=s0)
+        orc = H.oracle_units(wt, all_units(wt), K[:, :, :s0], V[:, :, :s0])
+        st = gc.state()
+        for u, key in enumerate(all_units(w)):
+            H.check_unit_state(st, u, orc[key])
+        half_seen += gc.h.n_quant % 32 == 16
+        gc.w = wt
+        check_decode(gc, wt, orc, q, acc_in=np.zeros((w.batch, w.n_kv_heads, s0), np.float32),
+                     tag=f"g16_b{bits}")
+    assert half_seen >= 3
 
 
 @pytest.mark.parametrize("T", [1, 7, 40, 72])
@@ -312,7 +361,8 @@ def test_snapshot_and_resume_match_unsplit_run():
     q = synth.queries(w)
     assert torch.equal(a.decode(q), b.decode(q))
     sa, sb = a.state(), b.state()
-    for key in ("kcodes", "vcodes", "kmeta", "vmeta", "mask", "counters", "pool_idx", "ev_idx"):
+    for key in ("kcodes", "vcodes", "kscale", "kzero", "vscale", "vzero", "pooled", "kres",
+                "vres", "counters", "pool_idx", "ev_idx"):
         assert np.array_equal(sa[key].view(np.uint8), sb[key].view(np.uint8)), key
 
 
@@ -394,6 +444,19 @@ def test_workload_llama8b_sampled_units():
     for (b, h) in units:
         H.check_unit_state(st, b * w.n_kv_heads + h, orc[(b, h)])
     check_decode(gc, w, orc, synth.queries(w))
+
+
+def test_workload_llama8b_g16_sampled_units():
+    """The Llama-3-8B layer with MiniKV's group size 16 (two key groups per chunk)."""
+    w = W["llama8b_g16"]
+    gc, K, V = run_appends(w, [w.tokens])
+    units = [(0, 0), (5, 2), (7, 7)]
+    orc = H.oracle_units(w, units, K, V)
+    st = gc.state()
+    for (b, h) in units:
+        H.check_unit_state(st, b * w.n_kv_heads + h, orc[(b, h)])
+    check_decode(gc, w, orc, synth.queries(w),
+                 acc_in=np.zeros((w.batch, w.n_kv_heads, w.tokens), np.float32))
 
 
 @pytest.mark.parametrize("name", ["long_b2g32", "long_b2g128", "long_b4g32", "long_b4g128"])
