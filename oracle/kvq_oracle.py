@@ -25,6 +25,8 @@ Page citations name the page title and the section they come from:
           Large Language Models"
 [POFE]    "KV cache quantization and eviction: FP8, INT4, H2O and attention
           sinks" (pofe.ai)
+[KVTC]    "KV Cache Transform Coding for Compact Storage in LLM Inference"
+          (arXiv 2511.01815)
 
 Readings taken where the pages leave a step open:
 
@@ -65,6 +67,13 @@ R11 Heavy-hitter selection keeps the k highest scores in [0, T - w) ordered by
     returns ascending indices. Index-descending tie order is what repeated
     first-occurrence argmin eviction leaves behind ([POFE] "Minimal
     implementation"; [MiniKV] Algorithm 1, heavy-hitter selection).
+R12 Attention sinks: the first S tokens of every unit stay in fp16 for good.
+    They are never quantized, never traced by OTT and never evicted; the
+    residual rule and the quantization groups apply to the tokens after them
+    ([POFE] "Attention sinks and StreamingLLM": the key-value states of the
+    first few tokens, four in StreamingLLM, are kept; "Failure modes": keep
+    sinks pinned; [KVTC] section 2, Preliminaries: s = 4 sink tokens are
+    left uncompressed).
 """
 from __future__ import annotations
 
@@ -247,6 +256,7 @@ class CacheParams:
     pool: int = 0
     evict_cap: int = 32
     head_dim: int = 128
+    sinks: int = 0  # S: the first S tokens stay fp16 (R12)
 
     @property
     def gv(self) -> int:
@@ -254,7 +264,8 @@ class CacheParams:
 
 
 class UnitCache:
-    """Keys/values of one unit: quantized groups, fp16 residual window, pools."""
+    """Keys/values of one unit: fp16 sinks, quantized groups, fp16 residual
+    window, pools. Tokens S .. S + n_q - 1 are the quantized ones (R12)."""
 
     def __init__(self, p: CacheParams):
         self.p = p
@@ -316,13 +327,14 @@ class UnitCache:
         return sum(x.shape[0] for x in self._k16)
 
     def append(self, k16: np.ndarray, v16: np.ndarray) -> None:
-        """Append fp16 rows; quantize every group that leaves the residual window."""
+        """Append fp16 rows; quantize every group that leaves the residual window
+        (the residual rule counts the tokens after the S sinks, R12)."""
         self._k16.append(np.asarray(k16, dtype=np.float16))
         self._v16.append(np.asarray(v16, dtype=np.float16))
-        G = self.p.group
+        G, S = self.p.group, self.p.sinks
         T = self.T
-        while self.n_q < n_quantized(T, self.p.residual, G):
-            self._quantize_group(self.n_q)
+        while self.n_q < n_quantized(max(0, T - S), self.p.residual, G):
+            self._quantize_group(S + self.n_q)
             self.n_q += G
 
     def _quantize_group(self, t0: int) -> None:
@@ -349,17 +361,17 @@ class UnitCache:
 
     def dequantized_kv(self):
         """K_hat, V_hat [T][d] in fp64, each cached token exactly once (R8)."""
-        G, gv, d = self.p.group, self.p.gv, self.p.head_dim
+        G, gv, d, S = self.p.group, self.p.gv, self.p.head_dim, self.p.sinks
         n_q = self.n_q
-        K = self.k16.astype(np.float64)  # residual rows stay as stored (fp16)
+        K = self.k16.astype(np.float64)  # sink and residual rows stay as stored (fp16)
         V = self.v16.astype(np.float64)
         if n_q:
             ks = np.repeat(self.kscale, G, axis=0)
             kz = np.repeat(self.kzero, G, axis=0)
-            K[:n_q] = dequantize(self.kcodes, ks, kz)
+            K[S:S + n_q] = dequantize(self.kcodes, ks, kz)
             vs = np.repeat(self.vscale, gv, axis=1)
             vz = np.repeat(self.vzero, gv, axis=1)
-            V[:n_q] = dequantize(self.vcodes, vs, vz)
+            V[S:S + n_q] = dequantize(self.vcodes, vs, vz)
         for m in self.tracer.pool + self.tracer.evicted:
             K[m.idx] = m.k.astype(np.float64)
             V[m.idx] = m.v.astype(np.float64)

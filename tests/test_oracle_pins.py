@@ -370,6 +370,53 @@ def test_dequantized_rows_rebuilt_token_by_token(bits, G, N, E):
 
 
 # ---------------------------------------------------------------------------
+# Attention sinks ("KV cache quantization and eviction", Attention sinks and
+# StreamingLLM; "KV Cache Transform Coding", section 2): the first S tokens
+# stay fp16 and everything else behaves as a cache of the remaining tokens.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S,G,N", [(4, 32, 0), (4, 16, 3), (1, 64, 2), (37, 32, 3)])
+def test_sinks_are_fp16_and_the_rest_is_a_cache_of_the_later_tokens(S, G, N):
+    rng = np.random.default_rng([41, S, G, N])
+    T, R = 400, 40
+    k = rng.standard_normal((T, 128)).astype(np.float32)
+    k[:, [5, 60]] *= 15
+    k[rng.choice(T, 30, replace=False)] *= 0.02
+    k16 = k.astype(np.float16)
+    v16 = rng.standard_normal((T, 128)).astype(np.float16)
+    a = O.UnitCache(O.CacheParams(bits=2, group=G, residual=R, pool=N, evict_cap=5, sinks=S))
+    for i0 in range(0, T, 53):  # ragged appends that cross the sink boundary
+        a.append(k16[i0:i0 + 53], v16[i0:i0 + 53])
+    b = O.UnitCache(O.CacheParams(bits=2, group=G, residual=R, pool=N, evict_cap=5))
+    b.append(k16[S:], v16[S:])
+    # the residual rule counts the tokens after the sinks
+    assert a.n_q == b.n_q == max(0, (T - S - R) // G * G)
+    assert R <= T - S - a.n_q < R + G
+    for f in ["kcodes", "kscale", "kzero", "vcodes", "vscale", "vzero", "replaced"]:
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f
+    assert a.pool_indices() == [i + S for i in b.pool_indices()]
+    assert a.evicted_indices() == [i + S for i in b.evicted_indices()]
+    Ka, Va = a.dequantized_kv()
+    Kb, Vb = b.dequantized_kv()
+    assert np.array_equal(Ka[:S], k16[:S].astype(np.float64))
+    assert np.array_equal(Va[:S], v16[:S].astype(np.float64))
+    assert np.array_equal(Ka[S:], Kb) and np.array_equal(Va[S:], Vb)
+    # no sink is ever a pool member
+    assert all(m.idx >= S for m in a.tracer.pool + a.tracer.evicted)
+
+
+def test_sinks_covering_everything_is_plain_fp16_attention():
+    rng = np.random.default_rng(43)
+    k = rng.standard_normal((20, 128)).astype(np.float16)
+    v = rng.standard_normal((20, 128)).astype(np.float16)
+    u = O.UnitCache(O.CacheParams(bits=2, group=16, residual=0, sinks=32))
+    u.append(k, v)
+    assert u.n_q == 0
+    K, V = u.dequantized_kv()
+    assert np.array_equal(K, k.astype(np.float64)) and np.array_equal(V, v.astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
 # OTT: score, mean replacement, pool competition ("Accurate KV Cache
 # Quantization with Outlier Tokens Tracing", Method details and appendix E).
 # ---------------------------------------------------------------------------
