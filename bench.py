@@ -207,6 +207,7 @@ ROWS = {
     "decode_h2o_minikv": ("minikv", "a8-a10: fused decode + merge with H2O accumulation"),
     "topk_minikv": ("minikv", "a11: heavy-hitter top-k + recent window"),
     "decode_llama8b_g16": ("llama8b_g16", "a8-a10: fused decode + merge at group size 16"),
+    "decode_llama8b_sinks": ("llama8b_sinks", "a8-a10 with 4 attention sinks in the fp16 partition"),
     "decode_long_b2g32": ("long_b2g32", "a8-a10: fused decode + merge, split-K over context"),
     "decode_long_b2g128": ("long_b2g128", "a8-a10: fused decode + merge, split-K over context"),
     "decode_long_b4g32": ("long_b4g32", "a8-a10: fused decode + merge, split-K over context"),
@@ -242,7 +243,8 @@ def rows_main(args):
     def cfg_of(w):
         return abi.make_config(bits=w.bits, group=w.group, residual=w.residual, pool=w.pool,
                                evict_cap=w.evict_cap, head_dim=w.head_dim, n_q_heads=w.n_q_heads,
-                               n_kv_heads=w.n_kv_heads, batch=w.batch, max_tokens=w.tokens)
+                               n_kv_heads=w.n_kv_heads, batch=w.batch, max_tokens=w.tokens,
+                               sinks=w.sinks)
 
     def timed(fn, reps):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -333,7 +335,7 @@ def rows_main(args):
             us = timed(call, args.reps)
             nbytes = BM.decode_step_bytes(units=U, gqa=w.gqa, head_dim=d, tokens=w.tokens,
                                           bits=w.bits, group=w.group, residual=w.residual,
-                                          h2o=w.h2o).total
+                                          h2o=w.h2o, sinks=w.sinks).total
             emit(name, w, us, nbytes, {"kernels": ["decode_kernel", "merge_kernel"]})
         else:  # top-k over the accumulated scores of a decode call
             for rep in reps:

@@ -29,6 +29,11 @@
  *    that share it ("H2O: Heavy-Hitter Oracle for Efficient Generative
  *    Inference of Large Language Models", accumulated attention scores;
  *    "KV cache quantization and eviction", section "Heavy hitters").
+ *  - Attention sinks: the first S tokens of every unit stay fp16 and are never
+ *    quantized, traced or evicted; the residual rule and the groups apply to
+ *    the tokens after them ("KV cache quantization and eviction", section
+ *    "Attention sinks and StreamingLLM"; "KV Cache Transform Coding for
+ *    Compact Storage in LLM Inference", section 2, s = 4 sinks).
  *  - Heavy-hitter selection: the k highest scores outside a recent window of
  *    w tokens, plus that window (MiniKV, Algorithm 1; "KV cache quantization
  *    and eviction", section "Minimal implementation").
@@ -97,6 +102,10 @@ const char* kvq_status_string(kvq_status status);
  *   n_q_heads   Hq, n_kv_heads Hkv: Hq / Hkv = r in {1, 2, 4}
  *   batch       B >= 1
  *   max_tokens  capacity in tokens per unit, in [1, 2^24]
+ *   sinks       S in [0, 64]: attention sinks kept fp16 (4 in StreamingLLM)
+ * With S > 0 the token indices of the quantized partition, the ring and the
+ * pools are those of the whole sequence (tokens S, S + 1, ...); the residual
+ * rule becomes n_q = max(0, floor((T - S - R) / G) * G).
  */
 typedef struct kvq_config {
     int32_t bits;
@@ -109,6 +118,7 @@ typedef struct kvq_config {
     int32_t n_kv_heads;
     int32_t batch;
     int32_t max_tokens;
+    int32_t sinks;
 } kvq_config;
 
 /*
@@ -138,6 +148,7 @@ typedef struct kvq_config {
  *             largest value scale held by the unit (fp16 bits; 0 while
  *             nothing is quantized), which bounds the decoder's lazy rescale
  *   scores    uint64 [U][Qcap] scratch for key L1 norms during an append
+ *   sink_k    fp16 [U][S][d] the attention-sink rows; sink_v likewise
  * Slots of pool_idx / ev_idx beyond the counters are unspecified.
  *
  * Packed code layout. Codes of 32 consecutive quantized tokens form a chunk
@@ -160,6 +171,7 @@ typedef struct kvq_cache {
     uint64_t off_kq, off_vq, off_kmeta, off_vmeta, off_mask, off_kring, off_vring;
     uint64_t off_pool_idx, off_pool_score, off_pool_k, off_pool_v;
     uint64_t off_ev_idx, off_ev_k, off_ev_v, off_counters, off_scores;
+    uint64_t off_sink_k, off_sink_v;
 } kvq_cache;
 
 /* Bytes of device memory a cache with this configuration needs (host only).
@@ -302,8 +314,11 @@ kvq_status kvq_unpack_codes(const kvq_cache* h, uint8_t* d_kcodes, uint8_t* d_vc
  *   vscale, vzero   fp16 [U][n_q][NG]: value scale and zero point per token
  *                   and channel group
  *   pooled          uint8 [U][n_q]: 1 when the token was admitted to the
- *                   outlier pool (its quantized slot holds the group mean)
- *   kres, vres      fp16 [U][T - n_q][d]: the fp16 residual rows, token order
+ *                   outlier pool (its quantized slot holds the group mean);
+ *                   the quantized tokens are S .. S + n_q - 1
+ * Pool and extra-pool indices are indices in the whole sequence.
+ *   kres, vres      fp16 [U][T - S - n_q][d]: the fp16 residual rows, token order
+ *   ksink, vsink    fp16 [U][min(T, S)][d]: the attention-sink rows
  *   counters        int32 [U][4]: pool count, extra-pool count, frozen flag,
  *                   largest value scale (fp16 bits)
  *   pool_idx        int32 [U][N], pool_score uint64 [U][N] (key L1 norm in
@@ -329,6 +344,8 @@ typedef struct kvq_debug_view {
     int32_t* ev_idx;
     uint16_t* ev_k;
     uint16_t* ev_v;
+    uint16_t* ksink;
+    uint16_t* vsink;
 } kvq_debug_view;
 
 /* Fill the non-NULL fields of *view (host struct of device pointers) on

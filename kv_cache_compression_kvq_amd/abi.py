@@ -34,7 +34,7 @@ EXPORTS = ("kvq_status_string", "kvq_cache_bytes", "kvq_cache_init", "kvq_quanti
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "bits", "group", "residual", "pool", "evict_cap", "head_dim",
-        "n_q_heads", "n_kv_heads", "batch", "max_tokens")]
+        "n_q_heads", "n_kv_heads", "batch", "max_tokens", "sinks")]
 
 
 class Cache(ctypes.Structure):
@@ -44,14 +44,15 @@ class Cache(ctypes.Structure):
         (n, ctypes.c_uint64) for n in (
             "off_kq", "off_vq", "off_kmeta", "off_vmeta", "off_mask", "off_kring", "off_vring",
             "off_pool_idx", "off_pool_score", "off_pool_k", "off_pool_v", "off_ev_idx",
-            "off_ev_k", "off_ev_v", "off_counters", "off_scores")]
+            "off_ev_k", "off_ev_v", "off_counters", "off_scores", "off_sink_k", "off_sink_v")]
 
 
 class DebugView(ctypes.Structure):
     """kvq_debug_view: device pointers (0 = skip) of the canonical cache view."""
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "kcodes", "vcodes", "kscale", "kzero", "vscale", "vzero", "pooled", "kres", "vres",
-        "counters", "pool_idx", "pool_score", "pool_k", "pool_v", "ev_idx", "ev_k", "ev_v")]
+        "counters", "pool_idx", "pool_score", "pool_k", "pool_v", "ev_idx", "ev_k", "ev_v",
+        "ksink", "vsink")]
 
 
 class KvqError(RuntimeError):
@@ -126,9 +127,9 @@ def status_string(status: int) -> str:
 
 
 def make_config(*, bits, group, residual, pool=0, evict_cap=32, head_dim=128, n_q_heads,
-                n_kv_heads, batch, max_tokens) -> Config:
+                n_kv_heads, batch, max_tokens, sinks=0) -> Config:
     return Config(bits, group, residual, pool, evict_cap, head_dim, n_q_heads, n_kv_heads,
-                  batch, max_tokens)
+                  batch, max_tokens, sinks)
 
 
 def cache_bytes(cfg: Config) -> int:

@@ -47,17 +47,18 @@ class StepBytes:
 
 def decode_step_bytes(*, units: int, gqa: int, head_dim: int, tokens: int, bits: int,
                       group: int, residual: int, pool_tokens: int = 0,
-                      h2o: bool = False) -> StepBytes:
+                      h2o: bool = False, sinks: int = 0) -> StepBytes:
     """Algorithmic bytes of one decode-attention step over all units.
 
     Per unit: n_q*(d*b/4 + 4d/G + 4d/Gv) + n_res*4d + pool_tokens*(4d + 4)
-    + r*d*2 (query) + r*d*4 (output) + [H2O] 8*T. Scratch (split partials,
-    logits) is implementation traffic and is not counted. ``pool_tokens`` is
-    the total over all units.
+    + r*d*2 (query) + r*d*4 (output) + [H2O] 8*T, with n_q counted after the
+    S attention sinks and n_res = T - n_q (sinks and residual window, fp16).
+    Scratch (split partials, logits) is implementation traffic and is not
+    counted. ``pool_tokens`` is the total over all units.
     """
     d, G = head_dim, group
     gv = min(G, d)
-    nq = n_quantized(tokens, residual, G)
+    nq = n_quantized(max(0, tokens - sinks), residual, G)
     nres = tokens - nq
     quant = units * nq * (d * bits // 4 + 4 * d // G + 4 * d // gv)
     resid = units * nres * 4 * d

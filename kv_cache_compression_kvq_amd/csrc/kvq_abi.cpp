@@ -28,7 +28,7 @@ int64_t n_quantized(int64_t T, int64_t R, int64_t G) {
 kvq_status check_config(const kvq_config* c) {
     if (!c) return KVQ_EINVAL;
     if (c->residual < 0 || c->pool < 0 || c->evict_cap < 0 || c->batch < 1 ||
-        c->n_kv_heads < 1 || c->n_q_heads < 1 || c->max_tokens < 1)
+        c->n_kv_heads < 1 || c->n_q_heads < 1 || c->max_tokens < 1 || c->sinks < 0)
         return KVQ_EINVAL;
     if (c->n_q_heads % c->n_kv_heads != 0) return KVQ_EINVAL;
     const int r = c->n_q_heads / c->n_kv_heads;
@@ -37,15 +37,18 @@ kvq_status check_config(const kvq_config* c) {
         return KVQ_EUNSUPPORTED;
     if (c->head_dim != kHeadDim) return KVQ_EUNSUPPORTED;
     if (r != 1 && r != 2 && r != 4) return KVQ_EUNSUPPORTED;
-    if (c->pool > kMaxPool || c->evict_cap > kMaxEvict) return KVQ_EUNSUPPORTED;
+    if (c->pool > kMaxPool || c->evict_cap > kMaxEvict || c->sinks > kMaxSinks)
+        return KVQ_EUNSUPPORTED;
     if (c->max_tokens > kMaxTokens) return KVQ_EUNSUPPORTED;
-    if ((int64_t)c->residual + c->group + c->pool + c->evict_cap > kMaxFp16Rows)
+    if ((int64_t)c->residual + c->group + c->pool + c->evict_cap + c->sinks > kMaxFp16Rows)
         return KVQ_EUNSUPPORTED;
     return KVQ_OK;
 }
 
+constexpr int kRegions = 18;
+
 struct Layout {
-    uint64_t off[16];
+    uint64_t off[kRegions];
     uint64_t total;
     int64_t q_cap, chunks, ring;
 };
@@ -55,11 +58,13 @@ Layout layout_of(const kvq_config* c) {
     const uint64_t U = (uint64_t)c->batch * c->n_kv_heads;
     const uint64_t d = kHeadDim;
     const uint64_t G = c->group, b = c->bits, N = c->pool, E = c->evict_cap;
-    L.q_cap = n_quantized(c->max_tokens, c->residual, c->group);
+    L.q_cap = n_quantized(c->max_tokens > c->sinks ? c->max_tokens - c->sinks : 0, c->residual,
+                          c->group);
     L.chunks = (L.q_cap + kChunk - 1) / kChunk;  // G = 16: the last chunk may be half used
     L.ring = (int64_t)c->residual + c->group;
     const uint64_t C = L.chunks, NG = d / G;
-    const uint64_t sizes[16] = {
+    const uint64_t S = c->sinks;
+    const uint64_t sizes[kRegions] = {
         U * C * 128 * b * 4,          // kq
         U * C * 128 * b * 4,          // vq
         U * key_groups_of(G, C) * d * 4,  // kmeta
@@ -76,9 +81,11 @@ Layout layout_of(const kvq_config* c) {
         U * E * d * 2,                // ev_v
         U * 4 * 4,                    // counters
         N > 0 ? U * L.q_cap * 8 : 0,  // scores
+        U * S * d * 2,                // sink_k
+        U * S * d * 2,                // sink_v
     };
     uint64_t o = 0;
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < kRegions; ++i) {
         L.off[i] = o;
         o = align_up(o + sizes[i]);
     }
@@ -86,10 +93,15 @@ Layout layout_of(const kvq_config* c) {
     return L;
 }
 
+// Quantized tokens after T appends: the residual rule over the tokens after
+// the S attention sinks.
+int64_t n_quant_of(const kvq_config& c, int64_t T) {
+    return n_quantized(T > c.sinks ? T - c.sinks : 0, c.residual, c.group);
+}
+
 bool valid_handle(const kvq_cache* h) {
     return h && check_config(&h->cfg) == KVQ_OK && h->arena != 0 && h->tokens >= 0 &&
-           h->n_quant == n_quantized(h->tokens, h->cfg.residual, h->cfg.group) &&
-           h->tokens <= h->cfg.max_tokens;
+           h->n_quant == n_quant_of(h->cfg, h->tokens) && h->tokens <= h->cfg.max_tokens;
 }
 
 kvq_status launch_status(int e) { return e == 0 ? KVQ_OK : KVQ_ELAUNCH; }
@@ -120,6 +132,9 @@ CacheView view_of(const kvq_cache* h) {
     v.ev_v = reinterpret_cast<uint16_t*>(a + h->off_ev_v);
     v.counters = reinterpret_cast<int32_t*>(a + h->off_counters);
     v.scores = reinterpret_cast<uint64_t*>(a + h->off_scores);
+    v.sink_k = reinterpret_cast<uint16_t*>(a + h->off_sink_k);
+    v.sink_v = reinterpret_cast<uint16_t*>(a + h->off_sink_v);
+    v.sinks = h->cfg.sinks;
     v.bits = h->cfg.bits;
     v.group = h->cfg.group;
     v.residual = h->cfg.residual;
@@ -149,6 +164,7 @@ DecodePlan plan_decode(const kvq_cache* h, bool want_scores) {
     decode_launch_shape(h->cfg.bits, (int)r, h->cfg.group, &cus, &resident);
     if (cus < 1) cus = 1;
     if (resident < 1) resident = 1;
+    // sinks + ring + full pools (tokens - n_quant counts the sinks and the ring)
     const int64_t fp16_rows = (h->tokens - h->n_quant) +
                               (h->cfg.pool > 0 ? h->cfg.pool + h->cfg.evict_cap : 0);
     const int64_t t_min = fp16_rows > 0 ? (fp16_rows + 63) / 64 : 1;
@@ -222,11 +238,12 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* d_arena, size_t bytes, kv
     c.arena_bytes = bytes;
     c.q_cap = L.q_cap;
     c.ring_slots = L.ring;
-    uint64_t* offs[16] = {&c.off_kq, &c.off_vq, &c.off_kmeta, &c.off_vmeta, &c.off_mask,
-                          &c.off_kring, &c.off_vring, &c.off_pool_idx, &c.off_pool_score,
-                          &c.off_pool_k, &c.off_pool_v, &c.off_ev_idx, &c.off_ev_k,
-                          &c.off_ev_v, &c.off_counters, &c.off_scores};
-    for (int i = 0; i < 16; ++i) *offs[i] = L.off[i];
+    uint64_t* offs[kRegions] = {&c.off_kq, &c.off_vq, &c.off_kmeta, &c.off_vmeta, &c.off_mask,
+                                &c.off_kring, &c.off_vring, &c.off_pool_idx, &c.off_pool_score,
+                                &c.off_pool_k, &c.off_pool_v, &c.off_ev_idx, &c.off_ev_k,
+                                &c.off_ev_v, &c.off_counters, &c.off_scores, &c.off_sink_k,
+                                &c.off_sink_v};
+    for (int i = 0; i < kRegions; ++i) *offs[i] = L.off[i];
     st = launch_status(launch_init(view_of(&c), stream));
     if (st == KVQ_OK) *h = c;
     return st;
@@ -239,7 +256,7 @@ kvq_status kvq_quantize_append(kvq_cache* h, const void* d_k, const void* d_v, i
     if (!d_k || !d_v) return KVQ_EINVAL;
     const int64_t t_new = h->tokens + n_new;
     if (t_new > h->cfg.max_tokens) return KVQ_ECAPACITY;
-    const int64_t nq_new = n_quantized(t_new, h->cfg.residual, h->cfg.group);
+    const int64_t nq_new = n_quant_of(h->cfg, t_new);
     kvq_status st = launch_status(launch_append(
         view_of(h), static_cast<const uint16_t*>(d_k), static_cast<const uint16_t*>(d_v),
         h->tokens, n_new, h->n_quant, nq_new, stream));
@@ -298,20 +315,23 @@ kvq_status kvq_decode_step_timed(kvq_cache* h, const void* d_k, const void* d_v,
     if (t_new > h->cfg.max_tokens) return KVQ_ECAPACITY;
     kvq_cache next = *h;
     next.tokens = t_new;
-    next.n_quant = n_quantized(t_new, h->cfg.residual, h->cfg.group);
+    next.n_quant = n_quant_of(h->cfg, t_new);
     const DecodePlan p = plan_decode(&next, d_acc != nullptr);
     if (ws_bytes < p.ws_bytes) return KVQ_EWORKSPACE;
     const uint16_t* kn = static_cast<const uint16_t*>(d_k);
     const uint16_t* vn = static_cast<const uint16_t*>(d_v);
     const CacheView v = view_of(h);
+    // The new token stays in the fp16 ring unless it is an attention sink or its
+    // own group was just quantized; in the ring case the attention kernel stores
+    // it, otherwise the append does.
+    const int64_t S = h->cfg.sinks;
+    const bool in_ring = t_old >= S && t_old - S >= next.n_quant;
     kvq_status st = launch_status(
-        launch_append(v, kn, vn, t_old, 1, h->n_quant, next.n_quant, stream, false));
+        launch_append(v, kn, vn, t_old, 1, h->n_quant, next.n_quant, stream, !in_ring));
     if (st != KVQ_OK) {
         invalidate(h);
         return st;
     }
-    // the new token stays fp16 unless its own group was just quantized
-    const bool in_ring = t_old >= next.n_quant;
     st = launch_status(launch_decode(v, t_new, next.n_quant, p, static_cast<const uint16_t*>(d_q),
                                      d_out, d_acc, d_ws, ev_start, ev_stop, stream,
                                      in_ring ? kn : nullptr, in_ring ? vn : nullptr));

@@ -128,6 +128,8 @@ struct DecodeArgs {
     const uint16_t* ev_k;
     const uint16_t* ev_v;
     const int32_t* counters;
+    const uint16_t* sink_k;  // attention sinks [U][sink_cap][d]
+    const uint16_t* sink_v;
     const uint16_t* k_new;  // decode step: the newest token's rows [U][d] (else null)
     const uint16_t* v_new;
     const uint16_t* q;
@@ -138,6 +140,8 @@ struct DecodeArgs {
     int64_t T, n_q, chunks, key_groups;
     int32_t units, n_kv_heads, ring_slots, splits_q, splits, fp16_tiles, pool, evict_cap;
     int32_t tile_rows;  // rows per fp16-partition tile (<= 64)
+    int32_t sink_cap;   // S: sinks per unit; the quantized tokens are S .. S + n_q - 1
+    int32_t sink_rows;  // min(T, S): sink rows present
     float qscale;  // log2(e) / sqrt(d)
 };
 
@@ -259,40 +263,51 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
     const uint32_t* qsrc =
         reinterpret_cast<const uint32_t*>(a.q + ((int64_t)b * a.n_kv_heads * R + hk * R) * D);
     for (int e = tid; e < R * D / 2; e += 256) qh[e] = qsrc[e];
-    const int64_t nres = a.T - a.n_q;
+    // Rows of the partition: the attention sinks, the residual ring tokens
+    // (sequence index S + n_q onwards), the pool, the extra pool.
+    const int64_t ns = a.sink_rows;
+    const int64_t nres = a.T - ns - a.n_q;
     const int pc = a.pool > 0 ? a.counters[(int64_t)u * 4] : 0;
     const int ec = a.pool > 0 ? a.counters[(int64_t)u * 4 + 1] : 0;
-    const int64_t ntot = nres + pc + ec;
+    const int64_t ntot = ns + nres + pc + ec;
     const int N = a.pool, E = a.evict_cap, RB = a.ring_slots;
     const int64_t base = (int64_t)tile * a.tile_rows;
     const int cnt = (int)(ntot - base < 0 ? 0 : ntot - base < a.tile_rows ? ntot - base : a.tile_rows);
-    // Row i of the tile: ring slot (n_q + base + i) % RB, or a pool / extra-pool row.
-    const int64_t slot0 = (a.n_q + base) % RB;
-    auto row_off = [&](int i, bool& in_ring) -> int64_t {
+    // Row i of the tile: kind 0 sink, 1 ring (slot (n_q + ring row) % RB),
+    // 2 pool, 3 extra pool; returns the row's element offset in its array.
+    auto row_off = [&](int i, int& kind) -> int64_t {
         const int64_t li = base + i;
-        in_ring = li < nres;
-        if (li < nres) {
-            int64_t sl = slot0 + i;
-            if (sl >= RB) sl -= RB;
+        if (li < ns) {
+            kind = 0;
+            return ((int64_t)u * a.sink_cap + li) * D;
+        }
+        if (li < ns + nres) {
+            kind = 1;
+            const uint32_t sl = (uint32_t)(a.n_q + (li - ns)) % (uint32_t)RB;
             return ((int64_t)u * RB + sl) * D;
         }
-        if (li < nres + pc) return ((int64_t)u * N + (li - nres)) * D;
-        return -1 - ((int64_t)u * E + (li - nres - pc)) * D;  // extra pool: encoded negative
+        if (li < ns + nres + pc) {
+            kind = 2;
+            return ((int64_t)u * N + (li - ns - nres)) * D;
+        }
+        kind = 3;
+        return ((int64_t)u * E + (li - ns - nres - pc)) * D;
     };
-    // With a decode step's input, the newest token (ring row nres - 1) is read
+    // With a decode step's input, the newest token (the last ring row) is read
     // from it; its ring slot is written below.
     const bool new_row = a.k_new != nullptr;
-    auto row_ptr = [&](int i, const uint16_t* ring, const uint16_t* pool, const uint16_t* ev,
-                       const uint16_t* nw) -> const uint16_t* {
-        bool in_ring;
-        const int64_t o = row_off(i, in_ring);
-        if (in_ring) return new_row && base + i == nres - 1 ? nw + (int64_t)u * D : ring + o;
-        return o >= 0 ? pool + o : ev + (-1 - o);
+    const int64_t last_ring = ns + nres - 1;
+    auto row_ptr = [&](int i, const uint16_t* sink, const uint16_t* ring, const uint16_t* pool,
+                       const uint16_t* ev, const uint16_t* nw) -> const uint16_t* {
+        int kind;
+        const int64_t o = row_off(i, kind);
+        if (kind == 1) return new_row && base + i == last_ring ? nw + (int64_t)u * D : ring + o;
+        return (kind == 0 ? sink : kind == 2 ? pool : ev) + o;
     };
-    if (new_row && h == 0 && lane < 32 && base <= nres - 1 && nres - 1 < base + cnt) {
-        // store the step's token into ring slot (T - 1) % RB: lanes 0-15 the
-        // key, 16-31 the value, 16 bytes each
-        const int64_t dst = ((int64_t)u * RB + (a.T - 1) % RB) * D;
+    if (new_row && h == 0 && lane < 32 && base <= last_ring && last_ring < base + cnt) {
+        // store the step's token (sequence index T - 1, ring token T - 1 - S)
+        // into its ring slot: lanes 0-15 the key, 16-31 the value, 16 bytes each
+        const int64_t dst = ((int64_t)u * RB + (a.T - 1 - a.sink_cap) % RB) * D;
         const int part = lane & 15;
         const uint16_t* src = (lane < 16 ? a.k_new : a.v_new) + (int64_t)u * D;
         uint16_t* ring = const_cast<uint16_t*>(lane < 16 ? a.kring : a.vring);
@@ -302,8 +317,8 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
     if (h >= R) return;
     float s = -INFINITY;
     if (lane < cnt) {
-        const uint4* kr =
-            reinterpret_cast<const uint4*>(row_ptr(lane, a.kring, a.pool_k, a.ev_k, a.k_new));
+        const uint4* kr = reinterpret_cast<const uint4*>(
+            row_ptr(lane, a.sink_k, a.kring, a.pool_k, a.ev_k, a.k_new));
         uint4 x[16];
 #pragma unroll
         for (int c8 = 0; c8 < 16; ++c8) x[c8] = kr[c8];
@@ -323,10 +338,13 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
         }
         s = acc * a.qscale;
         if (a.logits) {
+            // sequence index of the row's token
             const int64_t li = base + lane;
-            const int64_t t = li < nres ? a.n_q + li
-                              : li < nres + pc ? a.pool_idx[(int64_t)u * N + (li - nres)]
-                                               : a.ev_idx[(int64_t)u * E + (li - nres - pc)];
+            const int64_t t = li < ns ? li
+                              : li < ns + nres ? a.sink_cap + a.n_q + (li - ns)
+                              : li < ns + nres + pc
+                                  ? a.sink_cap + a.pool_idx[(int64_t)u * N + (li - ns - nres)]
+                                  : a.sink_cap + a.ev_idx[(int64_t)u * E + (li - ns - nres - pc)];
             a.logits[((int64_t)u * R + h) * a.T + t] = s;
         }
     }
@@ -348,7 +366,7 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
             const int i = i0 + 4 * r + rp;
             pv[r] = ph[i < 64 ? i : 63];
             w[r] = i < cnt ? reinterpret_cast<const uint4*>(
-                                 row_ptr(i, a.vring, a.pool_v, a.ev_v, a.v_new))[cb]
+                                 row_ptr(i, a.sink_v, a.vring, a.pool_v, a.ev_v, a.v_new))[cb]
                            : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
@@ -687,7 +705,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
                 if ((mw >> (own_tok + 1)) & 1u) s1 = -INFINITY;
             }
             if (a.logits) {
-                float* lg = a.logits + ((int64_t)u * R + hq) * a.T + tb + own_tok;
+                float* lg = a.logits + ((int64_t)u * R + hq) * a.T + a.sink_cap + tb + own_tok;
                 if (s0 != -INFINITY) lg[0] = s0;
                 if (s1 != -INFINITY) lg[1] = s1;
             }
@@ -747,7 +765,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
                 }
             }
             if (a.logits && j < R) {
-                float* lg = a.logits + ((int64_t)u * R + j) * a.T + tb + 4 * kb;
+                float* lg = a.logits + ((int64_t)u * R + j) * a.T + a.sink_cap + tb + 4 * kb;
 #pragma unroll
                 for (int sl = 0; sl < 8; ++sl)
                     if (s[sl] != -INFINITY) lg[16 * (sl / 4) + sl % 4] = s[sl];
@@ -1185,6 +1203,10 @@ int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& 
     a.ev_k = v.ev_k;
     a.ev_v = v.ev_v;
     a.counters = v.counters;
+    a.sink_k = v.sink_k;
+    a.sink_v = v.sink_v;
+    a.sink_cap = v.sinks;
+    a.sink_rows = (int32_t)(T < v.sinks ? T : v.sinks);
     a.k_new = k_new;
     a.v_new = v_new;
     a.q = q;

@@ -12,6 +12,7 @@ namespace kvq {
 constexpr int kHeadDim = 128;      // d
 constexpr int kChunk = 32;         // tokens per packed chunk
 constexpr int kMaxPool = 64;       // N limit
+constexpr int kMaxSinks = 64;      // S limit
 constexpr int kMaxEvict = 1024;    // E limit
 constexpr int kMaxFp16Rows = 2048; // R + G + N + E limit
 constexpr int kMaxFp16Tiles = 56;   // fp16-partition tiles per unit (each at most 64 rows)
@@ -36,6 +37,9 @@ struct CacheView {
     uint16_t* ev_v;
     int32_t* counters;
     uint64_t* scores;
+    uint16_t* sink_k;    // [U][S][d]
+    uint16_t* sink_v;
+    int32_t sinks;       // S
     int32_t bits, group, residual, pool, evict_cap;
     int32_t n_q_heads, n_kv_heads, batch;
     int32_t units;       // U = batch * n_kv_heads
@@ -62,8 +66,11 @@ DecodePlan plan_decode(const kvq_cache* h, bool want_scores);
 
 // Launchers (return hipError_t as int; 0 = success).
 int launch_init(const CacheView& v, void* stream);
-// ring_store = false leaves the appended tokens that stay fp16 out of the
-// ring (the decode step stores its one token itself).
+// t_old: tokens held before the call (whole sequence, sinks included); the
+// first max(0, S - t_old) appended rows go to the sink region. nq_old / nq_new
+// count quantized tokens (those after the sinks). ring_store = false leaves
+// the appended tokens that stay in the ring out of it (the decode step stores
+// its one token itself).
 int launch_append(const CacheView& v, const uint16_t* k_new, const uint16_t* v_new,
                   int64_t t_old, int32_t n_new, int64_t nq_old, int64_t nq_new, void* stream,
                   bool ring_store = true);

@@ -740,6 +740,23 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
     }
 }
 
+// Copy the appended rows that are attention sinks (tokens t_old .. t_old +
+// n_sink - 1 of the sequence, the first rows of each unit's input) to the
+// sink region.
+__global__ __launch_bounds__(256) void sink_store_kernel(CacheView v, const uint16_t* knew,
+                                                         const uint16_t* vnew, int64_t t_old,
+                                                         int32_t n_new, int32_t n_sink) {
+    const int u = blockIdx.y;
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= (int64_t)n_sink * 16) return;
+    const int64_t i = e / 16;
+    const int part = (int)(e % 16);
+    const int64_t src = ((int64_t)u * n_new + i) * D;
+    const int64_t dst = ((int64_t)u * v.sinks + t_old + i) * D;
+    reinterpret_cast<uint4*>(v.sink_k + dst)[part] = reinterpret_cast<const uint4*>(knew + src)[part];
+    reinterpret_cast<uint4*>(v.sink_v + dst)[part] = reinterpret_cast<const uint4*>(vnew + src)[part];
+}
+
 // Copy this call's tokens that stay fp16 into the residual ring (slot t % RB).
 __global__ __launch_bounds__(256) void ring_store_kernel(CacheView v, const uint16_t* knew,
                                                          const uint16_t* vnew, int64_t t_old,
@@ -808,7 +825,7 @@ __global__ __launch_bounds__(256) void unpack_kernel(CacheView v, int64_t n_q, u
 __global__ __launch_bounds__(256) void debug_view_kernel(CacheView v, int64_t T, int64_t n_q,
                                                          kvq_debug_view o) {
     const int G = v.group, NG = D / (G < D ? G : D);
-    const int64_t KG = n_q / G, nres = T - n_q;
+    const int64_t KG = n_q / G, nres = T - (T < v.sinks ? T : v.sinks) - n_q;
     const int64_t nk = (int64_t)v.units * KG * D, nv = (int64_t)v.units * n_q * NG;
     const int64_t np = (int64_t)v.units * n_q, nr = (int64_t)v.units * nres * D;
     const int64_t n = nk > nv ? nk : nv;
@@ -834,10 +851,32 @@ __global__ __launch_bounds__(256) void debug_view_kernel(CacheView v, int64_t T,
         }
         if (e < nr && (o.kres || o.vres)) {
             const int64_t u = e / (nres * D), i = (e / D) % nres, c = e % D;
-            const int64_t src = (u * v.ring_slots + (n_q + i) % v.ring_slots) * D + c;
+            const int64_t src = (u * v.ring_slots + (n_q + i) % v.ring_slots) * D + c;  // ring token n_q + i
             if (o.kres) o.kres[e] = v.kring[src];
             if (o.vres) o.vres[e] = v.vring[src];
         }
+    }
+}
+
+// Pool and extra-pool indices of the canonical view: sequence indices, i.e.
+// the stored index (counted from the first token after the sinks) plus S.
+__global__ __launch_bounds__(256) void index_view_kernel(int32_t* dst, const int32_t* src,
+                                                         int64_t n, int32_t add) {
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+         e += (int64_t)gridDim.x * blockDim.x)
+        dst[e] = src[e] + add;
+}
+
+// Sink rows of the canonical view: [U][rows][d] from the sink region [U][S][d].
+__global__ __launch_bounds__(256) void sink_view_kernel(CacheView v, int32_t rows, uint16_t* kd,
+                                                        uint16_t* vd) {
+    const int64_t n = (int64_t)v.units * rows * D;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t u = e / ((int64_t)rows * D), r = e % ((int64_t)rows * D);
+        const int64_t src = u * v.sinks * D + r;
+        if (kd) kd[e] = v.sink_k[src];
+        if (vd) vd[e] = v.sink_v[src];
     }
 }
 
@@ -873,10 +912,23 @@ int launch_init(const CacheView& v, void* stream) {
     return (int)hipGetLastError();
 }
 
-int launch_append(const CacheView& v, const uint16_t* kn, const uint16_t* vn, int64_t t_old,
+int launch_append(const CacheView& v, const uint16_t* kn, const uint16_t* vn, int64_t t_seq,
                   int32_t n_new, int64_t nq_old, int64_t nq_new, void* stream, bool ring_store) {
     (void)hipGetLastError();  // an error left by an earlier call is not this call's
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // Attention sinks first: rows of tokens below S go to the sink region.
+    const int64_t S = v.sinks;
+    const int32_t n_sink = t_seq < S ? (int32_t)(S - t_seq < n_new ? S - t_seq : n_new) : 0;
+    if (n_sink > 0) {
+        hipLaunchKernelGGL(sink_store_kernel, dim3((unsigned)((n_sink * 16 + 255) / 256), v.units),
+                           dim3(256), 0, s, v, kn, vn, t_seq, n_new, n_sink);
+        if (n_sink == n_new) return (int)hipGetLastError();
+    }
+    // The rest is a cache of the tokens after the sinks, in its own token
+    // numbering tau = t - S. Its rows sit n_sink rows into each unit's input
+    // (unit stride n_new): with n_sink > 0 that cache was empty, and the
+    // kernels address fresh row tau of the input at tau - t_old = tau + n_sink.
+    const int64_t t_old = (t_seq > S ? t_seq - S : 0) - n_sink;
     const int G = v.group;
     const int64_t g0 = nq_old / G, g1 = nq_new / G, ng = g1 - g0;
     if (ng > 0) {
@@ -941,8 +993,9 @@ int launch_debug_unpack(const CacheView& v, int64_t T, int64_t n_q, const kvq_de
     }
     {
         const int64_t KG = n_q / v.group, NG = D / (v.group < D ? v.group : D);
+        const int64_t ns = T < v.sinks ? T : v.sinks;
         int64_t m = (int64_t)v.units * KG * D;
-        const int64_t m2 = (int64_t)v.units * n_q * NG, m3 = (int64_t)v.units * (T - n_q) * D;
+        const int64_t m2 = (int64_t)v.units * n_q * NG, m3 = (int64_t)v.units * (T - ns - n_q) * D;
         if (m2 > m) m = m2;
         if (m3 > m) m = m3;
         if (m > 0 && (o.kscale || o.kzero || o.vscale || o.vzero || o.pooled || o.kres || o.vres)) {
@@ -953,14 +1006,23 @@ int launch_debug_unpack(const CacheView& v, int64_t T, int64_t n_q, const kvq_de
         }
     }
     const size_t U = (size_t)v.units, N = (size_t)v.pool, E = (size_t)v.evict_cap;
+    const int32_t ns = (int32_t)(T < v.sinks ? T : v.sinks);
+    if (ns > 0 && (o.ksink || o.vsink))
+        hipLaunchKernelGGL(sink_view_kernel, dim3((unsigned)((U * ns * D + 255) / 256)), dim3(256),
+                           0, s, v, ns, o.ksink, o.vsink);
+    if (o.pool_idx && U * N)
+        hipLaunchKernelGGL(index_view_kernel, dim3((unsigned)((U * N + 255) / 256)), dim3(256), 0,
+                           s, o.pool_idx, v.pool_idx, (int64_t)(U * N), v.sinks);
+    if (o.ev_idx && U * E)
+        hipLaunchKernelGGL(index_view_kernel, dim3((unsigned)((U * E + 255) / 256)), dim3(256), 0,
+                           s, o.ev_idx, v.ev_idx, (int64_t)(U * E), v.sinks);
     struct {
         void* dst;
         const void* src;
         size_t bytes;
     } cp[] = {
-        {o.counters, v.counters, U * 4 * 4},     {o.pool_idx, v.pool_idx, U * N * 4},
-        {o.pool_score, v.pool_score, U * N * 8}, {o.pool_k, v.pool_k, U * N * D * 2},
-        {o.pool_v, v.pool_v, U * N * D * 2},     {o.ev_idx, v.ev_idx, U * E * 4},
+        {o.counters, v.counters, U * 4 * 4},     {o.pool_score, v.pool_score, U * N * 8},
+        {o.pool_k, v.pool_k, U * N * D * 2},     {o.pool_v, v.pool_v, U * N * D * 2},
         {o.ev_k, v.ev_k, U * E * D * 2},         {o.ev_v, v.ev_v, U * E * D * 2},
     };
     for (const auto& c : cp) {

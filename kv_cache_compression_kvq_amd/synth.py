@@ -41,6 +41,7 @@ class Workload:
     residual: int          # R
     pool: int = 0          # N, outlier-pool capacity
     evict_cap: int = 32    # E, extra pool for displaced pool members
+    sinks: int = 0         # S, attention sinks kept in fp16
     outlier_channels: int = 0
     outlier_scale: float = 1.0
     key_dist: str = "normal"     # "normal" or "zipf"
@@ -80,6 +81,10 @@ WORKLOADS = {
     "llama8b_g16": Workload("llama8b_g16", 8, batch=8, n_q_heads=32, n_kv_heads=8,
                             head_dim=128, tokens=8192, bits=2, group=16, residual=128,
                             outlier_channels=6, outlier_scale=15.0),
+    # the same layer with four attention sinks kept in fp16
+    "llama8b_sinks": Workload("llama8b_sinks", 9, batch=8, n_q_heads=32, n_kv_heads=8,
+                              head_dim=128, tokens=8192, bits=2, group=32, residual=128,
+                              outlier_channels=6, outlier_scale=15.0, sinks=4),
     "long_b2g32": Workload("long_b2g32", 2, batch=1, n_q_heads=32, n_kv_heads=8,
                            head_dim=128, tokens=131072, bits=2, group=32, residual=128,
                            outlier_channels=6, outlier_scale=15.0),

@@ -116,8 +116,10 @@ int main() {
     for (int bits : {2, 4})
         for (int g : groups)
             for (int r : {1, 2, 4})
-                for (int pool : {0, 3}) {
+                for (int pool : {0, 3})
+                for (int sinks : {0, 5}) {
                     kvq_config k = cfg(bits, g, 40, pool, 8, 2 * r, 2, 3, 1000);
+                    k.sinks = sinks;
                     size_t bytes = 0;
                     const kvq_status st = kvq_cache_bytes(&k, &bytes);
                     CHECK(st == KVQ_OK || st == KVQ_EUNSUPPORTED);
@@ -133,7 +135,8 @@ int main() {
                                              h.off_mask, h.off_kring, h.off_vring,
                                              h.off_pool_idx, h.off_pool_score, h.off_pool_k,
                                              h.off_pool_v, h.off_ev_idx, h.off_ev_k, h.off_ev_v,
-                                             h.off_counters, h.off_scores};
+                                             h.off_counters, h.off_scores, h.off_sink_k,
+                                             h.off_sink_v};
                     for (size_t i = 0; i < sizeof(offs) / sizeof(offs[0]); ++i) {
                         CHECK(offs[i] % 256 == 0 && offs[i] <= bytes);
                         if (i) CHECK(offs[i] >= offs[i - 1]);
@@ -147,7 +150,7 @@ int main() {
                         CHECK(kvq_quantize_append(&h, kp, kp, s, nullptr) == KVQ_OK);
                         T += s;
                         CHECK(h.tokens == T);
-                        const int64_t nq = T > 40 ? (T - 40) / g * g : 0;
+                        const int64_t nq = T - sinks > 40 ? (T - sinks - 40) / g * g : 0;
                         CHECK(h.n_quant == nq);
                     }
                     CHECK(kvq_quantize_append(&h, kp, kp, -1, nullptr) == KVQ_EINVAL);
@@ -170,7 +173,7 @@ int main() {
                     size_t ws3 = 0;
                     kvq_cache next = h;
                     next.tokens += 1;
-                    next.n_quant = next.tokens > 40 ? (next.tokens - 40) / g * g : 0;
+                    next.n_quant = next.tokens - sinks > 40 ? (next.tokens - sinks - 40) / g * g : 0;
                     CHECK(kvq_decode_workspace(&next, 1, &ws3) == KVQ_OK);
                     float acc = 0.f;
                     CHECK(kvq_decode_step(&h, kp, kp, kp, &out, &acc, wsp, ws3, nullptr) ==

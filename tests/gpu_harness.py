@@ -41,12 +41,12 @@ def config_of(w: synth.Workload, max_tokens: int | None = None) -> abi.Config:
     return abi.make_config(bits=w.bits, group=w.group, residual=w.residual, pool=w.pool,
                            evict_cap=w.evict_cap, head_dim=w.head_dim, n_q_heads=w.n_q_heads,
                            n_kv_heads=w.n_kv_heads, batch=w.batch,
-                           max_tokens=max_tokens or w.tokens)
+                           max_tokens=max_tokens or w.tokens, sinks=w.sinks)
 
 
 def params_of(w: synth.Workload) -> O.CacheParams:
     return O.CacheParams(bits=w.bits, group=w.group, residual=w.residual, pool=w.pool,
-                         evict_cap=w.evict_cap, head_dim=w.head_dim)
+                         evict_cap=w.evict_cap, head_dim=w.head_dim, sinks=w.sinks)
 
 
 class GpuCache:
@@ -83,6 +83,7 @@ class GpuCache:
         U, d, G = cfg.batch * cfg.n_kv_heads, cfg.head_dim, cfg.group
         nq, T = h.n_quant, h.tokens
         NG, N, E = d // min(G, d), cfg.pool, cfg.evict_cap
+        ns = min(T, cfg.sinks)
         dev = "cuda"
         bufs = dict(
             kcodes=torch.empty((U, nq, d), dtype=torch.uint8, device=dev),
@@ -92,8 +93,10 @@ class GpuCache:
             vscale=torch.empty((U, nq, NG), dtype=torch.float16, device=dev),
             vzero=torch.empty((U, nq, NG), dtype=torch.float16, device=dev),
             pooled=torch.empty((U, nq), dtype=torch.uint8, device=dev),
-            kres=torch.empty((U, T - nq, d), dtype=torch.float16, device=dev),
-            vres=torch.empty((U, T - nq, d), dtype=torch.float16, device=dev),
+            kres=torch.empty((U, T - ns - nq, d), dtype=torch.float16, device=dev),
+            vres=torch.empty((U, T - ns - nq, d), dtype=torch.float16, device=dev),
+            ksink=torch.empty((U, ns, d), dtype=torch.float16, device=dev),
+            vsink=torch.empty((U, ns, d), dtype=torch.float16, device=dev),
             counters=torch.empty((U, 4), dtype=torch.int32, device=dev),
             pool_idx=torch.empty((U, N), dtype=torch.int32, device=dev),
             pool_score=torch.empty((U, N), dtype=torch.int64, device=dev),
@@ -125,8 +128,11 @@ def check_unit_state(st: dict, u: int, uc: O.UnitCache) -> None:
     # counters[3]: largest value scale of the unit, as fp16 bits
     vmax = int(uc.vscale.view(np.uint16).max()) if nq else 0
     assert int(st["counters"][u, 3]) == vmax, (int(st["counters"][u, 3]), vmax)
-    assert np.array_equal(st["kres"][u].view(np.uint16), uc.k16[nq:T].view(np.uint16))
-    assert np.array_equal(st["vres"][u].view(np.uint16), uc.v16[nq:T].view(np.uint16))
+    S = min(T, p.sinks)
+    assert np.array_equal(st["ksink"][u].view(np.uint16), uc.k16[:S].view(np.uint16))
+    assert np.array_equal(st["vsink"][u].view(np.uint16), uc.v16[:S].view(np.uint16))
+    assert np.array_equal(st["kres"][u].view(np.uint16), uc.k16[S + nq:T].view(np.uint16))
+    assert np.array_equal(st["vres"][u].view(np.uint16), uc.v16[S + nq:T].view(np.uint16))
     np.testing.assert_array_equal(st["pooled"][u].astype(bool), uc.replaced)
     tr = uc.tracer
     if p.pool > 0:

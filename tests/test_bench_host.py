@@ -42,3 +42,12 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_decode_step_bytes_with_sinks():
+    # the S sinks are fp16 rows; the residual rule runs on the tokens after them
+    s = BM.decode_step_bytes(units=1, gqa=4, head_dim=128, tokens=8192, bits=2, group=32,
+                             residual=128, sinks=4)
+    nq = BM.n_quantized(8192 - 4, 128, 32)
+    assert nq == 8032
+    assert s.quantized == nq * 96 and s.residual == (8192 - nq) * 512

@@ -321,6 +321,32 @@ def test_g16_half_chunks_through_appends_and_decodes(bits):
     assert half_seen >= 3
 
 
+@pytest.mark.parametrize("bits,group,pool", [(2, 32, 3), (4, 16, 3), (2, 16, 0), (4, 64, 0)])
+def test_sinks_state_and_decode(bits, group, pool):
+    """Four attention sinks ("KV cache quantization and eviction", Attention
+    sinks and StreamingLLM): appends that end before, at and after the sink
+    boundary, then groups behind the sinks, with OTT pools when pool > 0;
+    state bit-exact and attention with H2O scores after every append."""
+    w = small(bits=bits, group=group, residual=40, tokens=500, pool=pool, evict_cap=6,
+              inject_frac=0.03 if pool else 0.0, sinks=4)
+    K, V = synth.all_kv(w)
+    gc = H.GpuCache(w)
+    q = synth.queries(w)
+    s0 = 0
+    for n in [1, 2, 1, 3, 40, 16, 1, 200, 17, 219]:
+        gc.append(K[:, :, s0:s0 + n], V[:, :, s0:s0 + n])
+        s0 += n
+        wt = w.with_(tokens=s0)
+        orc = H.oracle_units(wt, all_units(wt), K[:, :, :s0], V[:, :, :s0])
+        st = gc.state()
+        for u, key in enumerate(all_units(w)):
+            H.check_unit_state(st, u, orc[key])
+        gc.w = wt
+        check_decode(gc, wt, orc, q, acc_in=np.zeros((w.batch, w.n_kv_heads, s0), np.float32),
+                     tag=f"sinks_b{bits}g{group}")
+    assert s0 == w.tokens
+
+
 @pytest.mark.parametrize("T", [1, 7, 40, 72])
 def test_decode_short_caches(T):
     w = small(tokens=T, residual=40, batch=1, hkv=2)

@@ -8,7 +8,8 @@ kvq_quantize_append(1) followed by kvq_decode_attention on a twin cache (which
 the oracle parity tests cover); the last step is also checked against the
 oracle. The cases cross key-group boundaries (the step that quantizes a group
 first), run a zero-width residual window (the new token is quantized at once
-and never enters the ring), the OTT pool, b = 4 with G = 128, and r = 1, 2.
+and never enters the ring), the OTT pool, b = 4 with G = 128, r = 1, 2, and
+attention sinks filled by the first steps of an empty cache.
 """
 import numpy as np
 import pytest
@@ -53,6 +54,11 @@ CASES = {
     "ott_pool": (W["ott"].with_(name="step_ott", batch=2, tokens=240, evict_cap=4), 40, False),
     "r1": (_small(n_q_heads=2, tokens=100), 30, True),
     "r2": (_small(n_q_heads=4, bits=4, tokens=100), 30, False),
+    # from an empty cache: the first 4 steps fill the attention sinks, then the
+    # ring, then G = 16 groups are quantized behind them
+    "sinks_from_empty": (_small(tokens=0, sinks=4, group=16, residual=16), 60, True),
+    "sinks_ott_pool": (W["ott"].with_(name="step_sinks_ott", batch=2, tokens=200, evict_cap=4,
+                                      sinks=4), 40, True),
 }
 
 
