@@ -74,6 +74,19 @@ R12 Attention sinks: the first S tokens of every unit stay in fp16 for good.
     first few tokens, four in StreamingLLM, are kept; "Failure modes": keep
     sinks pinned; [KVTC] section 2, Preliminaries: s = 4 sink tokens are
     left uncompressed).
+R13 H2O eviction during decoding: after a step, while the cache holds more
+    than B live tokens, the live token with the lowest accumulated score
+    outside the w most recent ones (and not a sink) is evicted, one per step
+    and per KV head ([H2O] greedy eviction; [POFE] "Heavy hitters" and
+    h2o_evict in "Minimal implementation"). Ties go to the older token (a
+    first-occurrence argmin); a NaN score ranks below every number (R11b).
+    An evicted token drops out of attention and gets no further score; in the
+    compressed cache its codes stay in place (its group's scale is shared).
+R14 Pyramid budgets ([MiniKV] section 4.2): with average budget x and depth
+    d over L layers the budgets fall linearly from 2x - x/d at the lowest
+    layer to x/d at the highest (the page calls the layer with x/d
+    "bottom-most" but also allocates more cache to lower layers, as the
+    pyramid policy it follows does; the latter is taken), rounded down.
 """
 from __future__ import annotations
 
@@ -389,15 +402,18 @@ class UnitCache:
 # [OTT] "Method details", decoding stage) and H2O scores.
 # --------------------------------------------------------------------------
 
-def unit_attention(K: np.ndarray, V: np.ndarray, q16: np.ndarray):
+def unit_attention(K: np.ndarray, V: np.ndarray, q16: np.ndarray, live=None):
     """Attention of the r query heads q16 [r][d] over one unit's K, V [T][d] (fp64).
 
     Returns out [r][d] and the normalized probabilities p [r][T]:
-    s = K q / sqrt(d); p = exp(s - max s) / sum; out = p V.
+    s = K q / sqrt(d); p = exp(s - max s) / sum; out = p V. With ``live`` (bool
+    [T]) only those tokens are attended; the others get p = 0 (R13).
     """
     d = K.shape[1]
     q = np.asarray(q16, dtype=np.float16).astype(np.float64)
     s = (q @ K.T) / math.sqrt(d)
+    if live is not None:
+        s[:, ~np.asarray(live, dtype=bool)] = -np.inf
     s -= s.max(axis=1, keepdims=True)
     e = np.exp(s)
     p = e / e.sum(axis=1, keepdims=True)
@@ -407,6 +423,41 @@ def unit_attention(K: np.ndarray, V: np.ndarray, q16: np.ndarray):
 def h2o_increment(p: np.ndarray) -> np.ndarray:
     """Score increment for one KV head: sum over its query heads of p [r][T] (R10)."""
     return p.sum(axis=0)
+
+
+def h2o_evict_one(scores: np.ndarray, live: np.ndarray, budget: int, recent: int, sinks: int):
+    """One H2O eviction step for one KV head (R13).
+
+    ``scores`` fp32 [T] accumulated attention, ``live`` bool [T] (updated in
+    place). If more than ``budget`` tokens are live, the live token in
+    [sinks, T - recent) with the lowest score is evicted; ties go to the lower
+    index and NaN ranks lowest. Returns the evicted index or -1.
+    """
+    T = len(scores)
+    if int(live.sum()) <= budget:
+        return -1
+    best, best_i = None, -1
+    for t in range(sinks, T - recent):
+        if not live[t]:
+            continue
+        v = float(scores[t])
+        key = (0, 0.0) if math.isnan(v) else (1, v)   # NaN first, then by value
+        if best is None or key < best:
+            best, best_i = key, t
+    if best_i >= 0:
+        live[best_i] = False
+    return best_i
+
+
+def pyramid_budgets(n_layers: int, avg: int, depth: int):
+    """Per-layer heavy-hitter budgets, lowest layer first (R14):
+    b_l = (2x - x/d) - l (2x - 2x/d) / (L - 1), rounded down (exact rationals)."""
+    from fractions import Fraction
+    x, d = Fraction(avg), Fraction(depth)
+    top, low = 2 * x - x / d, x / d
+    if n_layers == 1:
+        return [int(x)]
+    return [math.floor(top - (top - low) * l / (n_layers - 1)) for l in range(n_layers)]
 
 
 class CacheOracle:

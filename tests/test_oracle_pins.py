@@ -746,3 +746,79 @@ def test_topk_special_values_total_order():
                 return (0, 0.0, i) if x != x else (1, x, i)
             keep = sorted(sorted(range(n), key=rank, reverse=True)[:k])
             assert got[r].tolist() == keep + list(range(n, T))
+
+
+# ---------------------------------------------------------------------------
+# H2O eviction during decoding ("H2O: Heavy-Hitter Oracle", greedy eviction;
+# "KV cache quantization and eviction", h2o_evict) and MiniKV's pyramid
+# budgets (section 4.2).
+# ---------------------------------------------------------------------------
+
+def test_h2o_evict_one_is_a_first_occurrence_argmin():
+    rng = np.random.default_rng(50)
+    for trial in range(200):
+        T = int(rng.integers(5, 60))
+        sc = (rng.integers(0, 6, T) * 0.25).astype(np.float32)   # many exact ties
+        if trial % 5 == 0:
+            sc[rng.integers(T)] = np.nan
+        live = rng.random(T) < 0.8
+        S, w, B = int(rng.integers(0, 3)), int(rng.integers(0, 5)), int(rng.integers(1, T))
+        want_live = live.copy()
+        cand = [t for t in range(S, T - w) if live[t]]
+        got = O.h2o_evict_one(sc, live, B, w, S)
+        if int(want_live.sum()) <= B or not cand:
+            assert got == -1 and np.array_equal(live, want_live)
+            continue
+        # numpy's argmin: the first NaN if any, else the first minimum
+        sub = sc[cand].astype(np.float64)
+        want = cand[int(np.argmin(sub))]
+        assert got == want
+        want_live[want] = False
+        assert np.array_equal(live, want_live)
+
+
+@pytest.mark.parametrize("S", [0, 4])
+def test_repeated_eviction_on_static_scores_equals_one_shot_topk(S):
+    """Evicting one token at a time down to the budget keeps the sinks, the
+    recent window and the top-k of the rest: the one-shot selection."""
+    rng = np.random.default_rng(51)
+    T, w, B = 300, 20, 100
+    sc = (rng.integers(0, 40, T) / 7).astype(np.float32)
+    live = np.ones(T, dtype=bool)
+    while O.h2o_evict_one(sc, live, B, w, S) >= 0:
+        pass
+    k = B - w - S
+    keep_rest = O.topk_keep(sc[S:][None], k, w)[0] + S
+    want = np.zeros(T, dtype=bool)
+    want[:S] = True
+    want[keep_rest] = True
+    assert np.array_equal(live, want)
+
+
+def test_attention_over_live_tokens_equals_attention_over_the_kept_rows():
+    rng = np.random.default_rng(52)
+    K = rng.standard_normal((50, 128))
+    V = rng.standard_normal((50, 128))
+    q = rng.standard_normal((4, 128)).astype(np.float16)
+    live = rng.random(50) < 0.6
+    out, p = O.unit_attention(K, V, q, live)
+    out2, p2 = O.unit_attention(K[live], V[live], q)
+    assert np.allclose(out, out2, rtol=1e-12, atol=1e-13)
+    assert np.all(p[:, ~live] == 0) and np.allclose(p[:, live], p2, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("L,x,d", [(32, 100, 7), (32, 1024, 2), (5, 13, 3), (2, 8, 4), (9, 50, 1)])
+def test_pyramid_budgets(L, x, d):
+    """MiniKV section 4.2: linear from 2x - x/d (lowest layer) to x/d (highest),
+    average x. Checked against those endpoints, a constant step and the mean,
+    in exact rationals."""
+    b = O.pyramid_budgets(L, x, d)
+    hi, lo = Fraction(2 * x) - Fraction(x, d), Fraction(x, d)
+    assert b[0] == math.floor(hi) and b[-1] == math.floor(lo)
+    step = (hi - lo) / (L - 1)
+    exact = [hi - step * l for l in range(L)]
+    assert sum(exact) == L * x                      # the average budget is x
+    assert all(0 <= e - bl < 1 for e, bl in zip(exact, b))
+    assert all(b[i] >= b[i + 1] for i in range(L - 1))
+    if d == 1:
+        assert b == [x] * L
