@@ -206,6 +206,7 @@ ROWS = {
     "append_ott": ("ott", "a1-a7: OTT scores + pool scan, mean replacement, quantize + pack, ring"),
     "decode_h2o_minikv": ("minikv", "a8-a10: fused decode + merge with H2O accumulation"),
     "topk_minikv": ("minikv", "a11: heavy-hitter top-k + recent window"),
+    "evict_minikv": ("minikv", "f2: one H2O eviction per KV head (budget 20% + 256 recent)"),
     "decode_llama8b_g16": ("llama8b_g16", "a8-a10: fused decode + merge at group size 16"),
     "decode_llama8b_sinks": ("llama8b_sinks", "a8-a10 with 4 attention sinks in the fp16 partition"),
     "decode_long_b2g32": ("long_b2g32", "a8-a10: fused decode + merge, split-K over context"),
@@ -337,6 +338,21 @@ def rows_main(args):
                                           bits=w.bits, group=w.group, residual=w.residual,
                                           h2o=w.h2o, sinks=w.sinks).total
             emit(name, w, us, nbytes, {"kernels": ["decode_kernel", "merge_kernel"]})
+        elif name.startswith("evict"):  # one eviction step on accumulated scores
+            for rep in reps:
+                abi.decode_attention(rep["h"], q, out, rep["acc"], ws)
+            budget = w.topk_k + w.recent
+
+            def call(i, a, b):
+                rep = reps[i % len(reps)]
+                a.record()
+                abi.evict_step(rep["h"], rep["acc"], budget, w.recent)
+                b.record()
+
+            timed(call, 2)
+            us = timed(call, args.reps)
+            emit(name, w, us, BM.evict_step_bytes(rows=U, tokens=w.tokens, sinks=w.sinks),
+                 {"kernels": ["evict_step_kernel"], "budget": budget, "recent": w.recent})
         else:  # top-k over the accumulated scores of a decode call
             for rep in reps:
                 abi.decode_attention(rep["h"], q, out, rep["acc"], ws)

@@ -34,6 +34,12 @@
  *    the tokens after them ("KV cache quantization and eviction", section
  *    "Attention sinks and StreamingLLM"; "KV Cache Transform Coding for
  *    Compact Storage in LLM Inference", section 2, s = 4 sinks).
+ *  - H2O eviction while decoding: one token per step and KV head, the live
+ *    token with the lowest accumulated score outside the sinks and a recent
+ *    window, while more than a budget of tokens is live ("H2O: Heavy-Hitter
+ *    Oracle", greedy eviction; "KV cache quantization and eviction",
+ *    h2o_evict in "Minimal implementation"); per-layer budgets by MiniKV's
+ *    pyramid (section 4.2).
  *  - Heavy-hitter selection: the k highest scores outside a recent window of
  *    w tokens, plus that window (MiniKV, Algorithm 1; "KV cache quantization
  *    and eviction", section "Minimal implementation").
@@ -149,6 +155,9 @@ typedef struct kvq_config {
  *             nothing is quantized), which bounds the decoder's lazy rescale
  *   scores    uint64 [U][Qcap] scratch for key L1 norms during an append
  *   sink_k    fp16 [U][S][d] the attention-sink rows; sink_v likewise
+ *   evict     uint32 [U][ceil((max_tokens - S) / 32)]: bit i of word c set when
+ *             token S + 32c + i was evicted (kvq_evict_step)
+ *   evict_count int32 [U]: evicted tokens per unit
  * Slots of pool_idx / ev_idx beyond the counters are unspecified.
  *
  * Packed code layout. Codes of 32 consecutive quantized tokens form a chunk
@@ -172,6 +181,7 @@ typedef struct kvq_cache {
     uint64_t off_pool_idx, off_pool_score, off_pool_k, off_pool_v;
     uint64_t off_ev_idx, off_ev_k, off_ev_v, off_counters, off_scores;
     uint64_t off_sink_k, off_sink_v;
+    uint64_t off_evict, off_evict_count;
 } kvq_cache;
 
 /* Bytes of device memory a cache with this configuration needs (host only).
@@ -297,6 +307,34 @@ kvq_status kvq_topk_evict(const float* d_scores, int32_t rows, int32_t T, int32_
                           int32_t w, int32_t* d_idx, void* stream);
 
 /*
+ * One H2O eviction step ("H2O: Heavy-Hitter Oracle", greedy eviction of the
+ * lowest accumulated score, one token per step; "KV cache quantization and
+ * eviction", h2o_evict in "Minimal implementation"). For every unit that
+ * holds more than `budget` live tokens (sinks included), the live token t in
+ * [S, T - recent) with the lowest d_acc[u][t] is evicted: later decode calls
+ * skip it and add nothing to its score. Ties go to the older token (a
+ * first-occurrence argmin); a NaN score ranks below every number. Evicted
+ * tokens keep their storage (a quantized token shares its group's scale).
+ *   d_acc   device fp32 [B][Hkv][T], the scores after this step's decode call
+ * Errors: KVQ_EINVAL (invalid handle, null d_acc, budget < 0, recent < 0).
+ */
+kvq_status kvq_evict_step(kvq_cache* h, const float* d_acc, int32_t budget, int32_t recent,
+                          void* stream);
+
+/*
+ * Heavy-hitter budget per layer by MiniKV's pyramid ("MiniKV", section 4.2,
+ * Layer-Specific Selectivity): with average budget x = avg_budget and depth
+ * d >= 1 over L = n_layers layers, the budget falls linearly from 2x - x/d at
+ * the lowest layer (index 0) to x/d at the highest, each rounded down (exact
+ * integer arithmetic). The page names the x/d end "bottom-most" but also
+ * gives lower layers more cache; the latter reading is taken. Host only:
+ * writes host int32 out[L]. Errors: KVQ_EINVAL (null out, L outside [1, 4096],
+ * x outside [0, 2^24], d outside [1, 4096]).
+ */
+kvq_status kvq_pyramid_budgets(int32_t n_layers, int32_t avg_budget, int32_t depth,
+                               int32_t* out);
+
+/*
  * Inspection: canonical codes of the quantized tokens, one byte per code,
  * device uint8 [U][n_q][d] for keys and for values.
  */
@@ -319,6 +357,7 @@ kvq_status kvq_unpack_codes(const kvq_cache* h, uint8_t* d_kcodes, uint8_t* d_vc
  * Pool and extra-pool indices are indices in the whole sequence.
  *   kres, vres      fp16 [U][T - S - n_q][d]: the fp16 residual rows, token order
  *   ksink, vsink    fp16 [U][min(T, S)][d]: the attention-sink rows
+ *   live            uint8 [U][T]: 0 for tokens evicted by kvq_evict_step
  *   counters        int32 [U][4]: pool count, extra-pool count, frozen flag,
  *                   largest value scale (fp16 bits)
  *   pool_idx        int32 [U][N], pool_score uint64 [U][N] (key L1 norm in
@@ -346,6 +385,7 @@ typedef struct kvq_debug_view {
     uint16_t* ev_v;
     uint16_t* ksink;
     uint16_t* vsink;
+    uint8_t* live;
 } kvq_debug_view;
 
 /* Fill the non-NULL fields of *view (host struct of device pointers) on

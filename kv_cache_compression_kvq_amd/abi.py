@@ -28,7 +28,8 @@ NOALLOC_SCRATCH_BYTES = 32 << 20  # KVQ_NOALLOC_SCRATCH_BYTES
 EXPORTS = ("kvq_status_string", "kvq_cache_bytes", "kvq_cache_init", "kvq_quantize_append",
            "kvq_decode_workspace", "kvq_decode_attention", "kvq_decode_attention_timed",
            "kvq_decode_step", "kvq_decode_step_timed", "kvq_topk_evict", "kvq_unpack_codes",
-           "kvq_decode_attention_noalloc", "kvq_debug_unpack")
+           "kvq_decode_attention_noalloc", "kvq_debug_unpack", "kvq_evict_step",
+           "kvq_pyramid_budgets")
 
 
 class Config(ctypes.Structure):
@@ -44,7 +45,8 @@ class Cache(ctypes.Structure):
         (n, ctypes.c_uint64) for n in (
             "off_kq", "off_vq", "off_kmeta", "off_vmeta", "off_mask", "off_kring", "off_vring",
             "off_pool_idx", "off_pool_score", "off_pool_k", "off_pool_v", "off_ev_idx",
-            "off_ev_k", "off_ev_v", "off_counters", "off_scores", "off_sink_k", "off_sink_v")]
+            "off_ev_k", "off_ev_v", "off_counters", "off_scores", "off_sink_k", "off_sink_v",
+            "off_evict", "off_evict_count")]
 
 
 class DebugView(ctypes.Structure):
@@ -52,7 +54,7 @@ class DebugView(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "kcodes", "vcodes", "kscale", "kzero", "vscale", "vzero", "pooled", "kres", "vres",
         "counters", "pool_idx", "pool_score", "pool_k", "pool_v", "ev_idx", "ev_k", "ev_v",
-        "ksink", "vsink")]
+        "ksink", "vsink", "live")]
 
 
 class KvqError(RuntimeError):
@@ -90,6 +92,8 @@ def lib() -> ctypes.CDLL:
             "kvq_topk_evict": [P, I32, I32, I32, I32, P, P],
             "kvq_unpack_codes": [ctypes.POINTER(Cache), P, P, P],
             "kvq_debug_unpack": [ctypes.POINTER(Cache), ctypes.POINTER(DebugView), P],
+            "kvq_evict_step": [ctypes.POINTER(Cache), P, I32, I32, P],
+            "kvq_pyramid_budgets": [I32, I32, I32, ctypes.POINTER(I32)],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -210,3 +214,16 @@ def debug_unpack(h: Cache, stream=None, **bufs) -> None:
     view = DebugView(**{k: _ptr(v) for k, v in bufs.items()})
     _check("kvq_debug_unpack", lib().kvq_debug_unpack(ctypes.byref(h), ctypes.byref(view),
                                                       _stream(stream)))
+
+
+def evict_step(h: Cache, acc, budget: int, recent: int, stream=None) -> None:
+    """kvq_evict_step: one H2O eviction per unit holding more than ``budget`` live tokens."""
+    _check("kvq_evict_step", lib().kvq_evict_step(ctypes.byref(h), _ptr(acc), budget, recent,
+                                                  _stream(stream)))
+
+
+def pyramid_budgets(n_layers: int, avg_budget: int, depth: int) -> list:
+    """kvq_pyramid_budgets (host): per-layer heavy-hitter budgets, lowest layer first."""
+    out = (ctypes.c_int32 * n_layers)()
+    _check("kvq_pyramid_budgets", lib().kvq_pyramid_budgets(n_layers, avg_budget, depth, out))
+    return list(out)

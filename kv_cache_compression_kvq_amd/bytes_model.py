@@ -97,6 +97,13 @@ def bulk_append_bytes(*, units: int, head_dim: int, tokens: int, n_quant: int, b
     return units * (tokens * 4 * d + n_quant * per_q + (tokens - n_quant) * 4 * d)
 
 
+def evict_step_bytes(*, rows: int, tokens: int, sinks: int = 0) -> int:
+    """One H2O eviction step: every unit's fp32 scores and eviction bitmap read
+    once (the single word written per unit is not counted)."""
+    n = tokens - sinks
+    return rows * (tokens * 4 + (n + 31) // 32 * 4)
+
+
 def topk_bytes(*, rows: int, tokens: int, k: int, w: int) -> int:
     """fp32 scores read once, int32 kept indices written."""
     return rows * tokens * 4 + rows * (k + w) * 4

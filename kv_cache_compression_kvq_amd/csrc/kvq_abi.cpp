@@ -14,6 +14,12 @@ constexpr int64_t kMaxQuantSplits = 1000;  // merge keeps per-split weights in L
 
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Words of a unit's eviction bitmap: one bit per token after the sinks.
+uint64_t evict_words_of(const kvq_config* c) {
+    const int64_t n = c->max_tokens > c->sinks ? c->max_tokens - c->sinks : 0;
+    return (uint64_t)(n + 31) / 32;
+}
+
 // Key groups the kmeta region holds for C chunks: G = 16 keeps both groups of
 // every chunk, so that a half-used last chunk still has a (zeroed) second entry.
 uint64_t key_groups_of(uint64_t G, uint64_t C) { return G == 16 ? 2 * C : C * kChunk / G; }
@@ -45,7 +51,7 @@ kvq_status check_config(const kvq_config* c) {
     return KVQ_OK;
 }
 
-constexpr int kRegions = 18;
+constexpr int kRegions = 20;
 
 struct Layout {
     uint64_t off[kRegions];
@@ -83,6 +89,8 @@ Layout layout_of(const kvq_config* c) {
         N > 0 ? U * L.q_cap * 8 : 0,  // scores
         U * S * d * 2,                // sink_k
         U * S * d * 2,                // sink_v
+        U * evict_words_of(c) * 4,    // evict
+        U * 4,                        // evict_count
     };
     uint64_t o = 0;
     for (int i = 0; i < kRegions; ++i) {
@@ -135,6 +143,9 @@ CacheView view_of(const kvq_cache* h) {
     v.sink_k = reinterpret_cast<uint16_t*>(a + h->off_sink_k);
     v.sink_v = reinterpret_cast<uint16_t*>(a + h->off_sink_v);
     v.sinks = h->cfg.sinks;
+    v.evict = reinterpret_cast<uint32_t*>(a + h->off_evict);
+    v.evict_count = reinterpret_cast<int32_t*>(a + h->off_evict_count);
+    v.evict_words = (int64_t)evict_words_of(&h->cfg);
     v.bits = h->cfg.bits;
     v.group = h->cfg.group;
     v.residual = h->cfg.residual;
@@ -242,7 +253,7 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* d_arena, size_t bytes, kv
                                 &c.off_kring, &c.off_vring, &c.off_pool_idx, &c.off_pool_score,
                                 &c.off_pool_k, &c.off_pool_v, &c.off_ev_idx, &c.off_ev_k,
                                 &c.off_ev_v, &c.off_counters, &c.off_scores, &c.off_sink_k,
-                                &c.off_sink_v};
+                                &c.off_sink_v, &c.off_evict, &c.off_evict_count};
     for (int i = 0; i < kRegions; ++i) *offs[i] = L.off[i];
     st = launch_status(launch_init(view_of(&c), stream));
     if (st == KVQ_OK) *h = c;
@@ -361,6 +372,33 @@ kvq_status kvq_unpack_codes(const kvq_cache* h, uint8_t* d_kcodes, uint8_t* d_vc
     if (h->n_quant == 0) return KVQ_OK;
     if (!d_kcodes || !d_vcodes) return KVQ_EINVAL;
     return launch_status(launch_unpack(view_of(h), h->n_quant, d_kcodes, d_vcodes, stream));
+}
+
+kvq_status kvq_evict_step(kvq_cache* h, const float* d_acc, int32_t budget, int32_t recent,
+                          void* stream) {
+    if (!valid_handle(h) || !d_acc || budget < 0 || recent < 0) return KVQ_EINVAL;
+    if (h->tokens == 0) return KVQ_OK;
+    return launch_status(launch_evict_step(view_of(h), h->tokens, d_acc, budget, recent, stream));
+}
+
+kvq_status kvq_pyramid_budgets(int32_t n_layers, int32_t avg_budget, int32_t depth,
+                               int32_t* out) {
+    if (!out || n_layers < 1 || n_layers > 4096 || avg_budget < 0 || avg_budget > kMaxTokens ||
+        depth < 1 || depth > 4096)
+        return KVQ_EINVAL;
+    // b_l = (2x - x/d) - l (2x - 2x/d) / (L - 1)
+    //     = [(2xd - x)(L - 1) - l (2xd - 2x)] / (d (L - 1)), floored; all
+    //     terms are non-negative, so integer division floors
+    const int64_t x = avg_budget, d = depth, L = n_layers;
+    if (L == 1) {
+        out[0] = (int32_t)x;
+        return KVQ_OK;
+    }
+    for (int64_t l = 0; l < L; ++l) {
+        const int64_t num = (2 * x * d - x) * (L - 1) - l * (2 * x * d - 2 * x);
+        out[l] = (int32_t)(num / (d * (L - 1)));
+    }
+    return KVQ_OK;
 }
 
 kvq_status kvq_debug_unpack(const kvq_cache* h, const kvq_debug_view* view, void* stream) {

@@ -63,7 +63,7 @@ struct Ring {
     // then key scales (512 B per key group; G = 16: both groups of the chunk)
     static constexpr int kKmOff = G == 16 ? 1024 : 512;
     static constexpr int kMeta = kKmOff + (G == 16 ? 1024 : 512);
-    static constexpr int kStage = 2 * kCodes + kMeta + 16;  // + pool mask word
+    static constexpr int kStage = 2 * kCodes + kMeta + 16;  // + pool mask and eviction words
     static constexpr int kLoads = 2 * (kCodes / 1024) + (G == 16 ? 3 : 2);  // loads per stage
     static constexpr int kWave = kStages * kStage;          // ring bytes per wavefront
     static constexpr int kBlock = 4 * kWave > kFp16Bytes ? 4 * kWave : kFp16Bytes;
@@ -128,6 +128,8 @@ struct DecodeArgs {
     const uint16_t* ev_k;
     const uint16_t* ev_v;
     const int32_t* counters;
+    const uint32_t* evict;   // [U][evict_words] eviction bits of tokens S, S + 1, ...
+    int64_t evict_words;
     const uint16_t* sink_k;  // attention sinks [U][sink_cap][d]
     const uint16_t* sink_v;
     const uint16_t* k_new;  // decode step: the newest token's rows [U][d] (else null)
@@ -337,6 +339,18 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
                                          __builtin_bit_cast(half2_t, y.w), acc, false);
         }
         s = acc * a.qscale;
+        {
+            // an evicted ring, pool or extra-pool token (index after the sinks)
+            const int64_t li = base + lane;
+            if (li >= ns) {
+                const int64_t tau = li < ns + nres ? a.n_q + (li - ns)
+                                    : li < ns + nres + pc
+                                        ? a.pool_idx[(int64_t)u * N + (li - ns - nres)]
+                                        : a.ev_idx[(int64_t)u * E + (li - ns - nres - pc)];
+                if ((a.evict[(int64_t)u * a.evict_words + (tau >> 5)] >> (tau & 31)) & 1u)
+                    s = -INFINITY;
+            }
+        }
         if (a.logits) {
             // sequence index of the row's token
             const int64_t li = base + lane;
@@ -457,6 +471,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     const uint32_t* km_u = a.kmeta + (int64_t)u * a.key_groups * D;
     const uint32_t* vm_u = a.vmeta + (int64_t)u * a.chunks * NG * 32;
     const uint32_t* mk_u = a.mask + (int64_t)u * a.chunks;
+    const uint32_t* ev_u = a.evict + (int64_t)u * a.evict_words;
 
     // MFMA lane roles: j = column / row within a 16-lane row, kb = k-block.
     const int j = lane & 15, kb = lane >> 4, jj = j & 7;
@@ -508,7 +523,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
                 lane < 32 ? vm_u + ch * NG * 32 + lane * 4 : km_u + gi * D + (lane - 32) * 4;
             if (lane < 8 * NG || (lane >= 32 && cc == 0)) lds_load16(src, st + 2 * RG::kCodes);
         }
-        if (lane == 0) lds_load4(mk_u + ch, st + 2 * RG::kCodes + RG::kMeta);
+        // lane 0: the chunk's pool mask word; lane 1: its eviction word
+        if (lane < 2) lds_load4(lane == 0 ? mk_u + ch : ev_u + ch, st + 2 * RG::kCodes + RG::kMeta);
     };
     float* wsm = reinterpret_cast<float*>(wlds);
     unsigned char* btab = s_btab[wave];  // folded query, 2 KB per key group of a chunk
@@ -571,17 +587,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
             vm3 = ring_read<GPS * 128 + 64>(a_vm);
         }
         uint32_t mwv = ring_read32(meta + RG::kMeta);
+        uint32_t ewv = ring_read32(meta + RG::kMeta + 4);
         if (kG16 && BITS == 4) {
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(wk0), "+v"(wk1), "+v"(wv0), "+v"(wv1), "+v"(vm0), "+v"(vm1),
-                           "+v"(km0), "+v"(km1), "+v"(mwv), "+v"(km2), "+v"(km3), "+v"(vm2),
+                           "+v"(km0), "+v"(km1), "+v"(mwv), "+v"(ewv), "+v"(km2), "+v"(km3), "+v"(vm2),
                            "+v"(vm3)
                          :
                          : "memory");
         } else if (kG16) {
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(wk0), "+v"(wv0), "+v"(vm0), "+v"(vm1), "+v"(km0), "+v"(km1),
-                           "+v"(mwv), "+v"(km2), "+v"(km3), "+v"(vm2), "+v"(vm3)
+                           "+v"(mwv), "+v"(ewv), "+v"(km2), "+v"(km3), "+v"(vm2), "+v"(vm3)
                          :
                          : "memory");
             wk1 = wk0;
@@ -589,13 +606,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
         } else if (BITS == 4) {
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(wk0), "+v"(wk1), "+v"(wv0), "+v"(wv1), "+v"(vm0), "+v"(vm1),
-                           "+v"(km0), "+v"(km1), "+v"(mwv)
+                           "+v"(km0), "+v"(km1), "+v"(mwv), "+v"(ewv)
                          :
                          : "memory");
         } else {
             asm volatile("s_waitcnt lgkmcnt(0)"
                          : "+v"(wk0), "+v"(wv0), "+v"(vm0), "+v"(vm1), "+v"(km0), "+v"(km1),
-                           "+v"(mwv)
+                           "+v"(mwv), "+v"(ewv)
                          :
                          : "memory");
             wk1 = wk0;  // one 16-byte word group per lane at b = 2
@@ -689,7 +706,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
                 acc1[i] += dpp<0x141>(acc1[i]);
             }
         }
-        uint32_t mw = __builtin_amdgcn_readfirstlane(mwv);  // same word in every lane
+        // pool members (attended through their fp16 rows) and evicted tokens
+        // are skipped; the same words in every lane
+        uint32_t mw = __builtin_amdgcn_readfirstlane(mwv | ewv);
         // G = 16: a last chunk whose second group is not quantized yet (its
         // tokens are in the fp16 ring) has that half masked out
         if (kG16 && tb + 32 > a.n_q) mw |= 0xFFFF0000u;
@@ -1059,7 +1078,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     // r query heads of the normalized probabilities.
     constexpr int kPart = kH2OChunk / R;
     const int64_t t0 = (int64_t)(blockIdx.y - 1) * kH2OChunk + (int64_t)hb * kPart;
+    const uint32_t* ev_u = a.evict + (int64_t)u * a.evict_words;
     for (int64_t t = t0 + threadIdx.x; t < t0 + kPart && t < a.T; t += 256) {
+        const int64_t tau = t - a.sink_cap;
+        if (tau >= 0 && ((ev_u[tau >> 5] >> (tau & 31)) & 1u)) continue;  // evicted: no score
         float d = 0.f;
 #pragma unroll
         for (int h = 0; h < R; ++h)
@@ -1203,6 +1225,8 @@ int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& 
     a.ev_k = v.ev_k;
     a.ev_v = v.ev_v;
     a.counters = v.counters;
+    a.evict = v.evict;
+    a.evict_words = v.evict_words;
     a.sink_k = v.sink_k;
     a.sink_v = v.sink_v;
     a.sink_cap = v.sinks;

@@ -39,6 +39,9 @@ struct CacheView {
     uint64_t* scores;
     uint16_t* sink_k;    // [U][S][d]
     uint16_t* sink_v;
+    uint32_t* evict;     // [U][evict_words]: eviction bits of tokens S, S + 1, ...
+    int32_t* evict_count;  // [U]
+    int64_t evict_words;
     int32_t sinks;       // S
     int32_t bits, group, residual, pool, evict_cap;
     int32_t n_q_heads, n_kv_heads, batch;
@@ -83,6 +86,8 @@ int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& 
 int launch_topk(const float* scores, int32_t rows, int32_t T, int32_t k, int32_t w,
                 int32_t* idx, void* stream);
 int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, void* stream);
+int launch_evict_step(const CacheView& v, int64_t T, const float* acc, int32_t budget,
+                      int32_t recent, void* stream);
 int launch_debug_unpack(const CacheView& v, int64_t T, int64_t n_q, const kvq_debug_view& out,
                         void* stream);
 // Launch shape of the decode kernel on the current GPU: compute units and the

@@ -114,12 +114,16 @@ __global__ void init_kernel(CacheView v) {
     const int64_t nc = (int64_t)v.units * 4, nm = (int64_t)v.units * v.chunks;
     const int64_t nk = v.group == 16 ? (int64_t)v.units * v.key_groups * D : 0;
     const int64_t nv = v.group == 16 ? (int64_t)v.units * v.chunks * (D / 16) * kChunk : 0;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nc + nm + nk + nv;
+    const int64_t ne = (int64_t)v.units * v.evict_words, nu = v.units;
+    const int64_t n1 = nc + nm, n2 = n1 + nk, n3 = n2 + nv, n4 = n3 + ne, n5 = n4 + nu;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n5;
          i += (int64_t)gridDim.x * blockDim.x) {
         if (i < nc) v.counters[i] = 0;
-        else if (i < nc + nm) v.mask[i - nc] = 0;
-        else if (i < nc + nm + nk) v.kmeta[i - nc - nm] = 0;
-        else v.vmeta[i - nc - nm - nk] = 0;
+        else if (i < n1) v.mask[i - nc] = 0;
+        else if (i < n2) v.kmeta[i - n1] = 0;
+        else if (i < n3) v.vmeta[i - n2] = 0;
+        else if (i < n4) v.evict[i - n3] = 0;
+        else v.evict_count[i - n4] = 0;
     }
 }
 
@@ -858,6 +862,55 @@ __global__ __launch_bounds__(256) void debug_view_kernel(CacheView v, int64_t T,
     }
 }
 
+// One H2O eviction step: one block per unit. If more than `budget` tokens are
+// live, the live token in [S, T - recent) with the lowest score is evicted
+// ("H2O: Heavy-Hitter Oracle", greedy eviction; "KV cache quantization and
+// eviction", h2o_evict). Scores compare through an order-preserving key
+// with every NaN lowest and -0 equal to +0; the smallest (key, index) wins, so
+// ties go to the older token.
+__global__ __launch_bounds__(256) void evict_step_kernel(CacheView v, int64_t T, const float* acc,
+                                                         int32_t budget, int32_t recent) {
+    const int u = blockIdx.x, tid = threadIdx.x;
+    const int64_t live = T - v.evict_count[u];
+    if (live <= budget) return;  // uniform over the block
+    const int64_t S = v.sinks, end = T - recent;
+    const uint32_t* ev = v.evict + (int64_t)u * v.evict_words;
+    const float* sc = acc + (int64_t)u * T;
+    uint64_t best = ~0ull;
+    for (int64_t t = S + tid; t < end; t += 256) {
+        const int64_t tau = t - S;
+        if ((ev[tau >> 5] >> (tau & 31)) & 1u) continue;
+        const float f = sc[t];
+        uint32_t b = __builtin_bit_cast(uint32_t, f);
+        uint32_t key;
+        if (f != f) key = 0u;                      // NaN: lowest
+        else {
+            if (f == 0.0f) b = 0u;                 // -0 == +0
+            key = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+            if (key == 0u) key = 1u;               // keep 0 for NaN only
+        }
+        const uint64_t k = ((uint64_t)key << 32) | (uint64_t)t;
+        best = k < best ? k : best;
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t o = __shfl_xor(best, off);
+        best = o < best ? o : best;
+    }
+    __shared__ uint64_t wbest[4];
+    if ((tid & 63) == 0) wbest[tid >> 6] = best;
+    __syncthreads();
+    if (tid == 0) {
+        uint64_t b = wbest[0];
+        for (int w = 1; w < 4; ++w) b = wbest[w] < b ? wbest[w] : b;
+        if (b != ~0ull) {
+            const int64_t tau = (int64_t)(b & 0xFFFFFFFFu) - S;
+            uint32_t* word = v.evict + (int64_t)u * v.evict_words + (tau >> 5);
+            *word |= 1u << (tau & 31);
+            v.evict_count[u] += 1;
+        }
+    }
+}
+
 // Pool and extra-pool indices of the canonical view: sequence indices, i.e.
 // the stored index (counted from the first token after the sinks) plus S.
 __global__ __launch_bounds__(256) void index_view_kernel(int32_t* dst, const int32_t* src,
@@ -865,6 +918,17 @@ __global__ __launch_bounds__(256) void index_view_kernel(int32_t* dst, const int
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
          e += (int64_t)gridDim.x * blockDim.x)
         dst[e] = src[e] + add;
+}
+
+// Liveness of the canonical view: [U][T] bytes, 0 for evicted tokens.
+__global__ __launch_bounds__(256) void live_view_kernel(CacheView v, int64_t T, uint8_t* live) {
+    const int64_t n = (int64_t)v.units * T;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t u = e / T, t = e % T, tau = t - v.sinks;
+        live[e] = tau < 0 ? 1
+                          : (uint8_t)(((v.evict[u * v.evict_words + (tau >> 5)] >> (tau & 31)) & 1u) ^ 1u);
+    }
 }
 
 // Sink rows of the canonical view: [U][rows][d] from the sink region [U][S][d].
@@ -905,7 +969,7 @@ hipError_t launch_pack_t(const CacheView& v, const uint16_t* kn, const uint16_t*
 int launch_init(const CacheView& v, void* stream) {
     (void)hipGetLastError();  // an error left by an earlier call is not this call's
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t n = (int64_t)v.units * 4 + (int64_t)v.units * v.chunks;
+    const int64_t n = (int64_t)v.units * (4 + v.chunks + v.evict_words + 1);
     const int64_t blocks = (n + 255) / 256;
     hipLaunchKernelGGL(init_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0,
                        s, v);
@@ -980,6 +1044,14 @@ int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, voi
     return (int)hipGetLastError();
 }
 
+int launch_evict_step(const CacheView& v, int64_t T, const float* acc, int32_t budget,
+                      int32_t recent, void* stream) {
+    (void)hipGetLastError();  // an error left by an earlier call is not this call's
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(evict_step_kernel, dim3(v.units), dim3(256), 0, s, v, T, acc, budget, recent);
+    return (int)hipGetLastError();
+}
+
 int launch_debug_unpack(const CacheView& v, int64_t T, int64_t n_q, const kvq_debug_view& o,
                         void* stream) {
     (void)hipGetLastError();  // an error left by an earlier call is not this call's
@@ -1007,6 +1079,9 @@ int launch_debug_unpack(const CacheView& v, int64_t T, int64_t n_q, const kvq_de
     }
     const size_t U = (size_t)v.units, N = (size_t)v.pool, E = (size_t)v.evict_cap;
     const int32_t ns = (int32_t)(T < v.sinks ? T : v.sinks);
+    if (o.live && U * T)
+        hipLaunchKernelGGL(live_view_kernel, dim3((unsigned)((U * T + 255) / 256)), dim3(256), 0, s,
+                           v, T, o.live);
     if (ns > 0 && (o.ksink || o.vsink))
         hipLaunchKernelGGL(sink_view_kernel, dim3((unsigned)((U * ns * D + 255) / 256)), dim3(256),
                            0, s, v, ns, o.ksink, o.vsink);

@@ -51,6 +51,11 @@ int launch_unpack(const CacheView&, int64_t n_q, uint8_t*, uint8_t*, void*) {
     CHECK(n_q > 0);
     return stub();
 }
+int launch_evict_step(const CacheView& v, int64_t T, const float*, int32_t budget, int32_t recent,
+                      void*) {
+    CHECK(T >= 1 && budget >= 0 && recent >= 0 && v.evict_words * 32 >= v.q_cap);
+    return stub();
+}
 int launch_debug_unpack(const CacheView&, int64_t T, int64_t n_q, const kvq_debug_view&, void*) {
     CHECK(n_q <= T);
     return stub();
@@ -136,7 +141,7 @@ int main() {
                                              h.off_pool_idx, h.off_pool_score, h.off_pool_k,
                                              h.off_pool_v, h.off_ev_idx, h.off_ev_k, h.off_ev_v,
                                              h.off_counters, h.off_scores, h.off_sink_k,
-                                             h.off_sink_v};
+                                             h.off_sink_v, h.off_evict, h.off_evict_count};
                     for (size_t i = 0; i < sizeof(offs) / sizeof(offs[0]); ++i) {
                         CHECK(offs[i] % 256 == 0 && offs[i] <= bytes);
                         if (i) CHECK(offs[i] >= offs[i - 1]);
@@ -210,6 +215,17 @@ int main() {
         CHECK(kvq_decode_attention_noalloc(&h, &dummy, &out, nullptr, nullptr) == KVQ_OK);
         CHECK(g_launches == before + 1);
         CHECK(kvq_decode_attention_noalloc(&h, nullptr, &out, nullptr, nullptr) == KVQ_EINVAL);
+    }
+
+    // pyramid budgets: argument checks and the closed-form endpoints
+    {
+        int32_t b[32];
+        CHECK(kvq_pyramid_budgets(32, 100, 7, nullptr) == KVQ_EINVAL);
+        CHECK(kvq_pyramid_budgets(0, 100, 7, b) == KVQ_EINVAL);
+        CHECK(kvq_pyramid_budgets(32, 100, 0, b) == KVQ_EINVAL);
+        CHECK(kvq_pyramid_budgets(32, 100, 7, b) == KVQ_OK);
+        CHECK(b[0] == 185 && b[31] == 14);  // floor(200 - 100/7), floor(100/7)
+        CHECK(kvq_pyramid_budgets(1, 77, 3, b) == KVQ_OK && b[0] == 77);
     }
 
     // top-k argument checks

@@ -96,6 +96,7 @@ class GpuCache:
             kres=torch.empty((U, T - ns - nq, d), dtype=torch.float16, device=dev),
             vres=torch.empty((U, T - ns - nq, d), dtype=torch.float16, device=dev),
             ksink=torch.empty((U, ns, d), dtype=torch.float16, device=dev),
+            live=torch.empty((U, T), dtype=torch.uint8, device=dev),
             vsink=torch.empty((U, ns, d), dtype=torch.float16, device=dev),
             counters=torch.empty((U, 4), dtype=torch.int32, device=dev),
             pool_idx=torch.empty((U, N), dtype=torch.int32, device=dev),

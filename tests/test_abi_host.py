@@ -141,3 +141,12 @@ def test_decode_plan_covers_partials_and_logits(kvq):
         h = _fake_handle(kvq, cfg, T)
         a, b = kvq.decode_workspace(h, False), kvq.decode_workspace(h, True)
         assert b - a == 16 * 4 * T * 4
+
+
+@pytest.mark.parametrize("L,x,d", [(32, 100, 7), (32, 6553, 2), (5, 13, 3), (2, 8, 4), (1, 9, 5),
+                                   (40, 0, 3), (4096, 1 << 24, 4096)])
+def test_pyramid_budgets_match_the_oracle(kvq, L, x, d):
+    """kvq_pyramid_budgets (host C, integer arithmetic) against the oracle's
+    exact-rational budgets (MiniKV section 4.2)."""
+    from oracle import kvq_oracle as O
+    assert kvq.pyramid_budgets(L, x, d) == O.pyramid_budgets(L, x, d)

@@ -1,0 +1,125 @@
+"""H2O eviction while decoding, through the C ABI, against the CPU oracle.
+
+Each step: kvq_decode_step (append one token, attend, accumulate H2O scores),
+then kvq_evict_step (one eviction per KV head while more than the budget is
+live). After every step the outputs and score increments are checked against
+the oracle's attention over the live tokens, evicted tokens must keep their
+scores unchanged, and the set of live tokens must equal the oracle's bit for
+bit. The oracle takes each eviction decision on the GPU's fp32 scores, the
+precision the decision is made in ("H2O: Heavy-Hitter Oracle", greedy
+eviction; "KV cache quantization and eviction", h2o_evict).
+
+The recent window is shorter than the fp16 residual window, so tokens are
+also evicted while still in the ring and then quantized as evicted tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_compression_kvq_amd import abi, synth
+from oracle import kvq_oracle as O
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(kvq):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def _w(**kw):
+    base = dict(name="evict", cfg_id=400, batch=2, n_q_heads=8, n_kv_heads=2, bits=2, group=32,
+                residual=48, pool=0, evict_cap=8, tokens=300, sinks=4)
+    base.update(kw)
+    return W["llama8b"].with_(**base)
+
+
+CASES = {
+    # (workload, steps, budget, recent, extra evictions before the loop)
+    "b2g32_sinks": (_w(), 70, 260, 16, 50),
+    "b4g16_ott": (_w(bits=4, group=16, pool=3, inject_frac=0.03, outlier_channels=6,
+                     outlier_scale=15.0), 60, 250, 16, 60),
+    "b2g32_no_sinks_r2": (_w(n_q_heads=4, sinks=0, residual=32), 50, 280, 8, 30),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_decode_loop_with_h2o_eviction(name):
+    w, steps, budget, recent, pre = CASES[name]
+    T0, r, U = w.tokens, w.gqa, w.units
+    K, V = synth.all_kv(w, n=T0 + steps)
+    gc = H.GpuCache(w, max_tokens=T0 + steps)
+    gc.append(K[:, :, :T0], V[:, :, :T0])
+    units = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
+    orc = {key: O.UnitCache(H.params_of(w)) for key in units}
+    for (b, h), uc in orc.items():
+        uc.append(K[b, h, :T0], V[b, h, :T0])
+    live = {key: np.ones(T0 + steps, dtype=bool) for key in units}
+    dev = "cuda"
+    acc_all = torch.zeros((w.batch, w.n_kv_heads, T0 + steps), device=dev)
+    # scores of a first decode call, then `pre` evictions on them (a one-shot
+    # shrink through the same kernel)
+    q0 = torch.from_numpy(synth.queries(w, step=1000)).to(dev)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), device=dev)
+    acc = acc_all[..., :T0].contiguous()
+    ws = torch.empty(abi.decode_workspace(gc.h, True), dtype=torch.uint8, device=dev)
+    abi.decode_attention(gc.h, q0, out, acc, ws)
+    for _ in range(pre):
+        abi.evict_step(gc.h, acc, budget, recent)
+    torch.cuda.synchronize()
+    accn = acc.cpu().numpy()
+    for (b, h) in units:
+        for _ in range(pre):
+            O.h2o_evict_one(accn[b, h], live[(b, h)][:T0], budget, recent, w.sinks)
+    acc_all[..., :T0] = acc
+    n_evicted = 0
+    for i in range(steps):
+        T = T0 + i + 1
+        k = torch.from_numpy(np.ascontiguousarray(K[:, :, T - 1:T])).to(dev)
+        v = torch.from_numpy(np.ascontiguousarray(V[:, :, T - 1:T])).to(dev)
+        q = synth.queries(w, step=i)
+        acc_in = acc_all[..., :T].contiguous()
+        acc = acc_in.clone()
+        ws = torch.empty(_ws_after_step(gc.h), dtype=torch.uint8, device=dev)
+        out.fill_(float("nan"))
+        abi.decode_step(gc.h, k, v, torch.from_numpy(q).to(dev), out, acc, ws)
+        torch.cuda.synchronize()
+        outn, acc_in_n, acc_n = out.cpu().numpy(), acc_in.cpu().numpy(), acc.cpu().numpy()
+        for (b, h), uc in orc.items():
+            uc.append(K[b, h, T - 1:T], V[b, h, T - 1:T])
+            Kd, Vd = uc.dequantized_kv()
+            lv = live[(b, h)][:T]
+            ref, p = O.unit_attention(Kd, Vd, q[b, h * r:(h + 1) * r], lv)
+            H.check_outputs(outn[b, h * r:(h + 1) * r], ref, f"evict_{name} unit {(b, h)}")
+            d_ref = O.h2o_increment(p)
+            H.check_h2o(acc_n[b, h][lv], acc_in_n[b, h][lv], d_ref[lv],
+                        f"evict_{name} unit {(b, h)}")
+            assert np.array_equal(acc_n[b, h][~lv], acc_in_n[b, h][~lv]), "evicted scores moved"
+        # eviction on the scores just accumulated
+        abi.evict_step(gc.h, acc, budget, recent)
+        torch.cuda.synchronize()
+        for (b, h) in units:
+            n_evicted += O.h2o_evict_one(acc_n[b, h], live[(b, h)][:T], budget, recent,
+                                         w.sinks) >= 0
+        st = gc.state()
+        for u, key in enumerate(units):
+            assert np.array_equal(st["live"][u].astype(bool), live[key][:T]), f"step {i} unit {key}"
+            H.check_unit_state(st, u, orc[key])
+        acc_all[..., :T] = acc
+    assert n_evicted >= steps  # every step evicted on at least one unit
+
+
+def _ws_after_step(h):
+    """Workspace of kvq_decode_step: that of the cache after the append."""
+    import ctypes
+    nxt = abi.Cache()
+    ctypes.memmove(ctypes.byref(nxt), ctypes.byref(h), ctypes.sizeof(h))
+    nxt.tokens = h.tokens + 1
+    S = nxt.cfg.sinks
+    nxt.n_quant = max(0, (nxt.tokens - S - nxt.cfg.residual) // nxt.cfg.group * nxt.cfg.group)
+    return abi.decode_workspace(nxt, True)
