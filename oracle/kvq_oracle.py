@@ -87,6 +87,15 @@ R14 Pyramid budgets ([MiniKV] section 4.2): with average budget x and depth
     layer to x/d at the highest (the page calls the layer with x/d
     "bottom-most" but also allocates more cache to lower layers, as the
     pyramid policy it follows does; the latter is taken), rounded down.
+R15 FP8 codec (b = 8): every element is stored as FP8 E4M3 (OCP: bias 7,
+    largest finite 448, S.1111.111 is NaN, no infinity) of x / s, with one fp32
+    scale s per KV head for keys and one for values (1.0 unless set); the fp32
+    quotient is rounded to the nearest E4M3 value, ties to even, and saturates
+    at +-448 ([POFE] "FP8, KIVI and KVQuant": E4M3, largest finite value 448,
+    a scale per tensor or per head, 1.0 by default; "Failure modes": FP8 casts
+    must saturate instead of producing NaN). Dequantization is code value * s.
+    The residual window and the 32-token granularity of n_q stay as for the
+    integer codecs; there are no groups, zero points or outlier pools.
 """
 from __future__ import annotations
 
@@ -148,6 +157,63 @@ def quantize_value_rows(v16: np.ndarray, bits: int, gv: int):
 def dequantize(codes: np.ndarray, scale16: np.ndarray, zero16: np.ndarray) -> np.ndarray:
     """x_hat = code * scale + zero in fp64 from the stored fp16 parameters (R2)."""
     return codes.astype(np.float64) * scale16.astype(np.float64) + zero16.astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3 codec (R15).
+# --------------------------------------------------------------------------
+
+def e4m3_value(code: int) -> float:
+    """Value of an OCP E4M3 byte: (-1)^s 2^(e-7) (1 + m/8) for e > 0,
+    (-1)^s 2^-6 (m/8) for e = 0; S.1111.111 is NaN."""
+    sgn, e, m = code >> 7, (code >> 3) & 0xF, code & 7
+    if e == 15 and m == 7:
+        return math.nan
+    v = math.ldexp(1 + m / 8, e - 7) if e else math.ldexp(m / 8, -6)
+    return -v if sgn else v
+
+
+# the 127 finite non-negative magnitudes, ascending (codes 0x00 .. 0x7E)
+_E4M3_POS = np.array([e4m3_value(c) for c in range(0x7F)])
+
+
+def e4m3_encode(x32: np.ndarray) -> np.ndarray:
+    """Saturating round-to-nearest-even of fp32 values to E4M3 codes (R15).
+
+    Each |x| goes to the nearest finite magnitude; on a tie the even code
+    (even mantissa) wins; |x| above the largest finite value (inf included)
+    gives 448. The sign bit is the sign of x (so -0 -> 0x80)."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    out = np.empty(x.shape, dtype=np.uint8)
+    flat, res = x.reshape(-1), out.reshape(-1)
+    for i, v in enumerate(flat):
+        a = abs(v)
+        if math.isnan(a):
+            c = 0x7F
+        elif a >= _E4M3_POS[-1]:
+            c = 0x7E
+        else:
+            hi = int(np.searchsorted(_E4M3_POS, a))      # first magnitude >= a
+            if _E4M3_POS[hi] == a:
+                c = hi
+            else:
+                lo = hi - 1
+                dl, dh = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+                c = lo if dl < dh else hi if dh < dl else (lo if lo % 2 == 0 else hi)
+        res[i] = c | (0x80 if math.copysign(1.0, v) < 0 else 0)
+    return out
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """fp64 values of E4M3 codes."""
+    table = np.array([e4m3_value(c) for c in range(256)])
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def fp8_quantize(x16: np.ndarray, scale: float) -> np.ndarray:
+    """Codes of fp16 data with an fp32 scale: E4M3(fl32(x / s)) (R15)."""
+    q = np.asarray(x16, dtype=np.float16).astype(np.float32) / np.float32(scale)
+    return e4m3_encode(q)
 
 
 # --------------------------------------------------------------------------
@@ -270,6 +336,8 @@ class CacheParams:
     evict_cap: int = 32
     head_dim: int = 128
     sinks: int = 0  # S: the first S tokens stay fp16 (R12)
+    fp8_scale_k: float = 1.0  # b = 8: per-KV-head scales (R15)
+    fp8_scale_v: float = 1.0
 
     @property
     def gv(self) -> int:
@@ -354,6 +422,11 @@ class UnitCache:
         G = self.p.group
         kg = self.k16[t0:t0 + G].copy()
         vg = self.v16[t0:t0 + G].copy()
+        if self.p.bits == 8:  # FP8 codec: per element, no groups or pools (R15)
+            self._kcodes.append(fp8_quantize(kg, self.p.fp8_scale_k))
+            self._vcodes.append(fp8_quantize(vg, self.p.fp8_scale_v))
+            self._replaced.append(np.zeros(G, dtype=bool))
+            return
         idx = np.arange(t0, t0 + G)
         admitted = self.tracer.compete(idx, key_l1_score(kg), kg, vg)
         replaced = np.zeros(G, dtype=bool)
@@ -378,7 +451,10 @@ class UnitCache:
         n_q = self.n_q
         K = self.k16.astype(np.float64)  # sink and residual rows stay as stored (fp16)
         V = self.v16.astype(np.float64)
-        if n_q:
+        if n_q and self.p.bits == 8:
+            K[S:S + n_q] = e4m3_decode(self.kcodes) * float(np.float32(self.p.fp8_scale_k))
+            V[S:S + n_q] = e4m3_decode(self.vcodes) * float(np.float32(self.p.fp8_scale_v))
+        elif n_q:
             ks = np.repeat(self.kscale, G, axis=0)
             kz = np.repeat(self.kzero, G, axis=0)
             K[S:S + n_q] = dequantize(self.kcodes, ks, kz)

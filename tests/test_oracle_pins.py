@@ -822,3 +822,93 @@ def test_pyramid_budgets(L, x, d):
     assert all(b[i] >= b[i + 1] for i in range(L - 1))
     if d == 1:
         assert b == [x] * L
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 codec ("KV cache quantization and eviction", FP8, KIVI and KVQuant:
+# E4M3, largest finite value 448, a scale per head; Failure modes: casts must
+# saturate).
+# ---------------------------------------------------------------------------
+
+def _e4m3_magnitudes_by_construction():
+    """All finite non-negative E4M3 magnitudes as exact rationals, built binade
+    by binade: the subnormal run k * 2^-9 (k = 0..7), then for each binade
+    2^(e-7) with e = 1..15 its eight steps of 2^(e-10), the last binade
+    stopping before the NaN pattern."""
+    vals = [Fraction(k, 2 ** 9) for k in range(8)]
+    for e in range(1, 16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                break
+            vals.append(Fraction(2) ** (e - 7) + m * Fraction(2) ** (e - 10))
+    return vals
+
+
+def test_e4m3_table_matches_the_format(golden):
+    g = golden["fp8_e4m3"]
+    mags = _e4m3_magnitudes_by_construction()
+    assert len(mags) == 127
+    assert float(mags[-1]) == g["max_finite"] == O.e4m3_value(0x7E)
+    for c in range(256):
+        v = O.e4m3_value(c)
+        if c & 0x7F == 0x7F:
+            assert math.isnan(v)
+            continue
+        m = mags[c & 0x7F]
+        assert Fraction(abs(v)) == m and (c < 0x80 or math.copysign(1, v) < 0)
+
+
+def test_e4m3_encode_round_trips_rounds_to_even_and_saturates():
+    mags = _e4m3_magnitudes_by_construction()
+    codes = np.arange(256, dtype=np.uint8)
+    finite = (codes & 0x7F) != 0x7F
+    vals = O.e4m3_decode(codes[finite]).astype(np.float32)
+    assert np.array_equal(O.e4m3_encode(vals), codes[finite])          # exact values stay
+    # midpoints between neighbours go to the even code; just off them, to the nearer
+    for i in range(126):
+        mid = (mags[i] + mags[i + 1]) / 2
+        x = np.float32(float(mid))
+        assert Fraction(float(x)) == mid                                   # exact in fp32
+        want = i if i % 2 == 0 else i + 1
+        assert O.e4m3_encode(np.array([x]))[0] == want
+        assert O.e4m3_encode(np.array([-x]))[0] == want | 0x80
+        up, dn = np.nextafter(x, np.float32(np.inf)), np.nextafter(x, np.float32(0))
+        assert O.e4m3_encode(np.array([up]))[0] == i + 1
+        assert O.e4m3_encode(np.array([dn]))[0] == i
+    # saturation: the largest finite value and everything above it, infinity included
+    big = np.array([448, 449, 463.9, 464, 480, 1e6, np.inf], dtype=np.float32)
+    assert np.all(O.e4m3_encode(big) == 0x7E) and np.all(O.e4m3_encode(-big) == 0xFE)
+    assert O.e4m3_encode(np.array([-0.0], np.float32))[0] == 0x80
+
+
+def test_e4m3_nearest_value_brute_force():
+    rng = np.random.default_rng(60)
+    x = (rng.standard_normal(3000) * np.exp(rng.uniform(-12, 7, 3000))).astype(np.float32)
+    mags = np.array([float(m) for m in _e4m3_magnitudes_by_construction()])
+    got = O.e4m3_decode(O.e4m3_encode(x))
+    err = np.abs(np.abs(got) - np.abs(x.astype(np.float64)))
+    best = np.min(np.abs(mags[None, :] - np.minimum(np.abs(x), 448)[:, None]), axis=1)
+    assert np.all(err[np.abs(x) <= 448] == best[np.abs(x) <= 448])
+    assert np.all(np.signbit(got) == np.signbit(x))  # values that round to zero keep their sign
+
+
+def test_fp8_cache_rows_are_scaled_e4m3_values():
+    """b = 8 units: quantized rows decode to E4M3 values times the head's scale,
+    within half an E4M3 step of x / s (relative 2^-4 for normal values)."""
+    rng = np.random.default_rng(61)
+    k = (rng.standard_normal((300, 128)) * 3).astype(np.float16)
+    v = rng.standard_normal((300, 128)).astype(np.float16)
+    sk, sv = 0.0625, 1.5
+    u = O.UnitCache(O.CacheParams(bits=8, group=32, residual=40, fp8_scale_k=sk, fp8_scale_v=sv))
+    u.append(k[:77], v[:77])
+    u.append(k[77:], v[77:])
+    assert u.n_q == 256
+    K, V = u.dequantized_kv()
+    for X, x16, s in ((K, k, sk), (V, v, sv)):
+        xs = x16[:256].astype(np.float64) / s
+        xh = X[:256] / s
+        assert np.all(np.abs(xh) <= 448)
+        normal = np.abs(xs) >= 2 ** -6
+        assert np.all(np.abs(xh - xs)[normal] <= np.abs(xs)[normal] * 2.0 ** -4)
+        assert np.all(np.abs(xh - xs)[~normal] <= 2.0 ** -10)
+        assert np.array_equal(X[256:], x16[256:].astype(np.float64))
