@@ -209,6 +209,8 @@ ROWS = {
     "evict_minikv": ("minikv", "f2: one H2O eviction per KV head (budget 20% + 256 recent)"),
     "decode_llama8b_g16": ("llama8b_g16", "a8-a10: fused decode + merge at group size 16"),
     "decode_llama8b_sinks": ("llama8b_sinks", "a8-a10 with 4 attention sinks in the fp16 partition"),
+    "append_llama8b_fp8": ("llama8b_fp8", "f4: bulk FP8 E4M3 encode of the whole prefix, ring store"),
+    "decode_llama8b_fp8": ("llama8b_fp8", "f4: fused FP8 E4M3 decode + merge"),
     "decode_long_b2g32": ("long_b2g32", "a8-a10: fused decode + merge, split-K over context"),
     "decode_long_b2g128": ("long_b2g128", "a8-a10: fused decode + merge, split-K over context"),
     "decode_long_b4g32": ("long_b4g32", "a8-a10: fused decode + merge, split-K over context"),
@@ -311,7 +313,8 @@ def rows_main(args):
                                           bits=w.bits, group=w.group)
             emit(name, w, us, nbytes, {"kernels": ["ott_score_kernel", "ott_scan_kernel",
                                                    "pack_kernel", "ring_store_kernel"]
-                                       if w.pool else ["pack_kernel", "ring_store_kernel"]})
+                                       if w.pool else ["pack8_kernel" if w.bits == 8
+                                                       else "pack_kernel", "ring_store_kernel"]})
             continue
         srcs = source(w)
         cfg, reps = caches(w)
@@ -337,7 +340,8 @@ def rows_main(args):
             nbytes = BM.decode_step_bytes(units=U, gqa=w.gqa, head_dim=d, tokens=w.tokens,
                                           bits=w.bits, group=w.group, residual=w.residual,
                                           h2o=w.h2o, sinks=w.sinks).total
-            emit(name, w, us, nbytes, {"kernels": ["decode_kernel", "merge_kernel"]})
+            emit(name, w, us, nbytes, {"kernels": ["decode8_kernel" if w.bits == 8 else "decode_kernel",
+                                                   "merge_kernel"]})
         elif name.startswith("evict"):  # one eviction step on accumulated scores
             for rep in reps:
                 abi.decode_attention(rep["h"], q, out, rep["acc"], ws)

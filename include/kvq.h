@@ -40,6 +40,11 @@
  *    Oracle", greedy eviction; "KV cache quantization and eviction",
  *    h2o_evict in "Minimal implementation"); per-layer budgets by MiniKV's
  *    pyramid (section 4.2).
+ *  - A second codec, FP8 E4M3 (bits = 8): each element stored as the
+ *    saturating round-to-nearest-even E4M3 value of x / s, with one fp32
+ *    scale s per KV head for keys and one for values ("KV cache quantization
+ *    and eviction", sections "FP8, KIVI and KVQuant" and "Failure modes and
+ *    how to detect them").
  *  - Heavy-hitter selection: the k highest scores outside a recent window of
  *    w tokens, plus that window (MiniKV, Algorithm 1; "KV cache quantization
  *    and eviction", section "Minimal implementation").
@@ -96,7 +101,8 @@ const char* kvq_status_string(kvq_status status);
 
 /*
  * Cache configuration (host POD).
- *   bits        b in {2, 4}
+ *   bits        b in {2, 4}: integer codes; 8: the FP8 E4M3 codec (then group
+ *               must be 32 and pool 0: no groups, zero points or OTT)
  *   group       G in {32, 64, 128}: tokens per key group and, capped at d,
  *               channels per value group (one group size for both axes, MiniKV
  *               section 5.1)
@@ -158,6 +164,10 @@ typedef struct kvq_config {
  *   evict     uint32 [U][ceil((max_tokens - S) / 32)]: bit i of word c set when
  *             token S + 32c + i was evicted (kvq_evict_step)
  *   evict_count int32 [U]: evicted tokens per unit
+ *   fp8_scales fp32 [Hkv][2] (b = 8): key and value scale per KV head, 1.0
+ *             after kvq_cache_init
+ * At b = 8, kq / vq hold one E4M3 byte per element (4 KB per chunk each) in
+ * the decoder's operand order and kmeta / vmeta are empty.
  * Slots of pool_idx / ev_idx beyond the counters are unspecified.
  *
  * Packed code layout. Codes of 32 consecutive quantized tokens form a chunk
@@ -182,6 +192,7 @@ typedef struct kvq_cache {
     uint64_t off_ev_idx, off_ev_k, off_ev_v, off_counters, off_scores;
     uint64_t off_sink_k, off_sink_v;
     uint64_t off_evict, off_evict_count;
+    uint64_t off_fp8_scales;
 } kvq_cache;
 
 /* Bytes of device memory a cache with this configuration needs (host only).
@@ -305,6 +316,18 @@ kvq_status kvq_decode_step_timed(kvq_cache* h, const void* d_k, const void* d_v,
  */
 kvq_status kvq_topk_evict(const float* d_scores, int32_t rows, int32_t T, int32_t k,
                           int32_t w, int32_t* d_idx, void* stream);
+
+/*
+ * Set the FP8 scales of a b = 8 cache: d_scales is device fp32 [Hkv][2] (key
+ * scale, value scale per KV head), finite and positive (not checked on the
+ * device). Elements are stored as E4M3(x / s) and read back as E4M3 * s; set
+ * the scales before the first append, since stored codes are not re-encoded
+ * ("KV cache quantization and eviction", section "FP8, KIVI and KVQuant":
+ * scales set to 1.0 or calibrated, optionally per attention head).
+ * Errors: KVQ_EINVAL (invalid handle or null d_scales), KVQ_EUNSUPPORTED
+ * (b != 8).
+ */
+kvq_status kvq_fp8_set_scales(kvq_cache* h, const float* d_scales, void* stream);
 
 /*
  * One H2O eviction step ("H2O: Heavy-Hitter Oracle", greedy eviction of the

@@ -29,7 +29,7 @@ EXPORTS = ("kvq_status_string", "kvq_cache_bytes", "kvq_cache_init", "kvq_quanti
            "kvq_decode_workspace", "kvq_decode_attention", "kvq_decode_attention_timed",
            "kvq_decode_step", "kvq_decode_step_timed", "kvq_topk_evict", "kvq_unpack_codes",
            "kvq_decode_attention_noalloc", "kvq_debug_unpack", "kvq_evict_step",
-           "kvq_pyramid_budgets")
+           "kvq_pyramid_budgets", "kvq_fp8_set_scales")
 
 
 class Config(ctypes.Structure):
@@ -46,7 +46,7 @@ class Cache(ctypes.Structure):
             "off_kq", "off_vq", "off_kmeta", "off_vmeta", "off_mask", "off_kring", "off_vring",
             "off_pool_idx", "off_pool_score", "off_pool_k", "off_pool_v", "off_ev_idx",
             "off_ev_k", "off_ev_v", "off_counters", "off_scores", "off_sink_k", "off_sink_v",
-            "off_evict", "off_evict_count")]
+            "off_evict", "off_evict_count", "off_fp8_scales")]
 
 
 class DebugView(ctypes.Structure):
@@ -93,6 +93,7 @@ def lib() -> ctypes.CDLL:
             "kvq_unpack_codes": [ctypes.POINTER(Cache), P, P, P],
             "kvq_debug_unpack": [ctypes.POINTER(Cache), ctypes.POINTER(DebugView), P],
             "kvq_evict_step": [ctypes.POINTER(Cache), P, I32, I32, P],
+            "kvq_fp8_set_scales": [ctypes.POINTER(Cache), P, P],
             "kvq_pyramid_budgets": [I32, I32, I32, ctypes.POINTER(I32)],
         }
         for name, args in sigs.items():
@@ -227,3 +228,9 @@ def pyramid_budgets(n_layers: int, avg_budget: int, depth: int) -> list:
     out = (ctypes.c_int32 * n_layers)()
     _check("kvq_pyramid_budgets", lib().kvq_pyramid_budgets(n_layers, avg_budget, depth, out))
     return list(out)
+
+
+def fp8_set_scales(h: Cache, scales, stream=None) -> None:
+    """kvq_fp8_set_scales: device fp32 [Hkv][2] key / value scales of a b = 8 cache."""
+    _check("kvq_fp8_set_scales", lib().kvq_fp8_set_scales(ctypes.byref(h), _ptr(scales),
+                                                          _stream(stream)))

@@ -60,7 +60,8 @@ def decode_step_bytes(*, units: int, gqa: int, head_dim: int, tokens: int, bits:
     gv = min(G, d)
     nq = n_quantized(max(0, tokens - sinks), residual, G)
     nres = tokens - nq
-    quant = units * nq * (d * bits // 4 + 4 * d // G + 4 * d // gv)
+    meta = 0 if bits == 8 else 4 * d // G + 4 * d // gv  # FP8: no scale / zero words
+    quant = units * nq * (d * bits // 4 + meta)
     resid = units * nres * 4 * d
     pools = pool_tokens * (4 * d + 4)
     qo = units * gqa * d * (2 + 4)
@@ -93,7 +94,7 @@ def bulk_append_bytes(*, units: int, head_dim: int, tokens: int, n_quant: int, b
     """
     d, G = head_dim, group
     gv = min(G, d)
-    per_q = d * bits // 4 + 4 * d // G + 4 * d // gv
+    per_q = d * bits // 4 + (0 if bits == 8 else 4 * d // G + 4 * d // gv)
     return units * (tokens * 4 * d + n_quant * per_q + (tokens - n_quant) * 4 * d)
 
 

@@ -38,7 +38,9 @@ kvq_status check_config(const kvq_config* c) {
         return KVQ_EINVAL;
     if (c->n_q_heads % c->n_kv_heads != 0) return KVQ_EINVAL;
     const int r = c->n_q_heads / c->n_kv_heads;
-    if (c->bits != 2 && c->bits != 4) return KVQ_EUNSUPPORTED;
+    if (c->bits != 2 && c->bits != 4 && c->bits != 8) return KVQ_EUNSUPPORTED;
+    // the FP8 codec has no groups or outlier pools; 32 is its chunk size
+    if (c->bits == 8 && (c->group != 32 || c->pool != 0)) return KVQ_EUNSUPPORTED;
     if (c->group != 16 && c->group != 32 && c->group != 64 && c->group != 128)
         return KVQ_EUNSUPPORTED;
     if (c->head_dim != kHeadDim) return KVQ_EUNSUPPORTED;
@@ -51,7 +53,7 @@ kvq_status check_config(const kvq_config* c) {
     return KVQ_OK;
 }
 
-constexpr int kRegions = 20;
+constexpr int kRegions = 21;
 
 struct Layout {
     uint64_t off[kRegions];
@@ -73,8 +75,8 @@ Layout layout_of(const kvq_config* c) {
     const uint64_t sizes[kRegions] = {
         U * C * 128 * b * 4,          // kq
         U * C * 128 * b * 4,          // vq
-        U * key_groups_of(G, C) * d * 4,  // kmeta
-        U * C * NG * kChunk * 4,      // vmeta
+        b == 8 ? 0 : U * key_groups_of(G, C) * d * 4,  // kmeta
+        b == 8 ? 0 : U * C * NG * kChunk * 4,          // vmeta
         U * C * 4,                    // mask
         U * L.ring * d * 2,           // kring
         U * L.ring * d * 2,           // vring
@@ -91,6 +93,7 @@ Layout layout_of(const kvq_config* c) {
         U * S * d * 2,                // sink_v
         U * evict_words_of(c) * 4,    // evict
         U * 4,                        // evict_count
+        (uint64_t)c->n_kv_heads * 8,  // fp8_scales
     };
     uint64_t o = 0;
     for (int i = 0; i < kRegions; ++i) {
@@ -146,6 +149,7 @@ CacheView view_of(const kvq_cache* h) {
     v.evict = reinterpret_cast<uint32_t*>(a + h->off_evict);
     v.evict_count = reinterpret_cast<int32_t*>(a + h->off_evict_count);
     v.evict_words = (int64_t)evict_words_of(&h->cfg);
+    v.fp8_scales = reinterpret_cast<float*>(a + h->off_fp8_scales);
     v.bits = h->cfg.bits;
     v.group = h->cfg.group;
     v.residual = h->cfg.residual;
@@ -253,7 +257,8 @@ kvq_status kvq_cache_init(const kvq_config* cfg, void* d_arena, size_t bytes, kv
                                 &c.off_kring, &c.off_vring, &c.off_pool_idx, &c.off_pool_score,
                                 &c.off_pool_k, &c.off_pool_v, &c.off_ev_idx, &c.off_ev_k,
                                 &c.off_ev_v, &c.off_counters, &c.off_scores, &c.off_sink_k,
-                                &c.off_sink_v, &c.off_evict, &c.off_evict_count};
+                                &c.off_sink_v, &c.off_evict, &c.off_evict_count,
+                                &c.off_fp8_scales};
     for (int i = 0; i < kRegions; ++i) *offs[i] = L.off[i];
     st = launch_status(launch_init(view_of(&c), stream));
     if (st == KVQ_OK) *h = c;
@@ -372,6 +377,12 @@ kvq_status kvq_unpack_codes(const kvq_cache* h, uint8_t* d_kcodes, uint8_t* d_vc
     if (h->n_quant == 0) return KVQ_OK;
     if (!d_kcodes || !d_vcodes) return KVQ_EINVAL;
     return launch_status(launch_unpack(view_of(h), h->n_quant, d_kcodes, d_vcodes, stream));
+}
+
+kvq_status kvq_fp8_set_scales(kvq_cache* h, const float* d_scales, void* stream) {
+    if (!valid_handle(h) || !d_scales) return KVQ_EINVAL;
+    if (h->cfg.bits != 8) return KVQ_EUNSUPPORTED;
+    return launch_status(launch_fp8_scales(view_of(h), d_scales, stream));
 }
 
 kvq_status kvq_evict_step(kvq_cache* h, const float* d_acc, int32_t budget, int32_t recent,

@@ -145,6 +145,7 @@ struct DecodeArgs {
     int32_t sink_cap;   // S: sinks per unit; the quantized tokens are S .. S + n_q - 1
     int32_t sink_rows;  // min(T, S): sink rows present
     float qscale;  // log2(e) / sqrt(d)
+    const float* fp8_scales;  // b = 8: [Hkv][2] key and value scale per KV head
 };
 
 __device__ __forceinline__ float h2f(uint32_t h) {
@@ -971,6 +972,296 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     }
 }
 
+// FP8 E4M3 cache (b = 8): decode over 32-token chunks of E4M3 bytes, 4 KB of
+// keys and 4 KB of values each, in the operand order pack8_kernel writes.
+// Same block roles, split plan, softmax and partial records as decode_kernel;
+// differences: the key scale is one number per KV head, so the query is folded
+// (and split into fp16 hi + lo) once per wavefront; codes become exact fp16
+// operands with one v_cvt_scalef32_pk_f16_fp8 per pair (every E4M3 value is an
+// fp16 value); there are no zero points; the value scale multiplies the
+// block's output. A wavefront's chunks are loaded straight into registers one
+// chunk ahead ("KV cache quantization and eviction", section "FP8, KIVI and
+// KVQuant"; MiniKV, section 4.4: dequantization fused into the attention).
+__device__ __forceinline__ half8 fp8x8_to_half8(uint32_t w0, uint32_t w1) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+    const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+    const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+    const h2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+    return half8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+template <int R>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 4 ? 3 : 2))) void decode8_kernel(DecodeArgs a) {
+    constexpr bool kSplitExp = R == 4;
+    constexpr bool kMirror = kSplitExp;
+    constexpr int kWaveAcc = 8 * 64 * 4;  // floats: a wavefront's output accumulators
+    __shared__ __align__(16) float smem[4 * kWaveAcc > kFp16Bytes / 4 ? 4 * kWaveAcc : kFp16Bytes / 4];
+    __shared__ __align__(16) float s_pbuf[4][128];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if ((int)blockIdx.x < a.units * a.fp16_tiles) {
+        fp16_tile<R>(a, blockIdx.x / a.fp16_tiles, blockIdx.x % a.fp16_tiles, smem);
+        return;
+    }
+    const int idx = blockIdx.x - a.units * a.fp16_tiles;
+    const int u = idx / a.splits_q, split = idx % a.splits_q;
+    const int b = u / a.n_kv_heads, hk = u % a.n_kv_heads;
+    const uint32_t items = (uint32_t)(a.n_q / 32);
+    const uint32_t gs0 = (uint32_t)((int64_t)split * items / a.splits_q);
+    const uint32_t gs1 = (uint32_t)((int64_t)(split + 1) * items / a.splits_q);
+    const uint32_t n_items = gs1 - gs0 > (uint32_t)wave ? (gs1 - gs0 - wave + 3) / 4 : 0;
+    const uint4* kq_u = reinterpret_cast<const uint4*>(a.kq) + (int64_t)u * a.chunks * 256;
+    const uint4* vq_u = reinterpret_cast<const uint4*>(a.vq) + (int64_t)u * a.chunks * 256;
+    const uint32_t* mk_u = a.mask + (int64_t)u * a.chunks;
+    const uint32_t* ev_u = a.evict + (int64_t)u * a.evict_words;
+
+    // lane roles as in decode_kernel
+    const int j = lane & 15, kb = lane >> 4, jj = j & 7;
+    const int hq = kMirror ? (jj < 4 ? jj : 7 - jj) : j % R;
+    const int pq = jj < 4 ? 0 : 1;
+    const int cq = kMirror ? pq + 2 * (j >> 3) : j >> 2;
+    const int ha = j % R;
+    const int own_tok = 16 * (cq >> 1) + 4 * kb + 2 * (cq & 1);
+    const float sk = __builtin_bit_cast(float, scalar_load(a.fp8_scales + 2 * hk));
+    const float sv = __builtin_bit_cast(float, scalar_load(a.fp8_scales + 2 * hk + 1));
+
+    // Folded query, B operand of the key products: column j holds head hq,
+    // channels 32 ks + 8 kb .. + 7 of q * log2(e) / sqrt(d) * s_K, fp16 hi
+    // (pq = 0) or lo (pq = 1) with kMirror (kept in Bh); both hi (Bh) and lo
+    // (Bl) otherwise.
+    half8 Bh[4], Bl[4];
+    {
+        const uint32_t one = 0x3C00u;  // fp16 1.0 in the low half
+        const float f = a.qscale * sk;
+        const uint4* qr = reinterpret_cast<const uint4*>(
+            a.q + ((int64_t)b * a.n_kv_heads * R + hk * R + hq) * D);
+        uint4 qw[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qw[ks] = qr[(32 * ks + 8 * kb) / 8];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const uint32_t w[4] = {qw[ks].x, qw[ks].y, qw[ks].z, qw[ks].w};
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x0 = h2f(w[i] & 0xFFFF) * f, x1 = h2f(w[i] >> 16) * f;
+                hi[i] = mul_pk(x0, one, x1, one);
+                lo[i] = mul_pk_res(x0, one, x1, one, hi[i]);
+            }
+            Bh[ks] = kMirror && pq ? as_half8(lo[0], lo[1], lo[2], lo[3])
+                                   : as_half8(hi[0], hi[1], hi[2], hi[3]);
+            Bl[ks] = as_half8(lo[0], lo[1], lo[2], lo[3]);
+        }
+    }
+    float* pbuf = s_pbuf[wave];
+    float m_run = -INFINITY, lsum = 0.f, m_thr = -INFINITY;
+    constexpr float tau = 8.f;  // lazy rescale threshold: p < 2^8 in fp16
+    floatx4 O[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto load = [&](uint32_t k, uint4 (&kr)[4], uint4 (&vr)[4]) {
+        const uint32_t ch = gs0 + wave + 4 * k;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) kr[w] = kq_u[ch * 256 + w * 64 + lane];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) vr[w] = vq_u[ch * 256 + w * 64 + lane];
+    };
+    auto compute = [&](uint32_t k, const uint4 (&kr)[4], const uint4 (&vr)[4]) {
+        const uint32_t ch = gs0 + wave + 4 * k;
+        const int64_t tb = (int64_t)ch * 32;
+        floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const uint4 r0 = kr[ks / 2], r1 = kr[2 + ks / 2];  // tiles 0 and 1
+            const half8 A0 = ks % 2 ? fp8x8_to_half8(r0.z, r0.w) : fp8x8_to_half8(r0.x, r0.y);
+            const half8 A1 = ks % 2 ? fp8x8_to_half8(r1.z, r1.w) : fp8x8_to_half8(r1.x, r1.y);
+            if (kMirror) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bh[ks], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh[ks], acc1, 0, 0, 0);
+            } else {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bh[ks], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bh[ks], acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bl[ks], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bl[ks], acc1, 0, 0, 0);
+            }
+        }
+        if (kMirror) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc0[i] += dpp<0x141>(acc0[i]);  // hi + lo of the head
+                acc1[i] += dpp<0x141>(acc1[i]);
+            }
+        }
+        // pool members are never set at b = 8; evicted tokens are skipped
+        const uint32_t mw = scalar_load(mk_u + ch) | scalar_load(ev_u + ch);
+        float p[8];
+        if constexpr (kSplitExp) {
+            const float a0 = cq & 1 ? acc0[2] : acc0[0], b0 = cq & 1 ? acc1[2] : acc1[0];
+            const float a1 = cq & 1 ? acc0[3] : acc0[1], b1 = cq & 1 ? acc1[3] : acc1[1];
+            float s0 = cq < 2 ? a0 : b0, s1 = cq < 2 ? a1 : b1;
+            if (mw) {
+                if ((mw >> own_tok) & 1u) s0 = -INFINITY;
+                if ((mw >> (own_tok + 1)) & 1u) s1 = -INFINITY;
+            }
+            if (a.logits) {
+                float* lg = a.logits + ((int64_t)u * R + hq) * a.T + a.sink_cap + tb + own_tok;
+                if (s0 != -INFINITY) lg[0] = s0;
+                if (s1 != -INFINITY) lg[1] = s1;
+            }
+            const float lm = fmaxf(s0, s1);
+            if (__any(lm > m_thr)) {
+                float cm = fmaxf(lm, row_ror<8>(lm));
+                cm = fmaxf(cm, dpp<0x141>(cm));
+                cm = max_x32(max_x16(cm));
+                const float mnew = fmaxf(m_run, cm);
+                if (__builtin_amdgcn_readfirstlane(m_run != -INFINITY)) {
+                    const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+                    const float ah[4] = {readlane(alpha, 0), readlane(alpha, 1), readlane(alpha, 2),
+                                         readlane(alpha, 3)};
+                    lsum *= alpha;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int nt = 0; nt < 8; ++nt) O[nt][i] *= ah[i];
+                }
+                m_run = mnew;
+                m_thr = mnew + tau;
+            }
+            const float mu = m_run == -INFINITY ? 0.f : m_run;
+            const float p0 = __builtin_amdgcn_exp2f(s0 - mu), p1 = __builtin_amdgcn_exp2f(s1 - mu);
+            lsum += p0 + p1;
+            *reinterpret_cast<float2*>(pbuf + hq * 32 + own_tok) = float2{p0, p1};
+            wave_lds_fence();
+            const float* ph = pbuf + ha * 32;
+            const floatx4 pa = *reinterpret_cast<const floatx4*>(ph + 4 * kb);
+            const floatx4 pb = *reinterpret_cast<const floatx4*>(ph + 16 + 4 * kb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = pa[i];
+                p[4 + i] = pb[i];
+            }
+        } else {
+            float s[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s[i] = acc0[i];
+                s[4 + i] = acc1[i];
+            }
+            if (mw) {
+#pragma unroll
+                for (int sl = 0; sl < 8; ++sl) {
+                    const int tok = 16 * (sl / 4) + 4 * kb + sl % 4;
+                    if ((mw >> tok) & 1u) s[sl] = -INFINITY;
+                }
+            }
+            if (a.logits && j < R) {
+                float* lg = a.logits + ((int64_t)u * R + j) * a.T + a.sink_cap + tb + 4 * kb;
+#pragma unroll
+                for (int sl = 0; sl < 8; ++sl)
+                    if (s[sl] != -INFINITY) lg[16 * (sl / 4) + sl % 4] = s[sl];
+            }
+            float lm = s[0];
+#pragma unroll
+            for (int sl = 1; sl < 8; ++sl) lm = fmaxf(lm, s[sl]);
+            if (__any(lm > m_thr)) {
+                const float cm = max_x32(max_x16(lm));
+                const float mnew = fmaxf(m_run, cm);
+                if (__builtin_amdgcn_readfirstlane(m_run != -INFINITY)) {
+                    const float alpha = __builtin_amdgcn_exp2f(m_run - mnew);
+                    lsum *= alpha;
+                    float ah[4];
+                    ah[0] = quad_bcast<0>(alpha);
+                    if (R > 1) ah[1] = quad_bcast<1>(alpha);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int nt = 0; nt < 8; ++nt) O[nt][i] *= ah[i % R];
+                }
+                m_run = mnew;
+                m_thr = mnew + tau;
+            }
+            const float mu = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+            for (int sl = 0; sl < 8; ++sl) {
+                p[sl] = __builtin_amdgcn_exp2f(s[sl] - mu);
+                lsum += p[sl];
+            }
+        }
+        // values: A = fp16 hi / lo of p (rows: head j % r), B = the value codes
+        const uint32_t one = 0x3C00u;
+        uint32_t ahw[4], alw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ahw[i] = mul_pk(p[2 * i], one, p[2 * i + 1], one);
+            alw[i] = mul_pk_res(p[2 * i], one, p[2 * i + 1], one, ahw[i]);
+        }
+        const half8 Ahi = as_half8(ahw[0], ahw[1], ahw[2], ahw[3]);
+        const half8 Alo = as_half8(alw[0], alw[1], alw[2], alw[3]);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            const uint4 r = vr[nt / 2];
+            const half8 Bv = nt % 2 ? fp8x8_to_half8(r.z, r.w) : fp8x8_to_half8(r.x, r.y);
+            O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bv, O[nt], 0, 0, 0);
+            O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bv, O[nt], 0, 0, 0);
+        }
+    };
+    // two register sets, one chunk ahead
+    uint4 kA[4], vA[4], kB[4], vB[4];
+    if (n_items > 0) load(0, kA, vA);
+    for (uint32_t k = 0; k < n_items; k += 2) {
+        if (k + 1 < n_items) load(k + 1, kB, vB);
+        compute(k, kA, vA);
+        if (k + 1 < n_items) {
+            if (k + 2 < n_items) load(k + 2, kA, vA);
+            compute(k + 1, kB, vB);
+        }
+    }
+
+    // Wavefront epilogue, then the block combine of the four wavefronts.
+    float lt = lsum;
+    if (kSplitExp) {
+        lt += row_ror<8>(lt);
+        lt += dpp<0x141>(lt);
+    }
+    lt = sum_x32(sum_x16(lt));
+    float* obuf = smem + wave * kWaveAcc;  // [8][64][4] as in the accumulators
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+        *reinterpret_cast<floatx4*>(obuf + nt * 256 + lane * 4) = O[nt];
+    if (kb == 0 && j < R) {
+        pbuf[32 + j] = m_run;
+        pbuf[36 + j] = lt;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < R * D; e += 256) {
+        const int h = e / D, c = e % D, nt = c / 16;
+        const int src = (nt * 64 + (c % 16) + 16 * (h / 4)) * 4 + h % 4;  // accumulator row h
+        float mw[4], M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            mw[w] = s_pbuf[w][32 + h];
+            M = fmaxf(M, mw[w]);
+        }
+        float o = 0.f, l = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float f = mw[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[w] - M);
+                o += smem[w * kWaveAcc + src] * f;
+                l += s_pbuf[w][36 + h] * f;
+            }
+        }
+        float* rec = a.part + (((int64_t)u * a.splits + split) * R + h) * kRec;
+        rec[c] = o * sv;
+        if (c == 0) {
+            rec[D] = M;
+            rec[D + 1] = l;
+        }
+    }
+}
+
 // Merge of the split partials. Block x serves unit x / r. Blocks y = 0 write
 // the outputs of head x % r: wavefront w sums a contiguous quarter of the
 // splits, and the four partial sums are added in order, so results do not
@@ -1142,6 +1433,37 @@ void launch_decode_t(DecodeArgs a, hipEvent_t e0, hipEvent_t e1, hipStream_t s) 
     hipLaunchKernelGGL((merge_kernel<R>), dim3(a.units * R, ny), dim3(256), 0, s, a);
 }
 
+template <int R>
+int resident8_blocks() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int cus = 0, per = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per, reinterpret_cast<const void*>(decode8_kernel<R>), 256, 0) != hipSuccess)
+            cus = per = 0;
+        cached[dev] = cus * per > 0 ? cus * per : 512;
+    }
+    return cached[dev];
+}
+
+template <int R>
+void launch_decode8_t(DecodeArgs a, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
+    const int64_t fp16_rows = (a.T - a.n_q) + (a.pool > 0 ? (int64_t)a.pool + a.evict_cap : 0);
+    a.tile_rows = fp16_rows > 0 ? (int32_t)((fp16_rows + a.fp16_tiles - 1) / a.fp16_tiles) : 1;
+    const unsigned blocks = (unsigned)(a.units * a.fp16_tiles + a.units * a.splits_q);
+    (void)hipGetLastError();  // the device queries of the plan may have left an error
+    if (e0 || e1)
+        hipExtLaunchKernelGGL((decode8_kernel<R>), dim3(blocks), dim3(256), 0, s, e0, e1, 0, a);
+    else
+        hipLaunchKernelGGL((decode8_kernel<R>), dim3(blocks), dim3(256), 0, s, a);
+    const unsigned ny = 1 + (a.acc ? (unsigned)((a.T + kH2OChunk - 1) / kH2OChunk) : 0u);
+    hipLaunchKernelGGL((merge_kernel<R>), dim3(a.units * R, ny), dim3(256), 0, s, a);
+}
+
 template <int BITS, int R>
 void dispatch_g(const DecodeArgs& a, int G, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
     if (G == 16) launch_decode_t<BITS, R, 16>(a, e0, e1, s);
@@ -1169,7 +1491,10 @@ int resident_g(int G) {
 
 void decode_launch_shape(int bits, int r, int group, int* cus, int* resident) {
     *cus = cu_count();
-    if (bits == 2)
+    if (bits == 8)
+        *resident = r == 1 ? resident8_blocks<1>() : r == 2 ? resident8_blocks<2>()
+                                                            : resident8_blocks<4>();
+    else if (bits == 2)
         *resident = r == 1 ? resident_g<2, 1>(group) : r == 2 ? resident_g<2, 2>(group)
                                                               : resident_g<2, 4>(group);
     else
@@ -1256,8 +1581,16 @@ int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& 
     const int R = v.n_q_heads / v.n_kv_heads;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipEvent_t e0 = static_cast<hipEvent_t>(ev_start), e1 = static_cast<hipEvent_t>(ev_stop);
-    if (v.bits == 2) dispatch_r<2>(a, R, v.group, e0, e1, s);
-    else dispatch_r<4>(a, R, v.group, e0, e1, s);
+    a.fp8_scales = v.fp8_scales;
+    if (v.bits == 8) {
+        if (R == 1) launch_decode8_t<1>(a, e0, e1, s);
+        else if (R == 2) launch_decode8_t<2>(a, e0, e1, s);
+        else launch_decode8_t<4>(a, e0, e1, s);
+    } else if (v.bits == 2) {
+        dispatch_r<2>(a, R, v.group, e0, e1, s);
+    } else {
+        dispatch_r<4>(a, R, v.group, e0, e1, s);
+    }
     return (int)hipGetLastError();
 }
 

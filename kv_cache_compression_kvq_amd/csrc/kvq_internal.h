@@ -42,6 +42,7 @@ struct CacheView {
     uint32_t* evict;     // [U][evict_words]: eviction bits of tokens S, S + 1, ...
     int32_t* evict_count;  // [U]
     int64_t evict_words;
+    float* fp8_scales;   // [Hkv][2] (b = 8)
     int32_t sinks;       // S
     int32_t bits, group, residual, pool, evict_cap;
     int32_t n_q_heads, n_kv_heads, batch;
@@ -86,6 +87,7 @@ int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& 
 int launch_topk(const float* scores, int32_t rows, int32_t T, int32_t k, int32_t w,
                 int32_t* idx, void* stream);
 int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, void* stream);
+int launch_fp8_scales(const CacheView& v, const float* scales, void* stream);
 int launch_evict_step(const CacheView& v, int64_t T, const float* acc, int32_t budget,
                       int32_t recent, void* stream);
 int launch_debug_unpack(const CacheView& v, int64_t T, int64_t n_q, const kvq_debug_view& out,

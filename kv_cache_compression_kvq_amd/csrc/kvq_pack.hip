@@ -116,6 +116,8 @@ __global__ void init_kernel(CacheView v) {
     const int64_t nv = v.group == 16 ? (int64_t)v.units * v.chunks * (D / 16) * kChunk : 0;
     const int64_t ne = (int64_t)v.units * v.evict_words, nu = v.units;
     const int64_t n1 = nc + nm, n2 = n1 + nk, n3 = n2 + nv, n4 = n3 + ne, n5 = n4 + nu;
+    if (v.bits == 8 && blockIdx.x == 0 && threadIdx.x < 2 * v.n_kv_heads)
+        v.fp8_scales[threadIdx.x] = 1.0f;  // FP8 scales: 1.0 until set
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n5;
          i += (int64_t)gridDim.x * blockDim.x) {
         if (i < nc) v.counters[i] = 0;
@@ -744,6 +746,78 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
     }
 }
 
+// FP8 E4M3 code of an fp32 value, exactly: round to nearest, ties to even,
+// saturating at +-448 (OCP E4M3: bias 7, no infinity, S.1111.111 is NaN;
+// "KV cache quantization and eviction", sections "FP8, KIVI and KVQuant" and
+// "Failure modes and how to detect them": casts must saturate). Every step
+// below is exact in fp32 except the final rounding to the 3-bit mantissa.
+__device__ __forceinline__ uint32_t e4m3_sat(float x) {
+    const uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u;
+    const float a = fabsf(x);
+    if (a != a) return sign | 0x7Fu;
+    if (a >= 448.0f) return sign | 0x7Eu;
+    if (a < 0x1p-6f) return sign | (uint32_t)rintf(a * 512.0f);  // subnormal steps of 2^-9
+    int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFF) - 127;  // a is a normal fp32
+    const float mant = ldexpf(a, -e);                                    // in [1, 2)
+    uint32_t m = (uint32_t)rintf((mant - 1.0f) * 8.0f);
+    if (m == 8) {
+        m = 0;
+        ++e;
+    }
+    return sign | (uint32_t)((e + 7) << 3) | m;
+}
+
+// FP8 codec: one block per (unit, 32-token chunk). Keys and values are
+// encoded element by element as E4M3(x / s) with the KV head's scales and
+// written in the decoder's operand order: 4 KB per chunk and tensor, lane l
+// of 16-byte group w at byte w * 1024 + l * 16.
+//   keys:   group w = 2 tau + ks / 2; bytes 8 (ks % 2) + e hold channel
+//           32 ks + 8 (l / 16) + e of token 16 tau + l % 16;
+//   values: group w; bytes 8 i + sl hold channel 16 (2 w + i) + l % 16 of
+//           token 16 (sl / 4) + 4 (l / 16) + sl % 4.
+__global__ __launch_bounds__(256) void pack8_kernel(CacheView v, const uint16_t* knew,
+                                                    const uint16_t* vnew, int64_t t_old,
+                                                    int32_t n_new, int64_t c0) {
+    __shared__ __align__(16) uint16_t kx[kChunk][kPackRow], vx[kChunk][kPackRow];
+    const int u = (int)(blockIdx.x % (uint32_t)v.units), tid = threadIdx.x;
+    const int64_t ch = c0 + blockIdx.x / (uint32_t)v.units, t0 = ch * kChunk;
+    {
+        uint4 kr[2], vr[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int e = tid + 256 * j, i = e / 16, part = e % 16;
+            kr[j] = reinterpret_cast<const uint4*>(src_row(v.kring, knew, v, u, t0 + i, t_old, n_new))[part];
+            vr[j] = reinterpret_cast<const uint4*>(src_row(v.vring, vnew, v, u, t0 + i, t_old, n_new))[part];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int e = tid + 256 * j, i = e / 16, part = e % 16;
+            reinterpret_cast<uint4*>(&kx[i][0])[part] = kr[j];
+            reinterpret_cast<uint4*>(&vx[i][0])[part] = vr[j];
+        }
+    }
+    __syncthreads();
+    const int hk = u % v.n_kv_heads;
+    const float sk = v.fp8_scales[2 * hk], sv = v.fp8_scales[2 * hk + 1];
+    const int w = tid / 64, l = tid % 64, n = l % 16, kb = l / 16;
+    uint32_t kw[4] = {0, 0, 0, 0}, vw[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int byte = 0; byte < 16; ++byte) {
+        // key byte: k-step ks = 2 (w % 2) + byte / 8, element e = byte % 8
+        const int tau = w / 2, ks = 2 * (w % 2) + byte / 8, e = byte % 8;
+        const uint32_t ck = e4m3_sat(h2f(kx[16 * tau + n][32 * ks + 8 * kb + e]) / sk);
+        kw[byte / 4] |= ck << (8 * (byte % 4));
+        // value byte: tile 2 w + byte / 8, token slot sl = byte % 8
+        const int nt = 2 * w + byte / 8, sl = byte % 8;
+        const uint32_t cv =
+            e4m3_sat(h2f(vx[16 * (sl / 4) + 4 * kb + sl % 4][16 * nt + n]) / sv);
+        vw[byte / 4] |= cv << (8 * (byte % 4));
+    }
+    const int64_t base = ((int64_t)u * v.chunks + ch) * 1024 + w * 256 + l * 4;  // words
+    *reinterpret_cast<uint4*>(v.kq + base) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+    *reinterpret_cast<uint4*>(v.vq + base) = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+}
+
 // Copy the appended rows that are attention sinks (tokens t_old .. t_old +
 // n_sink - 1 of the sequence, the first rows of each unit's input) to the
 // sink region.
@@ -792,6 +866,18 @@ __global__ __launch_bounds__(256) void unpack_kernel(CacheView v, int64_t n_q, u
         const uint32_t* kbase = v.kq + ((int64_t)u * v.chunks + chunk) * wpc;
         const uint32_t* vbase = v.vq + ((int64_t)u * v.chunks + chunk) * wpc;
         const uint32_t mask = (1u << b) - 1;
+        if (b == 8) {
+            // FP8: byte offsets inside the chunk's 4 KB (see pack8_kernel)
+            const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(kbase);
+            const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(vbase);
+            const int tau = tt / 16, n = tt % 16, ks = c / 32, kbl = (c % 32) / 8, e8 = c % 8;
+            const int kw = 2 * tau + ks / 2, kl = n + 16 * kbl;
+            if (kc) kc[e] = kb8[kw * 1024 + kl * 16 + 8 * (ks % 2) + e8];
+            const int nt = c / 16, cn = c % 16, r16 = tt % 16, vkb = r16 / 4;
+            const int sl = 4 * tau + r16 % 4, vl = cn + 16 * vkb;
+            if (vc) vc[e] = vb8[(nt / 2) * 1024 + vl * 16 + 8 * (nt % 2) + sl];
+            continue;
+        }
         {   // key code
             const int tau = tt / 16, row = tt % 16;
             const int ks = c / 32, kb = (c % 32) / 8, s = c % 8, m = s / 2, hi = s % 2;
@@ -1005,7 +1091,12 @@ int launch_append(const CacheView& v, const uint16_t* kn, const uint16_t* vn, in
                                n_new, g0, g1);
         }
         hipError_t e = hipErrorInvalidValue;
-        if (G == 16) {
+        if (v.bits == 8) {
+            // FP8 codec: one block per (unit, chunk); ng groups of 32 tokens
+            hipLaunchKernelGGL(pack8_kernel, dim3((unsigned)(ng * v.units)), dim3(256), 0, s, v, kn,
+                               vn, t_old, n_new, g0);
+            e = hipSuccess;
+        } else if (G == 16) {
             // even groups, then odd groups: the two halves of a chunk are never
             // written by one launch
             const int64_t ge = g0 + (g0 & 1), go = g0 + 1 - (g0 & 1);
@@ -1044,6 +1135,12 @@ int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, voi
     return (int)hipGetLastError();
 }
 
+int launch_fp8_scales(const CacheView& v, const float* scales, void* stream) {
+    (void)hipGetLastError();  // an error left by an earlier call is not this call's
+    return (int)hipMemcpyAsync(v.fp8_scales, scales, (size_t)v.n_kv_heads * 2 * sizeof(float),
+                               hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream));
+}
+
 int launch_evict_step(const CacheView& v, int64_t T, const float* acc, int32_t budget,
                       int32_t recent, void* stream) {
     (void)hipGetLastError();  // an error left by an earlier call is not this call's
@@ -1070,11 +1167,14 @@ int launch_debug_unpack(const CacheView& v, int64_t T, int64_t n_q, const kvq_de
         const int64_t m2 = (int64_t)v.units * n_q * NG, m3 = (int64_t)v.units * (T - ns - n_q) * D;
         if (m2 > m) m = m2;
         if (m3 > m) m = m3;
-        if (m > 0 && (o.kscale || o.kzero || o.vscale || o.vzero || o.pooled || o.kres || o.vres)) {
+        if (v.bits == 8) m = m3 > (int64_t)v.units * n_q ? m3 : (int64_t)v.units * n_q;  // no meta
+        kvq_debug_view oo = o;
+        if (v.bits == 8) oo.kscale = oo.kzero = oo.vscale = oo.vzero = nullptr;
+        if (m > 0 && (oo.kscale || oo.kzero || oo.vscale || oo.vzero || oo.pooled || oo.kres || oo.vres)) {
             int64_t blocks = (m + 255) / 256;
             if (blocks > 65536) blocks = 65536;
             hipLaunchKernelGGL(debug_view_kernel, dim3((unsigned)blocks), dim3(256), 0, s, v, T, n_q,
-                               o);
+                               oo);
         }
     }
     const size_t U = (size_t)v.units, N = (size_t)v.pool, E = (size_t)v.evict_cap;

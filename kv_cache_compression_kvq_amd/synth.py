@@ -42,6 +42,8 @@ class Workload:
     pool: int = 0          # N, outlier-pool capacity
     evict_cap: int = 32    # E, extra pool for displaced pool members
     sinks: int = 0         # S, attention sinks kept in fp16
+    fp8_scale_k: float = 1.0  # b = 8: key / value scale of every KV head
+    fp8_scale_v: float = 1.0
     outlier_channels: int = 0
     outlier_scale: float = 1.0
     key_dist: str = "normal"     # "normal" or "zipf"
@@ -80,6 +82,10 @@ WORKLOADS = {
     # same layer shape; not one of the five headline workloads
     "llama8b_g16": Workload("llama8b_g16", 8, batch=8, n_q_heads=32, n_kv_heads=8,
                             head_dim=128, tokens=8192, bits=2, group=16, residual=128,
+                            outlier_channels=6, outlier_scale=15.0),
+    # the same layer with the FP8 E4M3 codec (scales 1.0, the default)
+    "llama8b_fp8": Workload("llama8b_fp8", 10, batch=8, n_q_heads=32, n_kv_heads=8,
+                            head_dim=128, tokens=8192, bits=8, group=32, residual=128,
                             outlier_channels=6, outlier_scale=15.0),
     # the same layer with four attention sinks kept in fp16
     "llama8b_sinks": Workload("llama8b_sinks", 9, batch=8, n_q_heads=32, n_kv_heads=8,

@@ -51,6 +51,10 @@ int launch_unpack(const CacheView&, int64_t n_q, uint8_t*, uint8_t*, void*) {
     CHECK(n_q > 0);
     return stub();
 }
+int launch_fp8_scales(const CacheView& v, const float*, void*) {
+    CHECK(v.bits == 8);
+    return stub();
+}
 int launch_evict_step(const CacheView& v, int64_t T, const float*, int32_t budget, int32_t recent,
                       void*) {
     CHECK(T >= 1 && budget >= 0 && recent >= 0 && v.evict_words * 32 >= v.q_cap);
@@ -96,7 +100,7 @@ int main() {
     CHECK(kvq_cache_bytes(&c, &n) == KVQ_OK && n > 0);
     CHECK(kvq_cache_bytes(nullptr, &n) == KVQ_EINVAL);
     CHECK(kvq_cache_bytes(&c, nullptr) == KVQ_EINVAL);
-    const int bad_bits[] = {0, 1, 3, 8, -2};
+    const int bad_bits[] = {0, 1, 3, 16, -2};
     for (int b : bad_bits) {
         kvq_config x = c;
         x.bits = b;
@@ -118,7 +122,7 @@ int main() {
 
     // every supported configuration: layout offsets ascending, aligned, inside
     const int groups[] = {16, 32, 64, 128};
-    for (int bits : {2, 4})
+    for (int bits : {2, 4, 8})
         for (int g : groups)
             for (int r : {1, 2, 4})
                 for (int pool : {0, 3})
@@ -141,7 +145,8 @@ int main() {
                                              h.off_pool_idx, h.off_pool_score, h.off_pool_k,
                                              h.off_pool_v, h.off_ev_idx, h.off_ev_k, h.off_ev_v,
                                              h.off_counters, h.off_scores, h.off_sink_k,
-                                             h.off_sink_v, h.off_evict, h.off_evict_count};
+                                             h.off_sink_v, h.off_evict, h.off_evict_count,
+                                             h.off_fp8_scales};
                     for (size_t i = 0; i < sizeof(offs) / sizeof(offs[0]); ++i) {
                         CHECK(offs[i] % 256 == 0 && offs[i] <= bytes);
                         if (i) CHECK(offs[i] >= offs[i - 1]);

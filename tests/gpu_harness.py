@@ -46,7 +46,8 @@ def config_of(w: synth.Workload, max_tokens: int | None = None) -> abi.Config:
 
 def params_of(w: synth.Workload) -> O.CacheParams:
     return O.CacheParams(bits=w.bits, group=w.group, residual=w.residual, pool=w.pool,
-                         evict_cap=w.evict_cap, head_dim=w.head_dim, sinks=w.sinks)
+                         evict_cap=w.evict_cap, head_dim=w.head_dim, sinks=w.sinks,
+                         fp8_scale_k=w.fp8_scale_k, fp8_scale_v=w.fp8_scale_v)
 
 
 class GpuCache:
@@ -58,6 +59,10 @@ class GpuCache:
         n = abi.cache_bytes(self.cfg)
         self.arena = torch.empty(n, dtype=torch.uint8, device="cuda")
         self.h = abi.cache_init(self.cfg, self.arena)
+        if w.bits == 8 and (w.fp8_scale_k != 1.0 or w.fp8_scale_v != 1.0):
+            sc = torch.tensor([[w.fp8_scale_k, w.fp8_scale_v]] * w.n_kv_heads,
+                              dtype=torch.float32, device="cuda")
+            abi.fp8_set_scales(self.h, sc)
 
     def append(self, K: np.ndarray, V: np.ndarray) -> None:
         k = torch.from_numpy(np.ascontiguousarray(K)).cuda()
@@ -122,6 +127,12 @@ def check_unit_state(st: dict, u: int, uc: O.UnitCache) -> None:
     assert nq == uc.n_q and T == uc.T
     np.testing.assert_array_equal(st["kcodes"][u], uc.kcodes)
     np.testing.assert_array_equal(st["vcodes"][u], uc.vcodes)
+    if p.bits == 8:  # FP8 codec: codes only (no scale / zero words, no pools)
+        S = min(T, p.sinks)
+        assert np.array_equal(st["kres"][u].view(np.uint16), uc.k16[S + nq:T].view(np.uint16))
+        assert np.array_equal(st["vres"][u].view(np.uint16), uc.v16[S + nq:T].view(np.uint16))
+        assert np.array_equal(st["ksink"][u].view(np.uint16), uc.k16[:S].view(np.uint16))
+        return
     assert np.array_equal(st["kscale"][u].view(np.uint16), uc.kscale.view(np.uint16))
     assert np.array_equal(st["kzero"][u], uc.kzero)  # as values: +0 and -0 agree
     assert np.array_equal(st["vscale"][u].view(np.uint16), uc.vscale.view(np.uint16))

@@ -13,7 +13,7 @@ from tests.conftest import ROOT
 def _header_functions():
     text = open(os.path.join(ROOT, "include", "kvq.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text))
+    return set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text))
 
 
 def test_library_exports_every_header_function(kvq):
@@ -37,7 +37,8 @@ def _cfg(kvq, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(bits=3), -2), (dict(bits=8), -2), (dict(group=8), -2), (dict(group=48), -2),
+    (dict(bits=3), -2), (dict(bits=8, group=16), -2), (dict(bits=8, pool=3), -2),
+    (dict(bits=16), -2), (dict(group=8), -2), (dict(group=48), -2),
     (dict(head_dim=64), -2), (dict(n_q_heads=64), -2), (dict(n_q_heads=12), -1),
     (dict(pool=65), -2), (dict(evict_cap=2000), -2), (dict(residual=-1), -1),
     (dict(batch=0), -1), (dict(max_tokens=0), -1), (dict(residual=1900, pool=64, evict_cap=64), -2),

@@ -51,3 +51,11 @@ def test_decode_step_bytes_with_sinks():
     nq = BM.n_quantized(8192 - 4, 128, 32)
     assert nq == 8032
     assert s.quantized == nq * 96 and s.residual == (8192 - nq) * 512
+
+
+def test_fp8_bytes_per_token():
+    # FP8 E4M3: one byte per element, no scale / zero words ("KV cache
+    # quantization and eviction", The bottleneck in numbers: FP8 halves BF16)
+    s = BM.decode_step_bytes(units=1, gqa=4, head_dim=128, tokens=64 * 32, bits=8, group=32,
+                             residual=0)
+    assert s.quantized == 64 * 32 * 256

@@ -45,6 +45,7 @@ CASES = {
     "b4g16_ott": (_w(bits=4, group=16, pool=3, inject_frac=0.03, outlier_channels=6,
                      outlier_scale=15.0), 60, 250, 16, 60),
     "b2g32_no_sinks_r2": (_w(n_q_heads=4, sinks=0, residual=32), 50, 280, 8, 30),
+    "fp8_sinks": (_w(bits=8), 40, 260, 16, 50),
 }
 
 

@@ -347,6 +347,42 @@ def test_sinks_state_and_decode(bits, group, pool):
     assert s0 == w.tokens
 
 
+@pytest.mark.parametrize("r,sk,sv,sinks", [(4, 1.0, 1.0, 0), (4, 0.02, 0.5, 4), (2, 1.0, 1.0, 0),
+                                           (1, 0.25, 2.0, 4)])
+def test_fp8_codec_state_and_decode(r, sk, sv, sinks):
+    """FP8 E4M3 cache ("KV cache quantization and eviction", FP8, KIVI and
+    KVQuant): codes bit-exact after ragged appends, attention and H2O scores
+    against the oracle. With s_K = 0.02 the x15 key channels exceed 448 * s_K
+    and must saturate to +-448 (0x7E / 0xFE), never NaN."""
+    w = small(bits=8, group=32, r=r, residual=40, tokens=900, sinks=sinks).with_(
+        fp8_scale_k=sk, fp8_scale_v=sv)
+    splits = [3, 200, 1, 64, 632]
+    gc, K, V = run_appends(w, splits)
+    orc = H.oracle_units(w, all_units(w), K, V, splits)
+    st = gc.state()
+    for u, key in enumerate(all_units(w)):
+        H.check_unit_state(st, u, orc[key])
+    kc = st["kcodes"]
+    assert not np.any((kc & 0x7F) == 0x7F)  # no NaN code
+    if sk < 0.1:
+        assert np.any((kc & 0x7F) == 0x7E)   # saturated
+    check_decode(gc, w, orc, synth.queries(w),
+                 acc_in=np.zeros((w.batch, w.n_kv_heads, w.tokens), np.float32),
+                 tag=f"fp8_r{r}")
+
+
+def test_workload_llama8b_fp8_sampled_units():
+    w = W["llama8b_fp8"]
+    gc, K, V = run_appends(w, [w.tokens])
+    units = [(0, 0), (4, 3), (7, 7)]
+    orc = H.oracle_units(w, units, K, V)
+    st = gc.state()
+    for (b, h) in units:
+        H.check_unit_state(st, b * w.n_kv_heads + h, orc[(b, h)])
+    check_decode(gc, w, orc, synth.queries(w),
+                 acc_in=np.zeros((w.batch, w.n_kv_heads, w.tokens), np.float32))
+
+
 @pytest.mark.parametrize("T", [1, 7, 40, 72])
 def test_decode_short_caches(T):
     w = small(tokens=T, residual=40, batch=1, hkv=2)

@@ -42,6 +42,10 @@ def _fresh_cache(w, max_tokens):
     gc = H.GpuCache(w, max_tokens=max_tokens)
     gc.arena.zero_()
     gc.h = abi.cache_init(gc.cfg, gc.arena)
+    if w.bits == 8:
+        sc = torch.tensor([[w.fp8_scale_k, w.fp8_scale_v]] * w.n_kv_heads, dtype=torch.float32,
+                          device="cuda")
+        abi.fp8_set_scales(gc.h, sc)
     torch.cuda.synchronize()
     return gc
 
@@ -57,6 +61,8 @@ CASES = {
     # from an empty cache: the first 4 steps fill the attention sinks, then the
     # ring, then G = 16 groups are quantized behind them
     "sinks_from_empty": (_small(tokens=0, sinks=4, group=16, residual=16), 60, True),
+    "fp8_sinks": (_small(bits=8, tokens=100, sinks=4).with_(fp8_scale_k=0.5, fp8_scale_v=2.0),
+                  40, True),
     "sinks_ott_pool": (W["ott"].with_(name="step_sinks_ott", batch=2, tokens=200, evict_cap=4,
                                       sinks=4), 40, True),
 }
