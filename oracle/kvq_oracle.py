@@ -96,6 +96,13 @@ R15 FP8 codec (b = 8): every element is stored as FP8 E4M3 (OCP: bias 7,
     must saturate instead of producing NaN). Dequantization is code value * s.
     The residual window and the 32-token granularity of n_q stay as for the
     integer codecs; there are no groups, zero points or outlier pools.
+R16 Prefill scores ([MiniKV] section 4.3, selective flash-attention, and
+    Algorithm 1, prefill): causal attention of the n prompt tokens gives the
+    outputs X_O and, per KV head, A_cumul[j] = sum over the query heads of the
+    head and over the query rows i >= j of the normalized probability P[i][j]
+    (the page's buffer shape names "headDim" where the number of heads is
+    meant). The heavy hitters of A_cumul plus a recent window are the tokens
+    kept and quantized ([MiniKV] section 4.1, persistent context selection).
 """
 from __future__ import annotations
 
@@ -499,6 +506,35 @@ def unit_attention(K: np.ndarray, V: np.ndarray, q16: np.ndarray, live=None):
 def h2o_increment(p: np.ndarray) -> np.ndarray:
     """Score increment for one KV head: sum over its query heads of p [r][T] (R10)."""
     return p.sum(axis=0)
+
+
+def prefill_attention(q16: np.ndarray, k16: np.ndarray, v16: np.ndarray):
+    """Causal attention of one KV head's r query heads over n prompt tokens (R16).
+
+    q16 [r][n][d], k16 / v16 [n][d] fp16. Returns the outputs [r][n][d] and
+    A_cumul [n] = sum_h sum_i P_h[i][j], in fp64: S = Q K^T / sqrt(d) with
+    keys after the query masked, P = softmax over each row."""
+    q = np.asarray(q16, dtype=np.float16).astype(np.float64)
+    k = np.asarray(k16, dtype=np.float16).astype(np.float64)
+    v = np.asarray(v16, dtype=np.float16).astype(np.float64)
+    r, n, d = q.shape
+    future = np.triu(np.ones((n, n), dtype=bool), k=1)
+    out = np.empty((r, n, d))
+    acum = np.zeros(n)
+    for h in range(r):
+        s = (q[h] @ k.T) / math.sqrt(d)
+        s[future] = -np.inf
+        s -= s.max(axis=1, keepdims=True)
+        e = np.exp(s)
+        p = e / e.sum(axis=1, keepdims=True)
+        out[h] = p @ v
+        acum += p.sum(axis=0)
+    return out, acum
+
+
+def gather_rows(x16: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Rows idx of x16 [n][d] (the tokens kept after prefill selection)."""
+    return np.asarray(x16)[np.asarray(idx, dtype=np.int64)]
 
 
 def h2o_evict_one(scores: np.ndarray, live: np.ndarray, budget: int, recent: int, sinks: int):

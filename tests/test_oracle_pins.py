@@ -912,3 +912,56 @@ def test_fp8_cache_rows_are_scaled_e4m3_values():
         assert np.all(np.abs(xh - xs)[normal] <= np.abs(xs)[normal] * 2.0 ** -4)
         assert np.all(np.abs(xh - xs)[~normal] <= 2.0 ** -10)
         assert np.array_equal(X[256:], x16[256:].astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
+# Prefill scores (MiniKV, section 4.3 selective flash-attention; Algorithm 1).
+# ---------------------------------------------------------------------------
+
+def test_prefill_attention_brute_force_loops():
+    rng = np.random.default_rng(70)
+    r, n, d = 2, 9, 128
+    q = rng.standard_normal((r, n, d)).astype(np.float16)
+    k = rng.standard_normal((n, d)).astype(np.float16)
+    v = rng.standard_normal((n, d)).astype(np.float16)
+    out, acum = O.prefill_attention(q, k, v)
+    want_acum = [0.0] * n
+    for h in range(r):
+        for i in range(n):
+            logits = [sum(float(q[h, i, c]) * float(k[j, c]) for c in range(d)) / math.sqrt(d)
+                      for j in range(i + 1)]
+            mx = max(logits)
+            e = [math.exp(x - mx) for x in logits]
+            tot = sum(e)
+            for c in range(0, d, 17):
+                o = sum(e[j] / tot * float(v[j, c]) for j in range(i + 1))
+                assert abs(out[h, i, c] - o) <= 1e-12 * (1 + abs(o))
+            for j in range(i + 1):
+                want_acum[j] += e[j] / tot
+    assert np.allclose(acum, want_acum, rtol=1e-12, atol=0)
+
+
+def test_prefill_column_sums_closed_forms():
+    """Equal keys: row i spreads 1/(i+1) over its i+1 keys, so A_cumul[j] is
+    r * (H_n - H_j) (harmonic numbers) and the outputs are running means of V;
+    in general the column sums add up to r * n (every row sums to 1)."""
+    rng = np.random.default_rng(71)
+    r, n, d = 3, 40, 128
+    q = rng.standard_normal((r, n, d)).astype(np.float16)
+    k = np.tile(rng.standard_normal((1, d)).astype(np.float16), (n, 1))
+    v = rng.standard_normal((n, d)).astype(np.float16)
+    out, acum = O.prefill_attention(q, k, v)
+    H = [sum(Fraction(1, m) for m in range(1, t + 1)) for t in range(n + 1)]
+    for j in range(n):
+        assert abs(acum[j] - float(r * (H[n] - H[j]))) <= 1e-12 * r * n
+    run = np.cumsum(v.astype(np.float64), axis=0) / np.arange(1, n + 1)[:, None]
+    assert np.allclose(out, run[None], rtol=1e-12, atol=1e-13)
+    q2 = rng.standard_normal((r, n, d)).astype(np.float16)
+    k2 = rng.standard_normal((n, d)).astype(np.float16)
+    _, a2 = O.prefill_attention(q2, k2, v)
+    assert abs(a2.sum() - r * n) <= 1e-9 and np.all(a2 > 0)
+    # the first token takes all of row 0 in every head; the last token appears
+    # in the last row only
+    assert a2[0] >= r - 1e-12 and a2[-1] <= r + 1e-12
+    _, a1 = O.prefill_attention(q2[:, :1], k2[:1], v[:1])
+    assert np.allclose(a1, [r])
