@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 
 METRIC = "compressed-KV decode attention GB/s and % of MI355X HBM peak; tokens·heads/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFS = 2500.0  # dense fp16 matrix-core peak of MI355X
 REPLICA_BYTES = 600e6  # total cache bytes the rotation spans (> 256 MB Infinity Cache)
 
 
@@ -209,6 +210,8 @@ ROWS = {
     "evict_minikv": ("minikv", "f2: one H2O eviction per KV head (budget 20% + 256 recent)"),
     "decode_llama8b_g16": ("llama8b_g16", "a8-a10: fused decode + merge at group size 16"),
     "decode_llama8b_sinks": ("llama8b_sinks", "a8-a10 with 4 attention sinks in the fp16 partition"),
+    "prefill_llama8b": ("prefill_llama8b", "f1: causal prefill attention + A_cumul column sums "
+                                          "(selective flash-attention)"),
     "append_llama8b_fp8": ("llama8b_fp8", "f4: bulk FP8 E4M3 encode of the whole prefix, ring store"),
     "decode_llama8b_fp8": ("llama8b_fp8", "f4: fused FP8 E4M3 decode + merge"),
     "decode_long_b2g32": ("long_b2g32", "a8-a10: fused decode + merge, split-K over context"),
@@ -293,6 +296,40 @@ def rows_main(args):
     for name in names:
         w = synth.WORKLOADS[ROWS[name][0]]
         U, d = w.units, w.head_dim
+        if name.startswith("prefill"):
+            # q, k, v of the prompt resident in HBM; replicas past the Infinity Cache
+            n, Hq, Hkv = w.tokens, w.n_q_heads, w.n_kv_heads
+            g = torch.Generator(device=dev).manual_seed(0)
+            per = (Hq + 2 * Hkv) * n * d * 2
+            n_rep = max(2, math.ceil(REPLICA_BYTES / per))
+            bufs = [(torch.randn((w.batch, Hq, n, d), generator=g, device=dev).half(),
+                     torch.randn((w.batch, Hkv, n, d), generator=g, device=dev).half(),
+                     torch.randn((w.batch, Hkv, n, d), generator=g, device=dev).half())
+                    for _ in range(n_rep)]
+            out = torch.empty((w.batch, Hq, n, d), device=dev)
+            acc = torch.empty((w.batch, Hkv, n), device=dev)
+            ws = torch.empty(abi.prefill_workspace(w.batch, Hq, n), dtype=torch.uint8, device=dev)
+
+            def call(i, a, b):
+                qq, kk, vv = bufs[i % n_rep]
+                a.record()
+                abi.prefill_attention(qq, kk, vv, w.batch, Hq, Hkv, n, out, acc, ws)
+                b.record()
+
+            timed(call, 2)
+            us = timed(call, args.reps)
+            fl = BM.prefill_flops(batch=w.batch, n_q_heads=Hq, head_dim=d, tokens=n)
+            tfs = fl / (us * 1e-6) / 1e12
+            line = {"row": name, "workload": w.name, "what": ROWS[name][1],
+                    "us_per_call": round(us, 3), "alg_flops": int(fl), "TFLOP/s": round(tfs, 2),
+                    "roofline": {"bound": "mfma", "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+                                 "frac": round(tfs / MFMA_F16_PEAK_TFS, 4)},
+                    "kernels": ["prefill_fwd_kernel", "prefill_colsum_kernel"],
+                    "prompt": n}
+            print(json.dumps(line), flush=True)
+            del bufs, out, acc, ws
+            torch.cuda.empty_cache()
+            continue
         if name.startswith("append"):
             srcs = source(w)
             cfg, reps = caches(w)

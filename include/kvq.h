@@ -318,6 +318,47 @@ kvq_status kvq_topk_evict(const float* d_scores, int32_t rows, int32_t T, int32_
                           int32_t w, int32_t* d_idx, void* stream);
 
 /*
+ * Prefill attention of one layer with heavy-hitter scores ("MiniKV: Pushing
+ * the Limits of LLM Inference via 2-Bit Layer-Discriminative KV Cache",
+ * section 4.3, selective flash-attention; Algorithm 1, prefill):
+ *   S = Q K^T / sqrt(d) with the keys after each query masked (causal),
+ *   P = softmax(S) per row, d_out = P V, and, when d_acc is given,
+ *   d_acc[b][h_kv][j] = sum over the r query heads of KV head h_kv and over
+ *   the rows i >= j of P[i][j] (A_cumul, written, not accumulated).
+ *   d_q    device fp16 [B][Hq][n][d]; d_k, d_v device fp16 [B][Hkv][n][d]
+ *   d_out  device fp32 [B][Hq][n][d]
+ *   d_acc  device fp32 [B][Hkv][n] or NULL (then only d_out is computed)
+ *   d_ws   device workspace of ws_bytes >= kvq_prefill_workspace (per-row
+ *          log-sum-exp of the softmax)
+ * d_acc feeds kvq_topk_evict (rows = B * Hkv, T = n), whose kept indices feed
+ * kvq_gather_kv and then kvq_quantize_append (MiniKV section 4.1, persistent
+ * context selection). Query head h reads KV head h / (Hq / Hkv).
+ * Errors: KVQ_EINVAL (null pointer with n > 0, bad sizes), KVQ_EUNSUPPORTED
+ * (head_dim != 128, Hq / Hkv not in {1, 2, 4}), KVQ_EWORKSPACE.
+ */
+kvq_status kvq_prefill_workspace(int32_t batch, int32_t n_q_heads, int32_t n, size_t* ws_bytes);
+kvq_status kvq_prefill_attention(const void* d_q, const void* d_k, const void* d_v, int32_t batch,
+                                 int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                 int32_t n, float* d_out, float* d_acc, void* d_ws,
+                                 size_t ws_bytes, void* stream);
+
+/*
+ * Rows of the kept tokens ("MiniKV", section 4.1, persistent context
+ * selection: the heavy hitters chosen at the end of the prefill are the
+ * tokens that are quantized): for every unit u = b * Hkv + h,
+ *   d_k_out[u][i] = d_k[u][d_idx[u][i]], likewise for values, i < n_keep.
+ *   d_k, d_v        device fp16 [B][Hkv][n][d]
+ *   d_idx           device int32 [B * Hkv][n_keep] (kvq_topk_evict's output);
+ *                   an index outside [0, n) gives a zero row
+ *   d_k_out, d_v_out device fp16 [B][Hkv][n_keep][d]
+ * Errors: KVQ_EINVAL (null pointer with n_keep > 0, n_keep > n, bad sizes),
+ * KVQ_EUNSUPPORTED (head_dim != 128).
+ */
+kvq_status kvq_gather_kv(const void* d_k, const void* d_v, int32_t batch, int32_t n_kv_heads,
+                         int32_t head_dim, int32_t n, const int32_t* d_idx, int32_t n_keep,
+                         void* d_k_out, void* d_v_out, void* stream);
+
+/*
  * Set the FP8 scales of a b = 8 cache: d_scales is device fp32 [Hkv][2] (key
  * scale, value scale per KV head), finite and positive (not checked on the
  * device). Elements are stored as E4M3(x / s) and read back as E4M3 * s; set

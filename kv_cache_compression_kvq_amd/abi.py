@@ -29,7 +29,8 @@ EXPORTS = ("kvq_status_string", "kvq_cache_bytes", "kvq_cache_init", "kvq_quanti
            "kvq_decode_workspace", "kvq_decode_attention", "kvq_decode_attention_timed",
            "kvq_decode_step", "kvq_decode_step_timed", "kvq_topk_evict", "kvq_unpack_codes",
            "kvq_decode_attention_noalloc", "kvq_debug_unpack", "kvq_evict_step",
-           "kvq_pyramid_budgets", "kvq_fp8_set_scales")
+           "kvq_pyramid_budgets", "kvq_fp8_set_scales", "kvq_prefill_workspace",
+           "kvq_prefill_attention", "kvq_gather_kv")
 
 
 class Config(ctypes.Structure):
@@ -94,6 +95,9 @@ def lib() -> ctypes.CDLL:
             "kvq_debug_unpack": [ctypes.POINTER(Cache), ctypes.POINTER(DebugView), P],
             "kvq_evict_step": [ctypes.POINTER(Cache), P, I32, I32, P],
             "kvq_fp8_set_scales": [ctypes.POINTER(Cache), P, P],
+            "kvq_prefill_workspace": [I32, I32, I32, ctypes.POINTER(SZ)],
+            "kvq_prefill_attention": [P, P, P, I32, I32, I32, I32, I32, P, P, P, SZ, P],
+            "kvq_gather_kv": [P, P, I32, I32, I32, I32, P, I32, P, P, P],
             "kvq_pyramid_budgets": [I32, I32, I32, ctypes.POINTER(I32)],
         }
         for name, args in sigs.items():
@@ -234,3 +238,27 @@ def fp8_set_scales(h: Cache, scales, stream=None) -> None:
     """kvq_fp8_set_scales: device fp32 [Hkv][2] key / value scales of a b = 8 cache."""
     _check("kvq_fp8_set_scales", lib().kvq_fp8_set_scales(ctypes.byref(h), _ptr(scales),
                                                           _stream(stream)))
+
+
+def prefill_workspace(batch: int, n_q_heads: int, n: int) -> int:
+    nb = ctypes.c_size_t()
+    _check("kvq_prefill_workspace", lib().kvq_prefill_workspace(batch, n_q_heads, n,
+                                                                ctypes.byref(nb)))
+    return nb.value
+
+
+def prefill_attention(q, k, v, batch: int, n_q_heads: int, n_kv_heads: int, n: int, out, acc,
+                      ws, head_dim: int = 128, ws_bytes: int | None = None, stream=None) -> None:
+    """kvq_prefill_attention: causal outputs and (acc not None) the column sums A_cumul."""
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check("kvq_prefill_attention", lib().kvq_prefill_attention(
+        _ptr(q), _ptr(k), _ptr(v), batch, n_q_heads, n_kv_heads, head_dim, n, _ptr(out),
+        _ptr(acc), _ptr(ws), nbytes, _stream(stream)))
+
+
+def gather_kv(k, v, batch: int, n_kv_heads: int, n: int, idx, n_keep: int, k_out, v_out,
+              head_dim: int = 128, stream=None) -> None:
+    """kvq_gather_kv: the kept rows of K and V, per unit, in idx order."""
+    _check("kvq_gather_kv", lib().kvq_gather_kv(
+        _ptr(k), _ptr(v), batch, n_kv_heads, head_dim, n, _ptr(idx), n_keep, _ptr(k_out),
+        _ptr(v_out), _stream(stream)))

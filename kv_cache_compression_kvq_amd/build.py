@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
 
-HIP_SOURCES = ["kvq_pack.hip", "kvq_decode.hip", "kvq_topk.hip"]
+HIP_SOURCES = ["kvq_pack.hip", "kvq_decode.hip", "kvq_topk.hip", "kvq_prefill.hip"]
 CXX_SOURCES = ["kvq_abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

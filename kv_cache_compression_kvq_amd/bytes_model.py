@@ -105,6 +105,15 @@ def evict_step_bytes(*, rows: int, tokens: int, sinks: int = 0) -> int:
     return rows * (tokens * 4 + (n + 31) // 32 * 4)
 
 
+def prefill_flops(*, batch: int, n_q_heads: int, head_dim: int, tokens: int) -> int:
+    """Causal attention of an n-token prompt: the two products Q K^T and P V,
+    2 flops per multiply-add, over the n (n + 1) / 2 unmasked query-key pairs
+    of every query head. Recomputing Q K^T for the column sums is
+    implementation work and is not counted."""
+    pairs = tokens * (tokens + 1) // 2
+    return batch * n_q_heads * pairs * head_dim * 2 * 2
+
+
 def topk_bytes(*, rows: int, tokens: int, k: int, w: int) -> int:
     """fp32 scores read once, int32 kept indices written."""
     return rows * tokens * 4 + rows * (k + w) * 4

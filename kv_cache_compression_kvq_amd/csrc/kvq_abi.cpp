@@ -379,6 +379,45 @@ kvq_status kvq_unpack_codes(const kvq_cache* h, uint8_t* d_kcodes, uint8_t* d_vc
     return launch_status(launch_unpack(view_of(h), h->n_quant, d_kcodes, d_vcodes, stream));
 }
 
+kvq_status kvq_prefill_workspace(int32_t batch, int32_t n_q_heads, int32_t n, size_t* ws_bytes) {
+    if (!ws_bytes || batch < 1 || n_q_heads < 1 || n < 0 || n > kMaxTokens) return KVQ_EINVAL;
+    *ws_bytes = (size_t)align_up((uint64_t)batch * n_q_heads * n * 4);
+    return KVQ_OK;
+}
+
+kvq_status kvq_prefill_attention(const void* d_q, const void* d_k, const void* d_v, int32_t batch,
+                                 int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                 int32_t n, float* d_out, float* d_acc, void* d_ws,
+                                 size_t ws_bytes, void* stream) {
+    if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || n < 0 || n > kMaxTokens ||
+        n_q_heads % n_kv_heads != 0)
+        return KVQ_EINVAL;
+    const int r = n_q_heads / n_kv_heads;
+    if (head_dim != kHeadDim || (r != 1 && r != 2 && r != 4)) return KVQ_EUNSUPPORTED;
+    if (n == 0) return KVQ_OK;
+    if (!d_q || !d_k || !d_v || !d_out || !d_ws) return KVQ_EINVAL;
+    size_t need = 0;
+    kvq_prefill_workspace(batch, n_q_heads, n, &need);
+    if (ws_bytes < need) return KVQ_EWORKSPACE;
+    return launch_status(launch_prefill(
+        static_cast<const uint16_t*>(d_q), static_cast<const uint16_t*>(d_k),
+        static_cast<const uint16_t*>(d_v), batch, n_q_heads, n_kv_heads, n, d_out, d_acc,
+        static_cast<float*>(d_ws), stream));
+}
+
+kvq_status kvq_gather_kv(const void* d_k, const void* d_v, int32_t batch, int32_t n_kv_heads,
+                         int32_t head_dim, int32_t n, const int32_t* d_idx, int32_t n_keep,
+                         void* d_k_out, void* d_v_out, void* stream) {
+    if (batch < 1 || n_kv_heads < 1 || n < 0 || n_keep < 0 || n_keep > n) return KVQ_EINVAL;
+    if (head_dim != kHeadDim) return KVQ_EUNSUPPORTED;
+    if (n_keep == 0) return KVQ_OK;
+    if (!d_k || !d_v || !d_idx || !d_k_out || !d_v_out) return KVQ_EINVAL;
+    return launch_status(launch_gather(static_cast<const uint16_t*>(d_k),
+                                       static_cast<const uint16_t*>(d_v), batch * n_kv_heads, n,
+                                       d_idx, n_keep, static_cast<uint16_t*>(d_k_out),
+                                       static_cast<uint16_t*>(d_v_out), stream));
+}
+
 kvq_status kvq_fp8_set_scales(kvq_cache* h, const float* d_scales, void* stream) {
     if (!valid_handle(h) || !d_scales) return KVQ_EINVAL;
     if (h->cfg.bits != 8) return KVQ_EUNSUPPORTED;

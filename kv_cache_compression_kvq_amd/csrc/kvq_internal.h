@@ -87,6 +87,11 @@ int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& 
 int launch_topk(const float* scores, int32_t rows, int32_t T, int32_t k, int32_t w,
                 int32_t* idx, void* stream);
 int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, void* stream);
+int launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, int32_t batch,
+                   int32_t n_q_heads, int32_t n_kv_heads, int32_t n, float* out, float* acc,
+                   float* lse, void* stream);
+int launch_gather(const uint16_t* k, const uint16_t* v, int32_t units, int32_t n,
+                  const int32_t* idx, int32_t n_keep, uint16_t* ko, uint16_t* vo, void* stream);
 int launch_fp8_scales(const CacheView& v, const float* scales, void* stream);
 int launch_evict_step(const CacheView& v, int64_t T, const float* acc, int32_t budget,
                       int32_t recent, void* stream);

@@ -83,6 +83,12 @@ WORKLOADS = {
     "llama8b_g16": Workload("llama8b_g16", 8, batch=8, n_q_heads=32, n_kv_heads=8,
                             head_dim=128, tokens=8192, bits=2, group=16, residual=128,
                             outlier_channels=6, outlier_scale=15.0),
+    # prefill of a 4096-token prompt through the same layer (MiniKV's prompt
+    # length), with the heavy-hitter column sums
+    "prefill_llama8b": Workload("prefill_llama8b", 11, batch=1, n_q_heads=32, n_kv_heads=8,
+                                head_dim=128, tokens=4096, bits=2, group=32, residual=128,
+                                outlier_channels=6, outlier_scale=15.0, h2o=True,
+                                topk_frac=0.2, recent=256),
     # the same layer with the FP8 E4M3 codec (scales 1.0, the default)
     "llama8b_fp8": Workload("llama8b_fp8", 10, batch=8, n_q_heads=32, n_kv_heads=8,
                             head_dim=128, tokens=8192, bits=8, group=32, residual=128,

@@ -51,6 +51,16 @@ int launch_unpack(const CacheView&, int64_t n_q, uint8_t*, uint8_t*, void*) {
     CHECK(n_q > 0);
     return stub();
 }
+int launch_prefill(const uint16_t*, const uint16_t*, const uint16_t*, int32_t batch, int32_t hq,
+                   int32_t hkv, int32_t n, float*, float*, float*, void*) {
+    CHECK(batch >= 1 && hq % hkv == 0 && n >= 1);
+    return stub();
+}
+int launch_gather(const uint16_t*, const uint16_t*, int32_t units, int32_t n, const int32_t*,
+                  int32_t n_keep, uint16_t*, uint16_t*, void*) {
+    CHECK(units >= 1 && n_keep >= 1 && n_keep <= n);
+    return stub();
+}
 int launch_fp8_scales(const CacheView& v, const float*, void*) {
     CHECK(v.bits == 8);
     return stub();

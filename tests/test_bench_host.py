@@ -59,3 +59,10 @@ def test_fp8_bytes_per_token():
     s = BM.decode_step_bytes(units=1, gqa=4, head_dim=128, tokens=64 * 32, bits=8, group=32,
                              residual=0)
     assert s.quantized == 64 * 32 * 256
+
+
+def test_prefill_flops_count_the_causal_pairs():
+    # 2 products x 2 flops x d per unmasked (query, key) pair, n (n + 1) / 2 pairs
+    assert BM.prefill_flops(batch=1, n_q_heads=1, head_dim=128, tokens=1) == 512
+    assert BM.prefill_flops(batch=2, n_q_heads=32, head_dim=128, tokens=4096) == \
+        2 * 32 * (4096 * 4097 // 2) * 512
