@@ -174,6 +174,18 @@ def cpu_baseline(w, seconds: float, picks=None):
             "bytes": total_bytes, "seconds": total_t, "steps": steps}
 
 
+def _cpu_model() -> str:
+    """The host CPU's model string (/proc/cpuinfo), or '' when unavailable."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def _cpu_worker(job):
     name, i, seconds = job
     from kv_cache_compression_kvq_amd import synth
@@ -192,7 +204,8 @@ def cpu_baselines(w, seconds: float):
         res = pool.map(_cpu_worker, [(w.name, i, seconds) for i in range(n)])
     value = sum(r["bytes"] / r["seconds"] for r in res) / 1e9
     steps = sum(r["steps"] for r in res)
-    out = {"value": value, "unit": "GB/s", "cores": n, "kind": "oracle",
+    out = {"value": value, "unit": "GB/s", "cores": n, "kind": "oracle", "cpu_model": _cpu_model(),
+           "host_cpus": os.cpu_count(),
            "sample": f"{n} worker processes, one (batch, KV head) unit each, running at once: "
                      f"{steps} single-unit decode steps of the same workload, numpy fp64, "
                      f"one BLAS thread per worker, about {seconds:.0f} s each; value = sum of "
@@ -469,15 +482,23 @@ def main():
     cache_bytes0 = abi.cache_bytes(cfg0)
     n_rep = max(2, math.ceil(REPLICA_BYTES / cache_bytes0))
     per_rep = math.ceil(n_total / n_rep) if append_mode else 0
-    max_tokens = w.tokens + per_rep
+    # Replica i starts (i * G / n_rep) tokens into its residual window, so that
+    # the steps reach the end of the window (and quantize a group) at evenly
+    # spread times: about 1 step in G packs a group, as in a long decode.
+    phases = [(i * w.group) // n_rep if append_mode else 0 for i in range(n_rep)]
+    max_tokens = w.tokens + max(phases) + per_rep
     reps = []
-    for _ in range(n_rep):
+    for i in range(n_rep):
         cfg = abi.make_config(bits=w.bits, group=w.group, residual=w.residual, pool=w.pool,
                               evict_cap=w.evict_cap, head_dim=d, n_q_heads=w.n_q_heads,
-                              n_kv_heads=w.n_kv_heads, batch=w.batch, max_tokens=max_tokens)
+                              n_kv_heads=w.n_kv_heads, batch=w.batch, max_tokens=max_tokens,
+                              sinks=w.sinks)
         arena = torch.empty(abi.cache_bytes(cfg), dtype=torch.uint8, device=dev)
         h = abi.cache_init(cfg, arena)
         abi.quantize_append(h, Kd, Vd, w.tokens)
+        if phases[i]:
+            abi.quantize_append(h, Kd[:, :, :phases[i]].contiguous(), Vd[:, :, :phases[i]].contiguous(),
+                                phases[i])
         acc = torch.zeros((w.batch, w.n_kv_heads, w.tokens), device=dev) if w.h2o else None
         reps.append({"arena": arena, "h": h, "acc": acc})
     del Kd, Vd
@@ -491,18 +512,22 @@ def main():
     n_q_rot = 8
     qs = torch.stack([torch.from_numpy(synth.queries(w, i)) for i in range(n_q_rot)]).to(dev)
     out = torch.empty((w.batch, w.n_q_heads, d), device=dev)
-    # workspace for the largest T any replica reaches
+    # workspace for every T a replica reaches (the plan depends on T)
     hmax = abi.Cache()
     ctypes.memmove(ctypes.byref(hmax), ctypes.byref(reps[0]["h"]), ctypes.sizeof(hmax))
-    hmax.tokens = max_tokens
-    hmax.n_quant = max(0, (max_tokens - w.residual) // w.group * w.group)
-    ws = torch.empty(abi.decode_workspace(hmax, w.h2o), dtype=torch.uint8, device=dev)
+    ws_bytes = 0
+    for T in range(w.tokens, max_tokens + 1):
+        hmax.tokens = T
+        hmax.n_quant = max(0, (T - w.sinks - w.residual) // w.group * w.group)
+        ws_bytes = max(ws_bytes, abi.decode_workspace(hmax, w.h2o))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     k_hh = w.topk_k
     idx = torch.empty((U, k_hh + w.recent), dtype=torch.int32, device=dev) if w.h2o else None
     torch.cuda.synchronize()
 
     step_bytes = []   # algorithmic bytes of each executed step (host bookkeeping)
     step_tokens = []  # cached token x KV-head entries read by each step
+    step_packs = []   # groups quantized by each step (per unit)
 
     def pool_tokens(rep):
         if w.pool == 0:
@@ -533,6 +558,7 @@ def main():
                 abi.decode_step(h, ks[i], vs[i], q, out, rep["acc"], ws)
             nb += BM.append_bytes(units=U, head_dim=d, n_new=1, bits=w.bits, group=w.group,
                                   groups_packed=(h.n_quant - nq0) // w.group)
+            step_packs.append((h.n_quant - nq0) // w.group)
         elif ev[0] is not None:
             abi.decode_attention_timed(rep["h"], q, out, rep["acc"], ws, ev[0], ev[1])
         else:
@@ -549,6 +575,7 @@ def main():
     torch.cuda.synchronize()
     step_bytes.clear()
     step_tokens.clear()
+    step_packs.clear()
 
     use_graph = not args.no_graph
     if use_graph:
@@ -605,6 +632,23 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # Same-run streaming ceiling: one read-only pass over 1 GiB (kvq_stream_read,
+    # every 16-byte word loaded once), event-timed, median of 5 runs: what
+    # this machine's HBM delivers to a plain stream of reads, next to the 8 TB/s peak.
+    big = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    abi.stream_read(big, sink)
+    times = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        abi.stream_read(big, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    stream_gbs = big.numel() / (sorted(times)[2] * 1e-3) / 1e9
+    del big, sink
+
     value = sum(step_bytes) / (total_ms * 1e-3) / 1e9
     tok_heads = sum(step_tokens) / (total_ms * 1e-3)
     h0 = reps[0]["h"]
@@ -625,13 +669,18 @@ def main():
                    "n_kv_heads": w.n_kv_heads, "head_dim": d, "tokens": w.tokens,
                    "bits": w.bits, "group": w.group, "residual": w.residual, "pool": w.pool,
                    "h2o": w.h2o, "replicas": n_rep, "hip_graph": use_graph,
-                   "step": "append 1 token + attention" if append_mode
-                   else "attention with H2O scores + top-k"},
+                   "step": "append 1 token + attention; replicas at spread window phases, so "
+                           "about 1 step in G also quantizes a group (every unit)"
+                   if append_mode else "attention with H2O scores + top-k",
+                   "groups_quantized_in_timed_steps": int(sum(step_packs))},
+        "stream_read_GBps": round(stream_gbs, 1),
+        "pct_of_stream_read": round(100 * value / stream_gbs, 2),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_heads_per_s": round(tok_heads, 1),
         "query_head_scores_per_s": round(tok_heads * r, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "frac_of_stream_read": round(achieved / stream_gbs, 4),
                      "traffic": None,
                      "kernel": "decode_kernel", "kernel_us": round(kernel_us, 3),
                      "kernel_alg_bytes": int(kernel_bytes), "source_sha": source_sha()},

@@ -359,6 +359,15 @@ kvq_status kvq_gather_kv(const void* d_k, const void* d_v, int32_t batch, int32_
                          void* d_k_out, void* d_v_out, void* stream);
 
 /*
+ * Measurement utility: one read-only pass over d_buf (device, bytes a multiple
+ * of 16, 16-byte aligned), every 16-byte word loaded once; writes device
+ * uint32 d_sink[4096] (an XOR of the data, so that no load can be dropped).
+ * Its bandwidth is the read ceiling the decode kernel is compared with.
+ * Errors: KVQ_EINVAL (null pointer, bytes % 16 != 0).
+ */
+kvq_status kvq_stream_read(const void* d_buf, size_t bytes, uint32_t* d_sink, void* stream);
+
+/*
  * Set the FP8 scales of a b = 8 cache: d_scales is device fp32 [Hkv][2] (key
  * scale, value scale per KV head), finite and positive (not checked on the
  * device). Elements are stored as E4M3(x / s) and read back as E4M3 * s; set

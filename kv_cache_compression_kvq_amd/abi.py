@@ -30,7 +30,7 @@ EXPORTS = ("kvq_status_string", "kvq_cache_bytes", "kvq_cache_init", "kvq_quanti
            "kvq_decode_step", "kvq_decode_step_timed", "kvq_topk_evict", "kvq_unpack_codes",
            "kvq_decode_attention_noalloc", "kvq_debug_unpack", "kvq_evict_step",
            "kvq_pyramid_budgets", "kvq_fp8_set_scales", "kvq_prefill_workspace",
-           "kvq_prefill_attention", "kvq_gather_kv")
+           "kvq_prefill_attention", "kvq_gather_kv", "kvq_stream_read")
 
 
 class Config(ctypes.Structure):
@@ -98,6 +98,7 @@ def lib() -> ctypes.CDLL:
             "kvq_prefill_workspace": [I32, I32, I32, ctypes.POINTER(SZ)],
             "kvq_prefill_attention": [P, P, P, I32, I32, I32, I32, I32, P, P, P, SZ, P],
             "kvq_gather_kv": [P, P, I32, I32, I32, I32, P, I32, P, P, P],
+            "kvq_stream_read": [P, SZ, P, P],
             "kvq_pyramid_budgets": [I32, I32, I32, ctypes.POINTER(I32)],
         }
         for name, args in sigs.items():
@@ -262,3 +263,9 @@ def gather_kv(k, v, batch: int, n_kv_heads: int, n: int, idx, n_keep: int, k_out
     _check("kvq_gather_kv", lib().kvq_gather_kv(
         _ptr(k), _ptr(v), batch, n_kv_heads, head_dim, n, _ptr(idx), n_keep, _ptr(k_out),
         _ptr(v_out), _stream(stream)))
+
+
+def stream_read(buf, sink, nbytes: int | None = None, stream=None) -> None:
+    """kvq_stream_read: one read-only pass over ``buf`` (the read ceiling)."""
+    n = nbytes if nbytes is not None else buf.numel() * buf.element_size()
+    _check("kvq_stream_read", lib().kvq_stream_read(_ptr(buf), n, _ptr(sink), _stream(stream)))

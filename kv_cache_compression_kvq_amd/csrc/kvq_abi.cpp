@@ -418,6 +418,12 @@ kvq_status kvq_gather_kv(const void* d_k, const void* d_v, int32_t batch, int32_
                                        static_cast<uint16_t*>(d_v_out), stream));
 }
 
+kvq_status kvq_stream_read(const void* d_buf, size_t bytes, uint32_t* d_sink, void* stream) {
+    if (!d_buf || !d_sink || bytes % 16 != 0) return KVQ_EINVAL;
+    if (bytes == 0) return KVQ_OK;
+    return launch_status(launch_stream_read(d_buf, bytes, d_sink, stream));
+}
+
 kvq_status kvq_fp8_set_scales(kvq_cache* h, const float* d_scales, void* stream) {
     if (!valid_handle(h) || !d_scales) return KVQ_EINVAL;
     if (h->cfg.bits != 8) return KVQ_EUNSUPPORTED;

@@ -129,6 +129,7 @@ struct DecodeArgs {
     const uint16_t* ev_v;
     const int32_t* counters;
     const uint32_t* evict;   // [U][evict_words] eviction bits of tokens S, S + 1, ...
+    const int32_t* evict_count;  // [U]
     int64_t evict_words;
     const uint16_t* sink_k;  // attention sinks [U][sink_cap][d]
     const uint16_t* sink_v;
@@ -278,6 +279,10 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
     const int cnt = (int)(ntot - base < 0 ? 0 : ntot - base < a.tile_rows ? ntot - base : a.tile_rows);
     // Row i of the tile: kind 0 sink, 1 ring (slot (n_q + ring row) % RB),
     // 2 pool, 3 extra pool; returns the row's element offset in its array.
+    // The ring rows of a tile are fewer than RB, so one slot computed per tile
+    // and at most one wrap give every row's slot.
+    const int64_t ring_first = base > ns ? base : ns;
+    const int32_t slot_first = (int32_t)((a.n_q + (ring_first - ns)) % RB);
     auto row_off = [&](int i, int& kind) -> int64_t {
         const int64_t li = base + i;
         if (li < ns) {
@@ -286,7 +291,8 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
         }
         if (li < ns + nres) {
             kind = 1;
-            const uint32_t sl = (uint32_t)(a.n_q + (li - ns)) % (uint32_t)RB;
+            int32_t sl = slot_first + (int32_t)(li - ring_first);
+            if (sl >= RB) sl -= RB;
             return ((int64_t)u * RB + sl) * D;
         }
         if (li < ns + nres + pc) {
@@ -318,8 +324,19 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
     }
     __syncthreads();
     if (h >= R) return;
+    const bool any_evicted = scalar_load(a.evict_count + u) != 0u;
     float s = -INFINITY;
     if (lane < cnt) {
+        // the row's token index after the sinks (-1 for a sink) and whether it
+        // was evicted, requested together with the row itself
+        const int64_t li = base + lane;
+        const int64_t tau = li < ns ? -1
+                            : li < ns + nres ? a.n_q + (li - ns)
+                            : li < ns + nres + pc
+                                ? a.pool_idx[(int64_t)u * N + (li - ns - nres)]
+                                : a.ev_idx[(int64_t)u * E + (li - ns - nres - pc)];
+        const uint32_t evw = tau >= 0 && any_evicted
+                                 ? a.evict[(int64_t)u * a.evict_words + (tau >> 5)] : 0u;
         const uint4* kr = reinterpret_cast<const uint4*>(
             row_ptr(lane, a.sink_k, a.kring, a.pool_k, a.ev_k, a.k_new));
         uint4 x[16];
@@ -340,26 +357,10 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
                                          __builtin_bit_cast(half2_t, y.w), acc, false);
         }
         s = acc * a.qscale;
-        {
-            // an evicted ring, pool or extra-pool token (index after the sinks)
-            const int64_t li = base + lane;
-            if (li >= ns) {
-                const int64_t tau = li < ns + nres ? a.n_q + (li - ns)
-                                    : li < ns + nres + pc
-                                        ? a.pool_idx[(int64_t)u * N + (li - ns - nres)]
-                                        : a.ev_idx[(int64_t)u * E + (li - ns - nres - pc)];
-                if ((a.evict[(int64_t)u * a.evict_words + (tau >> 5)] >> (tau & 31)) & 1u)
-                    s = -INFINITY;
-            }
-        }
+        if (tau >= 0 && ((evw >> (tau & 31)) & 1u)) s = -INFINITY;  // evicted
         if (a.logits) {
             // sequence index of the row's token
-            const int64_t li = base + lane;
-            const int64_t t = li < ns ? li
-                              : li < ns + nres ? a.sink_cap + a.n_q + (li - ns)
-                              : li < ns + nres + pc
-                                  ? a.sink_cap + a.pool_idx[(int64_t)u * N + (li - ns - nres)]
-                                  : a.sink_cap + a.ev_idx[(int64_t)u * E + (li - ns - nres - pc)];
+            const int64_t t = tau < 0 ? li : a.sink_cap + tau;
             a.logits[((int64_t)u * R + h) * a.T + t] = s;
         }
     }
@@ -1370,9 +1371,11 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     constexpr int kPart = kH2OChunk / R;
     const int64_t t0 = (int64_t)(blockIdx.y - 1) * kH2OChunk + (int64_t)hb * kPart;
     const uint32_t* ev_u = a.evict + (int64_t)u * a.evict_words;
+    const bool any_evicted = a.evict_count[u] != 0;
     for (int64_t t = t0 + threadIdx.x; t < t0 + kPart && t < a.T; t += 256) {
         const int64_t tau = t - a.sink_cap;
-        if (tau >= 0 && ((ev_u[tau >> 5] >> (tau & 31)) & 1u)) continue;  // evicted: no score
+        if (any_evicted && tau >= 0 && ((ev_u[tau >> 5] >> (tau & 31)) & 1u))
+            continue;  // evicted: no score
         float d = 0.f;
 #pragma unroll
         for (int h = 0; h < R; ++h)
@@ -1551,6 +1554,7 @@ int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& 
     a.ev_v = v.ev_v;
     a.counters = v.counters;
     a.evict = v.evict;
+    a.evict_count = v.evict_count;
     a.evict_words = v.evict_words;
     a.sink_k = v.sink_k;
     a.sink_v = v.sink_v;

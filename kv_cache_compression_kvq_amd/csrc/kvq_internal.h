@@ -92,6 +92,7 @@ int launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, int3
                    float* lse, void* stream);
 int launch_gather(const uint16_t* k, const uint16_t* v, int32_t units, int32_t n,
                   const int32_t* idx, int32_t n_keep, uint16_t* ko, uint16_t* vo, void* stream);
+int launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 int launch_fp8_scales(const CacheView& v, const float* scales, void* stream);
 int launch_evict_step(const CacheView& v, int64_t T, const float* acc, int32_t budget,
                       int32_t recent, void* stream);

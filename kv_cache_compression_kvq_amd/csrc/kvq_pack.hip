@@ -948,14 +948,30 @@ __global__ __launch_bounds__(256) void debug_view_kernel(CacheView v, int64_t T,
     }
 }
 
-// One H2O eviction step: one block per unit. If more than `budget` tokens are
-// live, the live token in [S, T - recent) with the lowest score is evicted
-// ("H2O: Heavy-Hitter Oracle", greedy eviction; "KV cache quantization and
-// eviction", h2o_evict). Scores compare through an order-preserving key
-// with every NaN lowest and -0 equal to +0; the smallest (key, index) wins, so
-// ties go to the older token.
-__global__ __launch_bounds__(256) void evict_step_kernel(CacheView v, int64_t T, const float* acc,
-                                                         int32_t budget, int32_t recent) {
+// One H2O eviction step: one 1024-thread block per unit. If more than
+// `budget` tokens are live, the live token in [S, T - recent) with the lowest
+// score is evicted ("H2O: Heavy-Hitter Oracle", greedy eviction; "KV cache
+// quantization and eviction", h2o_evict). Scores compare through an
+// order-preserving key with every NaN lowest and -0 equal to +0; the smallest
+// (key, index) wins, so ties go to the older token. Each thread reads four
+// consecutive scores at a time (16-byte loads when the row allows it), all of
+// its loads in flight before any is compared.
+__device__ __forceinline__ uint64_t evict_key(float f, int64_t t) {
+    uint32_t b = __builtin_bit_cast(uint32_t, f);
+    uint32_t key;
+    if (f != f) {
+        key = 0u;  // NaN: lowest
+    } else {
+        if (f == 0.0f) b = 0u;  // -0 == +0
+        key = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    }
+    return ((uint64_t)key << 32) | (uint64_t)t;
+}
+
+constexpr int kEvictThreads = 1024;
+__global__ __launch_bounds__(kEvictThreads) void evict_step_kernel(CacheView v, int64_t T,
+                                                                   const float* acc, int32_t budget,
+                                                                   int32_t recent) {
     const int u = blockIdx.x, tid = threadIdx.x;
     const int64_t live = T - v.evict_count[u];
     if (live <= budget) return;  // uniform over the block
@@ -963,31 +979,57 @@ __global__ __launch_bounds__(256) void evict_step_kernel(CacheView v, int64_t T,
     const uint32_t* ev = v.evict + (int64_t)u * v.evict_words;
     const float* sc = acc + (int64_t)u * T;
     uint64_t best = ~0ull;
-    for (int64_t t = S + tid; t < end; t += 256) {
-        const int64_t tau = t - S;
-        if ((ev[tau >> 5] >> (tau & 31)) & 1u) continue;
-        const float f = sc[t];
-        uint32_t b = __builtin_bit_cast(uint32_t, f);
-        uint32_t key;
-        if (f != f) key = 0u;                      // NaN: lowest
-        else {
-            if (f == 0.0f) b = 0u;                 // -0 == +0
-            key = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-            if (key == 0u) key = 1u;               // keep 0 for NaN only
+    // groups of 4 tokens t = 4 g .. 4 g + 3 (sequence indices), 8 groups per
+    // thread and pass
+    const int64_t g_first = S / 4, g_end = (end + 3) / 4;
+    const bool aligned = (T % 4) == 0;  // row start 16-byte aligned
+    const bool any_evicted = v.evict_count[u] != 0;
+    for (int64_t g0 = g_first + tid; g0 < g_end; g0 += 8 * kEvictThreads) {
+        float4 x[8];
+        uint32_t ew0[8], ew1[8];  // eviction words of the group's first and last token
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t g = g0 + (int64_t)k * kEvictThreads;
+            if (g < g_end && aligned && 4 * g + 3 < T) {
+                x[k] = reinterpret_cast<const float4*>(sc)[g];
+            } else {
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = g < g_end && 4 * g + e < T ? sc[4 * g + e] : 0.f;
+                x[k] = make_float4(y[0], y[1], y[2], y[3]);
+            }
+            // the group's first and last token inside the row (indices after the sinks)
+            const int64_t ta = 4 * g - S, tb = (4 * g + 3 < T ? 4 * g + 3 : T - 1) - S;
+            ew0[k] = any_evicted && g < g_end && ta >= 0 ? ev[ta >> 5] : 0u;
+            ew1[k] = any_evicted && g < g_end && tb >= 0 ? ev[tb >> 5] : 0u;
         }
-        const uint64_t k = ((uint64_t)key << 32) | (uint64_t)t;
-        best = k < best ? k : best;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t g = g0 + (int64_t)k * kEvictThreads;
+            if (g >= g_end) break;
+            const float y[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t t = 4 * g + e;
+                if (t < S || t >= end) continue;
+                const int64_t tau = t - S;
+                const uint32_t w = (tau >> 5) == ((4 * g - S) >> 5) ? ew0[k] : ew1[k];
+                if ((w >> (tau & 31)) & 1u) continue;
+                const uint64_t kk = evict_key(y[e], t);
+                best = kk < best ? kk : best;
+            }
+        }
     }
     for (int off = 32; off > 0; off >>= 1) {
         const uint64_t o = __shfl_xor(best, off);
         best = o < best ? o : best;
     }
-    __shared__ uint64_t wbest[4];
+    __shared__ uint64_t wbest[kEvictThreads / 64];
     if ((tid & 63) == 0) wbest[tid >> 6] = best;
     __syncthreads();
     if (tid == 0) {
         uint64_t b = wbest[0];
-        for (int w = 1; w < 4; ++w) b = wbest[w] < b ? wbest[w] : b;
+        for (int w = 1; w < kEvictThreads / 64; ++w) b = wbest[w] < b ? wbest[w] : b;
         if (b != ~0ull) {
             const int64_t tau = (int64_t)(b & 0xFFFFFFFFu) - S;
             uint32_t* word = v.evict + (int64_t)u * v.evict_words + (tau >> 5);
@@ -995,6 +1037,32 @@ __global__ __launch_bounds__(256) void evict_step_kernel(CacheView v, int64_t T,
             v.evict_count[u] += 1;
         }
     }
+}
+
+// Read-only streaming pass over a buffer, the memory ceiling the decode kernel
+// is compared with: every 16-byte word is loaded once (eight loads in flight
+// per thread), folded with XOR so no load can be dropped, one word written per
+// block.
+constexpr int kStreamBlocks = 4096;
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* buf, int64_t n16,
+                                                          uint32_t* sink) {
+    uint32_t f = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < n16; i0 += 8 * stride) {
+        uint4 x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t i = i0 + k * stride;
+            x[k] = i < n16 ? buf[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f ^= x[k].x ^ x[k].y ^ x[k].z ^ x[k].w;
+    }
+    for (int off = 32; off > 0; off >>= 1) f ^= __shfl_xor(f, off);
+    __shared__ uint32_t wf[4];
+    if ((threadIdx.x & 63) == 0) wf[threadIdx.x >> 6] = f;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = wf[0] ^ wf[1] ^ wf[2] ^ wf[3];
 }
 
 // Pool and extra-pool indices of the canonical view: sequence indices, i.e.
@@ -1135,6 +1203,14 @@ int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, voi
     return (int)hipGetLastError();
 }
 
+int launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    (void)hipGetLastError();  // an error left by an earlier call is not this call's
+    hipLaunchKernelGGL(stream_read_kernel, dim3(kStreamBlocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint4*>(buf),
+                       (int64_t)(bytes / 16), sink);
+    return (int)hipGetLastError();
+}
+
 int launch_fp8_scales(const CacheView& v, const float* scales, void* stream) {
     (void)hipGetLastError();  // an error left by an earlier call is not this call's
     return (int)hipMemcpyAsync(v.fp8_scales, scales, (size_t)v.n_kv_heads * 2 * sizeof(float),
@@ -1145,7 +1221,8 @@ int launch_evict_step(const CacheView& v, int64_t T, const float* acc, int32_t b
                       int32_t recent, void* stream) {
     (void)hipGetLastError();  // an error left by an earlier call is not this call's
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(evict_step_kernel, dim3(v.units), dim3(256), 0, s, v, T, acc, budget, recent);
+    hipLaunchKernelGGL(evict_step_kernel, dim3(v.units), dim3(kEvictThreads), 0, s, v, T, acc,
+                       budget, recent);
     return (int)hipGetLastError();
 }
 

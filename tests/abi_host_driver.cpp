@@ -61,6 +61,10 @@ int launch_gather(const uint16_t*, const uint16_t*, int32_t units, int32_t n, co
     CHECK(units >= 1 && n_keep >= 1 && n_keep <= n);
     return stub();
 }
+int launch_stream_read(const void*, size_t bytes, uint32_t*, void*) {
+    CHECK(bytes % 16 == 0 && bytes > 0);
+    return stub();
+}
 int launch_fp8_scales(const CacheView& v, const float*, void*) {
     CHECK(v.bits == 8);
     return stub();

@@ -575,3 +575,16 @@ def test_workload_minikv_h2o_and_topk():
     abi.topk_evict(acc, rows, w.tokens, k, wr, idx)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(idx.cpu().numpy(), O.topk_keep(accn.reshape(rows, -1), k, wr))
+
+
+def test_stream_read_touches_every_word(kvq):
+    """The measurement pass behind the bench's read ceiling reads the whole
+    buffer: the XOR of its per-block outputs is the XOR of all 32-bit words."""
+    rng = np.random.default_rng(9)
+    data = rng.integers(0, 2 ** 32, size=(64 << 20) // 4, dtype=np.uint32)
+    buf = torch.from_numpy(data.view(np.int32)).cuda()
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    kvq.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(data)
