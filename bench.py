@@ -221,6 +221,7 @@ ROWS = {
     "decode_h2o_minikv": ("minikv", "a8-a10: fused decode + merge with H2O accumulation"),
     "topk_minikv": ("minikv", "a11: heavy-hitter top-k + recent window"),
     "evict_minikv": ("minikv", "f2: one H2O eviction per KV head (budget 20% + 256 recent)"),
+    "topk_long": ("long_b2g32", "a11: heavy-hitter top-k (20% + 256 recent) over 131072-token rows"),
     "decode_llama8b_g16": ("llama8b_g16", "a8-a10: fused decode + merge at group size 16"),
     "decode_llama8b_sinks": ("llama8b_sinks", "a8-a10 with 4 attention sinks in the fp16 partition"),
     "prefill_llama8b": ("prefill_llama8b", "f1: causal prefill attention + A_cumul column sums "
@@ -343,6 +344,34 @@ def rows_main(args):
             del bufs, out, acc, ws
             torch.cuda.empty_cache()
             continue
+        if name == "topk_long":
+            # seeded exponential scores of every KV head's row, replicas past
+            # the Infinity Cache; the split (workspace) path, with the
+            # one-workgroup-per-row time beside it
+            T, k, wr = w.tokens, int(0.2 * w.tokens), 256
+            s0 = torch.from_numpy(synth.score_rows(U, T, seed=5)).to(dev)
+            n_rep = max(2, math.ceil(REPLICA_BYTES / s0.numel() / 4))
+            srows = [s0] + [s0.clone() for _ in range(n_rep - 1)]
+            idx = torch.empty((U, k + wr), dtype=torch.int32, device=dev)
+            nws = abi.topk_workspace(U, T, k, wr)
+            tws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+            times = {}
+            for with_ws in (False, True):
+                def call(i, a, b):
+                    a.record()
+                    abi.topk_evict(srows[i % n_rep], U, T, k, wr, idx, tws if with_ws else None,
+                                   nws if with_ws else 0)
+                    b.record()
+
+                timed(call, 2)
+                times[with_ws] = timed(call, args.reps)
+            emit(name, w, times[True], BM.topk_bytes(rows=U, tokens=T, k=k, w=wr),
+                 {"kernels": ["topk_slice_hist_kernel", "topk_slice_select_kernel"], "k": k,
+                  "recent": wr, "rows": U, "workspace_bytes": nws,
+                  "us_one_workgroup_per_row": round(times[False], 3)})
+            del srows, s0, tws, idx
+            torch.cuda.empty_cache()
+            continue
         if name.startswith("append"):
             srcs = source(w)
             cfg, reps = caches(w)
@@ -412,17 +441,21 @@ def rows_main(args):
                 abi.decode_attention(rep["h"], q, out, rep["acc"], ws)
             k, wr = w.topk_k, w.recent
             idx = torch.empty((U, k + wr), dtype=torch.int32, device=dev)
+            nws = abi.topk_workspace(U, w.tokens, k, wr)
+            tws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
 
             def call(i, a, b):
                 rep = reps[i % len(reps)]
                 a.record()
-                abi.topk_evict(rep["acc"], U, w.tokens, k, wr, idx)
+                abi.topk_evict(rep["acc"], U, w.tokens, k, wr, idx, tws, nws)
                 b.record()
 
             timed(call, 2)
             us = timed(call, args.reps)
+            kernels = (["topk_slice_hist_kernel", "topk_slice_select_kernel"] if nws
+                       else ["topk_reg_kernel"])
             emit(name, w, us, BM.topk_bytes(rows=U, tokens=w.tokens, k=k, w=wr),
-                 {"kernels": ["topk_reg_kernel"], "k": k, "recent": wr})
+                 {"kernels": kernels, "k": k, "recent": wr, "workspace_bytes": nws})
         del reps, ws, out
         torch.cuda.empty_cache()
     if args.copy_calibration:
@@ -523,6 +556,8 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     k_hh = w.topk_k
     idx = torch.empty((U, k_hh + w.recent), dtype=torch.int32, device=dev) if w.h2o else None
+    tk_nws = abi.topk_workspace(U, w.tokens, k_hh, w.recent) if w.h2o else 0
+    tk_ws = torch.empty(max(tk_nws, 1), dtype=torch.uint8, device=dev) if w.h2o else None
     torch.cuda.synchronize()
 
     step_bytes = []   # algorithmic bytes of each executed step (host bookkeeping)
@@ -565,7 +600,7 @@ def main():
             abi.decode_attention(rep["h"], q, out, rep["acc"], ws)
         nb += decode_bytes(h, pools_now[i % n_rep])
         if w.h2o:
-            abi.topk_evict(rep["acc"], U, w.tokens, k_hh, w.recent, idx)
+            abi.topk_evict(rep["acc"], U, w.tokens, k_hh, w.recent, idx, tk_ws, tk_nws)
             nb += BM.topk_bytes(rows=U, tokens=w.tokens, k=k_hh, w=w.recent)
         step_bytes.append(nb)
         step_tokens.append(U * h.tokens)

@@ -307,15 +307,34 @@ kvq_status kvq_decode_step_timed(kvq_cache* h, const void* d_k, const void* d_v,
                                  size_t ws_bytes, void* ev_start, void* ev_stop, void* stream);
 
 /*
- * Heavy-hitter selection on fp32 scores (device [rows][T]): for each row keep
- * the k largest scores among indices [0, T - w), ties broken toward the
- * larger index, plus the w most recent indices [T - w, T). Writes device
- * int32 [rows][k + w], ascending. +0 and -0 compare equal; a NaN score ranks
- * below every number and all NaNs compare equal. Errors: KVQ_EINVAL (null
- * pointer, rows < 0, k < 0, w < 0, k + w > T).
+ * Workspace bytes kvq_topk_evict can use for these sizes on the current GPU
+ * (0 when every row is served by one workgroup). Host only; the same checks
+ * as kvq_topk_evict (KVQ_EINVAL).
+ */
+kvq_status kvq_topk_workspace(int32_t rows, int32_t T, int32_t k, int32_t w, size_t* ws_bytes);
+
+/*
+ * Heavy-hitter selection on fp32 scores ("MiniKV: Pushing the Limits of LLM
+ * Inference via 2-Bit Layer-Discriminative KV Cache", Algorithm 1, heavy
+ * hitters plus recent window; "KV cache quantization and eviction", section
+ * "Minimal implementation": evicting the lowest score one token at a time,
+ * with ties going to the earlier token, keeps on fixed scores the k largest
+ * with ties toward the later index).
+ *   d_scores device fp32 [rows][T]
+ *   d_idx    device int32 [rows][k + w] (written): for each row the k largest
+ *            scores among indices [0, T - w), ties broken toward the larger
+ *            index, then the w most recent indices [T - w, T); ascending.
+ *   d_ws     device workspace of ws_bytes >= kvq_topk_workspace(rows, T, k, w),
+ *            or NULL. With it, rows are split over several workgroups when
+ *            one workgroup per row would leave compute units idle; without
+ *            it, one workgroup per row. Both give the same indices.
+ * +0 and -0 compare equal; a NaN score ranks below every number and all NaNs
+ * compare equal. Errors: KVQ_EINVAL (null pointer, rows < 0, k < 0, w < 0,
+ * k + w > T), KVQ_EWORKSPACE.
  */
 kvq_status kvq_topk_evict(const float* d_scores, int32_t rows, int32_t T, int32_t k,
-                          int32_t w, int32_t* d_idx, void* stream);
+                          int32_t w, int32_t* d_idx, void* d_ws, size_t ws_bytes,
+                          void* stream);
 
 /*
  * Prefill attention of one layer with heavy-hitter scores ("MiniKV: Pushing

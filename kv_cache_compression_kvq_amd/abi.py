@@ -27,7 +27,8 @@ NOALLOC_SCRATCH_BYTES = 32 << 20  # KVQ_NOALLOC_SCRATCH_BYTES
 # Entry points declared in include/kvq.h.
 EXPORTS = ("kvq_status_string", "kvq_cache_bytes", "kvq_cache_init", "kvq_quantize_append",
            "kvq_decode_workspace", "kvq_decode_attention", "kvq_decode_attention_timed",
-           "kvq_decode_step", "kvq_decode_step_timed", "kvq_topk_evict", "kvq_unpack_codes",
+           "kvq_decode_step", "kvq_decode_step_timed", "kvq_topk_workspace", "kvq_topk_evict",
+           "kvq_unpack_codes",
            "kvq_decode_attention_noalloc", "kvq_debug_unpack", "kvq_evict_step",
            "kvq_pyramid_budgets", "kvq_fp8_set_scales", "kvq_prefill_workspace",
            "kvq_prefill_attention", "kvq_gather_kv", "kvq_stream_read")
@@ -90,7 +91,8 @@ def lib() -> ctypes.CDLL:
             "kvq_decode_attention_noalloc": [ctypes.POINTER(Cache), P, P, P, P],
             "kvq_decode_step": [ctypes.POINTER(Cache), P, P, P, P, P, P, SZ, P],
             "kvq_decode_step_timed": [ctypes.POINTER(Cache), P, P, P, P, P, P, SZ, P, P, P],
-            "kvq_topk_evict": [P, I32, I32, I32, I32, P, P],
+            "kvq_topk_workspace": [I32, I32, I32, I32, ctypes.POINTER(SZ)],
+            "kvq_topk_evict": [P, I32, I32, I32, I32, P, P, SZ, P],
             "kvq_unpack_codes": [ctypes.POINTER(Cache), P, P, P],
             "kvq_debug_unpack": [ctypes.POINTER(Cache), ctypes.POINTER(DebugView), P],
             "kvq_evict_step": [ctypes.POINTER(Cache), P, I32, I32, P],
@@ -205,9 +207,20 @@ def decode_step_timed(h: Cache, k, v, q, out, acc, ws, ev_start: int, ev_stop: i
         ev_start, ev_stop, _stream(stream)))
 
 
-def topk_evict(scores, rows: int, T: int, k: int, w: int, idx, stream=None) -> None:
+def topk_workspace(rows: int, T: int, k: int, w: int) -> int:
+    n = ctypes.c_size_t()
+    _check("kvq_topk_workspace", lib().kvq_topk_workspace(rows, T, k, w, ctypes.byref(n)))
+    return n.value
+
+
+def topk_evict(scores, rows: int, T: int, k: int, w: int, idx, ws=None,
+               ws_bytes: int | None = None, stream=None) -> None:
+    """ws: device workspace of topk_workspace(...) bytes, or None (one
+    workgroup per row)."""
+    nbytes = ws_bytes if ws_bytes is not None else (
+        ws.numel() * ws.element_size() if ws is not None else 0)
     _check("kvq_topk_evict", lib().kvq_topk_evict(_ptr(scores), rows, T, k, w, _ptr(idx),
-                                                  _stream(stream)))
+                                                  _ptr(ws), nbytes, _stream(stream)))
 
 
 def unpack_codes(h: Cache, kcodes, vcodes, stream=None) -> None:

@@ -363,12 +363,23 @@ kvq_status kvq_decode_step(kvq_cache* h, const void* d_k, const void* d_v, const
                                  nullptr, stream);
 }
 
+kvq_status kvq_topk_workspace(int32_t rows, int32_t T, int32_t k, int32_t w, size_t* ws_bytes) {
+    if (!ws_bytes || rows < 0 || T < 0 || k < 0 || w < 0 || (int64_t)k + w > T) return KVQ_EINVAL;
+    *ws_bytes = rows == 0 || k + w == 0 ? 0 : topk_plan(rows, T, k, w).ws_bytes;
+    return KVQ_OK;
+}
+
 kvq_status kvq_topk_evict(const float* d_scores, int32_t rows, int32_t T, int32_t k, int32_t w,
-                          int32_t* d_idx, void* stream) {
+                          int32_t* d_idx, void* d_ws, size_t ws_bytes, void* stream) {
     if (rows < 0 || T < 0 || k < 0 || w < 0 || (int64_t)k + w > T) return KVQ_EINVAL;
     if (rows == 0 || k + w == 0) return KVQ_OK;
     if (!d_scores || !d_idx) return KVQ_EINVAL;
-    return launch_status(launch_topk(d_scores, rows, T, k, w, d_idx, stream));
+    TopkPlan plan{1, T - w, 0};
+    if (d_ws) {
+        plan = topk_plan(rows, T, k, w);
+        if (ws_bytes < plan.ws_bytes) return KVQ_EWORKSPACE;
+    }
+    return launch_status(launch_topk(d_scores, rows, T, k, w, d_idx, d_ws, plan, stream));
 }
 
 kvq_status kvq_unpack_codes(const kvq_cache* h, uint8_t* d_kcodes, uint8_t* d_vcodes,

@@ -84,8 +84,16 @@ int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& 
                   const uint16_t* q, float* out, float* acc, void* ws, void* ev_start,
                   void* ev_stop, void* stream, const uint16_t* k_new = nullptr,
                   const uint16_t* v_new = nullptr);
-int launch_topk(const float* scores, int32_t rows, int32_t T, int32_t k, int32_t w,
-                int32_t* idx, void* stream);
+// Heavy-hitter top-k: rows split over `slices` workgroups of slice_len keys
+// each (slices == 1: one workgroup per row, no workspace).
+struct TopkPlan {
+    int32_t slices;
+    int32_t slice_len;
+    size_t ws_bytes;
+};
+TopkPlan topk_plan(int32_t rows, int32_t T, int32_t k, int32_t w);
+int launch_topk(const float* scores, int32_t rows, int32_t T, int32_t k, int32_t w, int32_t* idx,
+                void* ws, const TopkPlan& plan, void* stream);
 int launch_unpack(const CacheView& v, int64_t n_q, uint8_t* kc, uint8_t* vc, void* stream);
 int launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, int32_t batch,
                    int32_t n_q_heads, int32_t n_kv_heads, int32_t n, float* out, float* acc,

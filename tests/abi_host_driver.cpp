@@ -43,8 +43,16 @@ int launch_decode(const CacheView& v, int64_t T, int64_t n_q, const DecodePlan& 
     CHECK(T >= 1 && n_q <= T && n_q <= v.q_cap && p.splits == p.splits_q + p.fp16_tiles);
     return stub();
 }
-int launch_topk(const float*, int32_t rows, int32_t T, int32_t k, int32_t w, int32_t*, void*) {
+TopkPlan topk_plan(int32_t rows, int32_t T, int32_t k, int32_t w) {
     CHECK(rows > 0 && k + w <= T);
+    // the host driver's stand-in: two slices once rows are long
+    if (T - w >= 8192 && k > 0 && k < T - w) return TopkPlan{2, (T - w + 7) / 8 * 4, 64};
+    return TopkPlan{1, T - w, 0};
+}
+int launch_topk(const float*, int32_t rows, int32_t T, int32_t k, int32_t w, int32_t*, void* ws,
+                const TopkPlan& plan, void*) {
+    CHECK(rows > 0 && k + w <= T);
+    CHECK(plan.slices == 1 || ws != nullptr);
     return stub();
 }
 int launch_unpack(const CacheView&, int64_t n_q, uint8_t*, uint8_t*, void*) {
@@ -250,11 +258,21 @@ int main() {
     // top-k argument checks
     float s = 0.f;
     int32_t idx = 0;
-    CHECK(kvq_topk_evict(&s, 2, 100, 90, 20, &idx, nullptr) == KVQ_EINVAL);
-    CHECK(kvq_topk_evict(&s, -1, 100, 10, 20, &idx, nullptr) == KVQ_EINVAL);
-    CHECK(kvq_topk_evict(nullptr, 2, 100, 10, 20, &idx, nullptr) == KVQ_EINVAL);
-    CHECK(kvq_topk_evict(&s, 0, 100, 10, 20, &idx, nullptr) == KVQ_OK);
-    CHECK(kvq_topk_evict(&s, 2, 100, 10, 20, &idx, nullptr) == KVQ_OK);
+    CHECK(kvq_topk_evict(&s, 2, 100, 90, 20, &idx, nullptr, 0, nullptr) == KVQ_EINVAL);
+    CHECK(kvq_topk_evict(&s, -1, 100, 10, 20, &idx, nullptr, 0, nullptr) == KVQ_EINVAL);
+    CHECK(kvq_topk_evict(nullptr, 2, 100, 10, 20, &idx, nullptr, 0, nullptr) == KVQ_EINVAL);
+    CHECK(kvq_topk_evict(&s, 0, 100, 10, 20, &idx, nullptr, 0, nullptr) == KVQ_OK);
+    CHECK(kvq_topk_evict(&s, 2, 100, 10, 20, &idx, nullptr, 0, nullptr) == KVQ_OK);
+    // workspace: none needed for short rows; a split plan needs its bytes
+    size_t tw = 1;
+    CHECK(kvq_topk_workspace(2, 100, 10, 20, &tw) == KVQ_OK && tw == 0);
+    CHECK(kvq_topk_workspace(2, 100, 90, 20, &tw) == KVQ_EINVAL);
+    CHECK(kvq_topk_workspace(2, 100, 10, 20, nullptr) == KVQ_EINVAL);
+    CHECK(kvq_topk_workspace(2, 20000, 4000, 128, &tw) == KVQ_OK && tw == 64);
+    char ws[64];
+    CHECK(kvq_topk_evict(&s, 2, 20000, 4000, 128, &idx, ws, 63, nullptr) == KVQ_EWORKSPACE);
+    CHECK(kvq_topk_evict(&s, 2, 20000, 4000, 128, &idx, ws, 64, nullptr) == KVQ_OK);
+    CHECK(kvq_topk_evict(&s, 2, 20000, 4000, 128, &idx, nullptr, 0, nullptr) == KVQ_OK);
 
     std::printf("%d checks, %d failed, %d stubbed launches\n", g_checks, g_bad, g_launches);
     return g_bad == 0 ? 0 : 1;

@@ -101,10 +101,13 @@ def test_validation_paths_launch_nothing(kvq):
     assert L.kvq_cache_init(ctypes.byref(cfg), P((1 << 40) + 8), 1 << 40, ctypes.byref(hh), None) == -1
     assert L.kvq_cache_init(ctypes.byref(cfg), P(1 << 40), 1024, ctypes.byref(hh), None) == -4
     # top-k argument checks; nothing to do for zero rows
-    assert L.kvq_topk_evict(P(1), 4, 100, 90, 20, P(1), None) == -1
-    assert L.kvq_topk_evict(P(1), -1, 100, 10, 20, P(1), None) == -1
-    assert L.kvq_topk_evict(None, 0, 100, 10, 20, None, None) == 0
-    assert L.kvq_topk_evict(None, 3, 100, 10, 20, P(1), None) == -1
+    assert L.kvq_topk_evict(P(1), 4, 100, 90, 20, P(1), None, 0, None) == -1
+    assert L.kvq_topk_evict(P(1), -1, 100, 10, 20, P(1), None, 0, None) == -1
+    assert L.kvq_topk_evict(None, 0, 100, 10, 20, None, None, 0, None) == 0
+    assert L.kvq_topk_evict(None, 3, 100, 10, 20, P(1), None, 0, None) == -1
+    n = ctypes.c_size_t(7)
+    assert L.kvq_topk_workspace(3, 100, 10, 20, ctypes.byref(n)) == 0 and n.value == 0
+    assert L.kvq_topk_workspace(3, 100, 90, 20, ctypes.byref(n)) == -1
 
 
 def test_decode_step_validation_launches_nothing(kvq):

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from kv_cache_compression_kvq_amd import synth
+from kv_cache_compression_kvq_amd import abi, synth
 from oracle import kvq_oracle as O
 from tests import gpu_harness as H
 
@@ -444,15 +444,28 @@ def test_snapshot_and_resume_match_unsplit_run():
     # k = 1 over more rows than compute units; k = n - 1 with ties
     (1000, 700, 1, 50, False), (3, 2000, 1949, 50, True),
 ])
-def test_topk_exact(kvq, rows, T, k, w, ties):
+@pytest.mark.parametrize("split", [False, True], ids=["one_wg_per_row", "workspace"])
+def test_topk_exact(kvq, rows, T, k, w, ties, split):
     s = synth.score_rows(rows, T, seed=3, ties=ties)
     if ties:
         s[:, ::7] = -0.0
     st = torch.from_numpy(s).cuda()
-    idx = torch.full((rows, k + w), -1, dtype=torch.int32, device="cuda")
-    kvq.topk_evict(st, rows, T, k, w, idx)
-    torch.cuda.synchronize()
+    idx = _topk(kvq, st, rows, T, k, w, split)
     np.testing.assert_array_equal(idx.cpu().numpy(), O.topk_keep(s, k, w))
+
+
+def _topk(kvq, st, rows, T, k, w, split):
+    """kvq_topk_evict without a workspace (one workgroup per row) or with the
+    workspace it asks for (rows split over workgroups where that fills the
+    GPU)."""
+    idx = torch.full((rows, k + w), -1, dtype=torch.int32, device="cuda")
+    ws = None
+    if split:
+        n = kvq.topk_workspace(rows, T, k, w)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+    kvq.topk_evict(st, rows, T, k, w, idx, ws)
+    torch.cuda.synchronize()
+    return idx
 
 
 def _special_rows(rows, T, seed):
@@ -476,13 +489,20 @@ def _special_rows(rows, T, seed):
 
 @pytest.mark.parametrize("T,k,w", [(1000, 300, 24), (20000, 4000, 128), (40000, 9000, 256),
                                    (70000, 14000, 256)])
-def test_topk_special_values(kvq, T, k, w):
+@pytest.mark.parametrize("split", [False, True], ids=["one_wg_per_row", "workspace"])
+def test_topk_special_values(kvq, T, k, w, split):
     s = _special_rows(4, T, seed=11)
     st = torch.from_numpy(s).cuda()
-    idx = torch.full((4, k + w), -1, dtype=torch.int32, device="cuda")
-    kvq.topk_evict(st, 4, T, k, w, idx)
-    torch.cuda.synchronize()
+    idx = _topk(kvq, st, 4, T, k, w, split)
     np.testing.assert_array_equal(idx.cpu().numpy(), O.topk_keep(s, k, w))
+
+
+def test_topk_split_plan_is_taken(kvq):
+    """The workspace path splits long rows and few rows; many short rows keep
+    one workgroup per row."""
+    assert kvq.topk_workspace(8, 131072, 26000, 256) > 0
+    assert kvq.topk_workspace(2, 20000, 4000, 128) > 0
+    assert kvq.topk_workspace(4096, 2000, 400, 64) == 0
 
 
 # ---------------------------------------------------------------------------
@@ -570,11 +590,10 @@ def test_workload_minikv_h2o_and_topk():
     # heavy hitters on the GPU-accumulated scores, all 128 rows
     rows = w.batch * w.n_kv_heads
     k, wr = w.topk_k, w.recent
-    idx = torch.empty((rows, k + wr), dtype=torch.int32, device="cuda")
-    from kv_cache_compression_kvq_amd import abi
-    abi.topk_evict(acc, rows, w.tokens, k, wr, idx)
-    torch.cuda.synchronize()
-    np.testing.assert_array_equal(idx.cpu().numpy(), O.topk_keep(accn.reshape(rows, -1), k, wr))
+    want = O.topk_keep(accn.reshape(rows, -1), k, wr)
+    for split in (False, True):
+        idx = _topk(abi, acc, rows, w.tokens, k, wr, split)
+        np.testing.assert_array_equal(idx.cpu().numpy(), want)
 
 
 def test_stream_read_touches_every_word(kvq):
