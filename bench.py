@@ -390,8 +390,8 @@ def rows_main(args):
             nq = BM.n_quantized(w.tokens, w.residual, w.group)
             nbytes = BM.bulk_append_bytes(units=U, head_dim=d, tokens=w.tokens, n_quant=nq,
                                           bits=w.bits, group=w.group)
-            emit(name, w, us, nbytes, {"kernels": ["ott_score_kernel", "ott_scan_kernel",
-                                                   "pack_kernel", "ring_store_kernel"]
+            emit(name, w, us, nbytes, {"kernels": ["pack_kernel (scores)", "ott_scan_kernel",
+                                                   "pack_kernel (repair)", "ring_store_kernel"]
                                        if w.pool else ["pack8_kernel" if w.bits == 8
                                                        else "pack_kernel", "ring_store_kernel"]})
             continue

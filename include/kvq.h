@@ -156,9 +156,11 @@ typedef struct kvq_config {
  *   pool_k    fp16 [U][N][d] original key row;  pool_v likewise
  *   ev_idx    int32 [U][E]; ev_k, ev_v fp16 [U][E][d] (extra pool, in the
  *             order members were displaced)
- *   counters  int32 [U][4]: pool count, extra-pool count, frozen flag, and the
- *             largest value scale held by the unit (fp16 bits; 0 while
- *             nothing is quantized), which bounds the decoder's lazy rescale
+ *   counters  int32 [U][4]: pool count, extra-pool count, frozen flag, and a
+ *             bound on the unit's value scales (fp16 bits; 0 while nothing
+ *             is quantized): the largest scale held, or computed for a token
+ *             before it joined the outlier pool; it bounds the decoder's lazy
+ *             softmax rescale
  *   scores    uint64 [U][Qcap] scratch for key L1 norms during an append
  *   sink_k    fp16 [U][S][d] the attention-sink rows; sink_v likewise
  *   evict     uint32 [U][ceil((max_tokens - S) / 32)]: bit i of word c set when
@@ -451,7 +453,7 @@ kvq_status kvq_unpack_codes(const kvq_cache* h, uint8_t* d_kcodes, uint8_t* d_vc
  *   ksink, vsink    fp16 [U][min(T, S)][d]: the attention-sink rows
  *   live            uint8 [U][T]: 0 for tokens evicted by kvq_evict_step
  *   counters        int32 [U][4]: pool count, extra-pool count, frozen flag,
- *                   largest value scale (fp16 bits)
+ *                   value-scale bound (fp16 bits, as in the arena)
  *   pool_idx        int32 [U][N], pool_score uint64 [U][N] (key L1 norm in
  *                   units of 2^-24), pool_k, pool_v fp16 [U][N][d]
  *   ev_idx          int32 [U][E], ev_k, ev_v fp16 [U][E][d] (extra pool)

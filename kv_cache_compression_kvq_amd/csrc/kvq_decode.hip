@@ -539,7 +539,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     for (int nt = 0; nt < 8; ++nt) O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     // Lazy rescale: the running max m_run only moves when a logit exceeds it
     // by more than tau (log2 units), so probabilities stay below 2^tau; tau is
-    // bounded so that p * s^V, s^V below the unit's largest value scale, stays
+    // bounded so that p * s^V, s^V below the unit's value-scale bound, stays
     // far inside fp16 (< 2^15).
     float m_thr = -INFINITY;
     float tau = 8.f;

@@ -129,47 +129,6 @@ __global__ void init_kernel(CacheView v) {
     }
 }
 
-// OTT token score: S_t = sum_c |K_{t,c}|, exact, as a multiple of 2^-24
-// ("Accurate KV Cache Quantization with Outlier Tokens Tracing", sections
-// "Method details" and appendix E: the L1 norm of the key). Sixteen lanes per
-// token, 16 bytes each; a block covers 32 tokens, each lane's two rows
-// requested together (smaller blocks than 64 or more tokens measured faster).
-constexpr int kScoreRows = 2;  // rows per lane
-constexpr int kScoreTokens = 16 * kScoreRows;
-__global__ __launch_bounds__(256) void ott_score_kernel(CacheView v, const uint16_t* knew,
-                                                        int64_t t_old, int32_t n_new, int64_t t0,
-                                                        int64_t ntok) {
-    const int u = blockIdx.y;
-    const int part = threadIdx.x % 16;
-    uint4 x[kScoreRows];
-#pragma unroll
-    for (int j = 0; j < kScoreRows; ++j) {
-        const int64_t tl = (int64_t)blockIdx.x * kScoreTokens + 16 * j + threadIdx.x / 16;
-        x[j] = tl < ntok ? reinterpret_cast<const uint4*>(
-                               src_row(v.kring, knew, v, u, t0 + tl, t_old, n_new))[part]
-                         : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int j = 0; j < kScoreRows; ++j) {
-        const int64_t tl = (int64_t)blockIdx.x * kScoreTokens + 16 * j + threadIdx.x / 16;
-        // Every |x| is a multiple of 2^-24 below 2^16, so any partial sum of
-        // the 128 magnitudes is a multiple of 2^-24 below 2^23: at most 47
-        // significant bits, exact in fp64 in any order. Scaled by 2^24 it is
-        // the integer score.
-        const uint32_t w[4] = {x[j].x, x[j].y, x[j].z, x[j].w};
-        double s = 0.0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            s += fabs((double)h2f((uint16_t)(w[i] & 0xFFFF)));
-            s += fabs((double)h2f((uint16_t)(w[i] >> 16)));
-        }
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off, 16);
-        if (part == 0 && tl < ntok)
-            v.scores[(int64_t)u * v.q_cap + t0 + tl] = (uint64_t)(s * 16777216.0);
-    }
-}
-
 // OTT pool competition, one wavefront per unit, groups in token order.
 // For each group the tokens ranked by (score, index) together with the pool
 // members and falling among the N best are admitted in that order; an
@@ -511,10 +470,17 @@ __device__ constexpr int kPos2[8] = {3, 4, 1, 2, 5, 6, 7, 0};
 // holds two groups: the even and the odd groups of an append run as two
 // launches (gstride 2), and a 2-bit key word, which holds codes of both
 // halves of its chunk, is rewritten keeping the other half's bits.
+// With an outlier pool the groups of an append are packed twice around the
+// pool scan (modes): mode 1 writes every token's exact key L1 score (OTT,
+// appendix E) from the rows it already holds and quantizes with no pool
+// member; the scan then admits tokens; mode 2 repacks the groups that
+// admitted one (mean replacement). Mode 0: one pass (no pool). The unit's
+// value-scale bound (counters[3]) is raised in every pass, so it also covers
+// the first-pass scales of tokens later replaced by the group mean.
 template <int BITS, int G>
-__global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* knew,
-                                                   const uint16_t* vnew, int64_t t_old,
-                                                   int32_t n_new, int64_t g0, int32_t gstride) {
+__device__ void pack_group(const CacheView& v, const uint16_t* knew, const uint16_t* vnew,
+                           int64_t t_old, int32_t n_new, int u, int64_t g, int32_t mode,
+                           uint32_t vmax_seen) {
     constexpr int NG = D / G;          // value groups per token
     constexpr bool kHalf = G == 16;    // the group is half a chunk
     constexpr int CPG = kHalf ? 1 : G / kChunk;  // chunks the group touches
@@ -530,19 +496,9 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
     uint16_t* vx = smem + G * RS;
     __shared__ uint16_t meank[D], meanv[D];
     __shared__ uint32_t vmax_w[2];
-    // Blocks walk the units fastest, so that the blocks resident at once
-    // spread over all units (and the units' counter words).
-    const int u = (int)(blockIdx.x % (uint32_t)v.units), tid = threadIdx.x;
-    const int64_t g = g0 + (int64_t)gstride * (blockIdx.x / (uint32_t)v.units), t0 = g * G;
+    const int tid = threadIdx.x;
+    const int64_t t0 = g * G;
     const int hf = kHalf ? (int)(g & 1) : 0;  // G = 16: which half of its chunk
-    // The unit's largest value scale so far, read at device scope (past this
-    // XCD's L2, where the atomics below do not land); a block only raises it
-    // with an atomic when its own maximum is larger. A stale value costs one
-    // atomic, no more.
-    const uint32_t vmax_seen =
-        tid == 0 ? __hip_atomic_load(reinterpret_cast<const uint32_t*>(v.counters) + (int64_t)u * 4 + 3,
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                 : 0u;
 
     {
         // all of this thread's row pieces are requested before any is stored
@@ -565,11 +521,33 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
     bool any = false;
 #pragma unroll
     for (int c = 0; c < CPG; ++c) {
-        mw[c] = v.pool > 0 ? v.mask[(int64_t)u * v.chunks + t0 / kChunk + c] : 0u;
+        mw[c] = v.pool > 0 && mode != 1 ? v.mask[(int64_t)u * v.chunks + t0 / kChunk + c] : 0u;
         if (kHalf) mw[c] = (mw[c] >> (16 * hf)) & 0xFFFFu;
         any |= mw[c] != 0;
     }
     __syncthreads();
+    if (mode == 1) {
+        // OTT token score: sum of |k_c| over the row, exact, as an integer in
+        // units of 2^-24; 256 / G threads per token
+        // (any partial sum is a multiple of 2^-24 below 2^23 with at most 47
+        // significant bits, so the fp64 sum is exact in any order)
+        constexpr int TPT = 256 / G, CPT = D / TPT;
+        const int i = tid / TPT, part = tid % TPT;
+        double sc = 0.0;
+#pragma unroll
+        for (int c8 = 0; c8 < CPT / 8; ++c8) {
+            const uint4 x = reinterpret_cast<const uint4*>(kx + i * RS + part * CPT)[c8];
+            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                sc += fabs((double)h2f((uint16_t)(w[m] & 0xFFFF)));
+                sc += fabs((double)h2f((uint16_t)(w[m] >> 16)));
+            }
+        }
+#pragma unroll
+        for (int off = TPT / 2; off > 0; off >>= 1) sc += __shfl_xor(sc, off, TPT);
+        if (part == 0) v.scores[(int64_t)u * v.q_cap + t0 + i] = (uint64_t)(sc * 16777216.0);
+    }
     if (any) {
         if (tid < 2 * D) {
             const uint16_t* x = tid < D ? kx + tid : vx + (tid - D);
@@ -743,6 +721,57 @@ __global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* 
             word |= v.kq[base + o] & keep;
         }
         (isv ? v.vq : v.kq)[base + o] = word;
+    }
+}
+
+// One block per (unit, group), units fastest so that the blocks resident at
+// once spread over all units (and their counter words); in mode 2 one block
+// per (unit, batch of kRepairBatch groups), repacking only the groups whose
+// tokens the scan admitted to the pool (a small share).
+constexpr int kRepairBatch = 4;
+template <int BITS, int G>
+__global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* knew,
+                                                   const uint16_t* vnew, int64_t t_old,
+                                                   int32_t n_new, int64_t g0, int32_t gstride,
+                                                   int64_t ng, int32_t mode) {
+    constexpr bool kHalf = G == 16;
+    constexpr int CPG = kHalf ? 1 : G / kChunk;
+    const int u = (int)(blockIdx.x % (uint32_t)v.units);
+    const int64_t b = blockIdx.x / (uint32_t)v.units;
+    // The unit's largest value scale so far, read at device scope (past this
+    // XCD's L2, where the atomics of the pack do not land); a block only
+    // raises it with an atomic when its own maximum is larger. A stale value
+    // costs one atomic, no more.
+    const uint32_t vmax_seen =
+        threadIdx.x == 0
+            ? __hip_atomic_load(reinterpret_cast<const uint32_t*>(v.counters) + (int64_t)u * 4 + 3,
+                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+            : 0u;
+    if (mode != 2) {
+        pack_group<BITS, G>(v, knew, vnew, t_old, n_new, u, g0 + gstride * b, mode, vmax_seen);
+        return;
+    }
+    // lane j of every wavefront reads the pool mask words of the batch's
+    // group j at once; one ballot lists the groups to repack
+    static_assert(kRepairBatch <= 64, "one lane per group of the batch");
+    const int lane = threadIdx.x & 63;
+    bool admitted = false;
+    if (lane < kRepairBatch && b * kRepairBatch + lane < ng) {
+        const int64_t g = g0 + gstride * (b * kRepairBatch + lane), t0 = g * G;
+#pragma unroll
+        for (int c = 0; c < CPG; ++c) {
+            uint32_t w = v.mask[(int64_t)u * v.chunks + t0 / kChunk + c];
+            if (kHalf) w = (w >> (16 * (int)(g & 1))) & 0xFFFFu;
+            admitted |= w != 0;
+        }
+    }
+    uint64_t todo = __ballot(admitted);
+    while (todo) {
+        const int j = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        __syncthreads();  // the previous group's LDS reads are done
+        pack_group<BITS, G>(v, knew, vnew, t_old, n_new, u, g0 + gstride * (b * kRepairBatch + j),
+                            2, vmax_seen);
     }
 }
 
@@ -1100,22 +1129,53 @@ __global__ __launch_bounds__(256) void sink_view_kernel(CacheView v, int32_t row
 
 template <int BITS, int G>
 hipError_t launch_pack_t(const CacheView& v, const uint16_t* kn, const uint16_t* vn, int64_t t_old,
-                         int32_t n_new, int64_t g0, int64_t ng, hipStream_t s, int32_t gstride) {
+                         int32_t n_new, int64_t g0, int64_t ng, hipStream_t s, int32_t gstride,
+                         int32_t mode) {
     const size_t lds = 2 * (size_t)G * kPackRow * sizeof(uint16_t);
     // the dynamic LDS limit is raised once per process; a failure is reported
     static const hipError_t attr =
         hipFuncSetAttribute(reinterpret_cast<const void*>(pack_kernel<BITS, G>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
-    // one block per (unit, group), units fastest; at most 2^22 blocks a launch.
-    // ng groups g0, g0 + gstride, ...
-    const int64_t step = (int64_t)1 << 22 >= v.units ? ((int64_t)1 << 22) / v.units : 1;
+    // one block per (unit, group) or, in mode 2, per (unit, batch of groups),
+    // units fastest; at most 2^22 blocks a launch. ng groups g0, g0 + gstride, ...
+    const int64_t per = mode == 2 ? kRepairBatch : 1;
+    const int64_t step = ((int64_t)1 << 22 >= v.units ? ((int64_t)1 << 22) / v.units : 1) * per;
     for (int64_t gs = 0; gs < ng; gs += step) {
         const int64_t n = ng - gs < step ? ng - gs : step;
-        hipLaunchKernelGGL((pack_kernel<BITS, G>), dim3((unsigned)(n * v.units)), dim3(256), lds, s,
-                           v, kn, vn, t_old, n_new, g0 + gs * gstride, gstride);
+        hipLaunchKernelGGL((pack_kernel<BITS, G>), dim3((unsigned)((n + per - 1) / per * v.units)),
+                           dim3(256), lds, s, v, kn, vn, t_old, n_new, g0 + gs * gstride, gstride,
+                           n, mode);
     }
     return hipSuccess;
+}
+
+// Every group g0 .. g1 - 1 of an append through pack_kernel in `mode`. With
+// G = 16 the even groups, then the odd ones: the two halves of a chunk are
+// never written by one launch.
+hipError_t launch_pack_groups(const CacheView& v, const uint16_t* kn, const uint16_t* vn,
+                              int64_t t_old, int32_t n_new, int64_t g0, int64_t g1, hipStream_t s,
+                              int32_t mode) {
+    const int G = v.group;
+    const int64_t ng = g1 - g0;
+    if (G == 16) {
+        const int64_t ge = g0 + (g0 & 1), go = g0 + 1 - (g0 & 1);
+        const int64_t ne = ge < g1 ? (g1 - ge + 1) / 2 : 0, no = go < g1 ? (g1 - go + 1) / 2 : 0;
+        hipError_t e = hipSuccess;
+        for (int pass = 0; pass < 2 && e == hipSuccess; ++pass) {
+            const int64_t gp = pass == 0 ? ge : go, np = pass == 0 ? ne : no;
+            if (np == 0) continue;
+            e = v.bits == 2 ? launch_pack_t<2, 16>(v, kn, vn, t_old, n_new, gp, np, s, 2, mode)
+                            : launch_pack_t<4, 16>(v, kn, vn, t_old, n_new, gp, np, s, 2, mode);
+        }
+        return e;
+    }
+#define KVQ_PACK(B_, G_)                                                                  \
+    if (v.bits == B_ && G == G_) return launch_pack_t<B_, G_>(v, kn, vn, t_old, n_new, g0, ng, s, 1, mode);
+    KVQ_PACK(2, 32) KVQ_PACK(2, 64) KVQ_PACK(2, 128)
+    KVQ_PACK(4, 32) KVQ_PACK(4, 64) KVQ_PACK(4, 128)
+#undef KVQ_PACK
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -1150,38 +1210,23 @@ int launch_append(const CacheView& v, const uint16_t* kn, const uint16_t* vn, in
     const int G = v.group;
     const int64_t g0 = nq_old / G, g1 = nq_new / G, ng = g1 - g0;
     if (ng > 0) {
-        if (v.pool > 0) {
-            const int64_t ntok = ng * G;
-            hipLaunchKernelGGL(ott_score_kernel,
-                               dim3((unsigned)((ntok + kScoreTokens - 1) / kScoreTokens), v.units),
-                               dim3(256), 0, s, v, kn, t_old, n_new, nq_old, ntok);
-            hipLaunchKernelGGL(ott_scan_kernel, dim3(v.units), dim3(64), 0, s, v, kn, vn, t_old,
-                               n_new, g0, g1);
-        }
-        hipError_t e = hipErrorInvalidValue;
+        hipError_t e = hipSuccess;
         if (v.bits == 8) {
             // FP8 codec: one block per (unit, chunk); ng groups of 32 tokens
             hipLaunchKernelGGL(pack8_kernel, dim3((unsigned)(ng * v.units)), dim3(256), 0, s, v, kn,
                                vn, t_old, n_new, g0);
-            e = hipSuccess;
-        } else if (G == 16) {
-            // even groups, then odd groups: the two halves of a chunk are never
-            // written by one launch
-            const int64_t ge = g0 + (g0 & 1), go = g0 + 1 - (g0 & 1);
-            const int64_t ne = ge < g1 ? (g1 - ge + 1) / 2 : 0, no = go < g1 ? (g1 - go + 1) / 2 : 0;
-            e = hipSuccess;
-            for (int pass = 0; pass < 2 && e == hipSuccess; ++pass) {
-                const int64_t gp = pass == 0 ? ge : go, np = pass == 0 ? ne : no;
-                if (np == 0) continue;
-                e = v.bits == 2 ? launch_pack_t<2, 16>(v, kn, vn, t_old, n_new, gp, np, s, 2)
-                                : launch_pack_t<4, 16>(v, kn, vn, t_old, n_new, gp, np, s, 2);
+        } else {
+            // With a pool: first pass with scores, the scan, then the repair
+            // pass; otherwise one pass.
+            const int npass = v.pool > 0 ? 2 : 1;
+            for (int pass = 0; pass < npass && e == hipSuccess; ++pass) {
+                const int32_t mode = v.pool > 0 ? 1 + pass : 0;
+                if (pass == 1)
+                    hipLaunchKernelGGL(ott_scan_kernel, dim3(v.units), dim3(64), 0, s, v, kn, vn,
+                                       t_old, n_new, g0, g1);
+                e = launch_pack_groups(v, kn, vn, t_old, n_new, g0, g1, s, mode);
             }
         }
-#define KVQ_PACK(B_, G_)                                                         \
-    if (v.bits == B_ && G == G_) e = launch_pack_t<B_, G_>(v, kn, vn, t_old, n_new, g0, ng, s, 1);
-        KVQ_PACK(2, 32) KVQ_PACK(2, 64) KVQ_PACK(2, 128)
-        KVQ_PACK(4, 32) KVQ_PACK(4, 64) KVQ_PACK(4, 128)
-#undef KVQ_PACK
         if (e != hipSuccess) return (int)e;
     }
     const int64_t ts = t_old > nq_new ? t_old : nq_new, te = t_old + n_new;

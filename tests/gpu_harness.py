@@ -137,8 +137,13 @@ def check_unit_state(st: dict, u: int, uc: O.UnitCache) -> None:
     assert np.array_equal(st["kzero"][u], uc.kzero)  # as values: +0 and -0 agree
     assert np.array_equal(st["vscale"][u].view(np.uint16), uc.vscale.view(np.uint16))
     assert np.array_equal(st["vzero"][u], uc.vzero)
-    # counters[3]: largest value scale of the unit, as fp16 bits
+    # counters[3]: the unit's value-scale bound, as fp16 bits: the largest
+    # value scale held, or computed for a token before it joined the pool
+    # (the scale of its own row, which the group mean then replaced)
     vmax = int(uc.vscale.view(np.uint16).max()) if nq else 0
+    for m in uc.tracer.pool + uc.tracer.evicted:
+        _, s_own, _ = O.quantize_value_rows(m.v[None, :], p.bits, p.gv)
+        vmax = max(vmax, int(s_own.view(np.uint16).max()))
     assert int(st["counters"][u, 3]) == vmax, (int(st["counters"][u, 3]), vmax)
     S = min(T, p.sinks)
     assert np.array_equal(st["ksink"][u].view(np.uint16), uc.k16[:S].view(np.uint16))
