@@ -350,7 +350,7 @@ kvq_status kvq_topk_evict(const float* d_scores, int32_t rows, int32_t T, int32_
  *   d_out  device fp32 [B][Hq][n][d]
  *   d_acc  device fp32 [B][Hkv][n] or NULL (then only d_out is computed)
  *   d_ws   device workspace of ws_bytes >= kvq_prefill_workspace (per-row
- *          log-sum-exp of the softmax)
+ *          log-sum-exp of the softmax, per query head partial column sums)
  * d_acc feeds kvq_topk_evict (rows = B * Hkv, T = n), whose kept indices feed
  * kvq_gather_kv and then kvq_quantize_append (MiniKV section 4.1, persistent
  * context selection). Query head h reads KV head h / (Hq / Hkv).

@@ -392,7 +392,10 @@ kvq_status kvq_unpack_codes(const kvq_cache* h, uint8_t* d_kcodes, uint8_t* d_vc
 
 kvq_status kvq_prefill_workspace(int32_t batch, int32_t n_q_heads, int32_t n, size_t* ws_bytes) {
     if (!ws_bytes || batch < 1 || n_q_heads < 1 || n < 0 || n > kMaxTokens) return KVQ_EINVAL;
-    *ws_bytes = (size_t)align_up((uint64_t)batch * n_q_heads * n * 4);
+    // per query row its log-sum-exp, then per (query head, key) a partial
+    // column sum (r partials per KV head, added in order)
+    *ws_bytes = (size_t)align_up((uint64_t)batch * n_q_heads * n * 4) +
+                (size_t)align_up((uint64_t)batch * n_q_heads * n * 4);
     return KVQ_OK;
 }
 

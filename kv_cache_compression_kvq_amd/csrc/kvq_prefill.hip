@@ -47,6 +47,59 @@ __device__ __forceinline__ float max_x32(float x) {
 __device__ __forceinline__ float sum_x16(float x) { return x + __shfl_xor(x, 16); }
 __device__ __forceinline__ float sum_x32(float x) { return x + __shfl_xor(x, 32); }
 
+// Block coordinates with all blocks of one unit on one compute die when the
+// unit count is a multiple of 8: workgroups are dealt to the 8 dies round
+// robin by linear index, so the unit's K/V (forward) or Q (column sums) stays
+// in that die's L2 instead of passing through all eight. A bijection of the
+// grid; only placement (speed) depends on the dealing order.
+__device__ __forceinline__ void die_local_block(int& x, int& y) {
+    x = blockIdx.x;
+    y = blockIdx.y;
+    if (gridDim.y % 8 == 0) {
+        const int lin = blockIdx.x + gridDim.x * blockIdx.y, die = lin % 8, idx = lin / 8;
+        y = die + 8 * (idx / (int)gridDim.x);
+        x = idx % (int)gridDim.x;
+    }
+}
+
+__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
+    // lane i's 16 bytes land at lds + 16 * i
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(const void* g, void* lds) {
+    // lane i's 4 bytes land at lds + 4 * i
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+// Wait until at most N of this wavefront's vector memory operations are in
+// flight (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier without the memory fence of __syncthreads, whose release
+// would wait for every LDS copy in flight (the ring's later stages too); the
+// ring's own waits order the copies.
+__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Reads of a ring stage, issued as inline assembly so that the compiler does
+// not wait for the copies in flight into other stages; lds_wait() then waits
+// for them and ties their results.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+__device__ __forceinline__ uint32_t lds_read4(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 struct PrefillArgs {
     const uint16_t* q;  // [B][Hq][n][d]
     const uint16_t* k;  // [B][Hkv][n][d]
@@ -54,6 +107,7 @@ struct PrefillArgs {
     float* out;         // [B][Hq][n][d]
     float* acc;         // [B][Hkv][n] or null
     float* lse;         // [B][Hq][n]: log2 of each row's softmax normaliser (log2 units)
+    float* part;        // [B][Hq][n]: column sums of each query head (added per KV head)
     int32_t n, n_kv_heads;
     float qscale;       // log2(e) / sqrt(d)
 };
@@ -68,8 +122,11 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(PrefillArgs a) {
     __shared__ __align__(16) uint16_t vt[D][VROW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = a.n;
-    const int unit = blockIdx.y, b = unit / a.n_kv_heads, hkv = unit % a.n_kv_heads;
-    const int q0 = blockIdx.x * QR;
+    int bx, by;
+    die_local_block(bx, by);
+    const int unit = by, b = unit / a.n_kv_heads, hkv = unit % a.n_kv_heads;
+    // the last query blocks see the most keys: they are dispatched first
+    const int q0 = ((int)gridDim.x - 1 - bx) * QR;
     const int hl = wave % R, row0 = q0 + (wave / R) * 32;
     const int hq = hkv * R + hl;
     const int64_t qbase = ((int64_t)b * a.n_kv_heads * R + hq) * n;
@@ -174,16 +231,28 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(PrefillArgs a) {
         for (int rt = 0; rt < 2; ++rt) {
             const int row = row0 + 16 * rt + j;
             float mx = -INFINITY;
+            if (k0 + KB - 1 <= row0 + 16 * rt && row0 + 16 * rt + 15 < n) {
+                // every key of the tile at or before every row of the row tile
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+                for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = k0 + 16 * kt + 4 * kb + i;
-                    float s = St[rt][kt][i] * a.qscale;
-                    if (key > row || key >= n || row >= n) s = -INFINITY;
-                    St[rt][kt][i] = s;
-                    mx = fmaxf(mx, s);
-                }
+                    for (int i = 0; i < 4; ++i) {
+                        const float s = St[rt][kt][i] * a.qscale;
+                        St[rt][kt][i] = s;
+                        mx = fmaxf(mx, s);
+                    }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = k0 + 16 * kt + 4 * kb + i;
+                        float s = St[rt][kt][i] * a.qscale;
+                        if (key > row || key >= n || row >= n) s = -INFINITY;
+                        St[rt][kt][i] = s;
+                        mx = fmaxf(mx, s);
+                    }
+            }
             mx = max_x32(max_x16(mx));
             const float mnew = fmaxf(m[rt], mx);
             // rows with nothing unmasked yet keep alpha = 1 and p = 0
@@ -251,15 +320,25 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(PrefillArgs a) {
 }
 
 // Column sums: block (key block x of 64 keys, unit y); wavefront w owns keys
-// k0 + 16 w .. + 15 and walks every query row at or after them, for each of
-// the r query heads, adding exp2(s - lse_row) (the normalized probability).
+// k0 + 16 w .. + 15 (k0 = 64 x). For each of the r query heads of the KV head,
+// the query rows from k0 on pass through a ring of LDS stages, 64 rows with
+// their log-sum-exp each, copied straight from memory three stages ahead of
+// use; each wavefront adds exp2(s - lse_row) of its keys over the stage's
+// rows at or after them: every column sum is produced by one wavefront in a
+// fixed order.
 template <int R>
 __global__ __launch_bounds__(256) void prefill_colsum_kernel(PrefillArgs a) {
+    constexpr int QT = 64;                       // query rows per stage
+    constexpr int kStages = 4;                   // stages in flight
+    constexpr int kTileBytes = QT * D * 2;       // 16 KB of query rows
+    __shared__ __align__(16) unsigned char ring[kStages][kTileBytes + QT * 4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = a.n;
-    const int unit = blockIdx.y, b = unit / a.n_kv_heads, hkv = unit % a.n_kv_heads;
-    const int kt0 = blockIdx.x * KB + 16 * wave;  // first key of this wavefront
-    if (kt0 >= n) return;
+    int bx, by;
+    die_local_block(bx, by);
+    const int unit = by / R, hh = by % R, b = unit / a.n_kv_heads, hkv = unit % a.n_kv_heads;
+    const int k0 = bx * KB, kt0 = k0 + 16 * wave;  // first key of the block, of this wavefront
+    const int64_t qhead = (int64_t)b * a.n_kv_heads * R + hkv * R + hh;
     const int64_t kvbase = (int64_t)unit * n;
     const int j = lane & 15, kb = lane >> 4;
     // key operands (A of S^T): key kt0 + j, channels 32 kst + 8 kb .. + 7
@@ -272,29 +351,87 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(PrefillArgs a) {
         Ak[kst] = __builtin_bit_cast(half8, w);
     }
     float cs[4] = {0.f, 0.f, 0.f, 0.f};  // keys kt0 + 4 kb + i, partial over this lane's rows
-    const int qt_first = kt0 / 16, qt_end = (n + 15) / 16;
-    for (int h = 0; h < R; ++h) {
-        const int64_t qbase = ((int64_t)b * a.n_kv_heads * R + hkv * R + h) * n;
-        for (int qt = qt_first; qt < qt_end; ++qt) {
-            const int row = 16 * qt + j;
-            half8 Bq[4];
+    const int t_first = k0 / QT, ntiles = (n + QT - 1) / QT, iters = ntiles - t_first;
+    // Stage it (rows r0 .. r0 + 63 of query head hh): 64 rows of 256 B
+    // with the 16-byte chunk c of row r stored at position c ^ (r % 16), so the
+    // sixteen rows of an operand read sit on distinct banks, then the rows'
+    // log-sum-exp. Each wavefront copies a quarter of both (five copies), and
+    // waits for its own copies of a stage before the barrier that publishes it.
+    const int64_t qbase = qhead * n;
+    // this thread's copies: row (16 wave + 4 i + lane / 16) of the stage, its
+    // chunk, as an element offset from the stage's first row
+    int coff[4], crow[4];
 #pragma unroll
-            for (int kst = 0; kst < 4; ++kst) {
-                uint4 w = make_uint4(0u, 0u, 0u, 0u);
-                if (row < n)
-                    w = *reinterpret_cast<const uint4*>(a.q + (qbase + row) * D + 32 * kst + 8 * kb);
-                Bq[kst] = __builtin_bit_cast(half8, w);
+    for (int i = 0; i < 4; ++i) {
+        const int slot = (4 * wave + i) * 64 + lane, row = slot / 16;
+        crow[i] = row;
+        coff[i] = row * D + 8 * ((slot % 16) ^ (row & 15));
+    }
+    auto issue = [&](int it) {
+        const int r0 = (t_first + it) * QT;
+        unsigned char* st = &ring[it % kStages][0];
+        const uint16_t* q0p = a.q + (qbase + r0) * D;
+        if (r0 + QT <= n) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lds_load16(q0p + coff[i], st + (4 * wave + i) * 1024);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // rows past n are read from row n - 1 (masked below)
+                const int back = r0 + crow[i] < n ? 0 : (r0 + crow[i] - (n - 1)) * D;
+                lds_load16(q0p + coff[i] - back, st + (4 * wave + i) * 1024);
             }
-            const float ls = row < n ? a.lse[qbase + row] : INFINITY;
+        }
+        if ((lane >> 4) == wave) {
+            const int rr = r0 + lane < n ? r0 + lane : n - 1;
+            lds_load4(a.lse + qbase + rr, st + kTileBytes);
+        }
+    };
+    for (int p = 0; p < kStages - 1 && p < iters; ++p) issue(p);
+    for (int it = 0; it < iters; ++it) {
+        bare_barrier();  // stage (it - 1) % kStages is no longer read
+        if (it + kStages - 1 < iters) issue(it + kStages - 1);
+        const int later = min(kStages - 1, iters - 1 - it);  // stages requested after this one
+        if (later >= 3) wait_vm<15>();
+        else if (later == 2) wait_vm<10>();
+        else if (later == 1) wait_vm<5>();
+        else wait_vm<0>();
+        bare_barrier();  // every wavefront's copies of stage it have landed
+        const int r0 = (t_first + it) * QT;
+        if (kt0 >= n) continue;
+        const uint32_t st = lds_addr(&ring[it % kStages][0]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const int rb = r0 + 16 * rt;  // first row of the 16-row tile
+            if (rb + 15 < kt0 || rb >= n) continue;  // every row before this wave's keys, or past n
+            const int row_l = 16 * rt + j;
+            u32x4 bw[4];
+#pragma unroll
+            for (int kst = 0; kst < 4; ++kst)
+                bw[kst] = lds_read16(st + row_l * 256 + (((4 * kst + kb) ^ (row_l & 15)) * 16));
+            uint32_t lsw = lds_read4(st + kTileBytes + 4 * row_l);
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(bw[0]), "+v"(bw[1]), "+v"(bw[2]), "+v"(bw[3]), "+v"(lsw)
+                         :
+                         : "memory");
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kst = 0; kst < 4; ++kst)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ak[kst], Bq[kst], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ak[kst], __builtin_bit_cast(half8, bw[kst]),
+                                                             acc, 0, 0, 0);
+            const int row = rb + j;
+            const float lsr = __builtin_bit_cast(float, lsw);
+            if (rb >= kt0 + 15 && rb + 15 < n && kt0 + 15 < n) {
+                // every row of the tile at or after every key of the wave
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = kt0 + 4 * kb + i;
-                if (key <= row && row < n && key < n)
-                    cs[i] += __builtin_amdgcn_exp2f(acc[i] * a.qscale - ls);
+                for (int i = 0; i < 4; ++i) cs[i] += __builtin_amdgcn_exp2f(fmaf(acc[i], a.qscale, -lsr));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = kt0 + 4 * kb + i;
+                    if (key <= row && row < n && key < n)
+                        cs[i] += __builtin_amdgcn_exp2f(fmaf(acc[i], a.qscale, -lsr));
+                }
             }
         }
     }
@@ -312,9 +449,22 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int key = kt0 + 4 * kb + i;
-            if (key < n) a.acc[kvbase + key] = cs[i];
+            if (key < n) a.part[qhead * n + key] = cs[i];
         }
     }
+}
+
+// A_cumul of each KV head: its r query heads' column sums, added in head order.
+template <int R>
+__global__ __launch_bounds__(256) void prefill_colsum_add_kernel(PrefillArgs a, int64_t total) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // unit * n + key
+    if (e >= total) return;
+    const int64_t unit = e / a.n, key = e % a.n;
+    const float* p = a.part + unit * R * a.n + key;
+    float s = p[0];
+#pragma unroll
+    for (int h = 1; h < R; ++h) s += p[(int64_t)h * a.n];
+    a.acc[e] = s;
 }
 
 template <int R>
@@ -324,7 +474,10 @@ void launch_prefill_t(const PrefillArgs& a, int batch, hipStream_t s) {
     hipLaunchKernelGGL((prefill_fwd_kernel<R>), dim3(qblocks, units), dim3(256), 0, s, a);
     if (a.acc) {
         const unsigned kblocks = (unsigned)((a.n + KB - 1) / KB);
-        hipLaunchKernelGGL((prefill_colsum_kernel<R>), dim3(kblocks, units), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((prefill_colsum_kernel<R>), dim3(kblocks, units * R), dim3(256), 0, s, a);
+        const int64_t total = (int64_t)units * a.n;
+        hipLaunchKernelGGL((prefill_colsum_add_kernel<R>), dim3((unsigned)((total + 255) / 256)),
+                           dim3(256), 0, s, a, total);
     }
 }
 
@@ -362,6 +515,8 @@ int launch_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, int3
     a.out = out;
     a.acc = acc;
     a.lse = lse;
+    // the partial column sums follow the log-sum-exp, 256-byte aligned
+    a.part = lse + ((int64_t)batch * n_q_heads * n * 4 + 255) / 256 * 64;
     a.n = n;
     a.n_kv_heads = n_kv_heads;
     a.qscale = 1.4426950408889634f / sqrtf((float)D);
