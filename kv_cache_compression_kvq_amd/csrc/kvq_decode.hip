@@ -46,8 +46,9 @@ constexpr int kRec = kPartRec;
 static_assert(kRec % 4 == 0 && kRec >= D + 2, "record holds o, m, l, 16-byte aligned");
 constexpr int kMaxSplits = 1056;
 constexpr int kH2OChunk = 2048;
-// LDS of the fp16 partition: queries and probabilities (4 x 256 B + 4 x 256 B).
-constexpr int kFp16Bytes = 4 * D * 2 + 4 * 64 * 4;
+// LDS of the fp16 partition: queries, probabilities and value-row addresses
+// (4 x 256 B + 4 x 256 B + 4 x 512 B).
+constexpr int kFp16Bytes = 4 * D * 2 + 4 * 64 * 4 + 4 * 64 * 8;
 
 // Per-wavefront LDS of the quantized path: a ring of two chunk stages filled
 // by direct global->LDS loads (codes, value scales, key scales, pool mask
@@ -255,7 +256,8 @@ __device__ __forceinline__ void wave_lds_fence() {
 // ring tokens [n_q, T), then the pool members, then the extra-pool members.
 // Wavefront h < r takes query head h. Logits: one row per lane, the row read
 // straight from memory and dotted with the query (fp16 x fp16 products are
-// exact in the fp32 dot2 accumulation). Outputs: lane (row phase l / 16,
+// exact in the fp32 dot2 accumulation). Each lane also resolves its row's
+// value address once and leaves it in LDS. Outputs: lane (row phase l / 16,
 // channel block l % 16) accumulates 8 channels over every fourth row, then the
 // four row phases are summed across lanes.
 template <int R>
@@ -263,6 +265,7 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
     const int tid = threadIdx.x, lane = tid & 63, h = tid >> 6;
     uint32_t* qh = reinterpret_cast<uint32_t*>(smem);      // [R][D/2] fp16 pairs
     float* ps = reinterpret_cast<float*>(qh + R * D / 2);  // [R][64]
+    const uint4** vp = reinterpret_cast<const uint4**>(ps + 4 * 64);  // [R][64] value rows
     const int b = u / a.n_kv_heads, hk = u % a.n_kv_heads;
     const uint32_t* qsrc =
         reinterpret_cast<const uint32_t*>(a.q + ((int64_t)b * a.n_kv_heads * R + hk * R) * D);
@@ -339,6 +342,8 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
                                  ? a.evict[(int64_t)u * a.evict_words + (tau >> 5)] : 0u;
         const uint4* kr = reinterpret_cast<const uint4*>(
             row_ptr(lane, a.sink_k, a.kring, a.pool_k, a.ev_k, a.k_new));
+        vp[h * 64 + lane] = reinterpret_cast<const uint4*>(
+            row_ptr(lane, a.sink_v, a.vring, a.pool_v, a.ev_v, a.v_new));
         uint4 x[16];
 #pragma unroll
         for (int c8 = 0; c8 < 16; ++c8) x[c8] = kr[c8];
@@ -374,6 +379,7 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
     const int rp = lane >> 4, cb = lane & 15;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const float* ph = ps + h * 64;
+    const uint4* const* vh = vp + h * 64;
     for (int i0 = 0; i0 < cnt; i0 += 16) {
         uint4 w[4];
         float pv[4];
@@ -381,9 +387,7 @@ __device__ void fp16_tile(const DecodeArgs& a, int u, int tile, float* smem) {
         for (int r = 0; r < 4; ++r) {
             const int i = i0 + 4 * r + rp;
             pv[r] = ph[i < 64 ? i : 63];
-            w[r] = i < cnt ? reinterpret_cast<const uint4*>(
-                                 row_ptr(i, a.sink_v, a.vring, a.pool_v, a.ev_v, a.v_new))[cb]
-                           : make_uint4(0u, 0u, 0u, 0u);
+            w[r] = i < cnt ? vh[i][cb] : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
