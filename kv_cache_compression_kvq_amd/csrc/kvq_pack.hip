@@ -796,10 +796,36 @@ __device__ __forceinline__ uint32_t e4m3_sat(float x) {
     return sign | (uint32_t)((e + 7) << 3) | m;
 }
 
+// Correctly rounded fp32 quotient x / s from y = RN(1 / s): q0 = RN(x y) is
+// within 1.5 ulp of x / s; one correction q1 = RN(q0 + r0 y), with the exact
+// residual r0 = x - q0 s (one FMA), is within one ulp, and a second
+// correction then rounds correctly (Markstein's theorem for a correctly
+// rounded reciprocal and a quotient within one ulp). With |x| <= 65504 and
+// 2^-100 <= s <= 2^100 nothing overflows and the residuals stay normal or 0.
+__device__ __forceinline__ float div_rn(float x, float s, float y) {
+    const float q0 = x * y;
+    const float q1 = fmaf(fmaf(-q0, s, x), y, q0);
+    return fmaf(fmaf(-q1, s, x), y, q1);
+}
+
+// E4M3 code of a finite x / s, saturating: the magnitude's quotient, clamped
+// to 448, converted by the hardware's round-to-nearest-even conversion, with
+// the sign of x (so -0 keeps its sign). Two codes per call, into bytes 2 hi,
+// 2 hi + 1 of w.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w, float x0, float x1, float s, float y) {
+    const float a0 = copysignf(fminf(div_rn(fabsf(x0), s, y), 448.0f), x0);
+    const float a1 = copysignf(fminf(div_rn(fabsf(x1), s, y), 448.0f), x1);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, w, HI);
+}
+
 // FP8 codec: one block per (unit, 32-token chunk). Keys and values are
 // encoded element by element as E4M3(x / s) with the KV head's scales and
 // written in the decoder's operand order: 4 KB per chunk and tensor, lane l
-// of 16-byte group w at byte w * 1024 + l * 16.
+// of 16-byte group w at byte w * 1024 + l * 16. A wavefront whose elements
+// are all finite, with scales in [2^-100, 2^100], takes the reciprocal
+// quotient and the hardware conversion; any other takes the IEEE division
+// and the encoder above (the same codes).
 //   keys:   group w = 2 tau + ks / 2; bytes 8 (ks % 2) + e hold channel
 //           32 ks + 8 (l / 16) + e of token 16 tau + l % 16;
 //   values: group w; bytes 8 i + sl hold channel 16 (2 w + i) + l % 16 of
@@ -829,18 +855,35 @@ __global__ __launch_bounds__(256) void pack8_kernel(CacheView v, const uint16_t*
     const int hk = u % v.n_kv_heads;
     const float sk = v.fp8_scales[2 * hk], sv = v.fp8_scales[2 * hk + 1];
     const int w = tid / 64, l = tid % 64, n = l % 16, kb = l / 16;
-    uint32_t kw[4] = {0, 0, 0, 0}, vw[4] = {0, 0, 0, 0};
+    float xk[16], xv[16];
+    bool special = false;
 #pragma unroll
     for (int byte = 0; byte < 16; ++byte) {
         // key byte: k-step ks = 2 (w % 2) + byte / 8, element e = byte % 8
         const int tau = w / 2, ks = 2 * (w % 2) + byte / 8, e = byte % 8;
-        const uint32_t ck = e4m3_sat(h2f(kx[16 * tau + n][32 * ks + 8 * kb + e]) / sk);
-        kw[byte / 4] |= ck << (8 * (byte % 4));
+        xk[byte] = h2f(kx[16 * tau + n][32 * ks + 8 * kb + e]);
         // value byte: tile 2 w + byte / 8, token slot sl = byte % 8
         const int nt = 2 * w + byte / 8, sl = byte % 8;
-        const uint32_t cv =
-            e4m3_sat(h2f(vx[16 * (sl / 4) + 4 * kb + sl % 4][16 * nt + n]) / sv);
-        vw[byte / 4] |= cv << (8 * (byte % 4));
+        xv[byte] = h2f(vx[16 * (sl / 4) + 4 * kb + sl % 4][16 * nt + n]);
+        special |= !__builtin_isfinite(xk[byte]) || !__builtin_isfinite(xv[byte]);
+    }
+    uint32_t kw[4] = {0, 0, 0, 0}, vw[4] = {0, 0, 0, 0};
+    const bool in_range = sk >= 0x1p-100f && sk <= 0x1p100f && sv >= 0x1p-100f && sv <= 0x1p100f;
+    if (in_range && !__any(special)) {
+        const float yk = 1.0f / sk, yv = 1.0f / sv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kw[i] = e4m3_pair<false>(0u, xk[4 * i], xk[4 * i + 1], sk, yk);
+            kw[i] = e4m3_pair<true>(kw[i], xk[4 * i + 2], xk[4 * i + 3], sk, yk);
+            vw[i] = e4m3_pair<false>(0u, xv[4 * i], xv[4 * i + 1], sv, yv);
+            vw[i] = e4m3_pair<true>(vw[i], xv[4 * i + 2], xv[4 * i + 3], sv, yv);
+        }
+    } else {
+#pragma unroll
+        for (int byte = 0; byte < 16; ++byte) {
+            kw[byte / 4] |= e4m3_sat(xk[byte] / sk) << (8 * (byte % 4));
+            vw[byte / 4] |= e4m3_sat(xv[byte] / sv) << (8 * (byte % 4));
+        }
     }
     const int64_t base = ((int64_t)u * v.chunks + ch) * 1024 + w * 256 + l * 4;  // words
     *reinterpret_cast<uint4*>(v.kq + base) = make_uint4(kw[0], kw[1], kw[2], kw[3]);

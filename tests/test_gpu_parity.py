@@ -371,6 +371,45 @@ def test_fp8_codec_state_and_decode(r, sk, sv, sinks):
                  tag=f"fp8_r{r}")
 
 
+@pytest.mark.parametrize("sk,sv", [(1.0, 1.0), (0.75, 3.0)])
+def test_fp8_codec_special_and_tie_values(sk, sv):
+    """FP8 codes of special and boundary inputs, bit-exact against the oracle
+    (reading R15: E4M3 of the fp32 quotient, ties to even, saturating, the
+    sign of -0 kept). Unit (0, 0) holds +-inf, NaN, +-0, fp16 subnormals and
+    +-65504 in its first chunk, so that chunk's wavefronts take the IEEE
+    division path; units (0, 1) and (1, 0) hold fp16 values at and next to
+    s times every E4M3 rounding midpoint (exact ties when s = 1) in chunks of
+    finite values only, which take the reciprocal-quotient path."""
+    w = small(bits=8, group=32, r=4, residual=40, tokens=300).with_(
+        fp8_scale_k=sk, fp8_scale_v=sv)
+    K, V = synth.all_kv(w)
+    K, V = K.copy(), V.copy()
+    spec = np.array([np.inf, -np.inf, np.nan, -0.0, 0.0, 6e-8, -6e-8, 65504, -65504,
+                     2.0 ** -14, -(2.0 ** -15)], np.float16)
+    K[0, 0, :4, :len(spec)] = spec
+    V[0, 0, 1:3, -len(spec):] = spec
+    mags = np.array(sorted({abs(float(O.e4m3_value(c))) for c in range(0x7F)}))
+    mids = (mags[:-1] + mags[1:]) / 2
+    for (b, h), sc, X in (((0, 1), sk, K), ((1, 0), sv, V)):
+        vals = np.concatenate([mids, -mids]) * sc
+        x16 = vals.astype(np.float16)
+        nxt = np.nextafter(x16, np.float16(np.inf))
+        prv = np.nextafter(x16, np.float16(-np.inf))
+        allv = np.concatenate([x16, nxt, prv])
+        allv = allv[np.isfinite(allv)]
+        flat = X[b, h, 32:160].reshape(-1)
+        flat[:allv.size] = allv
+        X[b, h, 32:160] = flat.reshape(128, -1)
+    gc = H.GpuCache(w)
+    gc.append(K, V)
+    orc = H.oracle_units(w, all_units(w), K, V)
+    st = gc.state()
+    for u, key in enumerate(all_units(w)):
+        H.check_unit_state(st, u, orc[key])
+    kc = st["kcodes"]
+    assert np.any(kc == 0x80) and np.any(kc == 0xFE) and np.any((kc & 0x7F) == 0x7F)
+
+
 def test_workload_llama8b_fp8_sampled_units():
     w = W["llama8b_fp8"]
     gc, K, V = run_appends(w, [w.tokens])
