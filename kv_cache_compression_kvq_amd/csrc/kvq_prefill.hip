@@ -32,8 +32,16 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = kHeadDim;
 constexpr int KB = 64;           // keys per block step
-constexpr int KROW = D + 8;      // LDS row stride of the key tile (fp16)
-constexpr int VROW = KB + 4;     // LDS row stride of the transposed value tile (fp16)
+// Transposed value tile: row c (channel) holds the 64 keys as 32 key-pair
+// dwords, dword p at position p ^ vt_swz(c). The swizzle is even, so the
+// 8-byte reads of two key pairs stay whole; it makes the staging writes
+// (lanes: 16 channels 8 apart x 2 key pairs) and the operand reads (lanes: 16
+// consecutive channels, one key pair) hit 32 distinct banks.
+__device__ __forceinline__ int vt_swz(int c) { return 2 * (((c >> 3) ^ c) & 15); }
+// Lazy rescaling ("online softmax" with a threshold): a row's reference
+// maximum moves only when a logit exceeds it by more than this (log2 units),
+// so its probabilities stay below 2^8 in the fp16 operand.
+constexpr float kLazyTau = 8.0f;
 
 __device__ __forceinline__ float h2f(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
@@ -116,10 +124,14 @@ struct PrefillArgs {
 // the r query heads of the KV head. Wavefront w takes head w % r and the 32
 // rows (w / r) * 32 .. + 31 of the block (two 16-row tiles).
 template <int R>
-__global__ __launch_bounds__(256) void prefill_fwd_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_fwd_kernel(PrefillArgs a) {
     constexpr int QR = 128 / R;  // query rows per block
-    __shared__ __align__(16) uint16_t ks[KB][KROW];
-    __shared__ __align__(16) uint16_t vt[D][VROW];
+    // key tiles, double-buffered and filled by direct global->LDS copies:
+    // 64 rows of 256 B, 16-byte chunk c of key row r at position c ^ (r % 16)
+    __shared__ __align__(16) unsigned char ks[2][KB * D * 2];
+    // value tiles as copied (row-major), double-buffered, and transposed
+    __shared__ __align__(16) unsigned char vs[2][KB * D * 2];
+    __shared__ __align__(16) uint32_t vt[D][KB / 2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = a.n;
     int bx, by;
@@ -131,6 +143,9 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(PrefillArgs a) {
     const int hq = hkv * R + hl;
     const int64_t qbase = ((int64_t)b * a.n_kv_heads * R + hq) * n;
     const int64_t kvbase = (int64_t)unit * n;
+    const uint16_t* kunit = a.k + kvbase * D;  // this unit's rows; offsets below are 32-bit
+    const uint16_t* vunit = a.v + kvbase * D;
+    const float qs = a.qscale;
     const int j = lane & 15, kb = lane >> 4;
 
     // query operands: tile rt, k-step kst: row row0 + 16 rt + j, channels
@@ -156,58 +171,59 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(PrefillArgs a) {
 
     const int kend = n < q0 + QR ? n : q0 + QR;  // keys any row of the block sees
     const int nkb = (kend + KB - 1) / KB;
-    // tile staging: 64 keys x 128 channels of K (row-major) and V (transposed)
-    uint4 kr[4], vr[4];
+    // tile staging: 64 keys x 128 channels of K and V copied to LDS, V then
+    // transposed through registers
     auto fetch = [&](int t) {
         const int k0 = t * KB;
+        unsigned char* kdst = &ks[t & 1][0];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int p = tid + 256 * i, key = p / 16, c8 = p % 16;
-            const bool ok = k0 + key < n;
-            kr[i] = ok ? *reinterpret_cast<const uint4*>(a.k + (kvbase + k0 + key) * D + 8 * c8)
-                       : make_uint4(0u, 0u, 0u, 0u);
+            // lane position pc of key row `key` receives that row's chunk
+            // pc ^ (key % 16); rows past n repeat row n - 1 (their logits are masked)
+            const int p = tid + 256 * i, key = p / 16, pc = p % 16;
+            const int row = k0 + key < n ? k0 + key : n - 1;
+            lds_load16(kunit + (uint32_t)(row * D + 8 * (pc ^ (key & 15))), kdst + (tid - lane + 256 * i) * 16);
         }
+        unsigned char* vdst = &vs[t & 1][0];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // chunk p % 16 of value row p / 16 (rows past n repeat row n - 1,
+            // whose probabilities are 0)
+            const int p = tid + 256 * i, key = p / 16, c8 = p % 16;
+            const int row = k0 + key < n ? k0 + key : n - 1;
+            lds_load16(vunit + (uint32_t)(row * D + 8 * c8), vdst + (tid - lane + 256 * i) * 16);
+        }
+    };
+    auto stage = [&](int t) {
+        const unsigned char* vsrc = &vs[t & 1][0];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             // two consecutive keys of the same 8 channels, stored as key pairs
             const int p = tid + 256 * i, kp = p / 16, c8 = p % 16;
-            const int key = 2 * kp;
-            vr[2 * i] = k0 + key < n
-                            ? *reinterpret_cast<const uint4*>(a.v + (kvbase + k0 + key) * D + 8 * c8)
-                            : make_uint4(0u, 0u, 0u, 0u);
-            vr[2 * i + 1] = k0 + key + 1 < n ? *reinterpret_cast<const uint4*>(
-                                                   a.v + (kvbase + k0 + key + 1) * D + 8 * c8)
-                                             : make_uint4(0u, 0u, 0u, 0u);
-        }
-    };
-    auto stage = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = tid + 256 * i, key = p / 16, c8 = p % 16;
-            *reinterpret_cast<uint4*>(&ks[key][8 * c8]) = kr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int p = tid + 256 * i, kp = p / 16, c8 = p % 16;
-            const uint32_t a0[4] = {vr[2 * i].x, vr[2 * i].y, vr[2 * i].z, vr[2 * i].w};
-            const uint32_t a1[4] = {vr[2 * i + 1].x, vr[2 * i + 1].y, vr[2 * i + 1].z,
-                                    vr[2 * i + 1].w};
+            const uint4 r0 = *reinterpret_cast<const uint4*>(vsrc + (2 * kp) * 256 + 16 * c8);
+            const uint4 r1 = *reinterpret_cast<const uint4*>(vsrc + (2 * kp + 1) * 256 + 16 * c8);
+            const uint32_t a0[4] = {r0.x, r0.y, r0.z, r0.w};
+            const uint32_t a1[4] = {r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (a0[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-                const uint32_t hi = (a1[e / 2] >> (16 * (e % 2))) & 0xFFFFu;
-                *reinterpret_cast<uint32_t*>(&vt[8 * c8 + e][2 * kp]) = lo | (hi << 16);
+                // channel 8 c8 + e of keys 2 kp (low half) and 2 kp + 1 (high half)
+                const int c = 8 * c8 + e;
+                vt[c][kp ^ vt_swz(c)] = __builtin_amdgcn_perm(a1[e / 2], a0[e / 2],
+                                                              e % 2 ? 0x07060302u : 0x05040100u);
             }
         }
     };
     if (nkb > 0) fetch(0);
     for (int t = 0; t < nkb; ++t) {
-        __syncthreads();  // the previous tile is no longer read
-        stage();
+        // the previous tile is no longer read; this tile's copies and value
+        // rows have landed (the barrier's fence waits for them)
+        __syncthreads();
+        stage(t);
         __syncthreads();
         if (t + 1 < nkb) fetch(t + 1);
         const int k0 = t * KB;
         if (k0 > row0 + 31 || row0 >= n) continue;  // every key of the tile is after this wave's rows
+        const unsigned char* kt_lds = &ks[t & 1][0];
         // S^T tiles: key tile kt, row tile rt; lane holds keys k0 + 16 kt + 4 kb + i
         // of row row0 + 16 rt + j
         floatx4 St[2][4];
@@ -216,7 +232,8 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(PrefillArgs a) {
             half8 Ak[4];
 #pragma unroll
             for (int kst = 0; kst < 4; ++kst)
-                Ak[kst] = *reinterpret_cast<const half8*>(&ks[16 * kt + j][32 * kst + 8 * kb]);
+                Ak[kst] = *reinterpret_cast<const half8*>(
+                    kt_lds + (16 * kt + j) * 256 + 16 * ((4 * kst + kb) ^ j));
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -230,53 +247,54 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(PrefillArgs a) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             const int row = row0 + 16 * rt + j;
+            // the row's maximum logit over the tile, from the unscaled products
+            // (the scale is positive) with masked keys at -inf
             float mx = -INFINITY;
             if (k0 + KB - 1 <= row0 + 16 * rt && row0 + 16 * rt + 15 < n) {
                 // every key of the tile at or before every row of the row tile
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float s = St[rt][kt][i] * a.qscale;
-                        St[rt][kt][i] = s;
-                        mx = fmaxf(mx, s);
-                    }
+                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, St[rt][kt][i]);
             } else {
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int key = k0 + 16 * kt + 4 * kb + i;
-                        float s = St[rt][kt][i] * a.qscale;
-                        if (key > row || key >= n || row >= n) s = -INFINITY;
-                        St[rt][kt][i] = s;
-                        mx = fmaxf(mx, s);
+                        if (key > row || key >= n || row >= n) St[rt][kt][i] = -INFINITY;
+                        mx = fmaxf(mx, St[rt][kt][i]);
                     }
             }
-            mx = max_x32(max_x16(mx));
-            const float mnew = fmaxf(m[rt], mx);
-            // rows with nothing unmasked yet keep alpha = 1 and p = 0
-            const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rt] - mnew);
-            const float mu = mnew == -INFINITY ? 0.f : mnew;
+            mx = max_x32(max_x16(mx)) * qs;
+            // the reference maximum moves (and the row's sums are rescaled) only
+            // when some row of the wavefront passes its own by more than tau
+            if (__any(mx > m[rt] + kLazyTau)) {
+                const float mnew = mx > m[rt] + kLazyTau ? mx : m[rt];
+                // rows with nothing unmasked yet keep alpha = 1 and p = 0
+                const float alpha = m[rt] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rt] - mnew);
+                l[rt] *= alpha;
+                m[rt] = mnew;
+                // rescale the output rows 4 kb + i of the tile by their rows' alpha
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha, 4 * kb + i);
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) O[rt][nt][i] *= ai;
+                }
+            }
+            const float nmu = m[rt] == -INFINITY ? 0.f : -m[rt];
             float ps = 0.f;
             float p[4][4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[kt][i] = __builtin_amdgcn_exp2f(St[rt][kt][i] - mu);
+                    p[kt][i] = __builtin_amdgcn_exp2f(fmaf(St[rt][kt][i], qs, nmu));
                     ps += p[kt][i];
                 }
             ps = sum_x32(sum_x16(ps));
-            l[rt] = l[rt] * alpha + ps;
-            m[rt] = mnew;
-            // rescale the output rows 4 kb + i of the tile by their rows' alpha
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float ai = __shfl(alpha, 4 * kb + i);
-#pragma unroll
-                for (int nt = 0; nt < 8; ++nt) O[rt][nt][i] *= ai;
-            }
+            l[rt] += ps;
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
                 Ap[rt][s2] = half8{(_Float16)p[2 * s2][0], (_Float16)p[2 * s2][1],
@@ -288,11 +306,12 @@ __global__ __launch_bounds__(256) void prefill_fwd_kernel(PrefillArgs a) {
         // k0 + 32 s2 + 4 kb + 0..3 and k0 + 32 s2 + 16 + 4 kb + 0..3
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
+            const int c = 16 * nt + j, sw = vt_swz(c);
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const half4 v0 = *reinterpret_cast<const half4*>(&vt[16 * nt + j][32 * s2 + 4 * kb]);
-                const half4 v1 =
-                    *reinterpret_cast<const half4*>(&vt[16 * nt + j][32 * s2 + 16 + 4 * kb]);
+                // key pairs 16 s2 + 2 kb (+1) and 16 s2 + 8 + 2 kb (+1)
+                const half4 v0 = *reinterpret_cast<const half4*>(&vt[c][(16 * s2 + 2 * kb) ^ sw]);
+                const half4 v1 = *reinterpret_cast<const half4*>(&vt[c][(16 * s2 + 8 + 2 * kb) ^ sw]);
                 const half8 Bv = half8{v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
@@ -340,6 +359,9 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(PrefillArgs a) {
     const int k0 = bx * KB, kt0 = k0 + 16 * wave;  // first key of the block, of this wavefront
     const int64_t qhead = (int64_t)b * a.n_kv_heads * R + hkv * R + hh;
     const int64_t kvbase = (int64_t)unit * n;
+    const uint16_t* kunit = a.k + kvbase * D;  // this unit's rows; offsets below are 32-bit
+    const uint16_t* vunit = a.v + kvbase * D;
+    const float qs = a.qscale;
     const int j = lane & 15, kb = lane >> 4;
     // key operands (A of S^T): key kt0 + j, channels 32 kst + 8 kb .. + 7
     half8 Ak[4];
