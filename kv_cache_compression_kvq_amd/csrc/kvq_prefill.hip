@@ -234,14 +234,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             for (int kst = 0; kst < 4; ++kst)
                 Ak[kst] = *reinterpret_cast<const half8*>(
                     kt_lds + (16 * kt + j) * 256 + 16 * ((4 * kst + kb) ^ j));
+            // the two row tiles as independent chains
+            St[0][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            St[1][kt] = St[0][kt];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kst = 0; kst < 4; ++kst)
 #pragma unroll
-                for (int kst = 0; kst < 4; ++kst)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ak[kst], Qo[rt][kst], acc, 0, 0, 0);
-                St[rt][kt] = acc;
-            }
+                for (int rt = 0; rt < 2; ++rt)
+                    St[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ak[kst], Qo[rt][kst], St[rt][kt], 0, 0, 0);
         }
         half8 Ap[2][2];  // P operands of the two 32-key k-steps
 #pragma unroll
@@ -341,14 +341,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 // Column sums: block (key block x of 64 keys, unit y); wavefront w owns keys
 // k0 + 16 w .. + 15 (k0 = 64 x). For each of the r query heads of the KV head,
 // the query rows from k0 on pass through a ring of LDS stages, 64 rows with
-// their log-sum-exp each, copied straight from memory three stages ahead of
+// their log-sum-exp each, copied straight from memory two stages ahead of
 // use; each wavefront adds exp2(s - lse_row) of its keys over the stage's
 // rows at or after them: every column sum is produced by one wavefront in a
 // fixed order.
 template <int R>
 __global__ __launch_bounds__(256) void prefill_colsum_kernel(PrefillArgs a) {
     constexpr int QT = 64;                       // query rows per stage
-    constexpr int kStages = 4;                   // stages in flight
+    constexpr int kStages = 3;                   // stages in flight
     constexpr int kTileBytes = QT * D * 2;       // 16 KB of query rows
     __shared__ __align__(16) unsigned char ring[kStages][kTileBytes + QT * 4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -422,6 +422,48 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(PrefillArgs a) {
         const int r0 = (t_first + it) * QT;
         if (kt0 >= n) continue;
         const uint32_t st = lds_addr(&ring[it % kStages][0]);
+        if (r0 >= kt0 + 15 && r0 + QT - 1 < n && kt0 + 15 < n) {
+            // every row of the stage at or after every key of the wavefront:
+            // the four row tiles' products as four independent chains
+            u32x4 bw[4][4];
+            uint32_t lsw[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int row_l = 16 * rt + j;
+#pragma unroll
+                for (int kst = 0; kst < 4; ++kst)
+                    bw[rt][kst] = lds_read16(st + row_l * 256 + (((4 * kst + kb) ^ (row_l & 15)) * 16));
+                lsw[rt] = lds_read4(st + kTileBytes + 4 * row_l);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(bw[0][0]), "+v"(bw[0][1]), "+v"(bw[0][2]), "+v"(bw[0][3]),
+                           "+v"(bw[1][0]), "+v"(bw[1][1]), "+v"(bw[1][2]), "+v"(bw[1][3]),
+                           "+v"(lsw[0]), "+v"(lsw[1])
+                         :
+                         : "memory");
+            asm volatile(""
+                         : "+v"(bw[2][0]), "+v"(bw[2][1]), "+v"(bw[2][2]), "+v"(bw[2][3]),
+                           "+v"(bw[3][0]), "+v"(bw[3][1]), "+v"(bw[3][2]), "+v"(bw[3][3]),
+                           "+v"(lsw[2]), "+v"(lsw[3])
+                         :
+                         : "memory");
+            floatx4 acc[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kst = 0; kst < 4; ++kst)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        Ak[kst], __builtin_bit_cast(half8, bw[rt][kst]), acc[rt], 0, 0, 0);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const float lsr = __builtin_bit_cast(float, lsw[rt]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) cs[i] += __builtin_amdgcn_exp2f(fmaf(acc[rt][i], qs, -lsr));
+            }
+            continue;
+        }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             const int rb = r0 + 16 * rt;  // first row of the 16-row tile
