@@ -84,6 +84,21 @@ __device__ __forceinline__ void lds_load16(const void* g, void* lds) {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                      (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
+// Buffer-resource form of the same copy: a wave-uniform descriptor (base and
+// size in bytes, raw access), a per-lane byte offset and a wave-uniform byte
+// offset, so a loop adds nothing per lane; every access here stays inside the
+// described range.
+constexpr uint32_t kRawBufferWord3 = 0x00020000u;  // raw (untyped) 32-bit access
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             (int)kRawBufferWord3);
+}
+__device__ __forceinline__ void lds_load16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                               void* lds) {
+    // lane i's 16 bytes land at lds + 16 * i
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff,
+                                             soff, 0, 0);
+}
 __device__ __forceinline__ void lds_load4(const void* g, void* lds) {
     // lane i's 4 bytes land at lds + 4 * i
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
@@ -182,25 +197,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int nkb = (kend + KB - 1) / KB;
     // tile staging: 64 keys x 128 channels of K and V copied to LDS, V then
     // transposed through registers
+    // this thread's copies (i = 0..3): key row p / 16 of the tile, p = tid + 256 i;
+    // K: lane position p % 16 receives chunk (p % 16) ^ (row % 16); V: chunk p % 16.
+    // Byte offsets from the tile's first row, fixed for the whole loop; the
+    // tile's own offset is wave-uniform.
+    uint32_t koff[4], voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = tid + 256 * i, key = p / 16, pc = p % 16;
+        koff[i] = (uint32_t)(2 * (key * D + 8 * (pc ^ (key & 15))));
+        voff[i] = (uint32_t)(2 * (key * D + 8 * pc));
+    }
+    const uint32_t unit_bytes = (uint32_t)n * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kunit, unit_bytes), vrs = buffer_rsrc(vunit, unit_bytes);
+    const int wbase = __builtin_amdgcn_readfirstlane(tid - lane);  // first thread of the wave
     auto fetch = [&](int t) {
         const int k0 = t * KB;
         unsigned char* kdst = &ks[t & 1][0];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // lane position pc of key row `key` receives that row's chunk
-            // pc ^ (key % 16); rows past n repeat row n - 1 (their logits are masked)
-            const int p = tid + 256 * i, key = p / 16, pc = p % 16;
-            const int row = k0 + key < n ? k0 + key : n - 1;
-            lds_load16(kunit + (uint32_t)(row * D + 8 * (pc ^ (key & 15))), kdst + (tid - lane + 256 * i) * 16);
-        }
         unsigned char* vdst = &vs[t & 1][0];
+        const uint32_t tb = (uint32_t)k0 * D * 2;  // the tile's first row
+        if (k0 + KB <= n) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // chunk p % 16 of value row p / 16 (rows past n repeat row n - 1,
-            // whose probabilities are 0)
-            const int p = tid + 256 * i, key = p / 16, c8 = p % 16;
-            const int row = k0 + key < n ? k0 + key : n - 1;
-            lds_load16(vunit + (uint32_t)(row * D + 8 * c8), vdst + (tid - lane + 256 * i) * 16);
+            for (int i = 0; i < 4; ++i) lds_load16_buf(krs, koff[i], tb, kdst + (wbase + 256 * i) * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lds_load16_buf(vrs, voff[i], tb, vdst + (wbase + 256 * i) * 16);
+        } else {
+            // last tile: rows past n repeat row n - 1 (their logits are masked,
+            // their probabilities 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = (tid + 256 * i) / 16;
+                const uint32_t back = k0 + key < n ? 0u : (uint32_t)((k0 + key - (n - 1)) * D * 2);
+                lds_load16_buf(krs, koff[i] - back, tb, kdst + (wbase + 256 * i) * 16);
+                lds_load16_buf(vrs, voff[i] - back, tb, vdst + (wbase + 256 * i) * 16);
+            }
         }
     };
     auto stage = [&](int t) {
