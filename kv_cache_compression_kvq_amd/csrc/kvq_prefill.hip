@@ -28,16 +28,20 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = kHeadDim;
 constexpr int KB = 64;           // keys per block step
-// Transposed value tile: row c (channel) holds the 64 keys as 32 key-pair
-// dwords, dword p at position p ^ vt_swz(c). The swizzle is even, so the
-// 8-byte reads of two key pairs stay whole; it makes the staging writes
-// (lanes: 16 channels 8 apart x 2 key pairs) and the operand reads (lanes: 16
-// consecutive channels, one key pair) hit 32 distinct banks.
-__device__ __forceinline__ int vt_swz(int c) { return 2 * (((c >> 3) ^ c) & 15); }
+// Value tile as copied, row-major (64 keys x 256 B), 16-byte chunk c of key
+// row r at position c ^ v_swz(r). The value operand is read with the gfx950
+// transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// 4 r + s reads 8 bytes, and lane i receives element i of the 16 values read
+// by lanes 4 r' .. 4 r' + 3, for r' = 0..3. Lane (16 g + 4 r + s) reads key row
+// 4 g + r (+ 16 h + 32 s2), channels 16 nt + 4 s .. + 3, so lane (g, i) gets
+// channel 16 nt + i of keys 4 g + r' (+ ...): the B operand layout. The
+// swizzle spreads those 16 reads of a group over all 32 banks.
+__device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3) + 8 * ((r >> 2) & 1); }
 // Lazy rescaling ("online softmax" with a threshold): a row's reference
 // maximum moves only when a logit exceeds it by more than this (log2 units),
 // so its probabilities stay below 2^8 in the fp16 operand.
@@ -153,9 +157,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // key tiles, double-buffered and filled by direct global->LDS copies:
     // 64 rows of 256 B, 16-byte chunk c of key row r at position c ^ (r % 16)
     __shared__ __align__(16) unsigned char ks[2][KB * D * 2];
-    // value tiles as copied (row-major), double-buffered, and transposed
+    // value tiles as copied (row-major, chunks swizzled by v_swz), double-buffered
     __shared__ __align__(16) unsigned char vs[2][KB * D * 2];
-    __shared__ __align__(16) uint32_t vt[D][KB / 2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = a.n;
     int bx, by;
@@ -198,7 +201,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // tile staging: 64 keys x 128 channels of K and V copied to LDS, V then
     // transposed through registers
     // this thread's copies (i = 0..3): key row p / 16 of the tile, p = tid + 256 i;
-    // K: lane position p % 16 receives chunk (p % 16) ^ (row % 16); V: chunk p % 16.
+    // lane position p % 16 receives chunk (p % 16) ^ (row % 16) (K) or
+    // (p % 16) ^ v_swz(row) (V).
     // Byte offsets from the tile's first row, fixed for the whole loop; the
     // tile's own offset is wave-uniform.
     uint32_t koff[4], voff[4];
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (int i = 0; i < 4; ++i) {
         const int p = tid + 256 * i, key = p / 16, pc = p % 16;
         koff[i] = (uint32_t)(2 * (key * D + 8 * (pc ^ (key & 15))));
-        voff[i] = (uint32_t)(2 * (key * D + 8 * pc));
+        voff[i] = (uint32_t)(2 * (key * D + 8 * (pc ^ v_swz(key))));
     }
     const uint32_t unit_bytes = (uint32_t)n * D * 2;
     const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kunit, unit_bytes), vrs = buffer_rsrc(vunit, unit_bytes);
@@ -233,31 +237,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             }
         }
     };
-    auto stage = [&](int t) {
-        const unsigned char* vsrc = &vs[t & 1][0];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            // two consecutive keys of the same 8 channels, stored as key pairs
-            const int p = tid + 256 * i, kp = p / 16, c8 = p % 16;
-            const uint4 r0 = *reinterpret_cast<const uint4*>(vsrc + (2 * kp) * 256 + 16 * c8);
-            const uint4 r1 = *reinterpret_cast<const uint4*>(vsrc + (2 * kp + 1) * 256 + 16 * c8);
-            const uint32_t a0[4] = {r0.x, r0.y, r0.z, r0.w};
-            const uint32_t a1[4] = {r1.x, r1.y, r1.z, r1.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                // channel 8 c8 + e of keys 2 kp (low half) and 2 kp + 1 (high half)
-                const int c = 8 * c8 + e;
-                vt[c][kp ^ vt_swz(c)] = __builtin_amdgcn_perm(a1[e / 2], a0[e / 2],
-                                                              e % 2 ? 0x07060302u : 0x05040100u);
-            }
-        }
-    };
     if (nkb > 0) fetch(0);
+    // lane parts of the value-operand reads: key row 4 g + r, 8-byte half s % 2
+    // of chunk 2 nt + s / 2 (swizzled per tile nt below)
+    const int vg = lane >> 4, vr = (lane >> 2) & 3, vsl = lane & 3;
+    const int vrow = 4 * vg + vr, vsw = v_swz(vrow);
+    const uint32_t vlane = (uint32_t)(vrow * 256 + 8 * (vsl & 1));
     for (int t = 0; t < nkb; ++t) {
-        // the previous tile is no longer read; this tile's copies and value
-        // rows have landed (the barrier's fence waits for them)
-        __syncthreads();
-        stage(t);
+        // every wavefront is done with tile t - 1 (whose buffers the next
+        // copies refill), and tile t's copies have landed (the barrier's fence
+        // waits for them)
         __syncthreads();
         if (t + 1 < nkb) fetch(t + 1);
         const int k0 = t * KB;
@@ -343,14 +332,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
         // O += P V: value operand of tile nt, k-step s2: channel 16 nt + j, keys
         // k0 + 32 s2 + 4 kb + 0..3 and k0 + 32 s2 + 16 + 4 kb + 0..3
+        const unsigned char* vtile = &vs[t & 1][0];
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
-            const int c = 16 * nt + j, sw = vt_swz(c);
+            const unsigned char* vb = vtile + vlane + 16 * ((2 * nt + (vsl >> 1)) ^ vsw);
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                // key pairs 16 s2 + 2 kb (+1) and 16 s2 + 8 + 2 kb (+1)
-                const half4 v0 = *reinterpret_cast<const half4*>(&vt[c][(16 * s2 + 2 * kb) ^ sw]);
-                const half4 v1 = *reinterpret_cast<const half4*>(&vt[c][(16 * s2 + 8 + 2 * kb) ^ sw]);
+                // keys 32 s2 + 4 kb + 0..3 (h = 0) and 32 s2 + 16 + 4 kb + 0..3 (h = 1)
+                const half4 v0 = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) short4_t*)(vb + (32 * s2) * 256)));
+                const half4 v1 = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) short4_t*)(vb + (32 * s2 + 16) * 256)));
                 const half8 Bv = half8{v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt)
