@@ -232,6 +232,10 @@ ROWS = {
     "decode_long_b2g128": ("long_b2g128", "a8-a10: fused decode + merge, split-K over context"),
     "decode_long_b4g32": ("long_b4g32", "a8-a10: fused decode + merge, split-K over context"),
     "decode_long_b4g128": ("long_b4g128", "a8-a10: fused decode + merge, split-K over context"),
+    "append_long_b2g32": ("long_b2g32", "a4-a7: bulk quantize + pack of the whole prefix, ring store"),
+    "append_long_b2g128": ("long_b2g128", "a4-a7: bulk quantize + pack of the whole prefix, ring store"),
+    "append_long_b4g32": ("long_b4g32", "a4-a7: bulk quantize + pack of the whole prefix, ring store"),
+    "append_long_b4g128": ("long_b4g128", "a4-a7: bulk quantize + pack of the whole prefix, ring store"),
 }
 
 

@@ -477,10 +477,19 @@ __device__ constexpr int kPos2[8] = {3, 4, 1, 2, 5, 6, 7, 0};
 // admitted one (mean replacement). Mode 0: one pass (no pool). The unit's
 // value-scale bound (counters[3]) is raised in every pass, so it also covers
 // the first-pass scales of tokens later replaced by the group mean.
+// Threads of a pack block: groups of 64 and 128 tokens take 512 and 1024, so
+// that each thread holds two 16-byte row pieces per tensor and the per-channel
+// and per-token passes split over several threads.
+template <int G>
+constexpr int pack_threads() { return G <= 32 ? 256 : G == 64 ? 512 : 1024; }
+
 template <int BITS, int G>
 __device__ void pack_group(const CacheView& v, const uint16_t* knew, const uint16_t* vnew,
                            int64_t t_old, int32_t n_new, int u, int64_t g, int32_t mode,
                            uint32_t vmax_seen) {
+    constexpr int NT = pack_threads<G>();
+    constexpr int KSL = NT / (2 * D);  // token slices per key channel
+    constexpr int VPP = NT / (2 * D);  // threads per (token, value group): D pairs per group
     constexpr int NG = D / G;          // value groups per token
     constexpr bool kHalf = G == 16;    // the group is half a chunk
     constexpr int CPG = kHalf ? 1 : G / kChunk;  // chunks the group touches
@@ -495,24 +504,25 @@ __device__ void pack_group(const CacheView& v, const uint16_t* knew, const uint1
     uint16_t* kx = smem;
     uint16_t* vx = smem + G * RS;
     __shared__ uint16_t meank[D], meanv[D];
-    __shared__ uint32_t vmax_w[2];
+    __shared__ uint32_t vmax_w[NT / 128];
+    __shared__ float kmin_s[KSL][D], kmax_s[KSL][D];  // key slices' extremes (KSL > 1)
     const int tid = threadIdx.x;
     const int64_t t0 = g * G;
     const int hf = kHalf ? (int)(g & 1) : 0;  // G = 16: which half of its chunk
 
     {
         // all of this thread's row pieces are requested before any is stored
-        constexpr int kPer = G * 16 / 256;  // 16-byte pieces per thread and tensor
+        constexpr int kPer = G * 16 / NT;  // 16-byte pieces per thread and tensor
         uint4 kr[kPer], vr[kPer];
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int e = tid + 256 * j, i = e / 16, part = e % 16;
+            const int e = tid + NT * j, i = e / 16, part = e % 16;
             kr[j] = reinterpret_cast<const uint4*>(src_row(v.kring, knew, v, u, t0 + i, t_old, n_new))[part];
             vr[j] = reinterpret_cast<const uint4*>(src_row(v.vring, vnew, v, u, t0 + i, t_old, n_new))[part];
         }
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int e = tid + 256 * j, i = e / 16, part = e % 16;
+            const int e = tid + NT * j, i = e / 16, part = e % 16;
             reinterpret_cast<uint4*>(kx + i * RS)[part] = kr[j];
             reinterpret_cast<uint4*>(vx + i * RS)[part] = vr[j];
         }
@@ -531,7 +541,7 @@ __device__ void pack_group(const CacheView& v, const uint16_t* knew, const uint1
         // units of 2^-24; 256 / G threads per token
         // (any partial sum is a multiple of 2^-24 below 2^23 with at most 47
         // significant bits, so the fp64 sum is exact in any order)
-        constexpr int TPT = 256 / G, CPT = D / TPT;
+        constexpr int TPT = NT / G, CPT = D / TPT;
         const int i = tid / TPT, part = tid % TPT;
         double sc = 0.0;
 #pragma unroll
@@ -556,7 +566,7 @@ __device__ void pack_group(const CacheView& v, const uint16_t* knew, const uint1
             (tid < D ? meank[tid] : meanv[tid - D]) = fixed_to_half(s, LG);
         }
         __syncthreads();
-        for (int e = tid; e < G * D; e += 256) {
+        for (int e = tid; e < G * D; e += NT) {
             const int i = e / D, c = e % D;
             if ((mw[i / kChunk] >> (i % kChunk)) & 1u) {
                 kx[i * RS + c] = meank[c];
@@ -565,71 +575,171 @@ __device__ void pack_group(const CacheView& v, const uint16_t* knew, const uint1
         }
         __syncthreads();
     }
-    if (tid < D) {
-        // keys: channel c over the G tokens
-        const int c = tid;
-        float mn = INFINITY, mx = -INFINITY;
-        for (int i = 0; i < G; ++i) {
-            const float x = h2f(kx[i * RS + c]);
-            mn = fminf(mn, x);
-            mx = fmaxf(mx, x);
-        }
-        const float q = fmaxf(mx - mn, range_floor()) / levels;
-        const float rq = 1.0f / q;
-        v.kmeta[((int64_t)u * v.key_groups + g) * D + c] = (uint32_t)f2h(q) | ((uint32_t)f2h(mn) << 16);
-        for (int i0 = 0; i0 < G; i0 += 8) {
-            float x[8];
-            uint32_t cd[8];
-#pragma unroll
-            for (int m = 0; m < 8; ++m) x[m] = h2f(kx[(i0 + m) * RS + c]);
-            quant_codes(x, mn, q, rq, levels, cd);
-#pragma unroll
-            for (int m = 0; m < 8; ++m) kx[(i0 + m) * RS + c] = (uint16_t)cd[m];
+    if constexpr (KSL == 1) {
+        // 256 threads: thread tid < D takes key channel tid over the G tokens,
+        // thread D + j the value pair (token j / NG, group j % NG)
+        if (tid < D) {
+            // keys: channel c over the G tokens
+            const int c = tid;
+            float mn = INFINITY, mx = -INFINITY;
+            for (int i = 0; i < G; ++i) {
+                const float x = h2f(kx[i * RS + c]);
+                mn = fminf(mn, x);
+                mx = fmaxf(mx, x);
+            }
+            const float q = fmaxf(mx - mn, range_floor()) / levels;
+            const float rq = 1.0f / q;
+            v.kmeta[((int64_t)u * v.key_groups + g) * D + c] = (uint32_t)f2h(q) | ((uint32_t)f2h(mn) << 16);
+            for (int i0 = 0; i0 < G; i0 += 8) {
+                float x[8];
+                uint32_t cd[8];
+    #pragma unroll
+                for (int m = 0; m < 8; ++m) x[m] = h2f(kx[(i0 + m) * RS + c]);
+                quant_codes(x, mn, q, rq, levels, cd);
+    #pragma unroll
+                for (int m = 0; m < 8; ++m) kx[(i0 + m) * RS + c] = (uint16_t)cd[m];
+            }
+        } else {
+            // values: token i, channels [gq*G, gq*G + G), eight at a time
+            const int j = tid - D, i = j / NG, gq = j % NG;
+            uint4* row = reinterpret_cast<uint4*>(vx + i * RS + gq * G);
+            float mn = INFINITY, mx = -INFINITY;
+            for (int c8 = 0; c8 < G / 8; ++c8) {
+                const uint4 x = row[c8];
+                const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    #pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float a = h2f((uint16_t)(w[m] & 0xFFFF)), b = h2f((uint16_t)(w[m] >> 16));
+                    mn = fminf(mn, fminf(a, b));
+                    mx = fmaxf(mx, fmaxf(a, b));
+                }
+            }
+            const float q = fmaxf(mx - mn, range_floor()) / levels;
+            const float rq = 1.0f / q;
+            const int64_t t = t0 + i;
+            const uint16_t qh = f2h(q);
+            v.vmeta[(((int64_t)u * v.chunks + t / kChunk) * NG + gq) * kChunk + t % kChunk] =
+                (uint32_t)qh | ((uint32_t)f2h(mn) << 16);
+            // Largest value scale of the unit (fp16 bits of a positive number order
+            // like the numbers): bounds the lazy softmax rescale of the decoder.
+            uint32_t mq = qh;
+            for (int off = 32; off > 0; off >>= 1) mq = max(mq, (uint32_t)__shfl_xor((int)mq, off));
+            if ((tid & 63) == 0) vmax_w[(tid - D) >> 6] = mq;
+            for (int c8 = 0; c8 < G / 8; ++c8) {
+                const uint4 x = row[c8];
+                const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+                float xf[8];
+                uint32_t cd[8];
+    #pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    xf[2 * m] = h2f((uint16_t)(w[m] & 0xFFFF));
+                    xf[2 * m + 1] = h2f((uint16_t)(w[m] >> 16));
+                }
+                quant_codes(xf, mn, q, rq, levels, cd);
+                row[c8] = make_uint4(cd[0] | cd[1] << 16, cd[2] | cd[3] << 16, cd[4] | cd[5] << 16,
+                                     cd[6] | cd[7] << 16);
+            }
         }
     } else {
-        // values: token i, channels [gq*G, gq*G + G), eight at a time
-        const int j = tid - D, i = j / NG, gq = j % NG;
-        uint4* row = reinterpret_cast<uint4*>(vx + i * RS + gq * G);
+        // Keys: thread tid < NT / 2 takes channel tid % D over token slice
+        // tid / D (G / KSL tokens). Values: thread NT / 2 + j takes (token, value
+        // group) pair j / VPP, channel part j % VPP (G / VPP channels); the parts of
+        // a pair are adjacent lanes.
+        constexpr int KT = G / KSL, VC = G / VPP;
+        const bool is_key = tid < NT / 2;
+        const int c = tid % D, ksl = (tid / D) % KSL;
+        const int j = tid - NT / 2, vpair = j / VPP, vpart = j % VPP;
+        const int vi = vpair / NG, vgq = vpair % NG;
         float mn = INFINITY, mx = -INFINITY;
-        for (int c8 = 0; c8 < G / 8; ++c8) {
-            const uint4 x = row[c8];
-            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float a = h2f((uint16_t)(w[m] & 0xFFFF)), b = h2f((uint16_t)(w[m] >> 16));
-                mn = fminf(mn, fminf(a, b));
-                mx = fmaxf(mx, fmaxf(a, b));
+        if (is_key) {
+            for (int i = ksl * KT; i < ksl * KT + KT; ++i) {
+                const float x = h2f(kx[i * RS + c]);
+                mn = fminf(mn, x);
+                mx = fmaxf(mx, x);
+            }
+            if (KSL > 1) {
+                kmin_s[ksl][c] = mn;
+                kmax_s[ksl][c] = mx;
+            }
+        } else {
+            const uint4* row = reinterpret_cast<const uint4*>(vx + vi * RS + vgq * G + vpart * VC);
+            for (int c8 = 0; c8 < VC / 8; ++c8) {
+                const uint4 x = row[c8];
+                const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    #pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float a = h2f((uint16_t)(w[m] & 0xFFFF)), b = h2f((uint16_t)(w[m] >> 16));
+                    mn = fminf(mn, fminf(a, b));
+                    mx = fmaxf(mx, fmaxf(a, b));
+                }
+            }
+    #pragma unroll
+            for (int off = 1; off < VPP; off <<= 1) {
+                mn = fminf(mn, __shfl_xor(mn, off, VPP));
+                mx = fmaxf(mx, __shfl_xor(mx, off, VPP));
+            }
+        }
+        if (KSL > 1) {
+            __syncthreads();
+            if (is_key) {
+                mn = kmin_s[0][c];
+                mx = kmax_s[0][c];
+    #pragma unroll
+                for (int sl = 1; sl < KSL; ++sl) {
+                    mn = fminf(mn, kmin_s[sl][c]);
+                    mx = fmaxf(mx, kmax_s[sl][c]);
+                }
             }
         }
         const float q = fmaxf(mx - mn, range_floor()) / levels;
         const float rq = 1.0f / q;
-        const int64_t t = t0 + i;
-        const uint16_t qh = f2h(q);
-        v.vmeta[(((int64_t)u * v.chunks + t / kChunk) * NG + gq) * kChunk + t % kChunk] =
-            (uint32_t)qh | ((uint32_t)f2h(mn) << 16);
-        // Largest value scale of the unit (fp16 bits of a positive number order
-        // like the numbers): bounds the lazy softmax rescale of the decoder.
-        uint32_t mq = qh;
-        for (int off = 32; off > 0; off >>= 1) mq = max(mq, (uint32_t)__shfl_xor((int)mq, off));
-        if ((tid & 63) == 0) vmax_w[(tid - D) >> 6] = mq;
-        for (int c8 = 0; c8 < G / 8; ++c8) {
-            const uint4 x = row[c8];
-            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-            float xf[8];
-            uint32_t cd[8];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                xf[2 * m] = h2f((uint16_t)(w[m] & 0xFFFF));
-                xf[2 * m + 1] = h2f((uint16_t)(w[m] >> 16));
+        if (is_key) {
+            // keys: channel c over its token slice
+            if (ksl == 0)
+                v.kmeta[((int64_t)u * v.key_groups + g) * D + c] = (uint32_t)f2h(q) | ((uint32_t)f2h(mn) << 16);
+            for (int i0 = ksl * KT; i0 < ksl * KT + KT; i0 += 8) {
+                float x[8];
+                uint32_t cd[8];
+    #pragma unroll
+                for (int m = 0; m < 8; ++m) x[m] = h2f(kx[(i0 + m) * RS + c]);
+                quant_codes(x, mn, q, rq, levels, cd);
+    #pragma unroll
+                for (int m = 0; m < 8; ++m) kx[(i0 + m) * RS + c] = (uint16_t)cd[m];
             }
-            quant_codes(xf, mn, q, rq, levels, cd);
-            row[c8] = make_uint4(cd[0] | cd[1] << 16, cd[2] | cd[3] << 16, cd[4] | cd[5] << 16,
-                                 cd[6] | cd[7] << 16);
+        } else {
+            // values: token vi, channels vgq * G + vpart * VC .. + VC - 1, eight at a time
+            uint4* row = reinterpret_cast<uint4*>(vx + vi * RS + vgq * G + vpart * VC);
+            const int64_t t = t0 + vi;
+            const uint16_t qh = f2h(q);
+            if (vpart == 0)
+                v.vmeta[(((int64_t)u * v.chunks + t / kChunk) * NG + vgq) * kChunk + t % kChunk] =
+                    (uint32_t)qh | ((uint32_t)f2h(mn) << 16);
+            // Largest value scale of the unit (fp16 bits of a positive number order
+            // like the numbers): bounds the lazy softmax rescale of the decoder.
+            uint32_t mq = qh;
+            for (int off = 32; off > 0; off >>= 1) mq = max(mq, (uint32_t)__shfl_xor((int)mq, off));
+            if ((j & 63) == 0) vmax_w[j >> 6] = mq;
+            for (int c8 = 0; c8 < VC / 8; ++c8) {
+                const uint4 x = row[c8];
+                const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+                float xf[8];
+                uint32_t cd[8];
+    #pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    xf[2 * m] = h2f((uint16_t)(w[m] & 0xFFFF));
+                    xf[2 * m + 1] = h2f((uint16_t)(w[m] >> 16));
+                }
+                quant_codes(xf, mn, q, rq, levels, cd);
+                row[c8] = make_uint4(cd[0] | cd[1] << 16, cd[2] | cd[3] << 16, cd[4] | cd[5] << 16,
+                                     cd[6] | cd[7] << 16);
+            }
         }
     }
     __syncthreads();
     if (tid == 0) {
-        const uint32_t mq = max(vmax_w[0], vmax_w[1]);
+        uint32_t mq = vmax_w[0];
+#pragma unroll
+        for (int w = 1; w < NT / 128; ++w) mq = max(mq, vmax_w[w]);
         if (mq > vmax_seen) atomicMax(reinterpret_cast<uint32_t*>(v.counters) + (int64_t)u * 4 + 3, mq);
     }
 
@@ -637,7 +747,7 @@ __device__ void pack_group(const CacheView& v, const uint16_t* knew, const uint1
     // LDS row of the token at position tc of chunk cc (with G = 16 only the
     // block's own half of the chunk is in LDS).
     auto row_of = [&](int cc, int tc) { return kHalf ? tc - 16 * hf : cc * kChunk + tc; };
-    for (int e = tid; e < 2 * CPG * WPC; e += 256) {
+    for (int e = tid; e < 2 * CPG * WPC; e += NT) {
         const bool isv = e >= CPG * WPC;
         const int r = isv ? e - CPG * WPC : e;
         const int cc = r / WPC, o = r % WPC;
@@ -730,7 +840,8 @@ __device__ void pack_group(const CacheView& v, const uint16_t* knew, const uint1
 // tokens the scan admitted to the pool (a small share).
 constexpr int kRepairBatch = 4;
 template <int BITS, int G>
-__global__ __launch_bounds__(256) void pack_kernel(CacheView v, const uint16_t* knew,
+__global__ __launch_bounds__(pack_threads<G>()) __attribute__((amdgpu_waves_per_eu(G == 128 ? 8 : 1)))
+void pack_kernel(CacheView v, const uint16_t* knew,
                                                    const uint16_t* vnew, int64_t t_old,
                                                    int32_t n_new, int64_t g0, int32_t gstride,
                                                    int64_t ng, int32_t mode) {
@@ -1187,8 +1298,8 @@ hipError_t launch_pack_t(const CacheView& v, const uint16_t* kn, const uint16_t*
     for (int64_t gs = 0; gs < ng; gs += step) {
         const int64_t n = ng - gs < step ? ng - gs : step;
         hipLaunchKernelGGL((pack_kernel<BITS, G>), dim3((unsigned)((n + per - 1) / per * v.units)),
-                           dim3(256), lds, s, v, kn, vn, t_old, n_new, g0 + gs * gstride, gstride,
-                           n, mode);
+                           dim3(pack_threads<G>()), lds, s, v, kn, vn, t_old, n_new, g0 + gs * gstride,
+                           gstride, n, mode);
     }
     return hipSuccess;
 }
