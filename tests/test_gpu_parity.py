@@ -321,7 +321,7 @@ def test_g16_half_chunks_through_appends_and_decodes(bits):
     assert half_seen >= 3
 
 
-@pytest.mark.parametrize("bits,group,pool", [(2, 32, 3), (4, 16, 3), (2, 16, 0), (4, 64, 0)])
+@pytest.mark.parametrize("bits,group,pool", [(2, 32, 3), (4, 16, 3), (2, 16, 0), (4, 64, 0), (2, 128, 3)])
 def test_sinks_state_and_decode(bits, group, pool):
     """Four attention sinks ("KV cache quantization and eviction", Attention
     sinks and StreamingLLM): appends that end before, at and after the sink
