@@ -170,8 +170,8 @@ DecodePlan plan_decode(const kvq_cache* h, bool want_scores) {
     // One resident round of blocks on the current GPU. The fp16 partition
     // (ring + pools) takes about one tile block per compute unit, 16 to 64 rows
     // each; the quantized tokens of each unit are split over the remaining
-    // resident blocks, every wavefront of a split taking whole key groups
-    // (four wavefronts per block, so at most ceil(groups / 4) useful splits).
+    // resident blocks, every wavefront of a split taking whole work items
+    // (four wavefronts per block, so at most ceil(items / 4) useful splits).
     DecodePlan p{};
     const int64_t U = (int64_t)h->cfg.batch * h->cfg.n_kv_heads;
     const int64_t r = h->cfg.n_q_heads / h->cfg.n_kv_heads;
@@ -190,9 +190,10 @@ DecodePlan plan_decode(const kvq_cache* h, bool want_scores) {
     if (t > t_max) t = t_max;
     if (t < t_min) t = t_min;
     p.fp16_tiles = (int32_t)t;
-    // work items: key groups, or with G = 16 chunks (two groups each)
-    const int64_t groups = h->cfg.group == 16 ? (h->n_quant + kChunk - 1) / kChunk
-                                              : h->n_quant / h->cfg.group;
+    // work items: key groups at G = 32, else chunks (two groups each at
+    // G = 16, part of a group at G = 64 and 128)
+    const int64_t groups = h->cfg.group == 32 ? h->n_quant / h->cfg.group
+                                              : (h->n_quant + kChunk - 1) / kChunk;
     int64_t s = groups > 0 ? (groups + 3) / 4 : 0;
     if (s > kMaxQuantSplits) s = kMaxQuantSplits;
     if (s > 0) {

@@ -465,11 +465,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     const int idx = blockIdx.x - a.units * a.fp16_tiles;
     const int u = idx / a.splits_q, split = idx % a.splits_q;
     const int b = u / a.n_kv_heads, hk = u % a.n_kv_heads;
-    const uint32_t groups = (uint32_t)(kG16 ? (a.n_q + 31) / 32 : a.n_q / G);  // work items
-    const uint32_t gs0 = (uint32_t)((int64_t)split * groups / a.splits_q);
-    const uint32_t gs1 = (uint32_t)((int64_t)(split + 1) * groups / a.splits_q);
+    // Work items: key groups (wavefronts of a block interleaved), or with
+    // G = 16 chunks (two groups each); with groups of several chunks (G = 64,
+    // 128) single chunks, each wavefront taking a contiguous quarter of its
+    // block's range, so that no wavefront holds a whole extra group; a
+    // wavefront that starts inside a group folds that group's scales first.
+    constexpr bool kChunkItems = CPG > 1;
+    const uint32_t items = (uint32_t)(kG16 || kChunkItems ? (a.n_q + 31) / 32 : a.n_q / G);
+    const uint32_t gs0 = (uint32_t)((int64_t)split * items / a.splits_q);
+    const uint32_t gs1 = (uint32_t)((int64_t)(split + 1) * items / a.splits_q);
+    const uint32_t wc0 = gs0 + (uint32_t)wave * (gs1 - gs0) / 4;  // chunk items: first chunk
+    const uint32_t wc1 = gs0 + (uint32_t)(wave + 1) * (gs1 - gs0) / 4;
     const uint32_t my_groups = gs1 - gs0 > (uint32_t)wave ? (gs1 - gs0 - wave + 3) / 4 : 0;
-    const uint32_t n_items = my_groups * CPG;
+    const uint32_t n_items = kChunkItems ? wc1 - wc0 : my_groups * CPG;
+    // chunk k of this wavefront: its index, key group and place in the group
+    auto chunk_of = [&](uint32_t k, uint32_t& gi, uint32_t& cc) {
+        if (kChunkItems) {
+            const uint32_t ch = wc0 + k;
+            gi = ch / CPG;
+            cc = ch % CPG;
+        } else {
+            gi = gs0 + wave + 4 * (k / CPG);
+            cc = k % CPG;
+        }
+    };
 
     // Per-unit base pointers (wave-uniform); per-lane offsets stay 32-bit.
     const uint32_t* kq_u = a.kq + (int64_t)u * a.chunks * WPC;
@@ -512,7 +531,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     // Stage k (chunk k of this wavefront) lands in ring slot k % kStages.
     char* wlds = reinterpret_cast<char*>(smem) + wave * RG::kWave;
     auto issue = [&](uint32_t k) {
-        const uint32_t gi = gs0 + wave + 4 * (k / CPG), cc = k % CPG, ch = gi * CPG + cc;
+        uint32_t gi, cc;
+        chunk_of(k, gi, cc);
+        const uint32_t ch = gi * CPG + cc;
+        const bool fold = cc == 0 || (kChunkItems && k == 0);  // the group's key scales
         char* st = wlds + (k % RG::kStages) * RG::kStage;
         lds_load16(kq_u + ch * WPC + lane * 4, st);
         if (BITS == 4) lds_load16(kq_u + ch * WPC + 256 + lane * 4, st + 1024);
@@ -527,7 +549,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
             // scales (lanes >= 32)
             const uint32_t* src =
                 lane < 32 ? vm_u + ch * NG * 32 + lane * 4 : km_u + gi * D + (lane - 32) * 4;
-            if (lane < 8 * NG || (lane >= 32 && cc == 0)) lds_load16(src, st + 2 * RG::kCodes);
+            if (lane < 8 * NG || (lane >= 32 && fold)) lds_load16(src, st + 2 * RG::kCodes);
         }
         // lane 0: the chunk's pool mask word; lane 1: its eviction word
         if (lane < 2) lds_load4(lane == 0 ? mk_u + ch : ev_u + ch, st + 2 * RG::kCodes + RG::kMeta);
@@ -563,7 +585,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     const uint32_t lane_vm = 2 * RG::kCodes + (gs * 32 + 4 * kb) * 4;
     const uint32_t lane_km = 2 * RG::kCodes + RG::kKmOff + cb0 * 4;
     auto step = [&](uint32_t k, uint32_t later) {
-        const uint32_t gi = gs0 + wave + 4 * (k / CPG), cc = k % CPG;
+        uint32_t gi, cc;
+        chunk_of(k, gi, cc);
+        const bool fold = cc == 0 || (kChunkItems && k == 0);
         const int64_t tb = (int64_t)(gi * CPG + cc) * 32;
         const uint32_t st = lds_addr(wlds + (k % RG::kStages) * RG::kStage);
         const uint32_t meta = st + 2 * RG::kCodes;
@@ -581,7 +605,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
         u32x4 vm0 = ring_read<0>(a_vm);
         u32x4 vm1 = ring_read<64>(a_vm);
         u32x4 km0 = vm0, km1 = vm1, km2 = vm0, km3 = vm1, vm2 = vm0, vm3 = vm1;
-        if (cc == 0) {
+        if (fold) {
             km0 = ring_read<0>(a_km);
             km1 = ring_read<16>(a_km);
         }
@@ -624,7 +648,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
             wk1 = wk0;  // one 16-byte word group per lane at b = 2
             wv1 = wv0;
         }
-        if (cc == 0) {
+        if (fold) {
             // Fold the key scale into the query: B = hi/lo of q~_c * s_c, and
             // the zero point into beta_h = sum_c q~_c (z_c - 2^b s_c); with
             // G = 16 once per key group of the chunk.
