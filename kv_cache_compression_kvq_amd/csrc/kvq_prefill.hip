@@ -14,10 +14,13 @@
 // sums exp(S - lse) over the rows below it, so every column sum is produced by
 // one wavefront in a fixed order (no atomics).
 //
-// Matrix-core layout (v_mfma_f32_16x16x32_f16): S^T = K Q^T is computed, so a
-// lane of an S^T tile holds four keys of one query row; two key tiles give
-// exactly the eight keys one lane contributes to a 32-key k-step of P V. The
-// value operand is read from V^T in LDS with the same key order.
+// Matrix-core layouts. The forward kernel computes S^T = K Q^T on
+// v_mfma_f32_32x32x16_f16, so a lane of an S^T tile holds sixteen keys of one
+// query row, and O^T = V^T P^T on the same shape, so a lane's P values are
+// already its B operand and a lane's output accumulators all belong to its
+// own query row (rescaling needs no cross-lane exchange). The column-sum
+// kernel computes S^T on v_mfma_f32_16x16x32_f16, four keys of one row per
+// lane.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -30,6 +33,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int D = kHeadDim;
 constexpr int KB = 64;           // keys per block step
@@ -37,11 +41,14 @@ constexpr int KB = 64;           // keys per block step
 // row r at position c ^ v_swz(r). The value operand is read with the gfx950
 // transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
 // 4 r + s reads 8 bytes, and lane i receives element i of the 16 values read
-// by lanes 4 r' .. 4 r' + 3, for r' = 0..3. Lane (16 g + 4 r + s) reads key row
-// 4 g + r (+ 16 h + 32 s2), channels 16 nt + 4 s .. + 3, so lane (g, i) gets
-// channel 16 nt + i of keys 4 g + r' (+ ...): the B operand layout. The
-// swizzle spreads those 16 reads of a group over all 32 banks.
-__device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3) + 8 * ((r >> 2) & 1); }
+// by lanes 4 r' .. 4 r' + 3, for r' = 0..3. Lane (16 g + 4 r + s) reads key
+// row 16 k + 4 (g / 2) + r (and the row 8 below), channels 32 nt + 16 (g % 2)
+// + 4 s .. + 3, so lane l gets channel 32 nt + l % 32 of four consecutive
+// keys: the A operand layout of the 32x32x16 product. A 32-lane half reads
+// four rows r = 0..3 (mod 4) and chunks 4 nt .. 4 nt + 3; the swizzle puts
+// those 16 pieces on 16 distinct chunk positions (and each 16-lane group's 8
+// on 8 distinct positions mod 8), so the reads are free of bank conflicts.
+__device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3) + 8 * (r & 1); }
 // Lazy rescaling ("online softmax" with a threshold): a row's reference
 // maximum moves only when a logit exceeds it by more than this (log2 units),
 // so its probabilities stay below 2^8 in the fp16 operand.
@@ -150,7 +157,9 @@ struct PrefillArgs {
 
 // Block (query block x, unit y = b * Hkv + h_kv): 128 / r query rows of each of
 // the r query heads of the KV head. Wavefront w takes head w % r and the 32
-// rows (w / r) * 32 .. + 31 of the block (two 16-row tiles).
+// rows (w / r) * 32 .. + 31 of the block: lane l holds row (l % 32) of the
+// S^T tiles and of the output, the two 32-lane halves different keys
+// (S^T) or channels (O^T) of it.
 template <int R>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_fwd_kernel(PrefillArgs a) {
     constexpr int QR = 128 / R;  // query rows per block
@@ -173,33 +182,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const uint16_t* kunit = a.k + kvbase * D;  // this unit's rows; offsets below are 32-bit
     const uint16_t* vunit = a.v + kvbase * D;
     const float qs = a.qscale;
-    const int j = lane & 15, kb = lane >> 4;
+    const int j = lane & 31, h = lane >> 5;
+    const int row = row0 + j;  // this lane's query row
 
-    // query operands: tile rt, k-step kst: row row0 + 16 rt + j, channels
-    // 32 kst + 8 kb .. + 7 (zero rows past n)
-    half8 Qo[2][4];
+    // query operands (B of S^T), k-step kst: row `row`, channels 16 kst + 8 h
+    // .. + 7 (zero rows past n)
+    half8 Qo[8];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const int row = row0 + 16 * rt + j;
-#pragma unroll
-        for (int kst = 0; kst < 4; ++kst) {
-            uint4 w = make_uint4(0u, 0u, 0u, 0u);
-            if (row < n)
-                w = *reinterpret_cast<const uint4*>(a.q + (qbase + row) * D + 32 * kst + 8 * kb);
-            Qo[rt][kst] = __builtin_bit_cast(half8, w);
-        }
+    for (int kst = 0; kst < 8; ++kst) {
+        uint4 w = make_uint4(0u, 0u, 0u, 0u);
+        if (row < n) w = *reinterpret_cast<const uint4*>(a.q + (qbase + row) * D + 16 * kst + 8 * h);
+        Qo[kst] = __builtin_bit_cast(half8, w);
     }
-    floatx4 O[2][8];
+    // O^T tile nt: lane holds channels 32 nt + 8 (i / 4) + 4 h + i % 4 of `row`
+    floatx16 O[4];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) O[rt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};  // of row row0 + 16 rt + j
+        for (int i = 0; i < 16; ++i) O[nt][i] = 0.f;
+    // the row's reference maximum and this lane's part of its sum (the two
+    // halves hold different keys; they are added at the end)
+    float m = -INFINITY, l = 0.f;
 
     const int kend = n < q0 + QR ? n : q0 + QR;  // keys any row of the block sees
     const int nkb = (kend + KB - 1) / KB;
-    // tile staging: 64 keys x 128 channels of K and V copied to LDS, V then
-    // transposed through registers
     // this thread's copies (i = 0..3): key row p / 16 of the tile, p = tid + 256 i;
     // lane position p % 16 receives chunk (p % 16) ^ (row % 16) (K) or
     // (p % 16) ^ v_swz(row) (V).
@@ -238,11 +244,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
     };
     if (nkb > 0) fetch(0);
-    // lane parts of the value-operand reads: key row 4 g + r, 8-byte half s % 2
-    // of chunk 2 nt + s / 2 (swizzled per tile nt below)
+    // key-operand reads (A of S^T): key row 32 kt + j, chunk 2 kst + h at
+    // position (2 kst + h) ^ (j % 16)
+    // value-operand reads: lane (16 g + 4 r + s) reads key row 4 (g / 2) + r
+    // (+ 16 k, + 8), chunk 4 nt + 2 (g % 2) + s / 2, 8-byte half s % 2; the
+    // chunk's position is swizzled by v_swz(r) (rows differ from r by
+    // multiples of 4); the four tiles' lane offsets are fixed for the loop
     const int vg = lane >> 4, vr = (lane >> 2) & 3, vsl = lane & 3;
-    const int vrow = 4 * vg + vr, vsw = v_swz(vrow);
-    const uint32_t vlane = (uint32_t)(vrow * 256 + 8 * (vsl & 1));
+    const int vsw = v_swz(vr);
+    uint32_t vlane[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+        vlane[nt] = (uint32_t)((4 * (vg >> 1) + vr) * 256 + 16 * ((4 * nt + 2 * (vg & 1) + (vsl >> 1)) ^ vsw) +
+                               8 * (vsl & 1));
     for (int t = 0; t < nkb; ++t) {
         // every wavefront is done with tile t - 1 (whose buffers the next
         // copies refill), and tile t's copies have landed (the barrier's fence
@@ -252,120 +266,101 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         const int k0 = t * KB;
         if (k0 > row0 + 31 || row0 >= n) continue;  // every key of the tile is after this wave's rows
         const unsigned char* kt_lds = &ks[t & 1][0];
-        // S^T tiles: key tile kt, row tile rt; lane holds keys k0 + 16 kt + 4 kb + i
-        // of row row0 + 16 rt + j
-        floatx4 St[2][4];
+        // S^T tiles kt = 0, 1: lane holds keys k0 + 32 kt + 8 (i / 4) + 4 h + i % 4
+        // of `row`; the two tiles as interleaved independent chains
+        floatx16 St[2];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            half8 Ak[4];
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int kst = 0; kst < 4; ++kst)
-                Ak[kst] = *reinterpret_cast<const half8*>(
-                    kt_lds + (16 * kt + j) * 256 + 16 * ((4 * kst + kb) ^ j));
-            // the two row tiles as independent chains
-            St[0][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-            St[1][kt] = St[0][kt];
+            for (int i = 0; i < 16; ++i) St[kt][i] = 0.f;
 #pragma unroll
-            for (int kst = 0; kst < 4; ++kst)
+        for (int kst = 0; kst < 8; ++kst) {
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-                    St[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ak[kst], Qo[rt][kst], St[rt][kt], 0, 0, 0);
-        }
-        half8 Ap[2][2];  // P operands of the two 32-key k-steps
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int row = row0 + 16 * rt + j;
-            // the row's maximum logit over the tile, from the unscaled products
-            // (the scale is positive) with masked keys at -inf
-            float mx = -INFINITY;
-            if (k0 + KB - 1 <= row0 + 16 * rt && row0 + 16 * rt + 15 < n) {
-                // every key of the tile at or before every row of the row tile
-#pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, St[rt][kt][i]);
-            } else {
-#pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = k0 + 16 * kt + 4 * kb + i;
-                        if (key > row || key >= n || row >= n) St[rt][kt][i] = -INFINITY;
-                        mx = fmaxf(mx, St[rt][kt][i]);
-                    }
+            for (int kt = 0; kt < 2; ++kt) {
+                const half8 Ak = *reinterpret_cast<const half8*>(
+                    kt_lds + (32 * kt + j) * 256 + 16 * ((2 * kst + h) ^ (j & 15)));
+                St[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ak, Qo[kst], St[kt], 0, 0, 0);
             }
-            mx = max_x32(max_x16(mx)) * qs;
-            // the reference maximum moves (and the row's sums are rescaled) only
-            // when some row of the wavefront passes its own by more than tau
-            if (__any(mx > m[rt] + kLazyTau)) {
-                const float mnew = mx > m[rt] + kLazyTau ? mx : m[rt];
-                // rows with nothing unmasked yet keep alpha = 1 and p = 0
-                const float alpha = m[rt] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[rt] - mnew);
-                l[rt] *= alpha;
-                m[rt] = mnew;
-                // rescale the output rows 4 kb + i of the tile by their rows' alpha
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float ai = __shfl(alpha, 4 * kb + i);
-#pragma unroll
-                    for (int nt = 0; nt < 8; ++nt) O[rt][nt][i] *= ai;
-                }
-            }
-            const float nmu = m[rt] == -INFINITY ? 0.f : -m[rt];
-            float ps = 0.f;
-            float p[4][4];
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[kt][i] = __builtin_amdgcn_exp2f(fmaf(St[rt][kt][i], qs, nmu));
-                    ps += p[kt][i];
-                }
-            ps = sum_x32(sum_x16(ps));
-            l[rt] += ps;
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-                Ap[rt][s2] = half8{(_Float16)p[2 * s2][0], (_Float16)p[2 * s2][1],
-                                   (_Float16)p[2 * s2][2], (_Float16)p[2 * s2][3],
-                                   (_Float16)p[2 * s2 + 1][0], (_Float16)p[2 * s2 + 1][1],
-                                   (_Float16)p[2 * s2 + 1][2], (_Float16)p[2 * s2 + 1][3]};
         }
-        // O += P V: value operand of tile nt, k-step s2: channel 16 nt + j, keys
-        // k0 + 32 s2 + 4 kb + 0..3 and k0 + 32 s2 + 16 + 4 kb + 0..3
+        // the row's maximum logit over the tile, from the unscaled products
+        // (the scale is positive) with masked keys at -inf
+        float mx = -INFINITY;
+        if (k0 + KB - 1 <= row0 && row0 + 31 < n) {
+            // every key of the tile at or before every row of the wavefront
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, St[kt][i]);
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = k0 + 32 * kt + 8 * (i >> 2) + 4 * h + (i & 3);
+                    if (key > row || key >= n || row >= n) St[kt][i] = -INFINITY;
+                    mx = fmaxf(mx, St[kt][i]);
+                }
+        }
+        mx = max_x32(mx) * qs;
+        // the reference maximum moves (and the row's sums are rescaled) only
+        // when some row of the wavefront passes its own by more than tau
+        if (__any(mx > m + kLazyTau)) {
+            const float mnew = mx > m + kLazyTau ? mx : m;
+            // rows with nothing unmasked yet keep alpha = 1 and p = 0
+            const float alpha = m == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+            l *= alpha;
+            m = mnew;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) O[nt][i] *= alpha;
+        }
+        const float nmu = m == -INFINITY ? 0.f : -m;
+        // P^T operands of the four 16-key k-steps: k-step s takes S^T tile
+        // s / 2, values 8 (s % 2) .. + 7, i.e. keys 16 s + 4 h + 0..3 and
+        // 16 s + 8 + 4 h + 0..3
+        half8 Bp[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = __builtin_amdgcn_exp2f(fmaf(St[s >> 1][8 * (s & 1) + e], qs, nmu));
+                l += p[e];
+            }
+            Bp[s] = half8{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3],
+                          (_Float16)p[4], (_Float16)p[5], (_Float16)p[6], (_Float16)p[7]};
+        }
+        // O^T += V^T P^T: value operand of tile nt, k-step s: channel 32 nt + j,
+        // keys 16 s + 4 h + 0..3 and 16 s + 8 + 4 h + 0..3
         const unsigned char* vtile = &vs[t & 1][0];
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const unsigned char* vb = vtile + vlane + 16 * ((2 * nt + (vsl >> 1)) ^ vsw);
+        for (int s = 0; s < 4; ++s) {
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                // keys 32 s2 + 4 kb + 0..3 (h = 0) and 32 s2 + 16 + 4 kb + 0..3 (h = 1)
+            for (int nt = 0; nt < 4; ++nt) {
+                const unsigned char* vb = vtile + vlane[nt] + (16 * s) * 256;
                 const half4 v0 = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) short4_t*)(vb + (32 * s2) * 256)));
+                    (__attribute__((address_space(3))) short4_t*)vb));
                 const half4 v1 = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) short4_t*)(vb + (32 * s2 + 16) * 256)));
-                const half8 Bv = half8{v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-                    O[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ap[rt][s2], Bv, O[rt][nt], 0, 0, 0);
+                    (__attribute__((address_space(3))) short4_t*)(vb + 8 * 256)));
+                const half8 Av = half8{v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                O[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Av, Bp[s], O[nt], 0, 0, 0);
             }
         }
     }
-    // outputs: rows 4 kb + i of each tile, channel 16 nt + j; log-sum-exp per row
+    // outputs: channels 32 nt + 8 (i / 4) + 4 h .. + 3 of `row`; log-sum-exp per row
+    const float lt = sum_x32(l);
+    if (row < n) {
+        const float linv = lt > 0.f ? 1.0f / lt : 0.f;
+        float* o = a.out + (qbase + row) * D + 4 * h;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        const float linv = l[rt] > 0.f ? 1.0f / l[rt] : 0.f;
+        for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = row0 + 16 * rt + 4 * kb + i;
-            const float li = __shfl(linv, 4 * kb + i);
-            if (row < n) {
-                float* o = a.out + (qbase + row) * D;
-#pragma unroll
-                for (int nt = 0; nt < 8; ++nt) o[16 * nt + j] = O[rt][nt][i] * li;
-            }
-        }
-        const int row = row0 + 16 * rt + j;
-        if (kb == 0 && row < n) a.lse[qbase + row] = m[rt] + log2f(l[rt]);
+            for (int ig = 0; ig < 4; ++ig)
+                *reinterpret_cast<float4*>(o + 32 * nt + 8 * ig) =
+                    make_float4(O[nt][4 * ig] * linv, O[nt][4 * ig + 1] * linv, O[nt][4 * ig + 2] * linv,
+                                O[nt][4 * ig + 3] * linv);
+        if (h == 0) a.lse[qbase + row] = m + log2f(lt);
     }
 }
 
