@@ -273,15 +273,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) St[kt][i] = 0.f;
+        // key operands requested two k-steps ahead of their products
+        half8 Ak[8][2];
 #pragma unroll
-        for (int kst = 0; kst < 8; ++kst) {
+        for (int kst = 0; kst < 8; ++kst)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const half8 Ak = *reinterpret_cast<const half8*>(
+            for (int kt = 0; kt < 2; ++kt)
+                Ak[kst][kt] = *reinterpret_cast<const half8*>(
                     kt_lds + (32 * kt + j) * 256 + 16 * ((2 * kst + h) ^ (j & 15)));
-                St[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ak, Qo[kst], St[kt], 0, 0, 0);
-            }
+#pragma unroll
+        for (int kst = 0; kst < 8; ++kst)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+                St[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ak[kst][kt], Qo[kst], St[kt], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
         // the row's maximum logit over the tile, from the unscaled products
         // (the scale is positive) with masked keys at -inf
         float mx = -INFINITY;
@@ -334,19 +345,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         // O^T += V^T P^T: value operand of tile nt, k-step s: channel 32 nt + j,
         // keys 16 s + 4 h + 0..3 and 16 s + 8 + 4 h + 0..3
         const unsigned char* vtile = &vs[t & 1][0];
+        half4 Vr[4][4][2];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 const unsigned char* vb = vtile + vlane[nt] + (16 * s) * 256;
-                const half4 v0 = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                Vr[s][nt][0] = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) short4_t*)vb));
-                const half4 v1 = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                Vr[s][nt][1] = __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) short4_t*)(vb + 8 * 256)));
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const half4 v0 = Vr[s][nt][0], v1 = Vr[s][nt][1];
                 const half8 Av = half8{v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
                 O[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Av, Bp[s], O[nt], 0, 0, 0);
             }
         }
+        // value reads: the first k-step's 8 first, then each k-step's products
+        // with the next k-step's reads behind them
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
     }
     // outputs: channels 32 nt + 8 (i / 4) + 4 h .. + 3 of `row`; log-sum-exp per row
     const float lt = sum_x32(l);
