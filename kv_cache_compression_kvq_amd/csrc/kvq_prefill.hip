@@ -392,45 +392,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
 }
 
-// Column sums: block (key block x of 64 keys, unit y); wavefront w owns keys
-// k0 + 16 w .. + 15 (k0 = 64 x). For each of the r query heads of the KV head,
-// the query rows from k0 on pass through a ring of LDS stages, 64 rows with
-// their log-sum-exp each, copied straight from memory two stages ahead of
-// use; each wavefront adds exp2(s - lse_row) of its keys over the stage's
-// rows at or after them: every column sum is produced by one wavefront in a
-// fixed order.
+// Column sums: block (key block x of 64 keys, query head y = unit * r + h).
+// The query rows of the head from the block's first key on pass through a
+// ring of LDS stages, 64 rows with their log-sum-exp each, copied straight
+// from memory two stages ahead of use. Wavefront w owns keys k0 + 32 (w % 2)
+// .. + 31 and rows 32 (w / 2) .. + 31 of every stage: it recomputes S^T for
+// them on v_mfma_f32_32x32x16_f16 (a lane holds sixteen keys of one row) and
+// adds exp2(s - lse_row) over the rows at or after each key. The two
+// wavefronts of a key half are added in a fixed order at the end, so every
+// column sum is produced in a fixed order (no atomics).
 template <int R>
 __global__ __launch_bounds__(256) void prefill_colsum_kernel(PrefillArgs a) {
     constexpr int QT = 64;                       // query rows per stage
     constexpr int kStages = 3;                   // stages in flight
     constexpr int kTileBytes = QT * D * 2;       // 16 KB of query rows
     __shared__ __align__(16) unsigned char ring[kStages][kTileBytes + QT * 4];
+    __shared__ float half_sums[2][32];           // the second row half's sums per key half
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = a.n;
     int bx, by;
     die_local_block(bx, by);
     const int unit = by / R, hh = by % R, b = unit / a.n_kv_heads, hkv = unit % a.n_kv_heads;
-    const int k0 = bx * KB, kt0 = k0 + 16 * wave;  // first key of the block, of this wavefront
+    const int kg = wave & 1, rh = wave >> 1;     // key half, row half
+    const int k0 = bx * KB, kt0 = k0 + 32 * kg;  // first key of the block, of this wavefront
     const int64_t qhead = (int64_t)b * a.n_kv_heads * R + hkv * R + hh;
     const int64_t kvbase = (int64_t)unit * n;
-    const uint16_t* kunit = a.k + kvbase * D;  // this unit's rows; offsets below are 32-bit
-    const uint16_t* vunit = a.v + kvbase * D;
     const float qs = a.qscale;
-    const int j = lane & 15, kb = lane >> 4;
-    // key operands (A of S^T): key kt0 + j, channels 32 kst + 8 kb .. + 7
-    half8 Ak[4];
+    const int j = lane & 31, h = lane >> 5;
+    // key operands (A of S^T): key kt0 + j, channels 16 kst + 8 h .. + 7
+    half8 Ak[8];
 #pragma unroll
-    for (int kst = 0; kst < 4; ++kst) {
+    for (int kst = 0; kst < 8; ++kst) {
         uint4 w = make_uint4(0u, 0u, 0u, 0u);
         if (kt0 + j < n)
-            w = *reinterpret_cast<const uint4*>(a.k + (kvbase + kt0 + j) * D + 32 * kst + 8 * kb);
+            w = *reinterpret_cast<const uint4*>(a.k + (kvbase + kt0 + j) * D + 16 * kst + 8 * h);
         Ak[kst] = __builtin_bit_cast(half8, w);
     }
-    float cs[4] = {0.f, 0.f, 0.f, 0.f};  // keys kt0 + 4 kb + i, partial over this lane's rows
+    // keys kt0 + 8 (i / 4) + 4 h + i % 4, partial over this lane's rows
+    float cs[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cs[i] = 0.f;
     const int t_first = k0 / QT, ntiles = (n + QT - 1) / QT, iters = ntiles - t_first;
     // Stage it (rows r0 .. r0 + 63 of query head hh): 64 rows of 256 B
     // with the 16-byte chunk c of row r stored at position c ^ (r % 16), so the
-    // sixteen rows of an operand read sit on distinct banks, then the rows'
+    // rows of an operand read sit on distinct banks, then the rows'
     // log-sum-exp. Each wavefront copies a quarter of both (five copies), and
     // waits for its own copies of a stage before the barrier that publishes it.
     const int64_t qbase = qhead * n;
@@ -463,6 +468,13 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(PrefillArgs a) {
             lds_load4(a.lse + qbase + rr, st + kTileBytes);
         }
     };
+    // query-operand reads (B of S^T): row 32 rh + j of a stage, chunk 2 kst + h
+    // at position (2 kst + h) ^ (j % 16); byte offsets from the stage's start
+    uint32_t qoff[8];
+#pragma unroll
+    for (int kst = 0; kst < 8; ++kst)
+        qoff[kst] = (uint32_t)((32 * rh + j) * 256 + 16 * ((2 * kst + h) ^ (j & 15)));
+    const uint32_t loff = (uint32_t)(kTileBytes + 4 * (32 * rh + j));
     for (int p = 0; p < kStages - 1 && p < iters; ++p) issue(p);
     for (int it = 0; it < iters; ++it) {
         bare_barrier();  // stage (it - 1) % kStages is no longer read
@@ -473,101 +485,61 @@ __global__ __launch_bounds__(256) void prefill_colsum_kernel(PrefillArgs a) {
         else if (later == 1) wait_vm<5>();
         else wait_vm<0>();
         bare_barrier();  // every wavefront's copies of stage it have landed
-        const int r0 = (t_first + it) * QT;
-        if (kt0 >= n) continue;
+        const int rb = (t_first + it) * QT + 32 * rh;  // this wavefront's first row of the stage
+        if (kt0 >= n || rb + 31 < kt0 || rb >= n) continue;  // no row at or after a key, or past n
         const uint32_t st = lds_addr(&ring[it % kStages][0]);
-        if (r0 >= kt0 + 15 && r0 + QT - 1 < n && kt0 + 15 < n) {
-            // every row of the stage at or after every key of the wavefront:
-            // the four row tiles' products as four independent chains
-            u32x4 bw[4][4];
-            uint32_t lsw[4];
+        u32x4 bw[8];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const int row_l = 16 * rt + j;
+        for (int kst = 0; kst < 8; ++kst) bw[kst] = lds_read16(st + qoff[kst]);
+        uint32_t lsw = lds_read4(st + loff);
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(bw[0]), "+v"(bw[1]), "+v"(bw[2]), "+v"(bw[3]), "+v"(bw[4]), "+v"(bw[5]),
+                       "+v"(bw[6]), "+v"(bw[7]), "+v"(lsw)
+                     :
+                     : "memory");
+        floatx16 acc;
 #pragma unroll
-                for (int kst = 0; kst < 4; ++kst)
-                    bw[rt][kst] = lds_read16(st + row_l * 256 + (((4 * kst + kb) ^ (row_l & 15)) * 16));
-                lsw[rt] = lds_read4(st + kTileBytes + 4 * row_l);
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(bw[0][0]), "+v"(bw[0][1]), "+v"(bw[0][2]), "+v"(bw[0][3]),
-                           "+v"(bw[1][0]), "+v"(bw[1][1]), "+v"(bw[1][2]), "+v"(bw[1][3]),
-                           "+v"(lsw[0]), "+v"(lsw[1])
-                         :
-                         : "memory");
-            asm volatile(""
-                         : "+v"(bw[2][0]), "+v"(bw[2][1]), "+v"(bw[2][2]), "+v"(bw[2][3]),
-                           "+v"(bw[3][0]), "+v"(bw[3][1]), "+v"(bw[3][2]), "+v"(bw[3][3]),
-                           "+v"(lsw[2]), "+v"(lsw[3])
-                         :
-                         : "memory");
-            floatx4 acc[4];
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int kst = 0; kst < 8; ++kst)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ak[kst], __builtin_bit_cast(half8, bw[kst]), acc, 0, 0,
+                                                         0);
+        const float nl = -__builtin_bit_cast(float, lsw);
+        const int row = rb + j;
+        if (rb >= kt0 + 31 && rb + 31 < n && kt0 + 31 < n) {
+            // every row of the wavefront at or after every key of it
 #pragma unroll
-            for (int kst = 0; kst < 4; ++kst)
+            for (int i = 0; i < 16; ++i) cs[i] += __builtin_amdgcn_exp2f(fmaf(acc[i], qs, nl));
+        } else {
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        Ak[kst], __builtin_bit_cast(half8, bw[rt][kst]), acc[rt], 0, 0, 0);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const float lsr = __builtin_bit_cast(float, lsw[rt]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) cs[i] += __builtin_amdgcn_exp2f(fmaf(acc[rt][i], qs, -lsr));
-            }
-            continue;
-        }
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const int rb = r0 + 16 * rt;  // first row of the 16-row tile
-            if (rb + 15 < kt0 || rb >= n) continue;  // every row before this wave's keys, or past n
-            const int row_l = 16 * rt + j;
-            u32x4 bw[4];
-#pragma unroll
-            for (int kst = 0; kst < 4; ++kst)
-                bw[kst] = lds_read16(st + row_l * 256 + (((4 * kst + kb) ^ (row_l & 15)) * 16));
-            uint32_t lsw = lds_read4(st + kTileBytes + 4 * row_l);
-            asm volatile("s_waitcnt lgkmcnt(0)"
-                         : "+v"(bw[0]), "+v"(bw[1]), "+v"(bw[2]), "+v"(bw[3]), "+v"(lsw)
-                         :
-                         : "memory");
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kst = 0; kst < 4; ++kst)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ak[kst], __builtin_bit_cast(half8, bw[kst]),
-                                                             acc, 0, 0, 0);
-            const int row = rb + j;
-            const float lsr = __builtin_bit_cast(float, lsw);
-            if (rb >= kt0 + 15 && rb + 15 < n && kt0 + 15 < n) {
-                // every row of the tile at or after every key of the wave
-#pragma unroll
-                for (int i = 0; i < 4; ++i) cs[i] += __builtin_amdgcn_exp2f(fmaf(acc[i], a.qscale, -lsr));
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = kt0 + 4 * kb + i;
-                    if (key <= row && row < n && key < n)
-                        cs[i] += __builtin_amdgcn_exp2f(fmaf(acc[i], a.qscale, -lsr));
-                }
+            for (int i = 0; i < 16; ++i) {
+                const int key = kt0 + 8 * (i >> 2) + 4 * h + (i & 3);
+                if (key <= row && row < n && key < n) cs[i] += __builtin_amdgcn_exp2f(fmaf(acc[i], qs, nl));
             }
         }
     }
-    // sum over the 16 rows of the lane group (lanes j = 0..15 of each kb)
+    // sum over the 32 rows of the lane half (lanes j = 0..31 of each h)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 16; ++i) {
         float x = cs[i];
+        x += __shfl_xor(x, 16);
         x += __shfl_xor(x, 8);
         x += __shfl_xor(x, 4);
         x += __shfl_xor(x, 2);
         x += __shfl_xor(x, 1);
         cs[i] = x;
     }
-    if (j == 0) {
+    // the second row half's sums, then the first half adds them (fixed order)
+    if (rh == 1 && j == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = kt0 + 4 * kb + i;
-            if (key < n) a.part[qhead * n + key] = cs[i];
+        for (int i = 0; i < 16; ++i) half_sums[kg][8 * (i >> 2) + 4 * h + (i & 3)] = cs[i];
+    }
+    __syncthreads();
+    if (rh == 0 && j == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int kl = 8 * (i >> 2) + 4 * h + (i & 3), key = kt0 + kl;
+            if (key < n) a.part[qhead * n + key] = cs[i] + half_sums[kg][kl];
         }
     }
 }
