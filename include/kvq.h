@@ -165,7 +165,8 @@ typedef struct kvq_config {
  *   sink_k    fp16 [U][S][d] the attention-sink rows; sink_v likewise
  *   evict     uint32 [U][ceil((max_tokens - S) / 32)]: bit i of word c set when
  *             token S + 32c + i was evicted (kvq_evict_step)
- *   evict_count int32 [U]: evicted tokens per unit
+ *   evict_count int32 [U]: evicted tokens per unit, followed (8-byte aligned)
+ *             by uint64 [U][2] of kvq_evict_step scratch, zero between calls
  *   fp8_scales fp32 [Hkv][2] (b = 8): key and value scale per KV head, 1.0
  *             after kvq_cache_init
  * At b = 8, kq / vq hold one E4M3 byte per element (4 KB per chunk each) in

@@ -92,7 +92,7 @@ Layout layout_of(const kvq_config* c) {
         U * S * d * 2,                // sink_k
         U * S * d * 2,                // sink_v
         U * evict_words_of(c) * 4,    // evict
-        U * 4,                        // evict_count
+        (U + 1) / 2 * 8 + U * 16,     // evict_count, then the eviction step's scratch
         (uint64_t)c->n_kv_heads * 8,  // fp8_scales
     };
     uint64_t o = 0;

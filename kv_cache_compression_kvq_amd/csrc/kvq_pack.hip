@@ -106,6 +106,14 @@ __device__ __forceinline__ const uint16_t* src_row(const uint16_t* ring, const u
                      : fresh + ((int64_t)u * n_new + (t - t_old)) * D;
 }
 
+// The eviction step's per-unit scratch, after the eviction counts (8-byte
+// aligned): word 0 the complement of the best (key, index) found so far (an
+// atomic maximum), word 1 the count of the unit's workgroups that are done.
+// Both are zero between calls: the unit's last workgroup resets them.
+__device__ __forceinline__ uint64_t* evict_scratch(const CacheView& v) {
+    return reinterpret_cast<uint64_t*>(v.evict_count + ((v.units + 1) & ~1));
+}
+
 // Counters and pool masks start at zero. With G = 16 the key and value
 // scale/zero words are zeroed too: a chunk whose second group is not yet
 // quantized is read by the decoder with that half masked out, and its
@@ -116,16 +124,19 @@ __global__ void init_kernel(CacheView v) {
     const int64_t nv = v.group == 16 ? (int64_t)v.units * v.chunks * (D / 16) * kChunk : 0;
     const int64_t ne = (int64_t)v.units * v.evict_words, nu = v.units;
     const int64_t n1 = nc + nm, n2 = n1 + nk, n3 = n2 + nv, n4 = n3 + ne, n5 = n4 + nu;
+    const int64_t n6 = n5 + 4 * nu;  // the eviction step's scratch, as 32-bit words
     if (v.bits == 8 && blockIdx.x == 0 && threadIdx.x < 2 * v.n_kv_heads)
         v.fp8_scales[threadIdx.x] = 1.0f;  // FP8 scales: 1.0 until set
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n5;
+    uint32_t* esc = reinterpret_cast<uint32_t*>(evict_scratch(v));
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n6;
          i += (int64_t)gridDim.x * blockDim.x) {
         if (i < nc) v.counters[i] = 0;
         else if (i < n1) v.mask[i - nc] = 0;
         else if (i < n2) v.kmeta[i - n1] = 0;
         else if (i < n3) v.vmeta[i - n2] = 0;
         else if (i < n4) v.evict[i - n3] = 0;
-        else v.evict_count[i - n4] = 0;
+        else if (i < n5) v.evict_count[i - n4] = 0;
+        else esc[i - n5] = 0;
     }
 }
 
@@ -1131,14 +1142,19 @@ __global__ __launch_bounds__(256) void debug_view_kernel(CacheView v, int64_t T,
     }
 }
 
-// One H2O eviction step: one 1024-thread block per unit. If more than
-// `budget` tokens are live, the live token in [S, T - recent) with the lowest
-// score is evicted ("H2O: Heavy-Hitter Oracle", greedy eviction; "KV cache
-// quantization and eviction", h2o_evict). Scores compare through an
-// order-preserving key with every NaN lowest and -0 equal to +0; the smallest
-// (key, index) wins, so ties go to the older token. Each thread reads four
-// consecutive scores at a time (16-byte loads when the row allows it), all of
-// its loads in flight before any is compared.
+// One H2O eviction step. If more than `budget` tokens of a unit are live,
+// the live token in [S, T - recent) with the lowest score is evicted ("H2O:
+// Heavy-Hitter Oracle", greedy eviction; "KV cache quantization and
+// eviction", h2o_evict). Scores compare through an order-preserving key with
+// every NaN lowest and -0 equal to +0; the smallest (key, index) wins, so ties
+// go to the older token. A unit's range is cut into slices of
+// kEvictThreads x kEvictGroups 4-token groups, one 256-thread workgroup each
+// (every compute unit pulls part of the scores: one workgroup per unit would
+// leave most idle). Each thread reads four consecutive scores at a time
+// (16-byte loads when the row allows it), all of its loads in flight before
+// any is compared. A workgroup folds its minimum into the unit's scratch word
+// with an atomic maximum of the complement, then takes a ticket; the unit's
+// last workgroup reads the result, resets the scratch and marks the token.
 __device__ __forceinline__ uint64_t evict_key(float f, int64_t t) {
     uint32_t b = __builtin_bit_cast(uint32_t, f);
     uint32_t key;
@@ -1151,28 +1167,31 @@ __device__ __forceinline__ uint64_t evict_key(float f, int64_t t) {
     return ((uint64_t)key << 32) | (uint64_t)t;
 }
 
-constexpr int kEvictThreads = 1024;
+constexpr int kEvictThreads = 256;
+constexpr int kEvictGroups = 8;  // 4-token groups per thread
+constexpr int64_t kEvictSlice = (int64_t)kEvictThreads * kEvictGroups;
 __global__ __launch_bounds__(kEvictThreads) void evict_step_kernel(CacheView v, int64_t T,
                                                                    const float* acc, int32_t budget,
                                                                    int32_t recent) {
-    const int u = blockIdx.x, tid = threadIdx.x;
+    const int u = blockIdx.y, tid = threadIdx.x;
     const int64_t live = T - v.evict_count[u];
-    if (live <= budget) return;  // uniform over the block
+    if (live <= budget) return;  // uniform over the unit's workgroups
     const int64_t S = v.sinks, end = T - recent;
     const uint32_t* ev = v.evict + (int64_t)u * v.evict_words;
     const float* sc = acc + (int64_t)u * T;
     uint64_t best = ~0ull;
-    // groups of 4 tokens t = 4 g .. 4 g + 3 (sequence indices), 8 groups per
-    // thread and pass
+    // groups of 4 tokens t = 4 g .. 4 g + 3 (sequence indices); this
+    // workgroup's slice starts at group gs
     const int64_t g_first = S / 4, g_end = (end + 3) / 4;
+    const int64_t gs = g_first + (int64_t)blockIdx.x * kEvictSlice;
     const bool aligned = (T % 4) == 0;  // row start 16-byte aligned
     const bool any_evicted = v.evict_count[u] != 0;
-    for (int64_t g0 = g_first + tid; g0 < g_end; g0 += 8 * kEvictThreads) {
-        float4 x[8];
-        uint32_t ew0[8], ew1[8];  // eviction words of the group's first and last token
+    {
+        float4 x[kEvictGroups];
+        uint32_t ew0[kEvictGroups], ew1[kEvictGroups];  // eviction words of a group's first and last token
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int64_t g = g0 + (int64_t)k * kEvictThreads;
+        for (int k = 0; k < kEvictGroups; ++k) {
+            const int64_t g = gs + tid + (int64_t)k * kEvictThreads;
             if (g < g_end && aligned && 4 * g + 3 < T) {
                 x[k] = reinterpret_cast<const float4*>(sc)[g];
             } else {
@@ -1187,8 +1206,8 @@ __global__ __launch_bounds__(kEvictThreads) void evict_step_kernel(CacheView v, 
             ew1[k] = any_evicted && g < g_end && tb >= 0 ? ev[tb >> 5] : 0u;
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int64_t g = g0 + (int64_t)k * kEvictThreads;
+        for (int k = 0; k < kEvictGroups; ++k) {
+            const int64_t g = gs + tid + (int64_t)k * kEvictThreads;
             if (g >= g_end) break;
             const float y[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
 #pragma unroll
@@ -1213,11 +1232,24 @@ __global__ __launch_bounds__(kEvictThreads) void evict_step_kernel(CacheView v, 
     if (tid == 0) {
         uint64_t b = wbest[0];
         for (int w = 1; w < kEvictThreads / 64; ++w) b = wbest[w] < b ? wbest[w] : b;
-        if (b != ~0ull) {
-            const int64_t tau = (int64_t)(b & 0xFFFFFFFFu) - S;
-            uint32_t* word = v.evict + (int64_t)u * v.evict_words + (tau >> 5);
-            *word |= 1u << (tau & 31);
-            v.evict_count[u] += 1;
+        uint64_t* scr = evict_scratch(v) + 2 * u;
+        // device-scope atomics: performed where every die sees them; the
+        // maximum has returned (so it is performed) before the ticket is taken
+        const uint64_t prev =
+            __hip_atomic_fetch_max(&scr[0], ~b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("" ::"v"(prev) : "memory");
+        const uint64_t ticket =
+            __hip_atomic_fetch_add(&scr[1], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (ticket == gridDim.x - 1) {
+            // the unit's last workgroup: every other one has folded its minimum
+            const uint64_t nb = __hip_atomic_exchange(&scr[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&scr[1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (nb != 0ull) {
+                const int64_t tau = (int64_t)((~nb) & 0xFFFFFFFFu) - S;
+                uint32_t* word = v.evict + (int64_t)u * v.evict_words + (tau >> 5);
+                *word |= 1u << (tau & 31);
+                v.evict_count[u] += 1;
+            }
         }
     }
 }
@@ -1420,8 +1452,11 @@ int launch_evict_step(const CacheView& v, int64_t T, const float* acc, int32_t b
                       int32_t recent, void* stream) {
     (void)hipGetLastError();  // an error left by an earlier call is not this call's
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(evict_step_kernel, dim3(v.units), dim3(kEvictThreads), 0, s, v, T, acc,
-                       budget, recent);
+    // slices of the groups [S / 4, (T - recent + 3) / 4), at least one per unit
+    const int64_t groups = (T - recent + 3) / 4 - v.sinks / 4;
+    const int64_t slices = groups > kEvictSlice ? (groups + kEvictSlice - 1) / kEvictSlice : 1;
+    hipLaunchKernelGGL(evict_step_kernel, dim3((unsigned)slices, v.units), dim3(kEvictThreads), 0, s, v,
+                       T, acc, budget, recent);
     return (int)hipGetLastError();
 }
 
