@@ -124,3 +124,36 @@ def _ws_after_step(h):
     S = nxt.cfg.sinks
     nxt.n_quant = max(0, (nxt.tokens - S - nxt.cfg.residual) // nxt.cfg.group * nxt.cfg.group)
     return abi.decode_workspace(nxt, True)
+
+
+def test_eviction_step_over_several_slices():
+    """Rows of 20000 tokens: the step's scan is cut into slices of 8192 tokens,
+    one workgroup each, whose minima meet in a per-unit scratch word. The
+    evicted token must still be the oracle's first-occurrence argmin when the
+    minimum or its ties lie in different slices, when NaN or -0 / +0 decide,
+    and when the lowest scores sit among the sinks or in the recent window;
+    six calls in a row also check that each leaves the scratch clean."""
+    w = _w(tokens=20000)
+    T, S = w.tokens, w.sinks
+    K, V = synth.all_kv(w, n=T)
+    gc = H.GpuCache(w, max_tokens=T)
+    gc.append(K, V)
+    units = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
+    s = np.random.default_rng(11).standard_exponential((w.batch, w.n_kv_heads, T)).astype(np.float32)
+    s[0, 0, 9000] = s[0, 0, 17000] = 1e-9   # equal minima in slices 1 and 2
+    s[0, 1, 18000] = np.nan                  # NaN ranks lowest, last slice
+    s[1, 0, 100] = -0.0                      # -0 == +0: the older one goes first
+    s[1, 0, 12000] = 0.0
+    s[1, 1, T - 5] = -1.0                    # recent window: not eligible
+    s[1, 1, 2] = -2.0                        # sink: not eligible
+    acc = torch.from_numpy(s).to("cuda")
+    live = {key: np.ones(T, dtype=bool) for key in units}
+    budget, recent = T - 10, 64
+    for step in range(6):
+        abi.evict_step(gc.h, acc, budget, recent)
+        torch.cuda.synchronize()
+        for (b, h) in units:
+            assert O.h2o_evict_one(s[b, h], live[(b, h)], budget, recent, S) >= 0
+        st = gc.state()
+        for u, key in enumerate(units):
+            assert np.array_equal(st["live"][u].astype(bool), live[key]), f"step {step} unit {key}"
