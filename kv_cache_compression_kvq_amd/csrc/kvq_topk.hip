@@ -33,6 +33,7 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 2048;  // histogram bins (11-bit digits)
 constexpr int kCand = 4096;  // candidate list after the first digit (long rows)
+constexpr int kFast = 512;   // first-digit bin resolved by one wavefront (register rows)
 constexpr int kMaxRegKeys = 32 * kThreads;  // rows held in registers
 
 // Order-preserving key of a score, in [0, 0xFF800000]: -0 and +0 compare
@@ -142,6 +143,7 @@ __global__ __launch_bounds__(kThreads) void topk_reg_kernel(const float* scores,
     __shared__ __align__(16) uint32_t hist[3][kBins];  // one per digit pass
     __shared__ uint32_t sel[2];                       // chosen digit, keys still needed
     __shared__ uint32_t wmin[kWaves], wmax[kWaves], cnt_gt[kWaves], cnt_eq[kWaves], tau_sh;
+    __shared__ uint32_t cand[kFast], ncand;           // keys of the first digit's bin
     const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = T - w;
     const float* sc = scores + (int64_t)row * T;
@@ -186,6 +188,7 @@ __global__ __launch_bounds__(kThreads) void topk_reg_kernel(const float* scores,
     }
     for (int i = tid; i < 3 * kBins / 4; i += kThreads)
         reinterpret_cast<uint4*>(&hist[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (tid == 0) ncand = 0;
     // range of the row's keys (slots past n take no part)
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
@@ -257,6 +260,68 @@ __global__ __launch_bounds__(kThreads) void topk_reg_kernel(const float* scores,
         need = sel[1];
         hi = lo;
         ++pass;
+        if (pass == 1 && hi > 0) {
+            // The keys of the chosen bin (a few hundred on H2O scores) are
+            // copied to an LDS list, and when they fit, one wavefront resolves
+            // the remaining hi bits on them bit by bit from the top, with one
+            // compare and ballot per held candidate and bit: no histogram
+            // passes over the registers, whose atomics collide on keys that
+            // lie close together.
+            const uint32_t lmask = (1u << hi) - 1u;
+#pragma unroll
+            for (int j = 0; j < kJ; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const bool m = (key[j][c] >> hi) == pref;
+                    const uint64_t bm = __ballot(m);
+                    if (bm) {
+                        const int leader = __builtin_ctzll(bm);
+                        uint32_t base = 0;
+                        if (lane == leader) base = atomicAdd(&ncand, (uint32_t)__popcll(bm));
+                        base = __builtin_amdgcn_readlane(base, leader);
+                        const uint32_t at = base + rank_in(bm);
+                        if (m && at < kFast) cand[at] = key[j][c] & lmask;
+                    }
+                }
+            __syncthreads();
+            const uint32_t nc = ncand;
+            if (nc <= kFast) {
+                if (wave == 0) {
+                    constexpr int kPer = kFast / 64;
+                    const int held = (int)(nc + 63) / 64;  // slots that hold candidates
+                    uint32_t cv[kPer];
+#pragma unroll
+                    for (int i = 0; i < kPer; ++i) {
+                        const uint32_t at = (uint32_t)(lane + 64 * i);
+                        // past the list: all ones above bit hi, never a match
+                        cv[i] = at < nc ? cand[at] : 0xFFFFFFFFu;
+                    }
+                    uint32_t sofar = 0, nd = need;  // the chosen bits above b
+                    for (int b = hi - 1; b >= 0; --b) {
+                        // candidates whose bits above b are sofar and whose bit b is set
+                        const uint32_t want = (sofar << 1) | 1u;
+                        uint32_t ones = 0;
+#pragma unroll
+                        for (int i = 0; i < kPer; ++i)
+                            if (i < held) ones += (uint32_t)__popcll(__ballot((cv[i] >> b) == want));
+                        if (nd <= ones) {
+                            sofar = want;
+                        } else {
+                            nd -= ones;
+                            sofar = want - 1u;
+                        }
+                    }
+                    if (lane == 0) {
+                        sel[0] = sofar;
+                        sel[1] = nd;
+                    }
+                }
+                __syncthreads();
+                pref = (pref << hi) | sel[0];
+                need = sel[1];
+                hi = 0;
+            }
+        }
     }
     const uint32_t tau = pref;  // offset of the k-th largest key
 
