@@ -356,7 +356,7 @@ kvq_status kvq_topk_evict(const float* d_scores, int32_t rows, int32_t T, int32_
  * kvq_gather_kv and then kvq_quantize_append (MiniKV section 4.1, persistent
  * context selection). Query head h reads KV head h / (Hq / Hkv).
  * Errors: KVQ_EINVAL (null pointer with n > 0, bad sizes), KVQ_EUNSUPPORTED
- * (head_dim != 128, Hq / Hkv not in {1, 2, 4}), KVQ_EWORKSPACE.
+ * (head_dim != 128, Hq / Hkv not in {1, 2, 4}, B * Hq > 65535), KVQ_EWORKSPACE.
  */
 kvq_status kvq_prefill_workspace(int32_t batch, int32_t n_q_heads, int32_t n, size_t* ws_bytes);
 kvq_status kvq_prefill_attention(const void* d_q, const void* d_k, const void* d_v, int32_t batch,
@@ -374,7 +374,7 @@ kvq_status kvq_prefill_attention(const void* d_q, const void* d_k, const void* d
  *                   an index outside [0, n) gives a zero row
  *   d_k_out, d_v_out device fp16 [B][Hkv][n_keep][d]
  * Errors: KVQ_EINVAL (null pointer with n_keep > 0, n_keep > n, bad sizes),
- * KVQ_EUNSUPPORTED (head_dim != 128).
+ * KVQ_EUNSUPPORTED (head_dim != 128, B * Hkv > 65535).
  */
 kvq_status kvq_gather_kv(const void* d_k, const void* d_v, int32_t batch, int32_t n_kv_heads,
                          int32_t head_dim, int32_t n, const int32_t* d_idx, int32_t n_keep,

@@ -12,6 +12,7 @@ namespace {
 constexpr uint64_t kAlign = 256;
 constexpr int64_t kMaxQuantSplits = 1000;  // merge keeps per-split weights in LDS
 
+constexpr int64_t kMaxGridY = 65535;  // largest second grid dimension of a launch
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Words of a unit's eviction bitmap: one bit per token after the sinks.
@@ -409,6 +410,8 @@ kvq_status kvq_prefill_attention(const void* d_q, const void* d_k, const void* d
         return KVQ_EINVAL;
     const int r = n_q_heads / n_kv_heads;
     if (head_dim != kHeadDim || (r != 1 && r != 2 && r != 4)) return KVQ_EUNSUPPORTED;
+    // query heads and units index the second grid dimension of the kernels
+    if ((int64_t)batch * n_q_heads > kMaxGridY) return KVQ_EUNSUPPORTED;
     if (n == 0) return KVQ_OK;
     if (!d_q || !d_k || !d_v || !d_out || !d_ws) return KVQ_EINVAL;
     size_t need = 0;
@@ -425,6 +428,7 @@ kvq_status kvq_gather_kv(const void* d_k, const void* d_v, int32_t batch, int32_
                          void* d_k_out, void* d_v_out, void* stream) {
     if (batch < 1 || n_kv_heads < 1 || n < 0 || n_keep < 0 || n_keep > n) return KVQ_EINVAL;
     if (head_dim != kHeadDim) return KVQ_EUNSUPPORTED;
+    if ((int64_t)batch * n_kv_heads > kMaxGridY) return KVQ_EUNSUPPORTED;  // units: second grid dimension
     if (n_keep == 0) return KVQ_OK;
     if (!d_k || !d_v || !d_idx || !d_k_out || !d_v_out) return KVQ_EINVAL;
     return launch_status(launch_gather(static_cast<const uint16_t*>(d_k),

@@ -1173,7 +1173,7 @@ constexpr int64_t kEvictSlice = (int64_t)kEvictThreads * kEvictGroups;
 __global__ __launch_bounds__(kEvictThreads) void evict_step_kernel(CacheView v, int64_t T,
                                                                    const float* acc, int32_t budget,
                                                                    int32_t recent) {
-    const int u = blockIdx.y, tid = threadIdx.x;
+    const int u = blockIdx.x, tid = threadIdx.x;  // slice blockIdx.y of unit u
     const int64_t live = T - v.evict_count[u];
     if (live <= budget) return;  // uniform over the unit's workgroups
     const int64_t S = v.sinks, end = T - recent;
@@ -1183,7 +1183,7 @@ __global__ __launch_bounds__(kEvictThreads) void evict_step_kernel(CacheView v, 
     // groups of 4 tokens t = 4 g .. 4 g + 3 (sequence indices); this
     // workgroup's slice starts at group gs
     const int64_t g_first = S / 4, g_end = (end + 3) / 4;
-    const int64_t gs = g_first + (int64_t)blockIdx.x * kEvictSlice;
+    const int64_t gs = g_first + (int64_t)blockIdx.y * kEvictSlice;
     const bool aligned = (T % 4) == 0;  // row start 16-byte aligned
     const bool any_evicted = v.evict_count[u] != 0;
     {
@@ -1240,7 +1240,7 @@ __global__ __launch_bounds__(kEvictThreads) void evict_step_kernel(CacheView v, 
         asm volatile("" ::"v"(prev) : "memory");
         const uint64_t ticket =
             __hip_atomic_fetch_add(&scr[1], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (ticket == gridDim.x - 1) {
+        if (ticket == gridDim.y - 1) {
             // the unit's last workgroup: every other one has folded its minimum
             const uint64_t nb = __hip_atomic_exchange(&scr[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&scr[1], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1455,7 +1455,7 @@ int launch_evict_step(const CacheView& v, int64_t T, const float* acc, int32_t b
     // slices of the groups [S / 4, (T - recent + 3) / 4), at least one per unit
     const int64_t groups = (T - recent + 3) / 4 - v.sinks / 4;
     const int64_t slices = groups > kEvictSlice ? (groups + kEvictSlice - 1) / kEvictSlice : 1;
-    hipLaunchKernelGGL(evict_step_kernel, dim3((unsigned)slices, v.units), dim3(kEvictThreads), 0, s, v,
+    hipLaunchKernelGGL(evict_step_kernel, dim3(v.units, (unsigned)slices), dim3(kEvictThreads), 0, s, v,
                        T, acc, budget, recent);
     return (int)hipGetLastError();
 }

@@ -108,6 +108,13 @@ def test_validation_paths_launch_nothing(kvq):
     n = ctypes.c_size_t(7)
     assert L.kvq_topk_workspace(3, 100, 10, 20, ctypes.byref(n)) == 0 and n.value == 0
     assert L.kvq_topk_workspace(3, 100, 90, 20, ctypes.byref(n)) == -1
+    # prefill and gather: query heads and units index the second grid dimension
+    assert L.kvq_prefill_attention(P(1), P(1), P(1), 2048, 32, 8, 128, 64, P(1), None, P(1),
+                                   1 << 40, None) == -2
+    assert L.kvq_prefill_attention(P(1), P(1), P(1), 2047, 32, 8, 128, 0, P(1), None, P(1),
+                                   1 << 40, None) == 0
+    assert L.kvq_gather_kv(P(1), P(1), 8192, 8, 128, 64, P(1), 16, P(1), P(1), None) == -2
+    assert L.kvq_gather_kv(P(1), P(1), 8191, 8, 128, 64, P(1), 0, P(1), P(1), None) == 0
 
 
 def test_decode_step_validation_launches_nothing(kvq):
