@@ -103,7 +103,7 @@ const char* kvq_status_string(kvq_status status);
  * Cache configuration (host POD).
  *   bits        b in {2, 4}: integer codes; 8: the FP8 E4M3 codec (then group
  *               must be 32 and pool 0: no groups, zero points or OTT)
- *   group       G in {32, 64, 128}: tokens per key group and, capped at d,
+ *   group       G in {16, 32, 64, 128}: tokens per key group and, capped at d,
  *               channels per value group (one group size for both axes, MiniKV
  *               section 5.1)
  *   residual    R >= 0, fp16 residual window
@@ -112,7 +112,7 @@ const char* kvq_status_string(kvq_status status);
  *   evict_cap   E in [0, 1024], OTT extra pool size (32 on the page)
  *   head_dim    d, must be 128
  *   n_q_heads   Hq, n_kv_heads Hkv: Hq / Hkv = r in {1, 2, 4}
- *   batch       B >= 1
+ *   batch       B >= 1, with B * Hkv <= 65535
  *   max_tokens  capacity in tokens per unit, in [1, 2^24]
  *   sinks       S in [0, 64]: attention sinks kept fp16 (4 in StreamingLLM)
  * With S > 0 the token indices of the quantized partition, the ring and the

@@ -49,6 +49,8 @@ kvq_status check_config(const kvq_config* c) {
     if (c->pool > kMaxPool || c->evict_cap > kMaxEvict || c->sinks > kMaxSinks)
         return KVQ_EUNSUPPORTED;
     if (c->max_tokens > kMaxTokens) return KVQ_EUNSUPPORTED;
+    // units index the second grid dimension of the ring and sink stores
+    if ((int64_t)c->batch * c->n_kv_heads > kMaxGridY) return KVQ_EUNSUPPORTED;
     if ((int64_t)c->residual + c->group + c->pool + c->evict_cap + c->sinks > kMaxFp16Rows)
         return KVQ_EUNSUPPORTED;
     return KVQ_OK;

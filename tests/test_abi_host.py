@@ -42,6 +42,7 @@ def _cfg(kvq, **kw):
     (dict(head_dim=64), -2), (dict(n_q_heads=64), -2), (dict(n_q_heads=12), -1),
     (dict(pool=65), -2), (dict(evict_cap=2000), -2), (dict(residual=-1), -1),
     (dict(batch=0), -1), (dict(max_tokens=0), -1), (dict(residual=1900, pool=64, evict_cap=64), -2),
+    (dict(batch=8192), -2),  # B * Hkv above 65535
 ])
 def test_bad_configs_rejected(kvq, kw, code):
     with pytest.raises(kvq.KvqError) as e:
