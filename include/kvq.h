@@ -48,6 +48,10 @@
  *  - Heavy-hitter selection: the k highest scores outside a recent window of
  *    w tokens, plus that window (MiniKV, Algorithm 1; "KV cache quantization
  *    and eviction", section "Minimal implementation").
+ *  - Prefill selection: causal attention over the prompt that also writes,
+ *    per KV head, the column sums of the normalized attention (A_cumul), whose
+ *    heavy hitters plus a recent window are gathered and quantized into the
+ *    cache (MiniKV, sections 4.3 and 4.1, Algorithm 1).
  *
  * Conventions for every entry point:
  *
