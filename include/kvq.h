@@ -208,7 +208,8 @@ kvq_status kvq_cache_bytes(const kvq_config* cfg, size_t* arena_bytes);
 
 /*
  * Bind an empty cache to the caller's arena (device, >= kvq_cache_bytes,
- * 256-byte aligned) and clear its counters and pool masks on `stream`.
+ * 256-byte aligned) and clear its counters, pool masks and eviction state on
+ * `stream`.
  * Fills *h (host). The arena stays owned by the caller and must outlive *h.
  */
 kvq_status kvq_cache_init(const kvq_config* cfg, void* d_arena, size_t arena_bytes,
@@ -245,7 +246,8 @@ kvq_status kvq_decode_workspace(const kvq_cache* h, int32_t want_scores, size_t*
  *   d_ws   device workspace of ws_bytes >= kvq_decode_workspace(h, d_acc != NULL)
  * Every cached token counts once: pool members with their fp16 rows (their
  * quantized slots are skipped), tokens at index >= n_q from the fp16 ring,
- * the rest dequantized on the fly from the packed codes. Softmax scale is
+ * the rest dequantized on the fly from the packed codes; tokens evicted by
+ * kvq_evict_step take no part and keep their scores. Softmax scale is
  * 1/sqrt(d).
  * Errors: KVQ_EINVAL (null pointer, T == 0), KVQ_EWORKSPACE.
  */
