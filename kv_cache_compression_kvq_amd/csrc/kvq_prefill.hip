@@ -218,7 +218,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         koff[i] = (uint32_t)(2 * (key * D + 8 * (pc ^ (key & 15))));
         voff[i] = (uint32_t)(2 * (key * D + 8 * (pc ^ v_swz(key))));
     }
-    const uint32_t unit_bytes = (uint32_t)n * D * 2;
+    // a unit's K (V) rows in bytes; 2^32 at n = 2^24 saturates (every offset
+    // the loop forms stays below 2^32)
+    const uint64_t ub = (uint64_t)n * D * 2;
+    const uint32_t unit_bytes = ub > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)ub;
     const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kunit, unit_bytes), vrs = buffer_rsrc(vunit, unit_bytes);
     const int wbase = __builtin_amdgcn_readfirstlane(tid - lane);  // first thread of the wave
     auto fetch = [&](int t) {
