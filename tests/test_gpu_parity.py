@@ -536,6 +536,43 @@ def test_topk_special_values(kvq, T, k, w, split):
     np.testing.assert_array_equal(idx.cpu().numpy(), O.topk_keep(s, k, w))
 
 
+def _first_digit_bin(row, k):
+    """Keys in the k-th largest key's bin of the register kernel's first pass:
+    order-preserving keys minus the row minimum, 11-bit digit from the top
+    bit of the row's key range."""
+    u = row.view(np.uint32).astype(np.uint64)
+    u = np.where((u & 0x7FFFFFFF) == 0, 0, u)
+    key = np.where(u & 0x80000000, (~u) & 0xFFFFFFFF, u | 0x80000000)
+    off = key - key.min()
+    L = int(off.max()).bit_length()
+    lo = max(L - 11, 0)
+    kth = np.sort(off)[::-1][k - 1]
+    return int(((off >> lo) == (kth >> lo)).sum())
+
+
+@pytest.mark.parametrize("m", [511, 512, 513, 2000])
+def test_topk_first_digit_bin_at_the_one_wavefront_limit(kvq, m):
+    """The register kernel resolves the k-th key's first-digit bin on one
+    wavefront when it holds at most 512 keys, and with two more histogram
+    passes otherwise: rows whose bin holds 511, 512, 513 and 2000 keys (with
+    ties inside it) pin both paths against the oracle."""
+    T, k, w = 32768 + 256, 6553, 256
+    n = T - w
+    rng = np.random.default_rng([17, m])
+    s = np.empty(n, dtype=np.float32)
+    above = k - m // 2                      # keys larger than the bin
+    s[:above] = rng.uniform(10.0, 100.0, above)
+    s[above:above + m] = 1.0 + (rng.integers(0, 400, m) * 1e-6)   # one bin, with ties
+    s[above + m:] = rng.uniform(0.001, 0.01, n - above - m)
+    recent = rng.uniform(0.0, 200.0, w).astype(np.float32)      # outside the selection
+    rows = np.stack([np.concatenate([s[rng.permutation(n)], recent]) for _ in range(2)])
+    for r in rows:
+        assert _first_digit_bin(r[:n], k) == m
+    st = torch.from_numpy(rows).cuda()
+    idx = _topk(kvq, st, 2, T, k, w, split=False)
+    np.testing.assert_array_equal(idx.cpu().numpy(), O.topk_keep(rows, k, w))
+
+
 def test_topk_split_plan_is_taken(kvq):
     """The workspace path splits long rows and few rows; many short rows keep
     one workgroup per row."""
