@@ -125,7 +125,7 @@ __global__ void init_kernel(CacheView v) {
     const int64_t ne = (int64_t)v.units * v.evict_words, nu = v.units;
     const int64_t n1 = nc + nm, n2 = n1 + nk, n3 = n2 + nv, n4 = n3 + ne, n5 = n4 + nu;
     const int64_t n6 = n5 + 4 * nu;  // the eviction step's scratch, as 32-bit words
-    if (v.bits == 8 && blockIdx.x == 0 && threadIdx.x < 2 * v.n_kv_heads)
+    if (v.bits == 8 && blockIdx.x == 0 && (int)threadIdx.x < 2 * v.n_kv_heads)
         v.fp8_scales[threadIdx.x] = 1.0f;  // FP8 scales: 1.0 until set
     uint32_t* esc = reinterpret_cast<uint32_t*>(evict_scratch(v));
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n6;

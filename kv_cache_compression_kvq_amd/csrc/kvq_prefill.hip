@@ -54,25 +54,15 @@ __device__ __forceinline__ int v_swz(int r) { return 2 * (r & 3) + 8 * (r & 1); 
 // so its probabilities stay below 2^8 in the fp16 operand.
 constexpr float kLazyTau = 8.0f;
 
-__device__ __forceinline__ float h2f(uint16_t h) {
-    return (float)__builtin_bit_cast(_Float16, h);
-}
-// x at lanes l and l ^ 16 (swap16) or l and l ^ 32 (swap32) as the pair
-// (a, b) in either order, through the gfx950 permlane swaps (VALU, no LDS
-// round trip); inline asm because the compiler's builtin drops one result.
-__device__ __forceinline__ void swap16(float x, float& a, float& b) {
-    a = x;
-    b = x;
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
+// x at lanes l and l ^ 32 as the pair (a, b) in either order, through the
+// gfx950 permlane swap (VALU, no LDS round trip); inline asm because the
+// compiler's builtin drops one result.
 __device__ __forceinline__ void swap32(float x, float& a, float& b) {
     a = x;
     b = x;
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
-__device__ __forceinline__ float max_x16(float x) { float a, b; swap16(x, a, b); return fmaxf(a, b); }
 __device__ __forceinline__ float max_x32(float x) { float a, b; swap32(x, a, b); return fmaxf(a, b); }
-__device__ __forceinline__ float sum_x16(float x) { float a, b; swap16(x, a, b); return a + b; }
 __device__ __forceinline__ float sum_x32(float x) { float a, b; swap32(x, a, b); return a + b; }
 
 // Block coordinates with all blocks of one unit on one compute die when the
